@@ -1,0 +1,216 @@
+/*
+ * eta.h -- C ABI of the MI355X (gfx950) block-sparse decode library, libeta.so.
+ *
+ * The library implements the inference-time decode path of Elastic Threshold
+ * Attention (paper: "Elastic Threshold Attention: Learned Contextual Sparsity
+ * for Long-Context Decoding"; method as summarised on the picx.dev page,
+ * Methodology sections 1-4).  One decode step for a batch of sequences is:
+ *
+ *   eta_append_kv        write the new token's k, v; statistics of a block
+ *                        that this token completes                 (Meth. 4)
+ *   eta_predict_tau      per-head threshold, linear in the query or frozen
+ *                                                                   (Eq. 1)
+ *   eta_screen           per-block upper bound vs. threshold, compacted list
+ *                        of admitted blocks, admitted-token counter (Eq. 5)
+ *   eta_decode           exact softmax attention over the admitted blocks only,
+ *                        split over chunks of blocks, log-sum-exp combine
+ *                                                        (Eq. 3, Fig. 6)
+ *
+ * plus eta_build_block_meta (statistics of many blocks, e.g. after prefill),
+ * eta_dense_decode (the same kernels over every key: plain dense decode) and
+ * eta_calibrate_threshold (per-head constants for a target density).
+ *
+ * Conventions shared by every call
+ *   - Every function returns eta_status; ETA_OK is 0.  All arguments are
+ *     validated on the host before any HIP call; on error nothing is launched
+ *     and eta_last_error() (thread-local) describes the first bad argument.
+ *   - Ownership: the caller allocates, owns and frees every buffer.  Device
+ *     pointers are hipMalloc'ed (or equivalent) device memory; the library
+ *     allocates nothing, keeps no state between calls and never synchronises.
+ *   - Streams: `stream` is a hipStream_t passed as void* (NULL: the null
+ *     stream).  Every call only enqueues kernels on that stream; results are
+ *     ready when the stream reaches them.  Two calls that write the same
+ *     buffers must not run concurrently on different streams.
+ *   - Types: q, tau, statistics and outputs are float32.  The K/V cache is
+ *     float32 (ETA_DT_F32) or bfloat16 (ETA_DT_BF16); bf16 is widened exactly
+ *     to float32 and every accumulation is float32.
+ *   - Supported shapes: head_dim in {64, 128}; block in {4, 8, 16, 32, 64,
+ *     128}.  Smaller head dimensions run zero-padded to 64 with `scale` given
+ *     explicitly (zero coordinates change no dot product, norm or variance).
+ *   - batch == 0 or heads == 0 is an empty problem: OK, nothing launched.
+ */
+#ifndef ETA_H_
+#define ETA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ETA_ABI_VERSION 1
+
+typedef int32_t eta_status;
+enum {
+  ETA_OK = 0,
+  ETA_ERR_NULL_PTR = 1,  /* a required pointer is NULL                        */
+  ETA_ERR_BAD_SHAPE = 2, /* unsupported head_dim/block, negative sizes, ...   */
+  ETA_ERR_BAD_ARG = 3,   /* NaN or out-of-range scalar, unknown mode/dtype    */
+  ETA_ERR_CAPACITY = 4,  /* a size exceeds the cache or index capacity        */
+  ETA_ERR_WORKSPACE = 5, /* workspace NULL or smaller than the size query     */
+  ETA_ERR_HIP = 6        /* a HIP launch or runtime call failed               */
+};
+
+enum { ETA_DT_F32 = 0, ETA_DT_BF16 = 1 };
+enum { ETA_LOGIT_GATED = 0, ETA_LOGIT_RAW = 1 };
+
+/*
+ * The KV cache of one attention layer (Methodology 4: the cache is split into
+ * contiguous blocks of `block` keys, and each complete block keeps its centroid
+ * mu, per-coordinate population variance var and largest key norm maxnorm).
+ *
+ *   k, v      device, [batch][heads][cap_tokens][head_dim], kv_dtype elements
+ *   mu, var   device, [batch][heads][cap_blocks][head_dim] float32
+ *   maxnorm   device, [batch][heads][cap_blocks] float32
+ *   seq_len   device, [batch] int32: current length T_b of sequence b
+ *             (ragged batches allowed, 0 <= T_b <= cap_tokens)
+ *
+ * cap_blocks = ceil(cap_tokens / block).  Statistics exist only for complete
+ * blocks j < floor(T_b / block); the partial last block has none.  The
+ * struct itself is read on the host during each call and may be a stack
+ * object.
+ */
+typedef struct eta_cache {
+  int32_t batch, heads, head_dim, block, cap_tokens, kv_dtype;
+  void* k;
+  void* v;
+  float* mu;
+  float* var;
+  float* maxnorm;
+  int32_t* seq_len;
+} eta_cache;
+
+int32_t eta_abi_version(void);
+const char* eta_status_string(eta_status s);
+const char* eta_last_error(void);
+/* ceil(cap_tokens / block), the row count of the statistics arrays. */
+int32_t eta_cache_blocks(const eta_cache* c);
+
+/*
+ * Append one token per sequence (decode step of the paper's Fig. 1 / Fig. 6
+ * pipeline): for every (b, h), k_new[b][h][:] and v_new[b][h][:] (device,
+ * [batch][heads][head_dim], kv_dtype) are written at position T_b, and when
+ * T_b + 1 is a multiple of `block` the statistics of that now-complete block
+ * are computed (Methodology 4).  Then T_b += 1.
+ * A sequence already at cap_tokens is left unchanged and, when `overflow`
+ * (device int32, optional) is not NULL, *overflow is set to 1; the flag is
+ * never cleared by the library.
+ */
+eta_status eta_append_kv(const eta_cache* c, const void* k_new, const void* v_new,
+                         int32_t* overflow, void* stream);
+
+/*
+ * Statistics (mu, var, maxnorm) of blocks first_block .. first_block+n_blocks-1
+ * of every (b, h) stream; blocks that are not complete for T_b are skipped.
+ * n_blocks = -1 means every block from first_block to cap_blocks-1.  Used once
+ * after prefill; the result equals what eta_append_kv computes block by block
+ * (same kernel code, same summation order).  Methodology 4 (population
+ * centroid, coordinate-wise variance over b keys, max norm).
+ */
+eta_status eta_build_block_meta(const eta_cache* c, int32_t first_block, int32_t n_blocks,
+                                void* stream);
+
+/*
+ * Threshold (Methodology 1, Eq. 1).  q: device [batch][heads*head_dim] float32
+ * (the concatenated per-head queries qbar).  Dynamic mode (W != NULL): W is
+ * device [heads*head_dim][heads] float32, bias_or_c device [heads] and
+ *     tau_gate[b][h] = sum_j q[b][j] W[j][h] + bias_or_c[h].
+ * Frozen mode (W == NULL): tau_gate[b][h] = bias_or_c[h] (offline-calibrated
+ * per-head constants).  Both modes: tau_screen = tau_gate - a (a is the
+ * threshold adjustment; 0 leaves them equal).  Outputs device [batch][heads].
+ * heads <= 256.  The sum over j runs in a fixed order (deterministic).
+ */
+eta_status eta_predict_tau(int32_t batch, int32_t heads, int32_t head_dim, const float* q,
+                           const float* W, const float* bias_or_c, float a, float* tau_gate,
+                           float* tau_screen, void* stream);
+
+/*
+ * Screen (Methodology 4, Eq. 5).  For every complete block j of stream (b, h):
+ *   s_j = scale * min(<q, mu_j> + z sqrt(sum_i q_i^2 var_j,i), ||q||_2 maxnorm_j)
+ * (z = +inf: the geometric term alone).  Block j is admitted iff
+ * s_j >= tau_screen[b][h]; the last block (the one holding position T_b - 1,
+ * complete or not) is always admitted.  Outputs, all device:
+ *   active_idx [batch][heads][cap_blocks] int32: admitted block indices of
+ *              (b, h), ascending, in the first active_cnt[b][h] entries
+ *              (the rest is left unspecified);
+ *   active_cnt [batch][heads] int32;
+ *   density_ctr (optional, one uint64): += number of admitted tokens summed
+ *              over all (b, h) (integer atomics: exact and order-free).
+ * q: device [batch][heads][head_dim]; tau_screen: device [batch][heads].
+ * Workspace: eta_screen_workspace_bytes(); contents need no initialisation.
+ */
+size_t eta_screen_workspace_bytes(int32_t batch, int32_t heads, int32_t cap_blocks);
+eta_status eta_screen(const eta_cache* c, const float* q, const float* tau_screen, float z,
+                      float scale, int32_t* active_idx, int32_t* active_cnt,
+                      uint64_t* density_ctr, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/*
+ * Block-sparse decode (Theoretical Foundation: attention restricted to the
+ * admitted set, normalised over it; Methodology 2, Eq. 3 for the logits;
+ * Fig. 6: only admitted blocks are loaded, online softmax).  For each (b, h)
+ * the admitted list is cut into chunks of blocks_per_split blocks; each chunk
+ * produces a partial (max, sum, weighted V) and one combine pass merges them
+ * by log-sum-exp into out [batch][heads][head_dim] float32 (device).
+ * Logits, with S_s = scale <q, k_s>:
+ *   ETA_LOGIT_GATED  l_s = S_s sigmoid(beta (S_s - tau_gate[b][h])) for
+ *                    s != T_b - 1, and l_{T_b-1} = S_{T_b-1} (the query's own
+ *                    key is never gated);
+ *   ETA_LOGIT_RAW    l_s = S_s   (tau_gate may be NULL).
+ * A stream with T_b == 0 yields zeros.  active_idx/active_cnt are eta_screen's
+ * outputs (any ascending list of distinct in-range blocks that contains the
+ * last block is valid input).  1 <= blocks_per_split <= 4096.
+ * Workspace: eta_decode_workspace_bytes(); contents need no initialisation.
+ */
+size_t eta_decode_workspace_bytes(int32_t batch, int32_t heads, int32_t head_dim,
+                                  int32_t cap_blocks, int32_t blocks_per_split);
+eta_status eta_decode(const eta_cache* c, const float* q, const float* tau_gate,
+                      const int32_t* active_idx, const int32_t* active_cnt, int32_t logit_mode,
+                      float beta, float scale, int32_t blocks_per_split, void* workspace,
+                      size_t workspace_bytes, float* out, void* stream);
+
+/*
+ * Dense decode over every key of every stream (Theoretical Foundation, dense
+ * form): the same split/combine kernels with all blocks admitted and RAW
+ * logits.  The in-house dense baseline.  Workspace as for eta_decode.
+ */
+eta_status eta_dense_decode(const eta_cache* c, const float* q, float scale,
+                            int32_t blocks_per_split, void* workspace, size_t workspace_bytes,
+                            float* out, void* stream);
+
+/*
+ * Offline calibration of frozen per-head constants (the pages' calibration
+ * algorithm freezes per-(layer, head) thresholds; its steps are not given, so
+ * this is the plain quantile reading).  For head h, pool over the n_sets
+ * query sets q_sets[n] (device [n_sets][batch][heads][head_dim]) and the
+ * sequences b the values x = s_j - tau0[n][b][h] of every complete block j
+ * except the always-admitted last block (s_j as in eta_screen; tau0 device
+ * [n_sets][batch][heads] or NULL for 0).  With F the tokens of the last
+ * blocks and sum T the tokens of all streams, k = round((rho sum T - F) /
+ * block) clamped to [0, N]; c_out[h] (device [heads] float32) is the midpoint
+ * of the k-th and (k+1)-th largest pooled value (-inf when k = N, +inf when
+ * k = 0).  Screening with tau_screen = tau0 + c_out then admits the top k.
+ * Pooled values per head must not exceed 2^31 - 1.
+ */
+size_t eta_calibrate_workspace_bytes(int32_t n_sets, int32_t batch, int32_t heads,
+                                     int32_t cap_blocks);
+eta_status eta_calibrate_threshold(const eta_cache* c, int32_t n_sets, const float* q_sets,
+                                   const float* tau0, float z, float scale,
+                                   float target_density, void* workspace,
+                                   size_t workspace_bytes, float* c_out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ETA_H_ */

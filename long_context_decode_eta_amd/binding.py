@@ -1,0 +1,270 @@
+"""Thin ctypes binding of libeta.so (C ABI in include/eta.h).
+
+The functions here only marshal arguments: they check that torch tensors sit
+on the GPU with the expected dtype and contiguity, pass ``data_ptr()`` values
+and the current HIP stream, and turn status codes into exceptions.  Every step
+of the decode path runs in the library's HIP kernels; torch provides device
+memory and streams and nothing else.  There is no CPU fallback: if
+``libeta.so`` is missing the import of :func:`lib` raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import c_float, c_int32, c_size_t, c_void_p
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libeta.so")
+
+ETA_OK, ETA_ERR_NULL_PTR, ETA_ERR_BAD_SHAPE, ETA_ERR_BAD_ARG = 0, 1, 2, 3
+ETA_ERR_CAPACITY, ETA_ERR_WORKSPACE, ETA_ERR_HIP = 4, 5, 6
+DT_F32, DT_BF16 = 0, 1
+GATED, RAW = 0, 1
+
+
+class EtaError(RuntimeError):
+    def __init__(self, status: int, fn: str, detail: str):
+        super().__init__(f"{fn}: status {status} ({detail})")
+        self.status = status
+
+
+class EtaCacheStruct(ctypes.Structure):
+    _fields_ = [("batch", c_int32), ("heads", c_int32), ("head_dim", c_int32),
+                ("block", c_int32), ("cap_tokens", c_int32), ("kv_dtype", c_int32),
+                ("k", c_void_p), ("v", c_void_p), ("mu", c_void_p), ("var", c_void_p),
+                ("maxnorm", c_void_p), ("seq_len", c_void_p)]
+
+
+_P = ctypes.POINTER(EtaCacheStruct)
+_SIGS = {
+    "eta_abi_version": ([], c_int32),
+    "eta_status_string": ([c_int32], ctypes.c_char_p),
+    "eta_last_error": ([], ctypes.c_char_p),
+    "eta_cache_blocks": ([_P], c_int32),
+    "eta_append_kv": ([_P, c_void_p, c_void_p, c_void_p, c_void_p], c_int32),
+    "eta_build_block_meta": ([_P, c_int32, c_int32, c_void_p], c_int32),
+    "eta_predict_tau": ([c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_float,
+                         c_void_p, c_void_p, c_void_p], c_int32),
+    "eta_screen_workspace_bytes": ([c_int32, c_int32, c_int32], c_size_t),
+    "eta_screen": ([_P, c_void_p, c_void_p, c_float, c_float, c_void_p, c_void_p, c_void_p,
+                    c_void_p, c_size_t, c_void_p], c_int32),
+    "eta_decode_workspace_bytes": ([c_int32, c_int32, c_int32, c_int32, c_int32], c_size_t),
+    "eta_decode": ([_P, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_float, c_float,
+                    c_int32, c_void_p, c_size_t, c_void_p, c_void_p], c_int32),
+    "eta_dense_decode": ([_P, c_void_p, c_float, c_int32, c_void_p, c_size_t, c_void_p,
+                          c_void_p], c_int32),
+    "eta_calibrate_workspace_bytes": ([c_int32, c_int32, c_int32, c_int32], c_size_t),
+    "eta_calibrate_threshold": ([_P, c_int32, c_void_p, c_void_p, c_float, c_float, c_float,
+                                 c_void_p, c_size_t, c_void_p, c_void_p], c_int32),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libeta.so (built in-tree by ``long_context_decode_eta_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} not found: build it with "
+                              "`python -m long_context_decode_eta_amd.build`")
+        h = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            f = getattr(h, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = h
+    return _lib
+
+
+def _check(status: int, fn: str) -> None:
+    if status != ETA_OK:
+        raise EtaError(status, fn, lib().eta_last_error().decode())
+
+
+def _stream(stream) -> c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return c_void_p(stream.cuda_stream)
+
+
+def _dev(t: torch.Tensor | None, dtype=None, name: str = "tensor") -> c_void_p:
+    if t is None:
+        return c_void_p(None)
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return c_void_p(t.data_ptr())
+
+
+# ---------------------------------------------------------------------------
+class KVCache:
+    """Device buffers of one layer's cache (layout as in include/eta.h)."""
+
+    def __init__(self, batch, heads, head_dim, block, cap_tokens, kv_dtype=torch.bfloat16,
+                 device="cuda", k=None, v=None):
+        self.batch, self.heads, self.head_dim = batch, heads, head_dim
+        self.block, self.cap_tokens = block, cap_tokens
+        self.cap_blocks = -(-cap_tokens // block)
+        self.kv_dtype = kv_dtype
+        shape = (batch, heads, cap_tokens, head_dim)
+        self.k = k if k is not None else torch.zeros(shape, dtype=kv_dtype, device=device)
+        self.v = v if v is not None else torch.zeros(shape, dtype=kv_dtype, device=device)
+        assert tuple(self.k.shape) == shape and tuple(self.v.shape) == shape
+        assert self.k.dtype == kv_dtype and self.v.dtype == kv_dtype
+        self.mu = torch.zeros((batch, heads, self.cap_blocks, head_dim), dtype=torch.float32,
+                              device=device)
+        self.var = torch.zeros_like(self.mu)
+        self.maxnorm = torch.zeros((batch, heads, self.cap_blocks), dtype=torch.float32,
+                                   device=device)
+        self.seq_len = torch.zeros((batch,), dtype=torch.int32, device=device)
+
+    def struct(self) -> EtaCacheStruct:
+        dt = {torch.float32: DT_F32, torch.bfloat16: DT_BF16}[self.kv_dtype]
+        return EtaCacheStruct(
+            self.batch, self.heads, self.head_dim, self.block, self.cap_tokens, dt,
+            _dev(self.k, self.kv_dtype, "k"), _dev(self.v, self.kv_dtype, "v"),
+            _dev(self.mu, torch.float32, "mu"), _dev(self.var, torch.float32, "var"),
+            _dev(self.maxnorm, torch.float32, "maxnorm"),
+            _dev(self.seq_len, torch.int32, "seq_len"))
+
+
+def _ref(cache: KVCache):
+    return ctypes.byref(cache.struct())
+
+
+# ---------------------------------------------------------------------------
+def append_kv(cache: KVCache, k_new, v_new, overflow=None, stream=None):
+    _check(lib().eta_append_kv(_ref(cache), _dev(k_new, cache.kv_dtype, "k_new"),
+                               _dev(v_new, cache.kv_dtype, "v_new"),
+                               _dev(overflow, torch.int32, "overflow"), _stream(stream)),
+           "eta_append_kv")
+
+
+def build_block_meta(cache: KVCache, first_block=0, n_blocks=-1, stream=None):
+    _check(lib().eta_build_block_meta(_ref(cache), first_block, n_blocks, _stream(stream)),
+           "eta_build_block_meta")
+
+
+def predict_tau(q, W, bias_or_c, a, tau_gate, tau_screen, stream=None):
+    B, H, D = q.shape
+    _check(lib().eta_predict_tau(B, H, D, _dev(q, torch.float32, "q"),
+                                 _dev(W, torch.float32, "W"),
+                                 _dev(bias_or_c, torch.float32, "bias_or_c"), float(a),
+                                 _dev(tau_gate, torch.float32, "tau_gate"),
+                                 _dev(tau_screen, torch.float32, "tau_screen"), _stream(stream)),
+           "eta_predict_tau")
+
+
+def screen_workspace_bytes(batch, heads, cap_blocks) -> int:
+    return int(lib().eta_screen_workspace_bytes(batch, heads, cap_blocks))
+
+
+def screen(cache: KVCache, q, tau_screen, z, scale, active_idx, active_cnt, density_ctr,
+           workspace, stream=None):
+    _check(lib().eta_screen(_ref(cache), _dev(q, torch.float32, "q"),
+                            _dev(tau_screen, torch.float32, "tau_screen"), float(z), float(scale),
+                            _dev(active_idx, torch.int32, "active_idx"),
+                            _dev(active_cnt, torch.int32, "active_cnt"),
+                            _dev(density_ctr, None, "density_ctr"),
+                            _dev(workspace, None, "workspace"),
+                            workspace.numel() * workspace.element_size(), _stream(stream)),
+           "eta_screen")
+
+
+def decode_workspace_bytes(batch, heads, head_dim, cap_blocks, blocks_per_split) -> int:
+    return int(lib().eta_decode_workspace_bytes(batch, heads, head_dim, cap_blocks,
+                                                blocks_per_split))
+
+
+def decode(cache: KVCache, q, tau_gate, active_idx, active_cnt, logit_mode, beta, scale,
+           blocks_per_split, workspace, out, stream=None):
+    _check(lib().eta_decode(_ref(cache), _dev(q, torch.float32, "q"),
+                            _dev(tau_gate, torch.float32, "tau_gate"),
+                            _dev(active_idx, torch.int32, "active_idx"),
+                            _dev(active_cnt, torch.int32, "active_cnt"), int(logit_mode),
+                            float(beta), float(scale), int(blocks_per_split),
+                            _dev(workspace, None, "workspace"),
+                            workspace.numel() * workspace.element_size(),
+                            _dev(out, torch.float32, "out"), _stream(stream)),
+           "eta_decode")
+
+
+def dense_decode(cache: KVCache, q, scale, blocks_per_split, workspace, out, stream=None):
+    _check(lib().eta_dense_decode(_ref(cache), _dev(q, torch.float32, "q"), float(scale),
+                                  int(blocks_per_split), _dev(workspace, None, "workspace"),
+                                  workspace.numel() * workspace.element_size(),
+                                  _dev(out, torch.float32, "out"), _stream(stream)),
+           "eta_dense_decode")
+
+
+def calibrate_workspace_bytes(n_sets, batch, heads, cap_blocks) -> int:
+    return int(lib().eta_calibrate_workspace_bytes(n_sets, batch, heads, cap_blocks))
+
+
+def calibrate_threshold(cache: KVCache, q_sets, tau0, z, scale, target_density, workspace,
+                        c_out, stream=None):
+    _check(lib().eta_calibrate_threshold(_ref(cache), int(q_sets.shape[0]),
+                                         _dev(q_sets, torch.float32, "q_sets"),
+                                         _dev(tau0, torch.float32, "tau0"), float(z),
+                                         float(scale), float(target_density),
+                                         _dev(workspace, None, "workspace"),
+                                         workspace.numel() * workspace.element_size(),
+                                         _dev(c_out, torch.float32, "c_out"), _stream(stream)),
+           "eta_calibrate_threshold")
+
+
+def workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    """A caller-owned byte workspace (torch allocation; 256-byte aligned)."""
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+# ---------------------------------------------------------------------------
+class Decoder:
+    """One decode step over a cache with every buffer preallocated:
+    predict_tau (skipped in frozen mode when tau is precomputed) -> screen ->
+    decode.  Pure orchestration of the C entry points."""
+
+    def __init__(self, cache: KVCache, *, z, scale=None, beta=5.0, a=0.0,
+                 logit_mode=GATED, blocks_per_split=16):
+        self.cache, self.z, self.beta, self.a = cache, float(z), float(beta), float(a)
+        self.scale = float(scale) if scale is not None else float(
+            torch.tensor(1.0 / cache.head_dim ** 0.5, dtype=torch.float32).item())
+        self.mode, self.split = logit_mode, int(blocks_per_split)
+        B, H, D, nbc = cache.batch, cache.heads, cache.head_dim, cache.cap_blocks
+        dev = cache.k.device
+        self.tau_gate = torch.zeros((B, H), dtype=torch.float32, device=dev)
+        self.tau_screen = torch.zeros_like(self.tau_gate)
+        self.active_idx = torch.zeros((B, H, nbc), dtype=torch.int32, device=dev)
+        self.active_cnt = torch.zeros((B, H), dtype=torch.int32, device=dev)
+        self.density_ctr = torch.zeros((1,), dtype=torch.int64, device=dev)
+        self.screen_ws = workspace(screen_workspace_bytes(B, H, nbc), dev)
+        self.decode_ws = workspace(decode_workspace_bytes(B, H, D, nbc, self.split), dev)
+        self.out = torch.zeros((B, H, D), dtype=torch.float32, device=dev)
+
+    def predict(self, q, W, bias_or_c, stream=None):
+        predict_tau(q, W, bias_or_c, self.a, self.tau_gate, self.tau_screen, stream)
+
+    def screen(self, q, stream=None):
+        screen(self.cache, q, self.tau_screen, self.z, self.scale, self.active_idx,
+               self.active_cnt, self.density_ctr, self.screen_ws, stream)
+
+    def attend(self, q, stream=None):
+        decode(self.cache, q, self.tau_gate, self.active_idx, self.active_cnt, self.mode,
+               self.beta, self.scale, self.split, self.decode_ws, self.out, stream)
+
+    def step(self, q, W=None, bias_or_c=None, stream=None):
+        if bias_or_c is not None:
+            self.predict(q, W, bias_or_c, stream)
+        self.screen(q, stream)
+        self.attend(q, stream)
+        return self.out
+
+    def dense(self, q, stream=None):
+        dense_decode(self.cache, q, self.scale, self.split, self.decode_ws, self.out, stream)
+        return self.out

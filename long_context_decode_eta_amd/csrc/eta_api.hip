@@ -1,0 +1,296 @@
+// eta_api.hip -- host side of the C ABI declared in include/eta.h.
+//
+// Every entry point validates all of its arguments on the host first, then
+// enqueues kernels on the caller's stream.  Nothing is allocated, nothing is
+// synchronised and no state survives a call.  Device-side values (sequence
+// lengths, admitted counts) are never read back: grids are sized from host
+// capacities and surplus work-groups exit at once.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "eta_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+eta_status fail(eta_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+eta_status ok() {
+  g_err[0] = '\0';
+  return ETA_OK;
+}
+
+bool pow2_block(int b) { return b == 4 || b == 8 || b == 16 || b == 32 || b == 64 || b == 128; }
+
+int ilog2(int b) {
+  int r = 0;
+  while ((1 << r) < b) ++r;
+  return r;
+}
+
+// Largest grid we launch is units * ceil(cap_blocks / small) work-groups; keep
+// every flattened grid below 2^31.
+constexpr long long kMaxGrid = 0x7fffffffLL;
+
+// Validates the cache descriptor.  `need_data` requires the K/V/statistics
+// pointers (all calls but none currently skip them for a non-empty problem).
+eta_status check_cache(const eta_cache* c, eta::CacheView* v) {
+  if (!c) return fail(ETA_ERR_NULL_PTR, "cache descriptor is NULL");
+  if (c->batch < 0 || c->heads < 0)
+    return fail(ETA_ERR_BAD_SHAPE, "batch (%d) and heads (%d) must be >= 0", c->batch, c->heads);
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return fail(ETA_ERR_BAD_SHAPE, "head_dim %d unsupported (64 or 128)", c->head_dim);
+  if (!pow2_block(c->block))
+    return fail(ETA_ERR_BAD_SHAPE, "block %d unsupported (4, 8, 16, 32, 64 or 128)", c->block);
+  if (c->cap_tokens < 1) return fail(ETA_ERR_BAD_SHAPE, "cap_tokens %d must be >= 1", c->cap_tokens);
+  if (c->kv_dtype != ETA_DT_F32 && c->kv_dtype != ETA_DT_BF16)
+    return fail(ETA_ERR_BAD_ARG, "kv_dtype %d unknown", c->kv_dtype);
+  if ((long long)c->batch * c->heads > (1LL << 24))
+    return fail(ETA_ERR_BAD_SHAPE, "batch*heads %lld too large", (long long)c->batch * c->heads);
+  if (c->batch > 0 && c->heads > 0) {
+    if (!c->k || !c->v) return fail(ETA_ERR_NULL_PTR, "cache k/v pointer is NULL");
+    if (!c->mu || !c->var || !c->maxnorm)
+      return fail(ETA_ERR_NULL_PTR, "cache statistics pointer is NULL");
+    if (!c->seq_len) return fail(ETA_ERR_NULL_PTR, "cache seq_len pointer is NULL");
+  }
+  v->B = c->batch;
+  v->H = c->heads;
+  v->D = c->head_dim;
+  v->bs = c->block;
+  v->log2bs = ilog2(c->block);
+  v->cap = c->cap_tokens;
+  v->cap_blocks = eta::ceil_div(c->cap_tokens, c->block);
+  v->dtype = c->kv_dtype;
+  v->k = c->k;
+  v->v = c->v;
+  v->mu = c->mu;
+  v->var = c->var;
+  v->maxnorm = c->maxnorm;
+  v->seq_len = c->seq_len;
+  return ETA_OK;
+}
+
+bool empty(const eta::CacheView& v) { return v.B == 0 || v.H == 0; }
+
+eta_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(ETA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t decode_ws(long long units, int D, int cap_blocks, int split) {
+  const long long maxc = (cap_blocks + split - 1) / split;
+  const size_t slots = (size_t)units * (size_t)maxc;
+  return align256(slots * 4) * 2 + align256(slots * (size_t)D * 4);
+}
+
+bool bad_float(float x) { return x != x; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t eta_abi_version(void) { return ETA_ABI_VERSION; }
+
+const char* eta_status_string(eta_status s) {
+  switch (s) {
+    case ETA_OK: return "ETA_OK";
+    case ETA_ERR_NULL_PTR: return "ETA_ERR_NULL_PTR";
+    case ETA_ERR_BAD_SHAPE: return "ETA_ERR_BAD_SHAPE";
+    case ETA_ERR_BAD_ARG: return "ETA_ERR_BAD_ARG";
+    case ETA_ERR_CAPACITY: return "ETA_ERR_CAPACITY";
+    case ETA_ERR_WORKSPACE: return "ETA_ERR_WORKSPACE";
+    case ETA_ERR_HIP: return "ETA_ERR_HIP";
+    default: return "ETA_ERR_UNKNOWN";
+  }
+}
+
+const char* eta_last_error(void) { return g_err; }
+
+int32_t eta_cache_blocks(const eta_cache* c) {
+  if (!c || c->block <= 0 || c->cap_tokens < 0) return -1;
+  return eta::ceil_div(c->cap_tokens, c->block);
+}
+
+eta_status eta_append_kv(const eta_cache* c, const void* k_new, const void* v_new,
+                         int32_t* overflow, void* stream) {
+  eta::CacheView v;
+  if (eta_status s = check_cache(c, &v)) return s;
+  if (empty(v)) return ok();
+  if (!k_new || !v_new) return fail(ETA_ERR_NULL_PTR, "k_new/v_new is NULL");
+  return hip_status(eta::launch_append(v, k_new, v_new, overflow, (hipStream_t)stream),
+                    "eta_append_kv launch");
+}
+
+eta_status eta_build_block_meta(const eta_cache* c, int32_t first_block, int32_t n_blocks,
+                                void* stream) {
+  eta::CacheView v;
+  if (eta_status s = check_cache(c, &v)) return s;
+  if (first_block < 0) return fail(ETA_ERR_BAD_ARG, "first_block %d < 0", first_block);
+  if (n_blocks < -1) return fail(ETA_ERR_BAD_ARG, "n_blocks %d < -1", n_blocks);
+  if (n_blocks == -1) n_blocks = first_block < v.cap_blocks ? v.cap_blocks - first_block : 0;
+  if ((long long)first_block + n_blocks > v.cap_blocks)
+    return fail(ETA_ERR_CAPACITY, "blocks [%d, %lld) exceed cap_blocks %d", first_block,
+                (long long)first_block + n_blocks, v.cap_blocks);
+  if (empty(v) || n_blocks == 0) return ok();
+  if ((long long)eta::ceil_div(n_blocks, 4) * v.B * v.H > kMaxGrid)
+    return fail(ETA_ERR_BAD_SHAPE, "grid too large");
+  return hip_status(eta::launch_block_meta(v, first_block, n_blocks, (hipStream_t)stream),
+                    "eta_build_block_meta launch");
+}
+
+eta_status eta_predict_tau(int32_t batch, int32_t heads, int32_t head_dim, const float* q,
+                           const float* W, const float* bias_or_c, float a, float* tau_gate,
+                           float* tau_screen, void* stream) {
+  if (batch < 0 || heads < 0 || head_dim < 1)
+    return fail(ETA_ERR_BAD_SHAPE, "batch %d, heads %d, head_dim %d", batch, heads, head_dim);
+  if (heads > 256) return fail(ETA_ERR_BAD_SHAPE, "heads %d > 256", heads);
+  if (bad_float(a)) return fail(ETA_ERR_BAD_ARG, "a is NaN");
+  if (batch == 0 || heads == 0) return ok();
+  if (!bias_or_c || !tau_gate || !tau_screen)
+    return fail(ETA_ERR_NULL_PTR, "bias_or_c/tau_gate/tau_screen is NULL");
+  if (W && !q) return fail(ETA_ERR_NULL_PTR, "q is NULL in dynamic mode");
+  return hip_status(eta::launch_predict(batch, heads, head_dim, q, W, bias_or_c, a, tau_gate,
+                                        tau_screen, (hipStream_t)stream),
+                    "eta_predict_tau launch");
+}
+
+size_t eta_screen_workspace_bytes(int32_t batch, int32_t heads, int32_t cap_blocks) {
+  if (batch <= 0 || heads <= 0 || cap_blocks <= 0) return 256;
+  return align256((size_t)batch * heads * (size_t)eta::ceil_div(cap_blocks, 64) * 8);
+}
+
+eta_status eta_screen(const eta_cache* c, const float* q, const float* tau_screen, float z,
+                      float scale, int32_t* active_idx, int32_t* active_cnt,
+                      uint64_t* density_ctr, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  eta::CacheView v;
+  if (eta_status s = check_cache(c, &v)) return s;
+  if (bad_float(z) || z < 0.f) return fail(ETA_ERR_BAD_ARG, "z must be >= 0 (or +inf)");
+  if (bad_float(scale) || !(scale > 0.f) || isinf(scale))
+    return fail(ETA_ERR_BAD_ARG, "scale must be finite and > 0");
+  if (empty(v)) return ok();
+  if (!q || !tau_screen || !active_idx || !active_cnt)
+    return fail(ETA_ERR_NULL_PTR, "q/tau_screen/active_idx/active_cnt is NULL");
+  const size_t need = eta_screen_workspace_bytes(v.B, v.H, v.cap_blocks);
+  if (!workspace || workspace_bytes < need)
+    return fail(ETA_ERR_WORKSPACE, "screen workspace %zu bytes < %zu", workspace_bytes, need);
+  if ((long long)eta::ceil_div(v.cap_blocks, 256) * v.B * v.H > kMaxGrid)
+    return fail(ETA_ERR_BAD_SHAPE, "grid too large");
+  return hip_status(eta::launch_screen(v, q, tau_screen, z, scale, active_idx, active_cnt,
+                                       density_ctr, static_cast<uint64_t*>(workspace),
+                                       (hipStream_t)stream),
+                    "eta_screen launch");
+}
+
+size_t eta_decode_workspace_bytes(int32_t batch, int32_t heads, int32_t head_dim,
+                                  int32_t cap_blocks, int32_t blocks_per_split) {
+  if (batch <= 0 || heads <= 0 || head_dim <= 0 || cap_blocks <= 0 || blocks_per_split <= 0)
+    return 256;
+  return decode_ws((long long)batch * heads, head_dim, cap_blocks, blocks_per_split);
+}
+
+static eta_status decode_common(const eta_cache* c, const float* q, const float* tau_gate,
+                                const int32_t* active_idx, const int32_t* active_cnt,
+                                int32_t mode, bool dense, float beta, float scale, int32_t split,
+                                void* ws, size_t ws_bytes, float* out, void* stream) {
+  eta::CacheView v;
+  if (eta_status s = check_cache(c, &v)) return s;
+  if (mode != ETA_LOGIT_GATED && mode != ETA_LOGIT_RAW)
+    return fail(ETA_ERR_BAD_ARG, "logit_mode %d unknown", mode);
+  if (mode == ETA_LOGIT_GATED && !dense && (bad_float(beta) || !(beta > 0.f) || isinf(beta)))
+    return fail(ETA_ERR_BAD_ARG, "beta must be finite and > 0");
+  if (bad_float(scale) || !(scale > 0.f) || isinf(scale))
+    return fail(ETA_ERR_BAD_ARG, "scale must be finite and > 0");
+  if (split < 1 || split > 4096)
+    return fail(ETA_ERR_BAD_ARG, "blocks_per_split %d outside [1, 4096]", split);
+  if (empty(v)) return ok();
+  if (!q || !out) return fail(ETA_ERR_NULL_PTR, "q/out is NULL");
+  if (!dense && (!active_idx || !active_cnt))
+    return fail(ETA_ERR_NULL_PTR, "active_idx/active_cnt is NULL");
+  if (!dense && mode == ETA_LOGIT_GATED && !tau_gate)
+    return fail(ETA_ERR_NULL_PTR, "tau_gate is NULL in GATED mode");
+  const long long units = (long long)v.B * v.H;
+  const int maxc = eta::ceil_div(v.cap_blocks, split);
+  if ((long long)maxc * units > kMaxGrid) return fail(ETA_ERR_BAD_SHAPE, "grid too large");
+  const size_t need = decode_ws(units, v.D, v.cap_blocks, split);
+  if (!ws || ws_bytes < need)
+    return fail(ETA_ERR_WORKSPACE, "decode workspace %zu bytes < %zu", ws_bytes, need);
+  const size_t slots = (size_t)units * maxc;
+  char* w = static_cast<char*>(ws);
+  eta::DecodeArgs a;
+  a.q = q;
+  a.tau = tau_gate;
+  a.active_idx = active_idx;
+  a.active_cnt = active_cnt;
+  a.mode = dense ? ETA_LOGIT_RAW : mode;
+  a.dense = dense;
+  a.beta = beta;
+  a.scale = scale;
+  a.split = split;
+  a.max_chunks = maxc;
+  a.part_m = reinterpret_cast<float*>(w);
+  a.part_l = reinterpret_cast<float*>(w + align256(slots * 4));
+  a.part_acc = reinterpret_cast<float*>(w + 2 * align256(slots * 4));
+  a.out = out;
+  return hip_status(eta::launch_decode(v, a, (hipStream_t)stream), "eta_decode launch");
+}
+
+eta_status eta_decode(const eta_cache* c, const float* q, const float* tau_gate,
+                      const int32_t* active_idx, const int32_t* active_cnt, int32_t logit_mode,
+                      float beta, float scale, int32_t blocks_per_split, void* workspace,
+                      size_t workspace_bytes, float* out, void* stream) {
+  return decode_common(c, q, tau_gate, active_idx, active_cnt, logit_mode, false, beta, scale,
+                       blocks_per_split, workspace, workspace_bytes, out, stream);
+}
+
+eta_status eta_dense_decode(const eta_cache* c, const float* q, float scale,
+                            int32_t blocks_per_split, void* workspace, size_t workspace_bytes,
+                            float* out, void* stream) {
+  return decode_common(c, q, nullptr, nullptr, nullptr, ETA_LOGIT_RAW, true, 1.f, scale,
+                       blocks_per_split, workspace, workspace_bytes, out, stream);
+}
+
+size_t eta_calibrate_workspace_bytes(int32_t n_sets, int32_t batch, int32_t heads,
+                                     int32_t cap_blocks) {
+  if (n_sets <= 0 || batch <= 0 || heads <= 0 || cap_blocks <= 0) return 256;
+  return align256((size_t)n_sets * batch * heads * (size_t)cap_blocks * 4);
+}
+
+eta_status eta_calibrate_threshold(const eta_cache* c, int32_t n_sets, const float* q_sets,
+                                   const float* tau0, float z, float scale,
+                                   float target_density, void* workspace,
+                                   size_t workspace_bytes, float* c_out, void* stream) {
+  eta::CacheView v;
+  if (eta_status s = check_cache(c, &v)) return s;
+  if (n_sets < 1) return fail(ETA_ERR_BAD_SHAPE, "n_sets %d < 1", n_sets);
+  if (bad_float(z) || z < 0.f) return fail(ETA_ERR_BAD_ARG, "z must be >= 0 (or +inf)");
+  if (bad_float(scale) || !(scale > 0.f) || isinf(scale))
+    return fail(ETA_ERR_BAD_ARG, "scale must be finite and > 0");
+  if (bad_float(target_density) || target_density < 0.f || target_density > 1.f)
+    return fail(ETA_ERR_BAD_ARG, "target_density must lie in [0, 1]");
+  if (empty(v)) return ok();
+  if (!q_sets || !c_out) return fail(ETA_ERR_NULL_PTR, "q_sets/c_out is NULL");
+  if ((long long)n_sets * v.B * v.cap_blocks > 0x7fffffffLL)
+    return fail(ETA_ERR_CAPACITY, "more than 2^31-1 pooled values per head");
+  if ((long long)eta::ceil_div(v.cap_blocks, 256) * n_sets * v.B * v.H > kMaxGrid)
+    return fail(ETA_ERR_BAD_SHAPE, "grid too large");
+  const size_t need = eta_calibrate_workspace_bytes(n_sets, v.B, v.H, v.cap_blocks);
+  if (!workspace || workspace_bytes < need)
+    return fail(ETA_ERR_WORKSPACE, "calibrate workspace %zu bytes < %zu", workspace_bytes, need);
+  return hip_status(eta::launch_calibrate(v, n_sets, q_sets, tau0, z, scale, target_density,
+                                          static_cast<float*>(workspace), c_out,
+                                          (hipStream_t)stream),
+                    "eta_calibrate_threshold launch");
+}
+
+}  // extern "C"

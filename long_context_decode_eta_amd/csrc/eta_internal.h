@@ -1,0 +1,143 @@
+// eta_internal.h -- shared device helpers and launcher declarations of libeta.
+//
+// Target: gfx950 (CDNA4), wave64.  Everything here is memory-bound GEMV-shaped
+// work, so the helpers are about 128-bit loads, lane-group reductions done
+// with DPP row permutations (no LDS round trip) and exact bf16 widening.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/eta.h"
+
+namespace eta {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// Element access.  A bfloat16 is the upper half of an IEEE binary32, so the
+// widening below is exact.
+template <int DT>
+struct Elt;
+template <>
+struct Elt<ETA_DT_F32> {
+  static constexpr int kBytes = 4;
+  static constexpr int kPer16B = 4;  // elements per 128-bit load
+};
+template <>
+struct Elt<ETA_DT_BF16> {
+  static constexpr int kBytes = 2;
+  static constexpr int kPer16B = 8;
+};
+
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Widen one 128-bit load into kPer16B floats.
+template <int DT>
+__device__ __forceinline__ void widen(const uint4& r, float* x) {
+  if constexpr (DT == ETA_DT_F32) {
+    x[0] = __uint_as_float(r.x);
+    x[1] = __uint_as_float(r.y);
+    x[2] = __uint_as_float(r.z);
+    x[3] = __uint_as_float(r.w);
+  } else {
+    x[0] = bf16lo(r.x); x[1] = bf16hi(r.x);
+    x[2] = bf16lo(r.y); x[3] = bf16hi(r.y);
+    x[4] = bf16lo(r.z); x[5] = bf16hi(r.z);
+    x[6] = bf16lo(r.w); x[7] = bf16hi(r.w);
+  }
+}
+
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// ---------------------------------------------------------------------------
+// Lane-group all-reductions.  Groups are aligned runs of N lanes.  The DPP
+// patterns used (quad xor-1, quad xor-2, half-row mirror, row mirror) pair
+// every lane with a partner whose partial sum covers the complementary set,
+// and a + b == b + a exactly, so every lane of a group ends with the
+// bit-identical result.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+constexpr int kQuadXor1 = 0xB1;    // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;    // quad_perm [2,3,0,1]
+constexpr int kRowMirror = 0x140;  // lane i <-> 15-i within a row of 16
+constexpr int kHalfMirror = 0x141; // lane i <-> 7-i within each half row
+
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16 || N == 32 || N == 64, "group");
+  if constexpr (N >= 2) x += dpp<kQuadXor1>(x);
+  if constexpr (N >= 4) x += dpp<kQuadXor2>(x);
+  if constexpr (N == 8) x += dpp<kHalfMirror>(x);
+  if constexpr (N >= 16) {
+    x += dpp<kRowMirror>(x);
+    x += dpp<kHalfMirror>(x);
+  }
+  if constexpr (N >= 32) x += __shfl_xor(x, 16, kWave);
+  if constexpr (N >= 64) x += __shfl_xor(x, 32, kWave);
+  return x;
+}
+
+template <int N>
+__device__ __forceinline__ float group_max(float x) {
+  if constexpr (N >= 2) x = fmaxf(x, dpp<kQuadXor1>(x));
+  if constexpr (N >= 4) x = fmaxf(x, dpp<kQuadXor2>(x));
+  if constexpr (N == 8) x = fmaxf(x, dpp<kHalfMirror>(x));
+  if constexpr (N >= 16) {
+    x = fmaxf(x, dpp<kRowMirror>(x));
+    x = fmaxf(x, dpp<kHalfMirror>(x));
+  }
+  if constexpr (N >= 32) x = fmaxf(x, __shfl_xor(x, 16, kWave));
+  if constexpr (N >= 64) x = fmaxf(x, __shfl_xor(x, 32, kWave));
+  return x;
+}
+
+// ---------------------------------------------------------------------------
+// Device view of the cache (plain values; built on the host per call).
+struct CacheView {
+  int B, H, D, bs, log2bs, cap, cap_blocks, dtype;
+  const void* k;
+  const void* v;
+  float* mu;
+  float* var;
+  float* maxnorm;
+  const int32_t* seq_len;
+};
+
+__host__ __device__ constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// ---------------------------------------------------------------------------
+// Launchers (defined in the kernel translation units).  Each returns the
+// hipError_t of its launch; shapes were validated by the caller.
+hipError_t launch_append(const CacheView& c, const void* k_new, const void* v_new,
+                         int32_t* overflow, hipStream_t s);
+hipError_t launch_block_meta(const CacheView& c, int first_block, int n_blocks, hipStream_t s);
+hipError_t launch_predict(int B, int H, int D, const float* q, const float* W, const float* bias,
+                          float a, float* tau_gate, float* tau_screen, hipStream_t s);
+hipError_t launch_screen(const CacheView& c, const float* q, const float* tau_screen, float z,
+                         float scale, int32_t* active_idx, int32_t* active_cnt, uint64_t* ctr,
+                         uint64_t* words, hipStream_t s);
+struct DecodeArgs {
+  const float* q;
+  const float* tau;
+  const int32_t* active_idx;
+  const int32_t* active_cnt;
+  int mode;  // ETA_LOGIT_GATED / ETA_LOGIT_RAW
+  bool dense;
+  float beta, scale;
+  int split;       // blocks per chunk
+  int max_chunks;  // ceil(cap_blocks / split)
+  float* part_m;   // [B*H][max_chunks]
+  float* part_l;   // [B*H][max_chunks]
+  float* part_acc; // [B*H][max_chunks][D]
+  float* out;
+};
+hipError_t launch_decode(const CacheView& c, const DecodeArgs& a, hipStream_t s);
+hipError_t launch_calibrate(const CacheView& c, int n_sets, const float* q_sets,
+                            const float* tau0, float z, float scale, float rho, float* values,
+                            float* c_out, hipStream_t s);
+
+}  // namespace eta

@@ -1,0 +1,216 @@
+// kernels_meta.hip -- KV append, block statistics, threshold predictor.
+//
+// Block statistics (paper: "Elastic Threshold Attention ...", Methodology 4):
+// per complete block of b keys, the centroid mu, the per-coordinate
+// population variance var (two passes) and the largest key norm maxnorm.
+// Threshold (Methodology 1, Eq. 1): tau = qbar W_tau + b_tau, or frozen
+// per-head constants.
+#include "eta_internal.h"
+
+namespace eta {
+
+// Statistics of block j of stream u, computed by one wavefront.
+// Lane layout: a key row of D elements is read by LPR lanes with one 128-bit
+// load each (bf16, D=128: 16 lanes x 8 elements), so one load instruction of
+// the wave covers RPI = 64 / LPR rows.  Each lane accumulates its EPL columns
+// over rows g, g+RPI, ...; the column sums of the RPI row groups are then
+// combined with an xor butterfly.  Row norms are reduced inside the lane group
+// with DPP.  `last_row`, when given, replaces row b-1 (the append path passes
+// the key it has just written, so the block is complete without re-reading).
+// Both the append and the bulk path call this function, so they produce
+// bit-identical statistics.
+template <int D, int DT>
+__device__ __forceinline__ void block_stats_wave(const CacheView& c, int u, int j,
+                                                 const void* last_row, int lane) {
+  constexpr int EPL = Elt<DT>::kPer16B;
+  constexpr int LPR = D / EPL;
+  constexpr int RPI = kWave / LPR;
+  constexpr int RB = D * Elt<DT>::kBytes;  // bytes per key row
+  const int g = lane / LPR, li = lane % LPR;
+  const char* base = static_cast<const char*>(c.k) + ((size_t)u * c.cap + ((size_t)j << c.log2bs)) * RB;
+
+  float sum[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) sum[e] = 0.f;
+  float best = 0.f;  // largest squared row norm
+  for (int r0 = 0; r0 < c.bs; r0 += RPI) {
+    const int r = r0 + g;
+    float x[EPL];
+    float n2 = 0.f;
+    if (r < c.bs) {
+      const char* src = (last_row && r == c.bs - 1) ? static_cast<const char*>(last_row)
+                                                    : base + (size_t)r * RB;
+      widen<DT>(ld16(src + li * 16), x);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        sum[e] += x[e];
+        n2 = fmaf(x[e], x[e], n2);
+      }
+    }
+    n2 = group_sum<LPR>(n2);
+    best = fmaxf(best, n2);
+  }
+#pragma unroll
+  for (int off = LPR; off < kWave; off <<= 1) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) sum[e] += __shfl_xor(sum[e], off, kWave);
+    best = fmaxf(best, __shfl_xor(best, off, kWave));
+  }
+  const float inv_b = 1.0f / (float)c.bs;  // exact: b is a power of two
+  float mean[EPL], ss[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    mean[e] = sum[e] * inv_b;
+    ss[e] = 0.f;
+  }
+  for (int r0 = 0; r0 < c.bs; r0 += RPI) {
+    const int r = r0 + g;
+    if (r < c.bs) {
+      const char* src = (last_row && r == c.bs - 1) ? static_cast<const char*>(last_row)
+                                                    : base + (size_t)r * RB;
+      float x[EPL];
+      widen<DT>(ld16(src + li * 16), x);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const float dlt = x[e] - mean[e];
+        ss[e] = fmaf(dlt, dlt, ss[e]);
+      }
+    }
+  }
+#pragma unroll
+  for (int off = LPR; off < kWave; off <<= 1) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) ss[e] += __shfl_xor(ss[e], off, kWave);
+  }
+  if (g == 0) {
+    const size_t row = ((size_t)u * c.cap_blocks + j) * D + li * EPL;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      c.mu[row + e] = mean[e];
+      c.var[row + e] = ss[e] * inv_b;
+    }
+    if (lane == 0) c.maxnorm[(size_t)u * c.cap_blocks + j] = sqrtf(best);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Append: one wavefront per (b, h) stream.
+template <int D, int DT>
+__global__ __launch_bounds__(64) void append_kernel(CacheView c, const void* k_new,
+                                                    const void* v_new, int32_t* overflow) {
+  constexpr int RB = D * Elt<DT>::kBytes;
+  const int u = blockIdx.x, lane = threadIdx.x;
+  const int pos = c.seq_len[u / c.H];
+  if (pos >= c.cap) {
+    if (overflow && lane == 0) *overflow = 1;
+    return;
+  }
+  const char* kn = static_cast<const char*>(k_new) + (size_t)u * RB;
+  const char* vn = static_cast<const char*>(v_new) + (size_t)u * RB;
+  const size_t off = ((size_t)u * c.cap + pos) * RB;
+  char* kd = static_cast<char*>(const_cast<void*>(c.k)) + off;
+  char* vd = static_cast<char*>(const_cast<void*>(c.v)) + off;
+  for (int p = lane; p < RB / 16; p += kWave) {
+    *reinterpret_cast<uint4*>(kd + p * 16) = ld16(kn + p * 16);
+    *reinterpret_cast<uint4*>(vd + p * 16) = ld16(vn + p * 16);
+  }
+  if (((pos + 1) & (c.bs - 1)) == 0) block_stats_wave<D, DT>(c, u, pos >> c.log2bs, kn, lane);
+}
+
+__global__ void bump_len_kernel(int B, int cap, int32_t* seq_len) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b < B && seq_len[b] < cap) seq_len[b] += 1;
+}
+
+// Bulk statistics: 4 wavefronts per work-group, one block each.
+// Flattened grid: blockIdx.x = tile * units + u.
+template <int D, int DT>
+__global__ __launch_bounds__(256) void block_meta_kernel(CacheView c, int first, int nblk) {
+  const int units = c.B * c.H;
+  const int u = blockIdx.x % units, tile = blockIdx.x / units;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int i = tile * 4 + wave;
+  if (i >= nblk) return;
+  const int j = first + i;
+  const int T = c.seq_len[u / c.H];
+  if (j >= (T >> c.log2bs)) return;
+  block_stats_wave<D, DT>(c, u, j, nullptr, lane);
+}
+
+// ---------------------------------------------------------------------------
+// Threshold (Eq. 1).  One work-group per sequence b.  Thread t owns head
+// h = t % H and the rows j = rg, rg + G, ... (rg = t / H, G = 256 / H) of the
+// H*D-long dot product; the G row-group partials are summed in LDS in a fixed
+// order.  Adjacent threads read adjacent W entries of one row.
+__global__ __launch_bounds__(256) void predict_kernel(int H, int D, const float* q, const float* W,
+                                                      const float* bias, float a, float* tau,
+                                                      float* tau_screen) {
+  __shared__ float red[256];
+  const int b = blockIdx.x, t = threadIdx.x;
+  const int G = 256 / H, h = t % H, rg = t / H;
+  const int n = H * D;
+  if (W) {
+    float s = 0.f;
+    if (rg < G) {
+      const float* qb = q + (size_t)b * n;
+      for (int j = rg; j < n; j += G) s = fmaf(qb[j], W[(size_t)j * H + h], s);
+    }
+    red[t] = s;
+    __syncthreads();
+  }
+  if (t < H) {
+    float v;
+    if (W) {
+      float acc = 0.f;
+      for (int r = 0; r < G; ++r) acc += red[r * H + t];
+      v = acc + bias[t];
+    } else {
+      v = bias[t];
+    }
+    tau[(size_t)b * H + t] = v;
+    tau_screen[(size_t)b * H + t] = v - a;
+  }
+}
+
+// ---------------------------------------------------------------------------
+template <int D, int DT>
+static hipError_t append_t(const CacheView& c, const void* kn, const void* vn, int32_t* of,
+                           hipStream_t s) {
+  hipLaunchKernelGGL((append_kernel<D, DT>), dim3(c.B * c.H), dim3(64), 0, s, c, kn, vn, of);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bump_len_kernel, dim3(ceil_div(c.B, 256)), dim3(256), 0, s, c.B, c.cap,
+                     const_cast<int32_t*>(c.seq_len));
+  return hipGetLastError();
+}
+
+hipError_t launch_append(const CacheView& c, const void* kn, const void* vn, int32_t* of,
+                         hipStream_t s) {
+  if (c.D == 128) return c.dtype == ETA_DT_BF16 ? append_t<128, ETA_DT_BF16>(c, kn, vn, of, s)
+                                                : append_t<128, ETA_DT_F32>(c, kn, vn, of, s);
+  return c.dtype == ETA_DT_BF16 ? append_t<64, ETA_DT_BF16>(c, kn, vn, of, s)
+                                : append_t<64, ETA_DT_F32>(c, kn, vn, of, s);
+}
+
+template <int D, int DT>
+static hipError_t meta_t(const CacheView& c, int first, int n, hipStream_t s) {
+  const long long grid = (long long)ceil_div(n, 4) * c.B * c.H;
+  hipLaunchKernelGGL((block_meta_kernel<D, DT>), dim3((unsigned)grid), dim3(256), 0, s, c, first, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_meta(const CacheView& c, int first, int n, hipStream_t s) {
+  if (c.D == 128) return c.dtype == ETA_DT_BF16 ? meta_t<128, ETA_DT_BF16>(c, first, n, s)
+                                                : meta_t<128, ETA_DT_F32>(c, first, n, s);
+  return c.dtype == ETA_DT_BF16 ? meta_t<64, ETA_DT_BF16>(c, first, n, s)
+                                : meta_t<64, ETA_DT_F32>(c, first, n, s);
+}
+
+hipError_t launch_predict(int B, int H, int D, const float* q, const float* W, const float* bias,
+                          float a, float* tau, float* tau_screen, hipStream_t s) {
+  hipLaunchKernelGGL(predict_kernel, dim3(B), dim3(256), 0, s, H, D, q, W, bias, a, tau,
+                     tau_screen);
+  return hipGetLastError();
+}
+
+}  // namespace eta

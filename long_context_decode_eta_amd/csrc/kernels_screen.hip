@@ -1,0 +1,321 @@
+// kernels_screen.hip -- block screen, active-list compaction, calibration.
+//
+// Screen (paper: "Elastic Threshold Attention ...", Methodology 4, Eq. 5):
+//   s_j = scale * min(<q, mu_j> + z sqrt(sum_i q_i^2 var_j,i), ||q|| maxnorm_j)
+// A block is skipped iff s_j < threshold; only the statistics (2D+1 floats per
+// block) are read, never the keys.  The block holding the newest key is always
+// admitted (it holds the query's own, never-gated key of Eq. 3).
+#include "eta_internal.h"
+
+namespace eta {
+
+constexpr int kLanesPerBlock = 8;      // lanes that read one block's statistics
+constexpr int kBlocksPerIter = kWave / kLanesPerBlock;  // 8 blocks per wave step
+constexpr int kBlocksPerWave = 64;     // one 64-bit admission word per wave
+constexpr int kBlocksPerTile = 4 * kBlocksPerWave;      // 4 waves per work-group
+
+// Per-lane share of the query: with 8 lanes per block, load t (t < D/32) of
+// lane li reads floats [32 t + 4 li, 32 t + 4 li + 4) of a statistics row, so
+// each load instruction covers one full 128-byte line of each of 8 blocks.
+template <int D>
+struct QShare {
+  static constexpr int kLoads = D / 32;
+  float q[4 * kLoads];
+  float q2[4 * kLoads];
+  float qn;  // ||q||_2
+};
+
+template <int D>
+__device__ __forceinline__ void load_qshare(const float* qu, int li, QShare<D>& s) {
+  float qq = 0.f;
+#pragma unroll
+  for (int t = 0; t < QShare<D>::kLoads; ++t) {
+    const float4 v = *reinterpret_cast<const float4*>(qu + 32 * t + 4 * li);
+    const float x[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      s.q[4 * t + e] = x[e];
+      s.q2[4 * t + e] = x[e] * x[e];
+      qq = fmaf(x[e], x[e], qq);
+    }
+  }
+  s.qn = sqrtf(group_sum<kLanesPerBlock>(qq));
+}
+
+// Eq. 5 score of block j of stream u.  All 8 lanes of the block's group must
+// call it together (DPP reductions); `valid` false yields garbage that the
+// caller ignores.  Every lane of the group returns the identical value.
+template <int D>
+__device__ __forceinline__ float block_score(const CacheView& c, int u, int j, bool valid,
+                                             const QShare<D>& s, int li, float z, bool z_inf,
+                                             float scale) {
+  float dot = 0.f, mom = 0.f, M = 0.f;
+  if (valid) {
+    const size_t row = ((size_t)u * c.cap_blocks + j) * D;
+    const float* mu = c.mu + row;
+    const float* var = c.var + row;
+#pragma unroll
+    for (int t = 0; t < QShare<D>::kLoads; ++t) {
+      const float4 m = *reinterpret_cast<const float4*>(mu + 32 * t + 4 * li);
+      const float4 v = *reinterpret_cast<const float4*>(var + 32 * t + 4 * li);
+      dot = fmaf(s.q[4 * t + 0], m.x, dot);
+      dot = fmaf(s.q[4 * t + 1], m.y, dot);
+      dot = fmaf(s.q[4 * t + 2], m.z, dot);
+      dot = fmaf(s.q[4 * t + 3], m.w, dot);
+      mom = fmaf(s.q2[4 * t + 0], v.x, mom);
+      mom = fmaf(s.q2[4 * t + 1], v.y, mom);
+      mom = fmaf(s.q2[4 * t + 2], v.z, mom);
+      mom = fmaf(s.q2[4 * t + 3], v.w, mom);
+    }
+    M = c.maxnorm[(size_t)u * c.cap_blocks + j];
+  }
+  dot = group_sum<kLanesPerBlock>(dot);
+  mom = group_sum<kLanesPerBlock>(mom);
+  const float geometric = s.qn * M;
+  if (z_inf) return scale * geometric;
+  return scale * fminf(fmaf(z, sqrtf(mom), dot), geometric);
+}
+
+// ---------------------------------------------------------------------------
+// Screen: each wave scores 64 consecutive blocks, 8 per step, and writes one
+// 64-bit admission word.  Flattened grid: blockIdx.x = tile * units + u, so
+// the low tiles of every stream are dispatched first and the surplus tiles of
+// short streams exit at once.
+template <int D>
+__global__ __launch_bounds__(256) void screen_kernel(CacheView c, const float* q,
+                                                     const float* tau_screen, float z, float scale,
+                                                     uint64_t* words, int words_per_unit) {
+  const int units = c.B * c.H;
+  const int u = blockIdx.x % units, tile = blockIdx.x / units;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int T = c.seq_len[u / c.H];
+  const int nb = (T + c.bs - 1) >> c.log2bs;
+  const int nbc = T >> c.log2bs;
+  const int j0 = (tile * 4 + wave) * kBlocksPerWave;
+  if (j0 >= nb) return;
+  const int gi = lane / kLanesPerBlock, li = lane % kLanesPerBlock;
+  QShare<D> qs;
+  load_qshare<D>(q + (size_t)u * D, li, qs);
+  const float ts = tau_screen[u];
+  const bool z_inf = __builtin_isinf(z);
+  uint64_t word = 0;
+#pragma unroll 2
+  for (int it = 0; it < kBlocksPerWave / kBlocksPerIter; ++it) {
+    const int j = j0 + it * kBlocksPerIter + gi;
+    const bool scored = j < nbc;
+    const float sc = block_score<D>(c, u, j, scored, qs, li, z, z_inf, scale);
+    const bool on = (j == nb - 1) || (scored && sc >= ts);
+    const uint64_t bal = __ballot(on);
+    uint64_t bits = 0;
+#pragma unroll
+    for (int g = 0; g < kBlocksPerIter; ++g) bits |= ((bal >> (g * kLanesPerBlock)) & 1ull) << g;
+    word |= bits << (it * kBlocksPerIter);
+  }
+  if (lane == 0) words[(size_t)u * words_per_unit + (j0 >> 6)] = word;
+}
+
+// Compaction: one work-group per stream turns the admission words into the
+// ascending index list.  Thread t owns a contiguous run of words, so an
+// exclusive scan of per-thread popcounts gives every thread its output offset
+// and the list comes out ascending with no sorting.
+__global__ __launch_bounds__(256) void compact_kernel(CacheView c, const uint64_t* words,
+                                                      int words_per_unit, int32_t* active_idx,
+                                                      int32_t* active_cnt, uint64_t* ctr) {
+  __shared__ int scan[256];
+  const int u = blockIdx.x, t = threadIdx.x;
+  const int T = c.seq_len[u / c.H];
+  const int nb = (T + c.bs - 1) >> c.log2bs;
+  const int nw = (nb + 63) >> 6;
+  const int per = (nw + 255) >> 8;
+  const int w0 = min(t * per, nw), w1 = min(w0 + per, nw);
+  const uint64_t* wu = words + (size_t)u * words_per_unit;
+  auto word_at = [&](int w) {
+    uint64_t x = wu[w];
+    const int rem = nb - (w << 6);
+    if (rem < 64) x &= (1ull << rem) - 1ull;
+    return x;
+  };
+  int mine = 0;
+  for (int w = w0; w < w1; ++w) mine += __popcll(word_at(w));
+  scan[t] = mine;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {  // Hillis-Steele inclusive scan
+    const int add = t >= off ? scan[t - off] : 0;
+    __syncthreads();
+    scan[t] += add;
+    __syncthreads();
+  }
+  int pos = scan[t] - mine;
+  const int total = scan[255];
+  int32_t* out = active_idx + (size_t)u * c.cap_blocks;
+  for (int w = w0; w < w1; ++w) {
+    uint64_t x = word_at(w);
+    while (x) {
+      const int bit = __ffsll((unsigned long long)x) - 1;
+      out[pos++] = (w << 6) + bit;
+      x &= x - 1ull;
+    }
+  }
+  if (t == 0) {
+    active_cnt[u] = total;
+    if (ctr && total > 0) {
+      const unsigned long long tokens =
+          (unsigned long long)(total - 1) * c.bs + (unsigned long long)(T - ((nb - 1) << c.log2bs));
+      atomicAdd(reinterpret_cast<unsigned long long*>(ctr), tokens);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Calibration, step 1: pooled values x = s_j - tau0 for every complete block
+// except the last one of its stream; other slots get NaN.  Layout
+// values[h][n][b][cap_blocks].  Grid: blockIdx.x = tile * (n_sets*units) + su.
+template <int D>
+__global__ __launch_bounds__(256) void calib_values_kernel(CacheView c, int n_sets,
+                                                           const float* q_sets, const float* tau0,
+                                                           float z, float scale, float* values) {
+  const int units = c.B * c.H;
+  const int su = blockIdx.x % (n_sets * units), tile = blockIdx.x / (n_sets * units);
+  const int n = su / units, u = su % units;
+  const int b = u / c.H, h = u % c.H;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int j0 = (tile * 4 + wave) * kBlocksPerWave;
+  if (j0 >= c.cap_blocks) return;
+  const int T = c.seq_len[b];
+  const int nb = (T + c.bs - 1) >> c.log2bs;
+  const int gi = lane / kLanesPerBlock, li = lane % kLanesPerBlock;
+  QShare<D> qs;
+  load_qshare<D>(q_sets + (size_t)su * D, li, qs);
+  const float t0 = tau0 ? tau0[su] : 0.f;
+  const bool z_inf = __builtin_isinf(z);
+  float* dst = values + (((size_t)h * n_sets + n) * c.B + b) * c.cap_blocks;
+  for (int it = 0; it < kBlocksPerWave / kBlocksPerIter; ++it) {
+    const int j = j0 + it * kBlocksPerIter + gi;
+    const bool cand = j < nb - 1;  // every block before the last is complete
+    const float sc = block_score<D>(c, u, j, cand, qs, li, z, z_inf, scale);
+    if (li == 0 && j < c.cap_blocks) dst[j] = cand ? sc - t0 : __builtin_nanf("");
+  }
+}
+
+// Order-preserving map float -> uint32 (larger float, larger key).
+__device__ __forceinline__ uint32_t fkey(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float funkey(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// k-th largest (1-based) non-NaN key among x[0..n) by 4 passes of an 8-bit
+// MSB-first radix select; all threads of the work-group call it.
+__device__ uint32_t radix_select_desc(const float* x, long long n, long long k, uint32_t* hist,
+                                      uint32_t* sh) {
+  uint32_t prefix = 0, mask = 0;
+  long long remaining = k;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int i = threadIdx.x; i < 256; i += blockDim.x) hist[i] = 0;
+    __syncthreads();
+    for (long long i = threadIdx.x; i < n; i += blockDim.x) {
+      const float f = x[i];
+      if (f != f) continue;
+      const uint32_t key = fkey(f);
+      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int dg = 255;
+      for (; dg > 0; --dg) {
+        if (remaining <= (long long)hist[dg]) break;
+        remaining -= hist[dg];
+      }
+      sh[0] = (uint32_t)dg;
+      sh[1] = (uint32_t)remaining;
+    }
+    __syncthreads();
+    prefix |= sh[0] << shift;
+    mask |= 255u << shift;
+    remaining = sh[1];
+    __syncthreads();
+  }
+  return prefix;
+}
+
+// Calibration, step 2: one work-group per head.
+__global__ __launch_bounds__(1024) void calib_select_kernel(CacheView c, int n_sets, float rho,
+                                                            const float* values, float* c_out) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t sh[2];
+  const int h = blockIdx.x;
+  long long N = 0, total = 0, forced = 0;
+  for (int b = 0; b < c.B; ++b) {
+    const int T = c.seq_len[b];
+    if (T <= 0) continue;
+    const int nb = (T + c.bs - 1) >> c.log2bs;
+    N += (long long)n_sets * (nb - 1);
+    total += (long long)n_sets * T;
+    forced += (long long)n_sets * (T - ((nb - 1) << c.log2bs));
+  }
+  const double want = ((double)rho * (double)total - (double)forced) / (double)c.bs;
+  long long k = (long long)floor(want + 0.5);
+  if (k < 0) k = 0;
+  if (k > N) k = N;
+  const float* x = values + (size_t)h * n_sets * c.B * c.cap_blocks;
+  const long long n = (long long)n_sets * c.B * c.cap_blocks;
+  float res;
+  if (k == N) {
+    res = -__builtin_inff();
+  } else if (k == 0) {
+    res = __builtin_inff();
+  } else {
+    const float hi = funkey(radix_select_desc(x, n, k, hist, sh));
+    const float lo = funkey(radix_select_desc(x, n, k + 1, hist, sh));
+    res = 0.5f * (hi + lo);
+  }
+  if (threadIdx.x == 0) c_out[h] = res;
+}
+
+// ---------------------------------------------------------------------------
+template <int D>
+static hipError_t screen_t(const CacheView& c, const float* q, const float* ts, float z, float scale,
+                           int32_t* idx, int32_t* cnt, uint64_t* ctr, uint64_t* words,
+                           hipStream_t s) {
+  const int units = c.B * c.H;
+  const int wpu = ceil_div(c.cap_blocks, 64);
+  const long long grid = (long long)ceil_div(c.cap_blocks, kBlocksPerTile) * units;
+  hipLaunchKernelGGL((screen_kernel<D>), dim3((unsigned)grid), dim3(256), 0, s, c, q, ts, z, scale,
+                     words, wpu);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(compact_kernel, dim3(units), dim3(256), 0, s, c, words, wpu, idx, cnt, ctr);
+  return hipGetLastError();
+}
+
+hipError_t launch_screen(const CacheView& c, const float* q, const float* ts, float z, float scale,
+                         int32_t* idx, int32_t* cnt, uint64_t* ctr, uint64_t* words,
+                         hipStream_t s) {
+  return c.D == 128 ? screen_t<128>(c, q, ts, z, scale, idx, cnt, ctr, words, s)
+                    : screen_t<64>(c, q, ts, z, scale, idx, cnt, ctr, words, s);
+}
+
+template <int D>
+static hipError_t calib_t(const CacheView& c, int n_sets, const float* q_sets, const float* tau0,
+                          float z, float scale, float rho, float* values, float* c_out,
+                          hipStream_t s) {
+  const long long grid = (long long)ceil_div(c.cap_blocks, kBlocksPerTile) * n_sets * c.B * c.H;
+  hipLaunchKernelGGL((calib_values_kernel<D>), dim3((unsigned)grid), dim3(256), 0, s, c, n_sets,
+                     q_sets, tau0, z, scale, values);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(calib_select_kernel, dim3(c.H), dim3(1024), 0, s, c, n_sets, rho, values,
+                     c_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_calibrate(const CacheView& c, int n_sets, const float* q_sets, const float* tau0,
+                            float z, float scale, float rho, float* values, float* c_out,
+                            hipStream_t s) {
+  return c.D == 128 ? calib_t<128>(c, n_sets, q_sets, tau0, z, scale, rho, values, c_out, s)
+                    : calib_t<64>(c, n_sets, q_sets, tau0, z, scale, rho, values, c_out, s);
+}
+
+}  // namespace eta

@@ -113,7 +113,8 @@ def _needles(g, spec, nb, device):
 def make(name: str, *, seed: int = 1234, device="cpu", T=None, B=None, cap=None, pad="zero",
          block=None, H=None, kv=None) -> Workload:
     """Draw the workload `name` (a key of CONFIGS).  T, B, cap, block, H and kv
-    override the configuration's sizes for reduced test cases; `pad` fills the
+    override the configuration's sizes for reduced test cases (T: one length,
+    a (lo, hi) uniform range, or a list of per-sequence lengths); `pad` fills the
     unused cache slots beyond each T_b with zeros or NaN ("nan")."""
     cfg = dict(CONFIGS[name])
     B = cfg["B"] if B is None else B
@@ -126,7 +127,11 @@ def make(name: str, *, seed: int = 1234, device="cpu", T=None, B=None, cap=None,
     g.manual_seed(seed)
 
     Tspec = cfg["T"] if T is None else T
-    if isinstance(Tspec, tuple):
+    if isinstance(Tspec, list):  # explicit per-sequence lengths
+        assert len(Tspec) == B
+        lens = torch.tensor(Tspec, dtype=torch.int32, device=device)
+        Tmax = max(Tspec)
+    elif isinstance(Tspec, tuple):
         lens = _uniform_int(g, Tspec[0], Tspec[1], B, device).to(torch.int32)
         Tmax = Tspec[1]
     else:

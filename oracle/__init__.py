@@ -74,12 +74,17 @@ def load(path: str | None = None):
     lib.eta_oracle_step_batch.argtypes = (
         [_i] * 6 + [_p] * 7 + [_p, _p] + [_d, _d, _d, _i, _d] + [_p] * 6 + [_p])
     lib.eta_oracle_step_batch.restype = None
+    lib.eta_oracle_screen_attend_batch.argtypes = (
+        [_i] * 6 + [_p] * 7 + [_p, _p] + [_d, _d, _i, _d] + [_p] * 5)
+    lib.eta_oracle_screen_attend_batch.restype = None
     lib.eta_oracle_attend_batch.argtypes = [_i] * 6 + [_p] * 5 + [_i, _d, _p, _d, _p]
     lib.eta_oracle_attend_batch.restype = None
     lib.eta_oracle_dense_batch.argtypes = [_i] * 5 + [_p] * 4 + [_d, _p]
     lib.eta_oracle_dense_batch.restype = None
     lib.eta_oracle_calibrate.argtypes = [_i] * 6 + [_p] * 6 + [_d, _d, _d, _p, _p]
     lib.eta_oracle_calibrate.restype = None
+    lib.eta_oracle_threads.argtypes = []
+    lib.eta_oracle_threads.restype = _i
     if path is None:
         _lib = lib
     return lib
@@ -204,6 +209,31 @@ def step_batch(q, K, V, seq_len, b, meta, W, bias_or_c, *, a=0.0, z=1.0, scale=N
                               _ptr(r["tau"]), _ptr(r["tau_screen"]), _ptr(r["score"]),
                               _ptr(r["active"]), _ptr(r["cnt"]), _ptr(r["tokens"]),
                               _ptr(r["out"]))
+    return r
+
+
+def screen_attend_batch(q, K, V, seq_len, b, meta, tau, tau_screen, *, z=1.0, scale=None,
+                        mode=GATED, beta=5.0, lib=None):
+    """Screen and attention for every stream given fp64 thresholds [B][H]."""
+    lib = lib or load()
+    q = _f32(q); K, dt = _kv(K); V, dt2 = _kv(V)
+    assert dt == dt2
+    B, H, cap, d = K.shape
+    nbcap = -(-cap // b)
+    if scale is None:
+        scale = float(np.float32(1.0 / np.sqrt(d)))
+    mu, var, M = (np.ascontiguousarray(x, dtype=np.float64) for x in meta)
+    sl = np.ascontiguousarray(seq_len, dtype=np.int32)
+    tau = np.ascontiguousarray(tau, dtype=np.float64).reshape(B, H)
+    ts = np.ascontiguousarray(tau_screen, dtype=np.float64).reshape(B, H)
+    r = dict(tau=tau, tau_screen=ts, score=np.zeros((B, H, nbcap)),
+             active=np.zeros((B, H, nbcap), np.uint8), cnt=np.zeros((B, H), np.int32),
+             tokens=np.zeros((B, H), np.int64), out=np.zeros((B, H, d)))
+    lib.eta_oracle_screen_attend_batch(B, H, d, b, cap, dt, _ptr(sl), _ptr(q), _ptr(K), _ptr(V),
+                                       _ptr(mu), _ptr(var), _ptr(M), _ptr(tau), _ptr(ts),
+                                       float(z), float(scale), int(mode), float(beta),
+                                       _ptr(r["score"]), _ptr(r["active"]), _ptr(r["cnt"]),
+                                       _ptr(r["tokens"]), _ptr(r["out"]))
     return r
 
 

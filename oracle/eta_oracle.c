@@ -45,6 +45,7 @@
  *   mu,var [B][H][nbcap][d], M [B][H][nbcap]   (nbcap = ceil(cap/b))
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -210,6 +211,9 @@ void eta_oracle_dense(const float* q, const void* K, const void* V, int dtype, i
   free(S);
 }
 
+/* Threads an OpenMP region of the batch drivers uses. */
+int eta_oracle_threads(void) { return omp_get_max_threads(); }
+
 /* ---------------------------------------------------------------------- */
 /* Batch drivers: the same steps for every (sequence, head) stream, one
  * OpenMP iteration per stream.  elt_bytes of K/V follows dtype. */
@@ -227,19 +231,18 @@ void eta_oracle_meta_batch(int B, int H, int d, int b, int cap, int dtype,
   }
 }
 
-/* One decode step for a batch: threshold, screen, attention.  Outputs:
- * tau/tau_screen [B][H], score [B][H][nbcap] (complete blocks only),
- * active [B][H][nbcap], cnt [B][H] admitted blocks, tokens [B][H] admitted
- * keys, out [B][H][d]. */
-void eta_oracle_step_batch(int B, int H, int d, int b, int cap, int dtype,
-                           const int32_t* seq_len, const float* q, const void* K,
-                           const void* V, const double* mu, const double* var,
-                           const double* maxnorm, const float* W, const float* bias_or_c,
-                           double a, double z, double scale, int mode, double beta,
-                           double* tau, double* tau_screen, double* score,
-                           uint8_t* active, int32_t* cnt, int64_t* tokens, double* out) {
+/* Screen and attention for a batch, given the thresholds (fp64):
+ * score [B][H][nbcap] (complete blocks only, NaN elsewhere), active
+ * [B][H][nbcap], cnt [B][H] admitted blocks, tokens [B][H] admitted keys,
+ * out [B][H][d]. */
+void eta_oracle_screen_attend_batch(int B, int H, int d, int b, int cap, int dtype,
+                                    const int32_t* seq_len, const float* q, const void* K,
+                                    const void* V, const double* mu, const double* var,
+                                    const double* maxnorm, const double* tau,
+                                    const double* tau_screen, double z, double scale, int mode,
+                                    double beta, double* score, uint8_t* active, int32_t* cnt,
+                                    int64_t* tokens, double* out) {
   int nbcap = (cap + b - 1) / b;
-  eta_oracle_predict_tau(B, H, d, q, W, bias_or_c, a, tau, tau_screen);
 #pragma omp parallel for schedule(dynamic, 1)
   for (int u = 0; u < B * H; ++u) {
     int T = seq_len[u / H];
@@ -260,6 +263,20 @@ void eta_oracle_step_batch(int B, int H, int d, int b, int cap, int dtype,
     eta_oracle_attend(qu, (const char*)K + kv_off, (const char*)V + kv_off, dtype, T, d, b,
                       act, mode, beta, tau[u], scale, out + (size_t)u * d);
   }
+}
+
+/* One decode step for a batch: threshold (Eq. 1), then screen and attention. */
+void eta_oracle_step_batch(int B, int H, int d, int b, int cap, int dtype,
+                           const int32_t* seq_len, const float* q, const void* K,
+                           const void* V, const double* mu, const double* var,
+                           const double* maxnorm, const float* W, const float* bias_or_c,
+                           double a, double z, double scale, int mode, double beta,
+                           double* tau, double* tau_screen, double* score,
+                           uint8_t* active, int32_t* cnt, int64_t* tokens, double* out) {
+  eta_oracle_predict_tau(B, H, d, q, W, bias_or_c, a, tau, tau_screen);
+  eta_oracle_screen_attend_batch(B, H, d, b, cap, dtype, seq_len, q, K, V, mu, var, maxnorm,
+                                 tau, tau_screen, z, scale, mode, beta, score, active, cnt,
+                                 tokens, out);
 }
 
 /* Attention of every stream over a given admission mask (used to re-evaluate

@@ -1,0 +1,193 @@
+"""Helpers of the GPU parity tests: run the HIP path through the C ABI and the
+fp64 oracle on the same seeded inputs and compare them.
+
+Bars (from the decode path's statement):
+  - admission mask: bit-exact, except blocks whose oracle score lies within
+    1e-5 * max(1, |tau|) of the screening threshold; those are reported and
+    may number at most 0.1% of the screened blocks;
+  - outputs, per (sequence, head): max|o_gpu - o_ref| <= tol * max|o_ref|,
+    tol = 1e-5 for a float32 cache and 2e-2 for a bfloat16 cache, with o_ref
+    evaluated by the oracle on the GPU's mask when allowed near-tie flips
+    occurred.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+import oracle
+from long_context_decode_eta_amd import binding as eb
+from long_context_decode_eta_amd import synth
+
+OUT_TOL = {torch.float32: 1e-5, torch.bfloat16: 2e-2}
+BAND_REL = 1e-5
+MAX_FLIP_FRAC = 1e-3
+
+
+def note(msg: str) -> None:
+    print(msg, flush=True)
+
+
+def to_gpu(w: synth.Workload) -> synth.Workload:
+    """Move a workload's tensors to cuda:0 (in place)."""
+    for name in ("q", "k", "v", "seq_len", "W", "tau_const", "q_cal"):
+        t = getattr(w, name)
+        if t is not None:
+            setattr(w, name, t.to("cuda"))
+    return w
+
+
+def make_cache(w: synth.Workload) -> eb.KVCache:
+    c = eb.KVCache(w.B, w.H, w.D, w.block, w.cap, w.kv_dtype, device="cuda", k=w.k, v=w.v)
+    c.seq_len.copy_(w.seq_len.to(torch.int32))
+    return c
+
+
+@dataclass
+class GpuResult:
+    tau_gate: np.ndarray
+    tau_screen: np.ndarray
+    idx: np.ndarray
+    cnt: np.ndarray
+    density: int
+    out: np.ndarray
+    mask: np.ndarray
+
+
+def gpu_mask(idx: np.ndarray, cnt: np.ndarray, nbcap: int) -> np.ndarray:
+    B, H = cnt.shape
+    m = np.zeros((B, H, nbcap), np.uint8)
+    for b in range(B):
+        for h in range(H):
+            sel = idx[b, h, : cnt[b, h]]
+            assert np.all(np.diff(sel) > 0), "active list not strictly ascending"
+            assert sel.size == 0 or (sel[0] >= 0 and sel[-1] < nbcap)
+            m[b, h, sel] = 1
+    return m
+
+
+def run_gpu(cache: eb.KVCache, q, *, W=None, bias_or_c=None, z, scale, mode=eb.GATED,
+            beta=5.0, a=0.0, split=16, build_meta=True) -> GpuResult:
+    if build_meta:
+        eb.build_block_meta(cache)
+    dec = eb.Decoder(cache, z=z, scale=scale, beta=beta, a=a, logit_mode=mode,
+                     blocks_per_split=split)
+    dec.step(q, W, bias_or_c)
+    torch.cuda.synchronize()
+    idx = dec.active_idx.cpu().numpy()
+    cnt = dec.active_cnt.cpu().numpy()
+    return GpuResult(dec.tau_gate.cpu().numpy(), dec.tau_screen.cpu().numpy(), idx, cnt,
+                     int(dec.density_ctr.cpu().item()), dec.out.cpu().numpy(),
+                     gpu_mask(idx, cnt, cache.cap_blocks))
+
+
+def gpu_tokens(cnt: np.ndarray, seq_len: np.ndarray, b: int) -> np.ndarray:
+    """Admitted tokens per stream implied by the GPU counts (the last block,
+    possibly partial, is always in the list)."""
+    T = seq_len[:, None].astype(np.int64)
+    nb = -(-T // b)
+    tail = T - (nb - 1) * b
+    return np.where(cnt > 0, (cnt.astype(np.int64) - 1) * b + tail, 0)
+
+
+def close(a, b, rel, what, atol=None):
+    """|a - b| <= rel * max(1, |b|) (+ atol, elementwise, when given); equal
+    infinities compare equal, any NaN or infinity mismatch fails."""
+    a = np.asarray(a, np.float64); b = np.asarray(b, np.float64)
+    fin = np.isfinite(a) & np.isfinite(b)
+    lim = rel * np.maximum(1.0, np.abs(b)) + (0.0 if atol is None else atol)
+    with np.errstate(invalid="ignore"):
+        bad = np.where(fin, np.abs(a - b) > lim, ~(a == b))
+    if np.any(bad):
+        i = np.argwhere(bad)[0]
+        raise AssertionError(f"{what}: {bad.sum()} entries off, first at {tuple(i)}: "
+                             f"gpu {a[tuple(i)]!r} vs oracle {b[tuple(i)]!r}")
+
+
+def compare_masks(o_active, o_score, o_tau_screen, g_mask, seq_len, b):
+    """Returns (n_flips, n_screened); asserts every flip is a near tie."""
+    B, H, nbcap = g_mask.shape
+    flips, screened = 0, 0
+    for bb in range(B):
+        T = int(seq_len[bb])
+        nb = -(-T // b) if T > 0 else 0
+        screened += H * (T // b)
+        for h in range(H):
+            diff = np.nonzero(g_mask[bb, h, :nb] != o_active[bb, h, :nb])[0]
+            for j in diff:
+                s, t = o_score[bb, h, j], o_tau_screen[bb, h]
+                if not (abs(s - t) <= BAND_REL * max(1.0, abs(t))):
+                    raise AssertionError(
+                        f"mask mismatch outside the near-tie band at (b={bb}, h={h}, block {j}): "
+                        f"oracle score {s!r}, tau {t!r}, gpu {g_mask[bb, h, j]}, "
+                        f"oracle {o_active[bb, h, j]}")
+                flips += 1
+            assert not np.any(g_mask[bb, h, nb:]), "admitted block beyond the stream"
+    assert flips <= math.floor(MAX_FLIP_FRAC * screened), (flips, screened)
+    if flips:
+        note(f"  near-tie flips: {flips} of {screened} screened blocks")
+    return flips, screened
+
+
+def compare_outputs(g_out, o_out, kv_dtype, what="out"):
+    tol = OUT_TOL[kv_dtype]
+    worst = 0.0
+    B, H, _ = g_out.shape
+    for bb in range(B):
+        for h in range(H):
+            ref = o_out[bb, h]
+            den = np.abs(ref).max()
+            err = np.abs(g_out[bb, h] - ref).max()
+            if den == 0.0:
+                assert err == 0.0, f"{what}[{bb},{h}]: expected zeros"
+                continue
+            rel = err / den
+            worst = max(worst, rel)
+            assert rel <= tol, f"{what}[{bb},{h}]: rel err {rel:.3e} > {tol:.0e}"
+    return worst
+
+
+def host_kv(w: synth.Workload):
+    return synth.kv_numpy(w.k), synth.kv_numpy(w.v)
+
+
+def check_against_oracle(w: synth.Workload, g: GpuResult, cache: eb.KVCache, *, W, bias_or_c,
+                         z, scale, mode, beta=5.0, a=0.0, check_meta=True, K=None, V=None):
+    """Full (every stream) comparison; returns a dict of the worst errors."""
+    if K is None:
+        K, V = host_kv(w)
+    sl = w.seq_len.cpu().numpy().astype(np.int32)
+    q = w.q.cpu().numpy()
+    meta = oracle.meta_batch(K, sl, w.block)
+    Wn = None if W is None else W.cpu().numpy()
+    cn = bias_or_c.cpu().numpy()
+    r = oracle.step_batch(q, K, V, sl, w.block, meta, Wn, cn, a=a, z=z, scale=scale,
+                          mode=mode, beta=beta)
+    stats = {}
+    if check_meta:
+        mu = cache.mu.cpu().numpy(); var = cache.var.cpu().numpy(); M = cache.maxnorm.cpu().numpy()
+        for bb in range(w.B):
+            nbc = int(sl[bb]) // w.block
+            close(mu[bb, :, :nbc], meta[0][bb, :, :nbc], 1e-5, "mu")
+            close(var[bb, :, :nbc], meta[1][bb, :, :nbc], 1e-5, "var")
+            close(M[bb, :, :nbc], meta[2][bb, :, :nbc], 1e-5, "maxnorm")
+    close(g.tau_gate, r["tau"], 1e-5, "tau_gate")
+    close(g.tau_screen, r["tau_screen"], 1e-5, "tau_screen")
+    flips, screened = compare_masks(r["active"], r["score"], r["tau_screen"], g.mask, sl, w.block)
+    toks = gpu_tokens(g.cnt, sl, w.block)
+    assert g.density == int(toks.sum()), (g.density, int(toks.sum()))
+    if flips == 0:
+        np.testing.assert_array_equal(g.cnt, r["cnt"])
+        np.testing.assert_array_equal(toks, r["tokens"])
+        ref = r["out"]
+    else:
+        ref = oracle.attend_batch(q, K, V, sl, w.block, g.mask, r["tau"], mode=mode, beta=beta,
+                                  scale=scale)
+    stats["out_rel"] = compare_outputs(g.out, ref, w.kv_dtype)
+    stats["flips"] = flips
+    stats["screened"] = screened
+    stats["density"] = float(toks.sum()) / max(1, int(sl.sum()) * w.H)
+    return stats

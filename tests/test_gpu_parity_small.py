@@ -1,0 +1,175 @@
+"""GPU parity on small cases: every stream checked against the fp64 oracle.
+
+Runs the HIP path (libeta.so) through its C ABI.  Cases: the hand example
+(b=4, T=16, zero-padded to d=64), the tiny fp32 workload (B=1, H=4, d=64,
+T=2048, b=16, z=1.5, frozen tau), ragged lengths with NaN-filled unused slots
+for every block size and head size, threshold extremes, split-size
+invariance, determinism, the threshold predictor and the dense baseline.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from long_context_decode_eta_amd import binding as eb
+from long_context_decode_eta_amd import synth
+from parity import (check_against_oracle, compare_outputs, close, make_cache, note, run_gpu,
+                    to_gpu)
+
+pytestmark = pytest.mark.gpu
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+@pytest.fixture(autouse=True)
+def _name(request):
+    note(f"[gpu] {request.node.name}")
+
+
+# --------------------------------------------------------------------------
+def hand_cache():
+    ex = json.load(open(os.path.join(HERE, "golden", "hand_b4_t16.json")))
+    K = np.zeros((1, 1, 16, 64), np.float32); K[0, 0, :, :4] = np.array(ex["K"], np.float32)
+    V = np.zeros((1, 1, 16, 64), np.float32)
+    V[0, 0, :, :4] = np.array([[s, 1, s % 2, s // 4] for s in range(16)], np.float32)
+    q = np.zeros((1, 1, 64), np.float32); q[0, 0, :4] = ex["q"]
+    w = synth.Workload(name="hand", B=1, H=1, D=64, block=4, cap=16, z=1.0,
+                       kv_dtype=torch.float32, seq_len=torch.tensor([16], dtype=torch.int32),
+                       q=torch.from_numpy(q), k=torch.from_numpy(K), v=torch.from_numpy(V),
+                       tau_kind="frozen")
+    return w
+
+
+@pytest.mark.parametrize("mode", [eb.GATED, eb.RAW])
+@pytest.mark.parametrize("z,tau", [(1.0, -math.inf), (1.0, 0.5), (1.0, 0.6), (1.0, 0.8),
+                                   (1.0, 3.0), (2.0, 0.8), (2.0, 1.2), (math.inf, 1.2),
+                                   (1.0, math.inf)])
+def test_hand_example(z, tau, mode):
+    w = to_gpu(hand_cache())
+    cache = make_cache(w)
+    c = torch.full((1,), tau, dtype=torch.float32, device="cuda")
+    g = run_gpu(cache, w.q, bias_or_c=c, z=z, scale=0.5, mode=mode, split=1)
+    st = check_against_oracle(w, g, cache, W=None, bias_or_c=c, z=z, scale=0.5, mode=mode)
+    assert st["flips"] == 0
+    assert g.out[0, 0, 1] == pytest.approx(1.0, abs=1e-6)
+    assert np.all(g.out[0, 0, 4:] == 0)
+
+
+@pytest.mark.parametrize("mode", [eb.GATED, eb.RAW])
+@pytest.mark.parametrize("split", [1, 7, 16, 128])
+def test_tiny_workload(mode, split):
+    w = to_gpu(synth.make("tiny", seed=1234))
+    cache = make_cache(w)
+    g = run_gpu(cache, w.q, bias_or_c=w.tau_const, z=w.z, scale=w.scale, mode=mode, split=split)
+    st = check_against_oracle(w, g, cache, W=None, bias_or_c=w.tau_const, z=w.z, scale=w.scale,
+                              mode=mode)
+    note(f"  density {st['density']:.3f} out_rel {st['out_rel']:.2e} flips {st['flips']}")
+    assert 0.0 < st["density"] < 1.0
+
+
+LENS = [0, 1, 3, 127, 128, 129, 700, 1024]
+
+
+@pytest.mark.parametrize("kv", ["bf16", "f32"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("block", [4, 8, 16, 32, 64, 128])
+def test_ragged_edges(kv, D, block):
+    # Lengths around block boundaries, an empty stream, unused slots NaN-filled.
+    name = "tiny" if D == 64 else "ctx32k"
+    w = synth.make(name, seed=7 + block, T=LENS, B=len(LENS), H=3, cap=1024, pad="nan",
+                   block=block, kv=kv)
+    to_gpu(w)
+    cache = make_cache(w)
+    c = torch.tensor([0.2, 0.6, 1.0], dtype=torch.float32, device="cuda")
+    for mode in (eb.GATED, eb.RAW):
+        g = run_gpu(cache, w.q, bias_or_c=c, z=1.0, scale=w.scale, mode=mode, split=3)
+        st = check_against_oracle(w, g, cache, W=None, bias_or_c=c, z=1.0, scale=w.scale,
+                                  mode=mode)
+        assert not np.isnan(g.out).any()
+        assert np.all(g.out[0] == 0)  # the empty stream
+    note(f"  density {st['density']:.3f} out_rel {st['out_rel']:.2e}")
+
+
+@pytest.mark.parametrize("tau", [math.inf, -math.inf])
+def test_threshold_extremes(tau):
+    w = to_gpu(synth.make("ctx128k", seed=3, T=(100, 3000), B=4, H=2, cap=3000, block=32))
+    cache = make_cache(w)
+    c = torch.full((2,), tau, dtype=torch.float32, device="cuda")
+    g = run_gpu(cache, w.q, bias_or_c=c, z=1.0, scale=w.scale, split=8)
+    sl = w.seq_len.cpu().numpy()
+    nb = -(-sl // 32)
+    if tau == math.inf:
+        assert np.all(g.cnt == 1)
+        for b in range(4):
+            assert np.all(g.idx[b, :, 0] == nb[b] - 1)
+    else:
+        assert np.all(g.cnt == nb[:, None])
+    check_against_oracle(w, g, cache, W=None, bias_or_c=c, z=1.0, scale=w.scale, mode=eb.GATED)
+
+
+def test_split_invariance_and_determinism():
+    w = to_gpu(synth.make("ctx128k", seed=11, T=(2000, 9000), B=3, H=4, cap=9000))
+    cache = make_cache(w)
+    eb.build_block_meta(cache)
+    c = torch.full((4,), 1.2, dtype=torch.float32, device="cuda")
+    outs, masks = {}, {}
+    for split in (1, 2, 5, 16, 64, 4096):
+        for rep in range(2):
+            g = run_gpu(cache, w.q, bias_or_c=c, z=1.0, scale=w.scale, split=split,
+                        build_meta=False)
+            if rep:
+                assert np.array_equal(g.out, outs[split]), "run-to-run difference"
+            outs[split], masks[split] = g.out, g.mask
+    ref = outs[1]
+    for split, o in outs.items():
+        assert np.array_equal(masks[split], masks[1])
+        np.testing.assert_allclose(o, ref, rtol=2e-6, atol=2e-6)
+
+
+def test_predictor_dynamic_and_frozen():
+    rng = np.random.default_rng(5)
+    for B, H, D in [(1, 4, 64), (8, 16, 128), (3, 5, 64), (2, 256, 64)]:
+        q = rng.standard_normal((B, H, D)).astype(np.float32)
+        W = (rng.standard_normal((H * D, H)) / math.sqrt(D)).astype(np.float32)
+        bias = rng.standard_normal(H).astype(np.float32)
+        for Wm in (W, None):
+            tg = torch.zeros((B, H), device="cuda"); ts = torch.zeros_like(tg)
+            eb.predict_tau(torch.from_numpy(q).cuda(), None if Wm is None else
+                           torch.from_numpy(Wm).cuda(), torch.from_numpy(bias).cuda(), 0.375,
+                           tg, ts)
+            tau, tsc = oracle.predict_tau(q, Wm, bias, a=0.375)
+            # fp32 forward-error bound of the kernel's sum: each thread adds
+            # ceil(H*D/G) products, then G partials and the bias are added
+            # (G = 256 // H), so |err| <= depth * 2^-24 * sum_j |q_j W_jh| (+|b|).
+            atol = None
+            if Wm is not None:
+                G = 256 // H
+                depth = -(-(H * D) // G) + G + 2
+                l1 = np.abs(q.reshape(B, H * D).astype(np.float64)) @ np.abs(Wm.astype(np.float64))
+                atol = depth * 2.0**-24 * (l1 + np.abs(bias))
+            close(tg.cpu().numpy(), tau, 1e-5, "tau", atol)
+            close(ts.cpu().numpy(), tsc, 1e-5, "tau_screen", atol)
+
+
+def test_predictor_zero_init():
+    q = torch.randn((2, 4, 64), device="cuda")
+    W = torch.zeros((256, 4), device="cuda")
+    tg = torch.zeros((2, 4), device="cuda"); ts = torch.zeros_like(tg)
+    eb.predict_tau(q, W, torch.full((4,), -8.0, device="cuda"), 0.0, tg, ts)
+    assert torch.all(tg == -8.0) and torch.all(ts == -8.0)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "f32"])
+def test_dense_decode(kv):
+    w = to_gpu(synth.make("ragged", seed=9, T=(1, 5000), B=5, H=3, cap=5000, kv=kv, pad="nan"))
+    cache = make_cache(w)
+    out = torch.zeros((5, 3, 128), device="cuda")
+    ws = eb.workspace(eb.decode_workspace_bytes(5, 3, 128, cache.cap_blocks, 8))
+    eb.dense_decode(cache, w.q, w.scale, 8, ws, out)
+    torch.cuda.synchronize()
+    K, V = synth.kv_numpy(w.k), synth.kv_numpy(w.v)
+    ref = oracle.dense_batch(w.q.cpu().numpy(), K, V, w.seq_len.cpu().numpy(), scale=w.scale)
+    compare_outputs(out.cpu().numpy(), ref, w.kv_dtype, "dense")

@@ -40,8 +40,8 @@ int ilog2(int b) {
 // every flattened grid below 2^31.
 constexpr long long kMaxGrid = 0x7fffffffLL;
 
-// Validates the cache descriptor.  `need_data` requires the K/V/statistics
-// pointers (all calls but none currently skip them for a non-empty problem).
+// Validates the cache descriptor; for a non-empty problem every data pointer
+// must be set.
 eta_status check_cache(const eta_cache* c, eta::CacheView* v) {
   if (!c) return fail(ETA_ERR_NULL_PTR, "cache descriptor is NULL");
   if (c->batch < 0 || c->heads < 0)
@@ -87,11 +87,33 @@ eta_status hip_status(hipError_t e, const char* what) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Decode workspace: [queue counter | chunk_start[units+1] | part_m | part_l |
+// part_acc], each 256-byte aligned.
 size_t decode_ws(long long units, int D, int cap_blocks, int split) {
   const long long maxc = (cap_blocks + split - 1) / split;
   const size_t slots = (size_t)units * (size_t)maxc;
-  return align256(slots * 4) * 2 + align256(slots * (size_t)D * 4);
+  return 256 + align256((size_t)(units + 1) * 4) + align256(slots * 4) * 2 +
+         align256(slots * (size_t)D * 4);
 }
+
+// Compute units of the current device (a device property, cached per device).
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+#ifndef ETA_QUEUE_WGS_PER_CU
+#define ETA_QUEUE_WGS_PER_CU 8
+#endif
 
 bool bad_float(float x) { return x != x; }
 
@@ -227,6 +249,8 @@ static eta_status decode_common(const eta_cache* c, const float* q, const float*
     return fail(ETA_ERR_WORKSPACE, "decode workspace %zu bytes < %zu", ws_bytes, need);
   const size_t slots = (size_t)units * maxc;
   char* w = static_cast<char*>(ws);
+  const size_t off_start = 256;
+  const size_t off_parts = off_start + align256((size_t)(units + 1) * 4);
   eta::DecodeArgs a;
   a.q = q;
   a.tau = tau_gate;
@@ -238,10 +262,16 @@ static eta_status decode_common(const eta_cache* c, const float* q, const float*
   a.scale = scale;
   a.split = split;
   a.max_chunks = maxc;
-  a.part_m = reinterpret_cast<float*>(w);
-  a.part_l = reinterpret_cast<float*>(w + align256(slots * 4));
-  a.part_acc = reinterpret_cast<float*>(w + 2 * align256(slots * 4));
+  a.part_m = reinterpret_cast<float*>(w + off_parts);
+  a.part_l = reinterpret_cast<float*>(w + off_parts + align256(slots * 4));
+  a.part_acc = reinterpret_cast<float*>(w + off_parts + 2 * align256(slots * 4));
   a.out = out;
+  // The queue kernel keeps the chunk table and one chunk's block list in LDS.
+  const bool queue = units <= eta::kMaxQueueUnits &&
+                     (size_t)(units + 1) * 4 + (size_t)split * 4 <= 48 * 1024;
+  a.queue = queue ? reinterpret_cast<int*>(w) : nullptr;
+  a.chunk_start = reinterpret_cast<int*>(w + off_start);
+  a.queue_grid = device_cus() * ETA_QUEUE_WGS_PER_CU;
   return hip_status(eta::launch_decode(v, a, (hipStream_t)stream), "eta_decode launch");
 }
 

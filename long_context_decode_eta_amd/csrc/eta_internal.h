@@ -51,6 +51,19 @@ __device__ __forceinline__ void widen(const uint4& r, float* x) {
 
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
+// Streaming 128-bit load with the nontemporal hint: data read once per step
+// (K/V rows, block statistics) should not displace reusable lines in L2/MALL.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld16_nt(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ float4 ld16f_nt(const float* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
+                     __uint_as_float(v.w));
+}
+
 // ---------------------------------------------------------------------------
 // Lane-group all-reductions.  Groups are aligned runs of N lanes.  The DPP
 // patterns used (quad xor-1, quad xor-2, half-row mirror, row mirror) pair
@@ -134,7 +147,12 @@ struct DecodeArgs {
   float* part_l;   // [B*H][max_chunks]
   float* part_acc; // [B*H][max_chunks][D]
   float* out;
+  int* queue;        // work counter of the queue kernel (NULL: flat grid)
+  int* chunk_start;  // [B*H + 1] chunk offsets of the queue kernel
+  int queue_grid;    // work-groups of the queue kernel
 };
+// Streams up to which the queue kernel is used (its chunk table lives in LDS).
+constexpr int kMaxQueueUnits = 8192;
 hipError_t launch_decode(const CacheView& c, const DecodeArgs& a, hipStream_t s);
 hipError_t launch_calibrate(const CacheView& c, int n_sets, const float* q_sets,
                             const float* tau0, float z, float scale, float rho, float* values,

@@ -20,7 +20,10 @@
 
 namespace eta {
 
-constexpr int kRows = 32;  // rows per wave tile
+#ifndef ETA_DECODE_ROWS
+#define ETA_DECODE_ROWS 16
+#endif
+constexpr int kRows = ETA_DECODE_ROWS;  // rows per wave tile
 
 __device__ __forceinline__ float fexp(float x) {
   return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
@@ -40,29 +43,29 @@ __device__ __forceinline__ void merge_state(float& m, float& l, float* a, float 
   m = mn;
 }
 
+// Attention of one chunk (chunk k of stream u) by the whole work-group.  The
+// chunk's block indices are first staged in LDS (s_list), so no key or value
+// load ever waits on an index load.  Writes the final output when the chunk is
+// the stream's only one, else the partial (max, sum, weighted V).
 template <int D, int DT, int MODE, bool DENSE>
-__global__ __launch_bounds__(256) void decode_kernel(CacheView c, DecodeArgs a) {
+__device__ __forceinline__ void chunk_attend(const CacheView& c, const DecodeArgs& a, int u, int k,
+                                             int T, int cnt, int* s_list, float (*s_acc)[D],
+                                             float (*s_ml)[2]) {
   constexpr int EPL = Elt<DT>::kPer16B;
   constexpr int LPR = D / EPL;
   constexpr int RPI = kWave / LPR;
   constexpr int NI = (kRows / RPI) > 0 ? (kRows / RPI) : 1;
   constexpr int RB = D * Elt<DT>::kBytes;
-  __shared__ float s_acc[4][D];
-  __shared__ float s_ml[4][2];
-
-  const int units = c.B * c.H;
-  const int u = blockIdx.x % units, k = blockIdx.x / units;
-  const int T = c.seq_len[u / c.H];
-  if (T <= 0) return;
   const int nb = (T + c.bs - 1) >> c.log2bs;
-  // The list is trusted only as far as it stays inside the stream.
-  const int cnt = DENSE ? nb : min(a.active_cnt[u], nb);
   const int first = k * a.split;
-  if (first >= cnt) return;
   const int nblk = min(a.split, cnt - first);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane / LPR, li = lane % LPR;
 
+  if constexpr (!DENSE) {
+    const int32_t* list = a.active_idx + (size_t)u * c.cap_blocks + first;
+    for (int i = threadIdx.x; i < nblk; i += blockDim.x) s_list[i] = list[i];
+  }
   float qs[EPL];
   {
     const float* qu = a.q + (size_t)u * D + li * EPL;
@@ -71,9 +74,9 @@ __global__ __launch_bounds__(256) void decode_kernel(CacheView c, DecodeArgs a) 
   }
   const float tau = (MODE == ETA_LOGIT_GATED) ? a.tau[u] : 0.f;
   const float beta = a.beta;
-  const int32_t* list = DENSE ? nullptr : a.active_idx + (size_t)u * c.cap_blocks + first;
   const char* kb = static_cast<const char*>(c.k) + (size_t)u * c.cap * RB + li * 16;
   const char* vb = static_cast<const char*>(c.v) + (size_t)u * c.cap * RB + li * 16;
+  __syncthreads();
 
   float m = -__builtin_inff(), l = 0.f, acc[EPL];
 #pragma unroll
@@ -81,28 +84,32 @@ __global__ __launch_bounds__(256) void decode_kernel(CacheView c, DecodeArgs a) 
 
   const int rows = nblk << c.log2bs;
   const int ntiles = (rows + NI * RPI - 1) / (NI * RPI);
-  for (int t = wave; t < ntiles; t += 4) {
-    uint4 kr[NI], vr[NI];
-    int sp[NI];
+
+  // Issue the K and V loads of tile t (rows t*NI*RPI ... of the chunk).
+  auto fetch = [&](int t, uint4* kr, uint4* vr, int* sp) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int rr = (t * NI + i) * RPI + g;  // row within the chunk
       int s = -1;
       if (rr < rows) {
         const int p = rr >> c.log2bs;
-        const int j = DENSE ? first + p : list[p];
+        const int j = DENSE ? first + p : s_list[p];
         s = (j << c.log2bs) + (rr & (c.bs - 1));
+        // The list is trusted only as far as it stays inside the stream.
         if ((unsigned)j >= (unsigned)nb || s >= T) s = -1;
       }
       sp[i] = s;
       if (s >= 0) {
-        kr[i] = ld16(kb + (size_t)s * RB);
-        vr[i] = ld16(vb + (size_t)s * RB);
+        kr[i] = ld16_nt(kb + (size_t)s * RB);
+        vr[i] = ld16_nt(vb + (size_t)s * RB);
       } else {
         kr[i] = make_uint4(0, 0, 0, 0);
         vr[i] = make_uint4(0, 0, 0, 0);
       }
     }
+  };
+  // Fold one loaded tile into the running (m, l, acc).
+  auto consume = [&](const uint4* kr, const uint4* vr, const int* sp) {
     float lg[NI];
     float tmax = -__builtin_inff();
 #pragma unroll
@@ -135,6 +142,19 @@ __global__ __launch_bounds__(256) void decode_kernel(CacheView c, DecodeArgs a) 
       for (int e = 0; e < EPL; ++e) acc[e] = fmaf(p, y[e], acc[e]);
     }
     m = mn;
+  };
+
+  // Two register buffers: the loads of a wave's next tile are in flight while
+  // its current tile is folded in.
+  uint4 ka[NI], va[NI], kq[NI], vq[NI];
+  int sa[NI], sq[NI];
+  if (wave < ntiles) fetch(wave, ka, va, sa);
+  for (int t = wave; t < ntiles; t += 8) {
+    const bool has_b = t + 4 < ntiles;
+    if (has_b) fetch(t + 4, kq, vq, sq);
+    consume(ka, va, sa);
+    if (t + 8 < ntiles) fetch(t + 8, ka, va, sa);
+    if (has_b) consume(kq, vq, sq);
   }
 
   // Merge the RPI row groups of the wave (xor butterfly: partners end equal).
@@ -178,17 +198,113 @@ __global__ __launch_bounds__(256) void decode_kernel(CacheView c, DecodeArgs a) 
   }
 }
 
+__device__ __forceinline__ int stream_chunks(const CacheView& c, const DecodeArgs& a, int u,
+                                             int* T_out, int* cnt_out) {
+  const int T = c.seq_len[u / c.H];
+  const int nb = T > 0 ? (T + c.bs - 1) >> c.log2bs : 0;
+  const int cnt = a.dense ? nb : max(0, min(a.active_cnt[u], nb));
+  *T_out = T;
+  *cnt_out = cnt;
+  return (cnt + a.split - 1) / a.split;
+}
+
+// Work list of the queue kernel: chunk_start[u] = number of chunks of streams
+// before u (exclusive scan, chunk_start[units] = total), and the queue counter
+// set to 0.  One work-group; streams in rounds of 1024 with a running carry.
+__global__ __launch_bounds__(1024) void decode_prepare_kernel(CacheView c, DecodeArgs a) {
+  __shared__ int scan[1024];
+  __shared__ int carry;
+  const int units = c.B * c.H, t = threadIdx.x;
+  if (t == 0) {
+    carry = 0;
+    a.queue[0] = 0;
+  }
+  __syncthreads();
+  for (int base = 0; base < units; base += 1024) {
+    const int u = base + t;
+    int T, cnt;
+    const int n = u < units ? stream_chunks(c, a, u, &T, &cnt) : 0;
+    scan[t] = n;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+      const int add = t >= off ? scan[t - off] : 0;
+      __syncthreads();
+      scan[t] += add;
+      __syncthreads();
+    }
+    if (u < units) a.chunk_start[u] = carry + scan[t] - n;
+    __syncthreads();
+    if (t == 1023) carry += scan[1023];
+    __syncthreads();
+  }
+  if (t == 0) a.chunk_start[units] = carry;
+}
+
+// Persistent decode: every work-group repeatedly takes the next chunk from a
+// global atomic queue (so the grid never holds empty work-groups and every CU
+// stays busy until the work runs out).  The next index is fetched while the
+// current chunk is processed.  Chunk -> stream by binary search of the
+// chunk_start table held in LDS.
+template <int D, int DT, int MODE, bool DENSE>
+__global__ __launch_bounds__(256) void decode_queue_kernel(CacheView c, DecodeArgs a) {
+  extern __shared__ int s_dyn[];
+  __shared__ float s_acc[4][D];
+  __shared__ float s_ml[4][2];
+  __shared__ int s_next;
+  const int units = c.B * c.H;
+  int* s_start = s_dyn;                // units + 1
+  int* s_list = s_dyn + units + 1;     // split
+  for (int i = threadIdx.x; i <= units; i += blockDim.x) s_start[i] = a.chunk_start[i];
+  if (threadIdx.x == 0) s_next = atomicAdd(a.queue, 1);
+  __syncthreads();
+  const int total = s_start[units];
+  int item = s_next;
+  while (item < total) {
+    __syncthreads();  // everyone has read s_next
+    if (threadIdx.x == 0) s_next = atomicAdd(a.queue, 1);
+    int lo = 0, hi = units - 1;  // last u with s_start[u] <= item
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_start[mid] <= item) lo = mid; else hi = mid - 1;
+    }
+    const int u = lo, k = item - s_start[u];
+    int T, cnt;
+    stream_chunks(c, a, u, &T, &cnt);
+    chunk_attend<D, DT, MODE, DENSE>(c, a, u, k, T, cnt, s_list, s_acc, s_ml);
+    __syncthreads();  // LDS reuse; s_next is visible
+    item = s_next;
+  }
+}
+
+// Flat-grid decode for very many streams: one work-group per possible chunk,
+// blockIdx.x = u * max_chunks + k (a stream's chunks are dispatched together,
+// which measured faster than chunk-major order); work-groups past a stream's
+// last chunk exit.
+template <int D, int DT, int MODE, bool DENSE>
+__global__ __launch_bounds__(256) void decode_grid_kernel(CacheView c, DecodeArgs a) {
+  extern __shared__ int s_list[];
+  __shared__ float s_acc[4][D];
+  __shared__ float s_ml[4][2];
+  const int u = blockIdx.x / a.max_chunks, k = blockIdx.x % a.max_chunks;
+  int T, cnt;
+  const int nch = stream_chunks(c, a, u, &T, &cnt);
+  if (k >= nch) return;
+  chunk_attend<D, DT, MODE, DENSE>(c, a, u, k, T, cnt, s_list, s_acc, s_ml);
+}
+
 // Log-sum-exp combine of the chunk partials of one stream; also writes the
-// zero output of empty streams.  Thread t owns column t % D and the chunks
-// t / D, t / D + G, ... (G = 256 / D); the G partial sums are added in a fixed
-// order.
+// zero output of empty streams.  One work-group per stream: wave w folds
+// chunks w, w+4, ... into a running (max, sum, weighted V) in one pass, with
+// kInflight chunks loaded before any of them is used; lane i owns columns
+// [i*CPL, i*CPL+CPL).  The 4 wave states are merged in a fixed order.
+constexpr int kInflight = 8;
 template <int D>
 __global__ __launch_bounds__(256) void combine_kernel(CacheView c, DecodeArgs a) {
-  __shared__ float s_red[256];
-  __shared__ float s_a[256 / D][D];
-  __shared__ float s_l[256 / D];
-  constexpr int G = 256 / D;
+  constexpr int CPL = D / kWave;
+  __shared__ float s_acc[4][D];
+  __shared__ float s_ml[4][2];
   const int u = blockIdx.x, t = threadIdx.x;
+  const int wave = t >> 6, lane = t & 63;
   const int T = c.seq_len[u / c.H];
   if (T <= 0) {
     if (t < D) a.out[(size_t)u * D + t] = 0.f;
@@ -204,46 +320,75 @@ __global__ __launch_bounds__(256) void combine_kernel(CacheView c, DecodeArgs a)
   if (nch <= 1) return;  // written by the decode kernel
   const float* pm = a.part_m + (size_t)u * a.max_chunks;
   const float* pl = a.part_l + (size_t)u * a.max_chunks;
-  const float* pa = a.part_acc + (size_t)u * a.max_chunks * D;
-  float mx = -__builtin_inff();
-  for (int ch = t; ch < nch; ch += 256) mx = fmaxf(mx, pm[ch]);
-  s_red[t] = mx;
-  __syncthreads();
-  for (int off = 128; off > 0; off >>= 1) {
-    if (t < off) s_red[t] = fmaxf(s_red[t], s_red[t + off]);
-    __syncthreads();
+  const float* pa = a.part_acc + (size_t)u * a.max_chunks * D + lane * CPL;
+  float m = -__builtin_inff(), l = 0.f, acc[CPL];
+#pragma unroll
+  for (int e = 0; e < CPL; ++e) acc[e] = 0.f;
+  for (int base = wave; base < nch; base += 4 * kInflight) {
+    float mc[kInflight], lc[kInflight], ac[kInflight][CPL];
+#pragma unroll
+    for (int i = 0; i < kInflight; ++i) {
+      const int ch = base + 4 * i;
+      const bool ok = ch < nch;
+      mc[i] = ok ? pm[ch] : -__builtin_inff();
+      lc[i] = ok ? pl[ch] : 0.f;
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) ac[i][e] = ok ? pa[(size_t)ch * D + e] : 0.f;
+    }
+    float mx = m;
+#pragma unroll
+    for (int i = 0; i < kInflight; ++i) mx = fmaxf(mx, mc[i]);
+    const float ms = (mx == -__builtin_inff()) ? 0.f : mx;
+    const float alpha = fexp(m - ms);
+    l *= alpha;
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) acc[e] *= alpha;
+#pragma unroll
+    for (int i = 0; i < kInflight; ++i) {
+      const float wgt = fexp(mc[i] - ms);
+      l = fmaf(wgt, lc[i], l);
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) acc[e] = fmaf(wgt, ac[i][e], acc[e]);
+    }
+    m = mx;
   }
-  const float M = s_red[0];
-  const int col = t % D, grp = t / D;
-  float A = 0.f, L = 0.f;
-  for (int ch = grp; ch < nch; ch += G) {
-    const float w = fexp(pm[ch] - M);
-    A = fmaf(w, pa[(size_t)ch * D + col], A);
-    L = fmaf(w, pl[ch], L);
+#pragma unroll
+  for (int e = 0; e < CPL; ++e) s_acc[wave][lane * CPL + e] = acc[e];
+  if (lane == 0) {
+    s_ml[wave][0] = m;
+    s_ml[wave][1] = l;
   }
-  s_a[grp][col] = A;
-  if (col == 0) s_l[grp] = L;
   __syncthreads();
   if (t < D) {
-    float At = 0.f, Lt = 0.f;
+    float mm = s_ml[0][0], ll = s_ml[0][1], aa[1] = {s_acc[0][t]};
 #pragma unroll
-    for (int g2 = 0; g2 < G; ++g2) {
-      At += s_a[g2][t];
-      Lt += s_l[g2];
+    for (int w = 1; w < 4; ++w) {
+      const float a2[1] = {s_acc[w][t]};
+      merge_state<1>(mm, ll, aa, s_ml[w][0], s_ml[w][1], a2);
     }
-    a.out[(size_t)u * D + t] = At / Lt;
+    a.out[(size_t)u * D + t] = aa[0] / ll;
   }
 }
 
 // ---------------------------------------------------------------------------
 template <int D, int DT, int MODE, bool DENSE>
 static hipError_t decode_t(const CacheView& c, const DecodeArgs& a, hipStream_t s) {
-  const long long grid = (long long)a.max_chunks * c.B * c.H;
-  hipLaunchKernelGGL((decode_kernel<D, DT, MODE, DENSE>), dim3((unsigned)grid), dim3(256), 0, s, c,
-                     a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((combine_kernel<D>), dim3(c.B * c.H), dim3(256), 0, s, c, a);
+  const int units = c.B * c.H;
+  const size_t list_bytes = DENSE ? 0 : (size_t)a.split * 4;
+  hipError_t e;
+  if (a.queue) {
+    hipLaunchKernelGGL(decode_prepare_kernel, dim3(1), dim3(1024), 0, s, c, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const size_t lds = (size_t)(units + 1) * 4 + list_bytes;
+    hipLaunchKernelGGL((decode_queue_kernel<D, DT, MODE, DENSE>), dim3(a.queue_grid), dim3(256),
+                       lds, s, c, a);
+  } else {
+    const long long grid = (long long)a.max_chunks * units;
+    hipLaunchKernelGGL((decode_grid_kernel<D, DT, MODE, DENSE>), dim3((unsigned)grid), dim3(256),
+                       list_bytes, s, c, a);
+  }
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL((combine_kernel<D>), dim3(units), dim3(256), 0, s, c, a);
   return hipGetLastError();
 }
 

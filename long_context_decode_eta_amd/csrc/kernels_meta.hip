@@ -138,37 +138,48 @@ __global__ __launch_bounds__(256) void block_meta_kernel(CacheView c, int first,
 }
 
 // ---------------------------------------------------------------------------
-// Threshold (Eq. 1).  One work-group per sequence b.  Thread t owns head
-// h = t % H and the rows j = rg, rg + G, ... (rg = t / H, G = 256 / H) of the
-// H*D-long dot product; the G row-group partials are summed in LDS in a fixed
-// order.  Adjacent threads read adjacent W entries of one row.
+// Threshold (Eq. 1).  Grid (B, ceil(H / 16)): work-group (b, y) computes heads
+// h0 .. h0+15 (h0 = 16 y) of sequence b.  Thread t owns rows j = t, t+256, ...
+// of the H*D-long sum and keeps 16 partial sums, one per head; every row is
+// one 64-byte run of W, and all of a thread's loads are independent.  The 256
+// partials per head are then added by a fixed-order LDS tree (deterministic).
+constexpr int kPredHeads = 16;
 __global__ __launch_bounds__(256) void predict_kernel(int H, int D, const float* q, const float* W,
                                                       const float* bias, float a, float* tau,
                                                       float* tau_screen) {
-  __shared__ float red[256];
-  const int b = blockIdx.x, t = threadIdx.x;
-  const int G = 256 / H, h = t % H, rg = t / H;
+  __shared__ float red[256][kPredHeads + 1];
+  const int b = blockIdx.x, h0 = blockIdx.y * kPredHeads, t = threadIdx.x;
+  const int hw = min(kPredHeads, H - h0);
   const int n = H * D;
   if (W) {
-    float s = 0.f;
-    if (rg < G) {
-      const float* qb = q + (size_t)b * n;
-      for (int j = rg; j < n; j += G) s = fmaf(qb[j], W[(size_t)j * H + h], s);
+    float acc[kPredHeads];
+#pragma unroll
+    for (int e = 0; e < kPredHeads; ++e) acc[e] = 0.f;
+    const float* qb = q + (size_t)b * n;
+#pragma unroll 4
+    for (int j = t; j < n; j += 256) {
+      const float qj = qb[j];
+      const float* wr = W + (size_t)j * H + h0;
+#pragma unroll
+      for (int e = 0; e < kPredHeads; ++e)
+        if (e < hw) acc[e] = fmaf(qj, wr[e], acc[e]);
     }
-    red[t] = s;
+#pragma unroll
+    for (int e = 0; e < kPredHeads; ++e) red[t][e] = acc[e];
     __syncthreads();
-  }
-  if (t < H) {
-    float v;
-    if (W) {
-      float acc = 0.f;
-      for (int r = 0; r < G; ++r) acc += red[r * H + t];
-      v = acc + bias[t];
-    } else {
-      v = bias[t];
+    for (int s = 128; s > 0; s >>= 1) {
+      if (t < s) {
+#pragma unroll
+        for (int e = 0; e < kPredHeads; ++e) red[t][e] += red[t + s][e];
+      }
+      __syncthreads();
     }
-    tau[(size_t)b * H + t] = v;
-    tau_screen[(size_t)b * H + t] = v - a;
+  }
+  if (t < hw) {
+    const int h = h0 + t;
+    const float v = W ? red[0][t] + bias[h] : bias[h];
+    tau[(size_t)b * H + h] = v;
+    tau_screen[(size_t)b * H + h] = v - a;
   }
 }
 
@@ -208,8 +219,8 @@ hipError_t launch_block_meta(const CacheView& c, int first, int n, hipStream_t s
 
 hipError_t launch_predict(int B, int H, int D, const float* q, const float* W, const float* bias,
                           float a, float* tau, float* tau_screen, hipStream_t s) {
-  hipLaunchKernelGGL(predict_kernel, dim3(B), dim3(256), 0, s, H, D, q, W, bias, a, tau,
-                     tau_screen);
+  hipLaunchKernelGGL(predict_kernel, dim3(B, ceil_div(H, kPredHeads)), dim3(256), 0, s, H, D, q,
+                     W, bias, a, tau, tau_screen);
   return hipGetLastError();
 }
 

@@ -56,8 +56,8 @@ __device__ __forceinline__ float block_score(const CacheView& c, int u, int j, b
     const float* var = c.var + row;
 #pragma unroll
     for (int t = 0; t < QShare<D>::kLoads; ++t) {
-      const float4 m = *reinterpret_cast<const float4*>(mu + 32 * t + 4 * li);
-      const float4 v = *reinterpret_cast<const float4*>(var + 32 * t + 4 * li);
+      const float4 m = ld16f_nt(mu + 32 * t + 4 * li);
+      const float4 v = ld16f_nt(var + 32 * t + 4 * li);
       dot = fmaf(s.q[4 * t + 0], m.x, dot);
       dot = fmaf(s.q[4 * t + 1], m.y, dot);
       dot = fmaf(s.q[4 * t + 2], m.z, dot);

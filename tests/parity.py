@@ -191,3 +191,65 @@ def check_against_oracle(w: synth.Workload, g: GpuResult, cache: eb.KVCache, *, 
     stats["screened"] = screened
     stats["density"] = float(toks.sum()) / max(1, int(sl.sum()) * w.H)
     return stats
+
+
+def check_units(w: synth.Workload, g: GpuResult, units, *, W, bias_or_c, z, scale,
+                mode=eb.GATED, beta=5.0, a=0.0):
+    """Sampled comparison at full size: for each (b, h) in `units`, the oracle
+    recomputes that stream alone (statistics, score, admission, attention) from
+    the same cache bits, with the threshold of Eq. 1 from the full query batch.
+    Returns (worst output error, flips, screened)."""
+    q = w.q.cpu().numpy()
+    Wn = None if W is None else W.cpu().numpy()
+    tau, ts = oracle.predict_tau(q, Wn, bias_or_c.cpu().numpy(), a=a)
+    close(g.tau_gate, tau, 1e-5, "tau_gate")
+    worst, flips, screened = 0.0, 0, 0
+    for b, h in units:
+        T = int(w.seq_len[b])
+        K = synth.kv_numpy(w.k[b:b + 1, h:h + 1, :T])
+        V = synth.kv_numpy(w.v[b:b + 1, h:h + 1, :T])
+        sl = np.array([T], np.int32)
+        meta = oracle.meta_batch(K, sl, w.block)
+        r = oracle.screen_attend_batch(q[b:b + 1, h:h + 1], K, V, sl, w.block, meta,
+                                       tau[b, h], ts[b, h], z=z, scale=scale, mode=mode,
+                                       beta=beta)
+        nb = -(-T // w.block)
+        assert not g.mask[b, h, nb:].any(), "admitted block beyond the stream"
+        gm = g.mask[b:b + 1, h:h + 1, :max(nb, 1)]
+        f, sc = compare_masks(r["active"], r["score"], r["tau_screen"], gm[:, :, :r["active"].shape[2]],
+                              sl, w.block)
+        flips += f
+        screened += sc
+        if f == 0:
+            assert g.cnt[b, h] == r["cnt"][0, 0]
+            ref = r["out"]
+        else:
+            ref = oracle.attend_batch(q[b:b + 1, h:h + 1], K, V, sl, w.block, gm, r["tau"],
+                                      mode=mode, beta=beta, scale=scale)
+        worst = max(worst, compare_outputs(g.out[b:b + 1, h:h + 1], ref, w.kv_dtype,
+                                           f"out[{b},{h}]"))
+    sl_all = w.seq_len.cpu().numpy()
+    toks = gpu_tokens(g.cnt, sl_all, w.block)
+    assert g.density == int(toks.sum())
+    return worst, flips, screened
+
+
+def oracle_constants(w: synth.Workload, rho: float, seqs=None, sets=None):
+    """Per-head constants for a target density from the oracle's calibration,
+    pooled over the sequences `seqs` (default: all).  Dynamic workloads pool
+    x = score - qbar W (the timed query); frozen-calibrated ones pool the
+    calibration query sets."""
+    seqs = list(range(w.B)) if seqs is None else list(seqs)
+    K = synth.kv_numpy(w.k[seqs])
+    sl = w.seq_len.cpu().numpy()[seqs].astype(np.int32)
+    meta = oracle.meta_batch(K, sl, w.block)
+    if w.W is not None:
+        q = w.q.cpu().numpy()[seqs]
+        tau0, _ = oracle.predict_tau(q, w.W.cpu().numpy(), np.zeros(w.H, np.float32))
+        c, k = oracle.calibrate(q[None], sl, w.block, w.cap, meta, tau0=tau0[None], z=w.z,
+                                scale=w.scale, rho=float(np.float32(rho)))
+    else:
+        qc = w.q_cal.cpu().numpy()[:, seqs]
+        c, k = oracle.calibrate(qc, sl, w.block, w.cap, meta, z=w.z, scale=w.scale,
+                                rho=float(np.float32(rho)))
+    return torch.from_numpy(c.astype(np.float32)), k

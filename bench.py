@@ -44,12 +44,21 @@ def parse():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--seed", type=int, default=1234)
+    ap.add_argument("--copy-reference", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB five times "
+                         "(reference dispatches for calibrating HBM byte counters)")
     return ap.parse_args()
 
 
-def auto_split(block: int) -> int:
-    # about 512 keys (256 KiB of bf16 K+V at d=128) per work-group
-    return max(1, 512 // block)
+def copy_reference(mib: int) -> None:
+    import torch
+    n = mib << 20
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_reference_bytes": n, "dispatches": 5}), flush=True)
 
 
 class Timer:
@@ -82,6 +91,9 @@ def main():
               "(the decode path runs on a single GPU; see the sharding notes in the design).",
               file=sys.stderr)
         sys.exit(2)
+    if args.copy_reference:
+        copy_reference(args.copy_reference)
+        return
     import numpy as np
     import torch
 
@@ -93,16 +105,16 @@ def main():
     t0 = time.time()
     w = synth.make(args.workload, seed=args.seed, device=dev)
     B, H, D, bs = w.B, w.H, w.D, w.block
-    split = args.split or auto_split(bs)
     cache = eb.KVCache(B, H, D, bs, w.cap, w.kv_dtype, device=dev, k=w.k, v=w.v)
     cache.seq_len.copy_(w.seq_len)
     eb.build_block_meta(cache)
     sl = w.seq_len.cpu().numpy().astype(np.int64)
     sumT = int(sl.sum())
+    dec = eb.Decoder(cache, z=w.z, scale=w.scale, blocks_per_split=args.split or None)
+    split = dec.split
     print(f"[bench] workload {args.workload}: B={B} H={H} D={D} b={bs} sumT={sumT} "
-          f"split={split} ({time.time() - t0:.1f}s setup)", file=sys.stderr, flush=True)
-
-    dec = eb.Decoder(cache, z=w.z, scale=w.scale, blocks_per_split=split)
+          f"split={split} dense split={dec.dense_split} ({time.time() - t0:.1f}s setup)",
+          file=sys.stderr, flush=True)
     W = w.W
     # Per-head constants for each target density, from the library's calibration.
     if w.tau_kind == "dynamic":
@@ -128,6 +140,9 @@ def main():
     torch.cuda.synchronize()
 
     def run(rho, steps, warmup):
+        """Eager steps timed per kernel with HIP events, then the same step
+        captured once in a HIP graph (checked bit for bit against the eager
+        output) and timed over `steps` replays."""
         c = consts[rho]
         if frozen:
             set_tau(c)
@@ -151,19 +166,46 @@ def main():
             tscr.around(lambda: dec.screen(w.q))
             tdec.around(lambda: dec.attend(w.q))
         torch.cuda.synchronize()
-        wall = time.perf_counter() - a
+        eager = time.perf_counter() - a
         toks = (int(dec.density_ctr.item()) - ctr0) // steps
         cnt = dec.active_cnt.cpu().numpy().astype(np.int64)
-        return dict(ms=wall * 1e3 / steps, decode_ms=tdec.mean_ms(), screen_ms=tscr.mean_ms(),
-                    density=toks / (H * sumT), tokens=toks, cnt=cnt)
+        ref = dec.out.clone()
 
-    def run_dense(steps, warmup):
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(3):  # every replay must reproduce the eager result exactly
+            dec.out.zero_()
+            graph.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(dec.out, ref), "graph replay differs from eager decode"
         for _ in range(warmup):
-            dec.dense(w.q)
+            graph.replay()
         torch.cuda.synchronize()
         a = time.perf_counter()
         for _ in range(steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - a
+        del graph
+        return dict(ms=wall * 1e3 / steps, eager_ms=eager * 1e3 / steps,
+                    decode_ms=tdec.mean_ms(), screen_ms=tscr.mean_ms(),
+                    density=toks / (H * sumT), tokens=toks, cnt=cnt)
+
+    def run_dense(steps, warmup):
+        """The in-house dense decode at the same shape, captured in a HIP graph
+        like the sparse step."""
+        graph = torch.cuda.CUDAGraph()
+        dec.dense(w.q)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
             dec.dense(w.q)
+        for _ in range(warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        a = time.perf_counter()
+        for _ in range(steps):
+            graph.replay()
         torch.cuda.synchronize()
         return (time.perf_counter() - a) * 1e3 / steps
 
@@ -191,7 +233,8 @@ def main():
         r["decode_bytes"] = decode_bytes(r)
         sweep[rho] = r
         print(f"[bench] rho={rho:.2f}: density {r['density']:.4f} step {r['ms']:.4f} ms "
-              f"(screen {r['screen_ms']:.4f}, decode {r['decode_ms']:.4f}) "
+              f"(eager {r['eager_ms']:.4f}; screen {r['screen_ms']:.4f}, "
+              f"decode {r['decode_ms']:.4f}) "
               f"{r['step_bytes'] / r['ms'] / 1e6:.0f} GB/s", file=sys.stderr, flush=True)
         if rho == args.rho:
             main = r
@@ -212,7 +255,7 @@ def main():
         cj = json.load(open(COUNTERS))
         if cj.get("kernel_hash") == kernel_hash() and cj.get("workload") == args.workload:
             traffic = cj.get("hbm_bytes_per_launch")
-    roofline = {"bound": "hbm", "kernel": "eta_decode (decode + combine launches)",
+    roofline = {"bound": "hbm", "kernel": "decode_queue_kernel (eta_decode)",
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "algorithmic_bytes_per_launch": int(r["decode_bytes"]),
@@ -228,6 +271,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(r["ms"], 5),
+        "eager_ms_per_step": round(r["eager_ms"], 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -241,6 +285,7 @@ def main():
                         f"{args.rho:.0%} target density",
             "global_batch": B, "seq_len": int(sl.max()), "parallelism": "single GPU",
             "kv_dtype": "bf16" if elt == 2 else "f32", "blocks_per_split": split,
+            "dense_blocks_per_split": dec.dense_split,
         },
         "density": round(r["density"], 4),
         "step_hbm_gbs": round(r["step_bytes"] / r["ms"] / 1e6, 1),
@@ -248,6 +293,7 @@ def main():
         "dense_ms": round(dense_ms, 5),
         "speedup_vs_dense": round(dense_ms / r["ms"], 3),
         "sweep": {f"{k:.2f}": {"density": round(v["density"], 4), "ms": round(v["ms"], 5),
+                               "eager_ms": round(v["eager_ms"], 5),
                                "tokens_per_s": round(sumT / (v["ms"] * 1e-3), 1),
                                "step_gbs": round(v["step_bytes"] / v["ms"] / 1e6, 1),
                                "decode_gbs": round(v["decode_bytes"] / v["decode_ms"] / 1e6, 1),

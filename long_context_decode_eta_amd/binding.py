@@ -225,18 +225,33 @@ def workspace(nbytes: int, device="cuda") -> torch.Tensor:
 
 
 # ---------------------------------------------------------------------------
+def auto_split(units: int, cap_blocks: int, block: int, dense: bool = False) -> int:
+    """Blocks per split-K chunk.  Big enough to amortise a chunk's fixed cost
+    (list staging, merge, partial write): up to 512 keys per chunk (2048 for
+    the dense baseline, whose chunks are contiguous); smaller for a small cache
+    so that it still yields enough chunks to fill the chip
+    (units*cap_blocks/1024, or /2048 dense).  Chosen from sweeps on MI355X
+    over the 32K..512K workloads (e.g. 32K x 16 heads, b=64: 8 blocks)."""
+    if dense:
+        return max(1, min(2048 // block, (units * cap_blocks) // 2048))
+    return max(1, min(512 // block, (units * cap_blocks) // 1024))
+
+
 class Decoder:
     """One decode step over a cache with every buffer preallocated:
     predict_tau (skipped in frozen mode when tau is precomputed) -> screen ->
     decode.  Pure orchestration of the C entry points."""
 
     def __init__(self, cache: KVCache, *, z, scale=None, beta=5.0, a=0.0,
-                 logit_mode=GATED, blocks_per_split=16):
+                 logit_mode=GATED, blocks_per_split=None, dense_blocks_per_split=None):
         self.cache, self.z, self.beta, self.a = cache, float(z), float(beta), float(a)
         self.scale = float(scale) if scale is not None else float(
             torch.tensor(1.0 / cache.head_dim ** 0.5, dtype=torch.float32).item())
-        self.mode, self.split = logit_mode, int(blocks_per_split)
         B, H, D, nbc = cache.batch, cache.heads, cache.head_dim, cache.cap_blocks
+        self.mode = logit_mode
+        self.split = int(blocks_per_split or auto_split(B * H, nbc, cache.block))
+        self.dense_split = int(dense_blocks_per_split or
+                               auto_split(B * H, nbc, cache.block, dense=True))
         dev = cache.k.device
         self.tau_gate = torch.zeros((B, H), dtype=torch.float32, device=dev)
         self.tau_screen = torch.zeros_like(self.tau_gate)
@@ -244,7 +259,8 @@ class Decoder:
         self.active_cnt = torch.zeros((B, H), dtype=torch.int32, device=dev)
         self.density_ctr = torch.zeros((1,), dtype=torch.int64, device=dev)
         self.screen_ws = workspace(screen_workspace_bytes(B, H, nbc), dev)
-        self.decode_ws = workspace(decode_workspace_bytes(B, H, D, nbc, self.split), dev)
+        self.decode_ws = workspace(decode_workspace_bytes(
+            B, H, D, nbc, min(self.split, self.dense_split)), dev)
         self.out = torch.zeros((B, H, D), dtype=torch.float32, device=dev)
 
     def predict(self, q, W, bias_or_c, stream=None):
@@ -266,5 +282,5 @@ class Decoder:
         return self.out
 
     def dense(self, q, stream=None):
-        dense_decode(self.cache, q, self.scale, self.split, self.decode_ws, self.out, stream)
+        dense_decode(self.cache, q, self.scale, self.dense_split, self.decode_ws, self.out, stream)
         return self.out

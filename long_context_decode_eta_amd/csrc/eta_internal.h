@@ -147,8 +147,9 @@ struct DecodeArgs {
   float* part_l;   // [B*H][max_chunks]
   float* part_acc; // [B*H][max_chunks][D]
   float* out;
-  int* queue;        // work counter of the queue kernel (NULL: flat grid)
+  int* queue;        // work counter of the queue kernel
   int* chunk_start;  // [B*H + 1] chunk offsets of the queue kernel
+  bool use_queue;    // queue kernel (else one work-group per possible chunk)
   int queue_grid;    // work-groups of the queue kernel
 };
 // Streams up to which the queue kernel is used (its chunk table lives in LDS).

@@ -9,7 +9,8 @@
 // block with raw logits (plain decode attention, the in-house baseline).
 //
 // Work decomposition: the admitted list of stream u is cut into chunks of
-// `split` blocks; one work-group of 4 waves handles one chunk.  The chunk's
+// `split` blocks; one work-group of 4 waves handles one chunk, and a combine
+// kernel merges the partials of every multi-chunk stream (log-sum-exp).  The chunk's
 // rows are cut into tiles of kRows rows; wave w takes tiles w, w+4, ...  A key
 // row of D elements is read by LPR lanes with one 128-bit load each (bf16,
 // D=128: 16 lanes), so one load instruction of a wave covers RPI = 64/LPR rows
@@ -208,9 +209,75 @@ __device__ __forceinline__ int stream_chunks(const CacheView& c, const DecodeArg
   return (cnt + a.split - 1) / a.split;
 }
 
-// Work list of the queue kernel: chunk_start[u] = number of chunks of streams
-// before u (exclusive scan, chunk_start[units] = total), and the queue counter
-// set to 0.  One work-group; streams in rounds of 1024 with a running carry.
+// Log-sum-exp merge of the nch chunk partials of stream u into out[u], by the
+// whole work-group of kCombWaves waves: wave w folds chunks w, w+kCombWaves,
+// ... into a running (max, sum, weighted V) in one pass with kInflight chunks
+// loaded before any is used; lane i owns columns [i*CPL, i*CPL+CPL).  The wave
+// states are then merged in a fixed order (deterministic).
+constexpr int kInflight = 8;
+constexpr int kCombWaves = 16;
+template <int D>
+__device__ void combine_stream(const DecodeArgs& a, int u, int nch, float (*s_acc)[D],
+                               float (*s_ml)[2]) {
+  constexpr int CPL = D / kWave;
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+  const float* pm = a.part_m + (size_t)u * a.max_chunks;
+  const float* pl = a.part_l + (size_t)u * a.max_chunks;
+  const float* pa = a.part_acc + (size_t)u * a.max_chunks * D + lane * CPL;
+  float m = -__builtin_inff(), l = 0.f, acc[CPL];
+#pragma unroll
+  for (int e = 0; e < CPL; ++e) acc[e] = 0.f;
+  for (int base = wave; base < nch; base += kCombWaves * kInflight) {
+    float mc[kInflight], lc[kInflight], ac[kInflight][CPL];
+#pragma unroll
+    for (int i = 0; i < kInflight; ++i) {
+      const int ch = base + kCombWaves * i;
+      const bool ok = ch < nch;
+      mc[i] = ok ? pm[ch] : -__builtin_inff();
+      lc[i] = ok ? pl[ch] : 0.f;
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) ac[i][e] = ok ? pa[(size_t)ch * D + e] : 0.f;
+    }
+    float mx = m;
+#pragma unroll
+    for (int i = 0; i < kInflight; ++i) mx = fmaxf(mx, mc[i]);
+    const float ms = (mx == -__builtin_inff()) ? 0.f : mx;
+    const float alpha = fexp(m - ms);
+    l *= alpha;
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) acc[e] *= alpha;
+#pragma unroll
+    for (int i = 0; i < kInflight; ++i) {
+      const float wgt = fexp(mc[i] - ms);
+      l = fmaf(wgt, lc[i], l);
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) acc[e] = fmaf(wgt, ac[i][e], acc[e]);
+    }
+    m = mx;
+  }
+#pragma unroll
+  for (int e = 0; e < CPL; ++e) s_acc[wave][lane * CPL + e] = acc[e];
+  if (lane == 0) {
+    s_ml[wave][0] = m;
+    s_ml[wave][1] = l;
+  }
+  __syncthreads();
+  if (t < D) {
+    float mm = s_ml[0][0], ll = s_ml[0][1], aa[1] = {s_acc[0][t]};
+#pragma unroll
+    for (int w = 1; w < kCombWaves; ++w) {
+      const float a2[1] = {s_acc[w][t]};
+      merge_state<1>(mm, ll, aa, s_ml[w][0], s_ml[w][1], a2);
+    }
+    a.out[(size_t)u * D + t] = aa[0] / ll;
+  }
+}
+
+// Per-call set-up, one work-group: chunk_start[u] = chunks of the streams
+// before u (exclusive scan; chunk_start[units] = total), the queue counter set
+// to 0, and the zero output of every stream with no chunk (T_b = 0).  Streams
+// in rounds of 1024 with a running carry.
+template <int D>
 __global__ __launch_bounds__(1024) void decode_prepare_kernel(CacheView c, DecodeArgs a) {
   __shared__ int scan[1024];
   __shared__ int carry;
@@ -224,6 +291,8 @@ __global__ __launch_bounds__(1024) void decode_prepare_kernel(CacheView c, Decod
     const int u = base + t;
     int T, cnt;
     const int n = u < units ? stream_chunks(c, a, u, &T, &cnt) : 0;
+    if (u < units && n == 0)
+      for (int i = 0; i < D; ++i) a.out[(size_t)u * D + i] = 0.f;
     scan[t] = n;
     __syncthreads();
     for (int off = 1; off < 1024; off <<= 1) {
@@ -292,82 +361,16 @@ __global__ __launch_bounds__(256) void decode_grid_kernel(CacheView c, DecodeArg
   chunk_attend<D, DT, MODE, DENSE>(c, a, u, k, T, cnt, s_list, s_acc, s_ml);
 }
 
-// Log-sum-exp combine of the chunk partials of one stream; also writes the
-// zero output of empty streams.  One work-group per stream: wave w folds
-// chunks w, w+4, ... into a running (max, sum, weighted V) in one pass, with
-// kInflight chunks loaded before any of them is used; lane i owns columns
-// [i*CPL, i*CPL+CPL).  The 4 wave states are merged in a fixed order.
-constexpr int kInflight = 8;
+// Combine: one work-group per stream with two or more chunks.
 template <int D>
-__global__ __launch_bounds__(256) void combine_kernel(CacheView c, DecodeArgs a) {
-  constexpr int CPL = D / kWave;
-  __shared__ float s_acc[4][D];
-  __shared__ float s_ml[4][2];
-  const int u = blockIdx.x, t = threadIdx.x;
-  const int wave = t >> 6, lane = t & 63;
-  const int T = c.seq_len[u / c.H];
-  if (T <= 0) {
-    if (t < D) a.out[(size_t)u * D + t] = 0.f;
-    return;
-  }
-  const int nb = (T + c.bs - 1) >> c.log2bs;
-  const int cnt = a.dense ? nb : min(a.active_cnt[u], nb);
-  if (cnt <= 0) {  // not a list eta_screen produces (it always holds the last block)
-    if (t < D) a.out[(size_t)u * D + t] = 0.f;
-    return;
-  }
-  const int nch = (cnt + a.split - 1) / a.split;
-  if (nch <= 1) return;  // written by the decode kernel
-  const float* pm = a.part_m + (size_t)u * a.max_chunks;
-  const float* pl = a.part_l + (size_t)u * a.max_chunks;
-  const float* pa = a.part_acc + (size_t)u * a.max_chunks * D + lane * CPL;
-  float m = -__builtin_inff(), l = 0.f, acc[CPL];
-#pragma unroll
-  for (int e = 0; e < CPL; ++e) acc[e] = 0.f;
-  for (int base = wave; base < nch; base += 4 * kInflight) {
-    float mc[kInflight], lc[kInflight], ac[kInflight][CPL];
-#pragma unroll
-    for (int i = 0; i < kInflight; ++i) {
-      const int ch = base + 4 * i;
-      const bool ok = ch < nch;
-      mc[i] = ok ? pm[ch] : -__builtin_inff();
-      lc[i] = ok ? pl[ch] : 0.f;
-#pragma unroll
-      for (int e = 0; e < CPL; ++e) ac[i][e] = ok ? pa[(size_t)ch * D + e] : 0.f;
-    }
-    float mx = m;
-#pragma unroll
-    for (int i = 0; i < kInflight; ++i) mx = fmaxf(mx, mc[i]);
-    const float ms = (mx == -__builtin_inff()) ? 0.f : mx;
-    const float alpha = fexp(m - ms);
-    l *= alpha;
-#pragma unroll
-    for (int e = 0; e < CPL; ++e) acc[e] *= alpha;
-#pragma unroll
-    for (int i = 0; i < kInflight; ++i) {
-      const float wgt = fexp(mc[i] - ms);
-      l = fmaf(wgt, lc[i], l);
-#pragma unroll
-      for (int e = 0; e < CPL; ++e) acc[e] = fmaf(wgt, ac[i][e], acc[e]);
-    }
-    m = mx;
-  }
-#pragma unroll
-  for (int e = 0; e < CPL; ++e) s_acc[wave][lane * CPL + e] = acc[e];
-  if (lane == 0) {
-    s_ml[wave][0] = m;
-    s_ml[wave][1] = l;
-  }
-  __syncthreads();
-  if (t < D) {
-    float mm = s_ml[0][0], ll = s_ml[0][1], aa[1] = {s_acc[0][t]};
-#pragma unroll
-    for (int w = 1; w < 4; ++w) {
-      const float a2[1] = {s_acc[w][t]};
-      merge_state<1>(mm, ll, aa, s_ml[w][0], s_ml[w][1], a2);
-    }
-    a.out[(size_t)u * D + t] = aa[0] / ll;
-  }
+__global__ __launch_bounds__(kCombWaves * kWave) void combine_kernel(CacheView c, DecodeArgs a) {
+  __shared__ float s_acc[kCombWaves][D];
+  __shared__ float s_ml[kCombWaves][2];
+  const int u = blockIdx.x;
+  int T, cnt;
+  const int nch = stream_chunks(c, a, u, &T, &cnt);
+  if (nch <= 1) return;  // no chunk (zeros from the prepare kernel) or a single chunk
+  combine_stream<D>(a, u, nch, s_acc, s_ml);
 }
 
 // ---------------------------------------------------------------------------
@@ -376,9 +379,9 @@ static hipError_t decode_t(const CacheView& c, const DecodeArgs& a, hipStream_t 
   const int units = c.B * c.H;
   const size_t list_bytes = DENSE ? 0 : (size_t)a.split * 4;
   hipError_t e;
-  if (a.queue) {
-    hipLaunchKernelGGL(decode_prepare_kernel, dim3(1), dim3(1024), 0, s, c, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_prepare_kernel<D>), dim3(1), dim3(1024), 0, s, c, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (a.use_queue) {
     const size_t lds = (size_t)(units + 1) * 4 + list_bytes;
     hipLaunchKernelGGL((decode_queue_kernel<D, DT, MODE, DENSE>), dim3(a.queue_grid), dim3(256),
                        lds, s, c, a);
@@ -388,7 +391,7 @@ static hipError_t decode_t(const CacheView& c, const DecodeArgs& a, hipStream_t 
                        list_bytes, s, c, a);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((combine_kernel<D>), dim3(units), dim3(256), 0, s, c, a);
+  hipLaunchKernelGGL((combine_kernel<D>), dim3(units), dim3(kCombWaves * kWave), 0, s, c, a);
   return hipGetLastError();
 }
 

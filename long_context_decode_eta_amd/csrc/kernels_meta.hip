@@ -140,10 +140,13 @@ __global__ __launch_bounds__(256) void block_meta_kernel(CacheView c, int first,
 // ---------------------------------------------------------------------------
 // Threshold (Eq. 1).  Grid (B, ceil(H / 16)): work-group (b, y) computes heads
 // h0 .. h0+15 (h0 = 16 y) of sequence b.  Thread t owns rows j = t, t+256, ...
-// of the H*D-long sum and keeps 16 partial sums, one per head; every row is
-// one 64-byte run of W, and all of a thread's loads are independent.  The 256
+// of the H*D-long sum and keeps 16 partial sums, one per head; a row's 16
+// weights are one 64-byte run of W (four 128-bit loads when H is a multiple of
+// 16), and all of a thread's loads are issued before its arithmetic.  The 256
 // partials per head are then added by a fixed-order LDS tree (deterministic).
 constexpr int kPredHeads = 16;
+constexpr int kPredRows = 8;  // rows per thread per round (loads in flight)
+template <bool VEC>
 __global__ __launch_bounds__(256) void predict_kernel(int H, int D, const float* q, const float* W,
                                                       const float* bias, float a, float* tau,
                                                       float* tau_screen) {
@@ -156,13 +159,31 @@ __global__ __launch_bounds__(256) void predict_kernel(int H, int D, const float*
 #pragma unroll
     for (int e = 0; e < kPredHeads; ++e) acc[e] = 0.f;
     const float* qb = q + (size_t)b * n;
-#pragma unroll 4
-    for (int j = t; j < n; j += 256) {
-      const float qj = qb[j];
-      const float* wr = W + (size_t)j * H + h0;
+    for (int j0 = t; j0 < n; j0 += 256 * kPredRows) {
+      float qj[kPredRows], wv[kPredRows][kPredHeads];
 #pragma unroll
-      for (int e = 0; e < kPredHeads; ++e)
-        if (e < hw) acc[e] = fmaf(qj, wr[e], acc[e]);
+      for (int r = 0; r < kPredRows; ++r) {
+        const int j = j0 + 256 * r;
+        const bool ok = j < n;
+        qj[r] = ok ? qb[j] : 0.f;
+        const float* wr = W + (size_t)(ok ? j : 0) * H + h0;
+        if constexpr (VEC) {
+#pragma unroll
+          for (int v = 0; v < kPredHeads / 4; ++v) {
+            const float4 x = ok ? *reinterpret_cast<const float4*>(wr + 4 * v)
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
+            wv[r][4 * v] = x.x; wv[r][4 * v + 1] = x.y;
+            wv[r][4 * v + 2] = x.z; wv[r][4 * v + 3] = x.w;
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < kPredHeads; ++e) wv[r][e] = (ok && e < hw) ? wr[e] : 0.f;
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < kPredRows; ++r)
+#pragma unroll
+        for (int e = 0; e < kPredHeads; ++e) acc[e] = fmaf(qj[r], wv[r][e], acc[e]);
     }
 #pragma unroll
     for (int e = 0; e < kPredHeads; ++e) red[t][e] = acc[e];
@@ -219,8 +240,13 @@ hipError_t launch_block_meta(const CacheView& c, int first, int n, hipStream_t s
 
 hipError_t launch_predict(int B, int H, int D, const float* q, const float* W, const float* bias,
                           float a, float* tau, float* tau_screen, hipStream_t s) {
-  hipLaunchKernelGGL(predict_kernel, dim3(B, ceil_div(H, kPredHeads)), dim3(256), 0, s, H, D, q,
-                     W, bias, a, tau, tau_screen);
+  const dim3 grid(B, ceil_div(H, kPredHeads));
+  if (H % kPredHeads == 0)
+    hipLaunchKernelGGL(predict_kernel<true>, grid, dim3(256), 0, s, H, D, q, W, bias, a, tau,
+                       tau_screen);
+  else
+    hipLaunchKernelGGL(predict_kernel<false>, grid, dim3(256), 0, s, H, D, q, W, bias, a, tau,
+                       tau_screen);
   return hipGetLastError();
 }
 

@@ -11,8 +11,9 @@ namespace eta {
 
 constexpr int kLanesPerBlock = 8;      // lanes that read one block's statistics
 constexpr int kBlocksPerIter = kWave / kLanesPerBlock;  // 8 blocks per wave step
-constexpr int kBlocksPerWave = 64;     // one 64-bit admission word per wave
-constexpr int kBlocksPerTile = 4 * kBlocksPerWave;      // 4 waves per work-group
+// Calibration values: each wave of a work-group scores 64 consecutive blocks.
+constexpr int kBlocksPerWave = 64;
+constexpr int kBlocksPerTile = 4 * kBlocksPerWave;
 
 // Per-lane share of the query: with 8 lanes per block, load t (t < D/32) of
 // lane li reads floats [32 t + 4 li, 32 t + 4 li + 4) of a statistics row, so
@@ -77,41 +78,83 @@ __device__ __forceinline__ float block_score(const CacheView& c, int u, int j, b
 }
 
 // ---------------------------------------------------------------------------
-// Screen: each wave scores 64 consecutive blocks, 8 per step, and writes one
-// 64-bit admission word.  Flattened grid: blockIdx.x = tile * units + u, so
-// the low tiles of every stream are dispatched first and the surplus tiles of
-// short streams exit at once.
+// Screen: one work-group per 64-block admission word.  Wave w scores blocks
+// 16 w .. 16 w + 15 of the word in two steps of 8 blocks whose statistics
+// loads are all issued before any reduction, so a wave has its whole share in
+// flight at once; the four 16-bit wave masks are merged in LDS and one 64-bit
+// word is written.  Flattened grid: blockIdx.x = word * units + u, so the low
+// words of every stream are dispatched first and the surplus words of short
+// streams exit at once.
+constexpr int kScreenSteps = 2;  // steps of 8 blocks per wave
+static_assert(4 * kScreenSteps * kBlocksPerIter == 64, "one word per work-group");
 template <int D>
 __global__ __launch_bounds__(256) void screen_kernel(CacheView c, const float* q,
                                                      const float* tau_screen, float z, float scale,
                                                      uint64_t* words, int words_per_unit) {
+  constexpr int NL = QShare<D>::kLoads;
+  __shared__ uint32_t s_bits[4];
   const int units = c.B * c.H;
-  const int u = blockIdx.x % units, tile = blockIdx.x / units;
+  const int u = blockIdx.x % units, wd = blockIdx.x / units;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int T = c.seq_len[u / c.H];
   const int nb = (T + c.bs - 1) >> c.log2bs;
   const int nbc = T >> c.log2bs;
-  const int j0 = (tile * 4 + wave) * kBlocksPerWave;
-  if (j0 >= nb) return;
+  if ((wd << 6) >= nb) return;  // uniform over the work-group
   const int gi = lane / kLanesPerBlock, li = lane % kLanesPerBlock;
   QShare<D> qs;
   load_qshare<D>(q + (size_t)u * D, li, qs);
   const float ts = tau_screen[u];
   const bool z_inf = __builtin_isinf(z);
-  uint64_t word = 0;
-#pragma unroll 2
-  for (int it = 0; it < kBlocksPerWave / kBlocksPerIter; ++it) {
-    const int j = j0 + it * kBlocksPerIter + gi;
-    const bool scored = j < nbc;
-    const float sc = block_score<D>(c, u, j, scored, qs, li, z, z_inf, scale);
-    const bool on = (j == nb - 1) || (scored && sc >= ts);
-    const uint64_t bal = __ballot(on);
-    uint64_t bits = 0;
+  const int jw = (wd << 6) + wave * (kScreenSteps * kBlocksPerIter) + gi;
+  float4 m4[kScreenSteps][NL], v4[kScreenSteps][NL];
+  float M[kScreenSteps];
 #pragma unroll
-    for (int g = 0; g < kBlocksPerIter; ++g) bits |= ((bal >> (g * kLanesPerBlock)) & 1ull) << g;
-    word |= bits << (it * kBlocksPerIter);
+  for (int it = 0; it < kScreenSteps; ++it) {
+    const int j = jw + it * kBlocksPerIter;
+    const size_t row = ((size_t)u * c.cap_blocks + j) * D;
+    const bool scored = j < nbc;
+#pragma unroll
+    for (int t = 0; t < NL; ++t) {
+      m4[it][t] = scored ? ld16f_nt(c.mu + row + 32 * t + 4 * li) : make_float4(0, 0, 0, 0);
+      v4[it][t] = scored ? ld16f_nt(c.var + row + 32 * t + 4 * li) : make_float4(0, 0, 0, 0);
+    }
+    M[it] = scored ? c.maxnorm[(size_t)u * c.cap_blocks + j] : 0.f;
   }
-  if (lane == 0) words[(size_t)u * words_per_unit + (j0 >> 6)] = word;
+  uint32_t bits = 0;
+#pragma unroll
+  for (int it = 0; it < kScreenSteps; ++it) {
+    const int j = jw + it * kBlocksPerIter;
+    float dot = 0.f, mom = 0.f;
+#pragma unroll
+    for (int t = 0; t < NL; ++t) {
+      dot = fmaf(qs.q[4 * t + 0], m4[it][t].x, dot);
+      dot = fmaf(qs.q[4 * t + 1], m4[it][t].y, dot);
+      dot = fmaf(qs.q[4 * t + 2], m4[it][t].z, dot);
+      dot = fmaf(qs.q[4 * t + 3], m4[it][t].w, dot);
+      mom = fmaf(qs.q2[4 * t + 0], v4[it][t].x, mom);
+      mom = fmaf(qs.q2[4 * t + 1], v4[it][t].y, mom);
+      mom = fmaf(qs.q2[4 * t + 2], v4[it][t].z, mom);
+      mom = fmaf(qs.q2[4 * t + 3], v4[it][t].w, mom);
+    }
+    dot = group_sum<kLanesPerBlock>(dot);
+    mom = group_sum<kLanesPerBlock>(mom);
+    const float geometric = qs.qn * M[it];
+    const float sc = z_inf ? scale * geometric
+                           : scale * fminf(fmaf(z, sqrtf(mom), dot), geometric);
+    const bool on = (j == nb - 1) || (j < nbc && sc >= ts);
+    const uint64_t bal = __ballot(on);
+#pragma unroll
+    for (int g = 0; g < kBlocksPerIter; ++g)
+      bits |= (uint32_t)((bal >> (g * kLanesPerBlock)) & 1ull) << (it * kBlocksPerIter + g);
+  }
+  if (lane == 0) s_bits[wave] = bits;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    constexpr int WB = kScreenSteps * kBlocksPerIter;  // 16 bits per wave
+    const uint64_t word = (uint64_t)s_bits[0] | ((uint64_t)s_bits[1] << WB) |
+                          ((uint64_t)s_bits[2] << (2 * WB)) | ((uint64_t)s_bits[3] << (3 * WB));
+    words[(size_t)u * words_per_unit + wd] = word;
+  }
 }
 
 // Compaction: one work-group per stream turns the admission words into the
@@ -281,7 +324,7 @@ static hipError_t screen_t(const CacheView& c, const float* q, const float* ts, 
                            hipStream_t s) {
   const int units = c.B * c.H;
   const int wpu = ceil_div(c.cap_blocks, 64);
-  const long long grid = (long long)ceil_div(c.cap_blocks, kBlocksPerTile) * units;
+  const long long grid = (long long)wpu * units;
   hipLaunchKernelGGL((screen_kernel<D>), dim3((unsigned)grid), dim3(256), 0, s, c, q, ts, z, scale,
                      words, wpu);
   hipError_t e = hipGetLastError();

@@ -70,7 +70,7 @@ def gpu_mask(idx: np.ndarray, cnt: np.ndarray, nbcap: int) -> np.ndarray:
 
 
 def run_gpu(cache: eb.KVCache, q, *, W=None, bias_or_c=None, z, scale, mode=eb.GATED,
-            beta=5.0, a=0.0, split=16, build_meta=True) -> GpuResult:
+            beta=5.0, a=0.0, split=None, build_meta=True) -> GpuResult:
     if build_meta:
         eb.build_block_meta(cache)
     dec = eb.Decoder(cache, z=z, scale=scale, beta=beta, a=a, logit_mode=mode,

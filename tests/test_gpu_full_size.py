@@ -1,5 +1,5 @@
 """GPU parity at the benchmark sizes, in the launch configuration bench.py
-times (blocks_per_split = 512 / block), on sampled (sequence, head) streams
+times (the Decoder's automatic blocks_per_split), on sampled (sequence, head) streams
 that the oracle recomputes one by one, plus whole-batch properties.
 
 Workloads (seeded, synthetic; shapes of the decode benchmarks):
@@ -47,9 +47,7 @@ def test_full_size_sampled_streams(name):
     if units is None:  # ragged: shortest, longest and two fixed streams
         sl = w.seq_len.cpu().numpy()
         units = [(int(sl.argmin()), 0), (int(sl.argmax()), 15), (5, 3), (17, 9)]
-    split = max(1, 512 // w.block)
-    g = run_gpu(cache, w.q, W=w.W, bias_or_c=c, z=w.z, scale=w.scale, split=split,
-                build_meta=False)
+    g = run_gpu(cache, w.q, W=w.W, bias_or_c=c, z=w.z, scale=w.scale, build_meta=False)
     worst, flips, screened = check_units(w, g, units, W=w.W, bias_or_c=c, z=w.z,
                                          scale=w.scale)
     sl = w.seq_len.cpu().numpy()

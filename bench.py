@@ -29,7 +29,9 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 COUNTERS = os.path.join(ROOT, "profiles", "decode_counters.json")
-DECODE_SRC = os.path.join(ROOT, "long_context_decode_eta_amd", "csrc", "kernels_decode.hip")
+# the decode kernels and the host code that picks their launch path
+DECODE_SRC = [os.path.join(ROOT, "long_context_decode_eta_amd", "csrc", f)
+              for f in ("kernels_decode.hip", "eta_api.hip")]
 
 
 def parse():
@@ -81,7 +83,10 @@ class Timer:
 
 
 def kernel_hash() -> str:
-    return hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in DECODE_SRC:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def main():
@@ -255,7 +260,7 @@ def main():
         cj = json.load(open(COUNTERS))
         if cj.get("kernel_hash") == kernel_hash() and cj.get("workload") == args.workload:
             traffic = cj.get("hbm_bytes_per_launch")
-    roofline = {"bound": "hbm", "kernel": "decode_queue_kernel (eta_decode)",
+    roofline = {"bound": "hbm", "kernel": "eta_decode (prepare + decode + combine kernels)",
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "algorithmic_bytes_per_launch": int(r["decode_bytes"]),

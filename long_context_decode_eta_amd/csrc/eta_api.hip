@@ -266,11 +266,16 @@ static eta_status decode_common(const eta_cache* c, const float* q, const float*
   a.part_l = reinterpret_cast<float*>(w + off_parts + align256(slots * 4));
   a.part_acc = reinterpret_cast<float*>(w + off_parts + 2 * align256(slots * 4));
   a.out = out;
-  // The queue kernel keeps the chunk table and one chunk's block list in LDS.
-  // Dense decode has no empty chunks to skip and streams its contiguous
-  // chunks fastest from the flat stream-major grid (measured: 6.95 vs 6.46
-  // TB/s on 8 x 128K), so only the sparse path uses the queue.
-  const bool queue = !dense && units <= eta::kMaxQueueUnits &&
+  // Sparse chunks run on the flat stream-major grid (one work-group per
+  // possible chunk) unless that grid would be mostly empty work-groups: when
+  // it exceeds kQueueAboveGrid work-groups (a ragged batch padded to a long
+  // capacity), chunks come from the queue kernel instead.  Measured on MI355X:
+  // flat 507 vs queue 544 us (8 x 128K, 38%), 82 vs 128 us (512K, 10%); queue
+  // 236 vs flat 394 us (ragged 32 x 8K..64K, 10%).  Dense decode has no empty
+  // chunks and always uses the flat grid.  The queue kernel keeps the chunk
+  // table and one chunk's block list in LDS.
+  const bool queue = !dense && (long long)maxc * units > eta::kQueueAboveGrid &&
+                     units <= eta::kMaxQueueUnits &&
                      (size_t)(units + 1) * 4 + (size_t)split * 4 <= 48 * 1024;
   a.use_queue = queue;
   a.queue = reinterpret_cast<int*>(w);

@@ -152,8 +152,10 @@ struct DecodeArgs {
   bool use_queue;    // queue kernel (else one work-group per possible chunk)
   int queue_grid;    // work-groups of the queue kernel
 };
-// Streams up to which the queue kernel is used (its chunk table lives in LDS).
+// Streams up to which the queue kernel can be used (its chunk table lives in
+// LDS), and the flat-grid size above which it is.
 constexpr int kMaxQueueUnits = 8192;
+constexpr long long kQueueAboveGrid = 49152;
 hipError_t launch_decode(const CacheView& c, const DecodeArgs& a, hipStream_t s);
 hipError_t launch_calibrate(const CacheView& c, int n_sets, const float* q_sets,
                             const float* tau0, float z, float scale, float rho, float* values,

@@ -173,3 +173,17 @@ def test_dense_decode(kv):
     K, V = synth.kv_numpy(w.k), synth.kv_numpy(w.v)
     ref = oracle.dense_batch(w.q.cpu().numpy(), K, V, w.seq_len.cpu().numpy(), scale=w.scale)
     compare_outputs(out.cpu().numpy(), ref, w.kv_dtype, "dense")
+
+
+def test_queue_scheduled_decode_path():
+    # 1024 streams with one block per chunk: the flat grid would hold
+    # 1024 x 256 work-groups, so eta_decode takes chunks from its work queue.
+    w = to_gpu(synth.make("ragged", seed=13, T=(1, 4096), B=64, H=16, cap=4096, pad="nan"))
+    cache = make_cache(w)
+    assert w.B * w.H * cache.cap_blocks > 49152
+    c = torch.linspace(1.5, 2.5, 16, device="cuda")
+    for mode in (eb.GATED, eb.RAW):
+        g = run_gpu(cache, w.q, bias_or_c=c, z=w.z, scale=w.scale, mode=mode, split=1)
+        st = check_against_oracle(w, g, cache, W=None, bias_or_c=c, z=w.z, scale=w.scale,
+                                  mode=mode)
+    note(f"  density {st['density']:.3f} out_rel {st['out_rel']:.2e}")

@@ -108,7 +108,11 @@ def main():
     dev = "cuda"
     torch.cuda.set_device(0)
     t0 = time.time()
-    w = synth.make(args.workload, seed=args.seed, device=dev)
+    blk = synth.CONFIGS[args.workload]["block"]
+    Tmax = synth.CONFIGS[args.workload]["T"]
+    Tmax = Tmax[1] if isinstance(Tmax, tuple) else Tmax
+    # room for the appends of the upkeep measurement (4 blocks per stream)
+    w = synth.make(args.workload, seed=args.seed, device=dev, cap=Tmax + 4 * blk)
     B, H, D, bs = w.B, w.H, w.D, w.block
     cache = eb.KVCache(B, H, D, bs, w.cap, w.kv_dtype, device=dev, k=w.k, v=w.v)
     cache.seq_len.copy_(w.seq_len)
@@ -266,6 +270,9 @@ def main():
                 "algorithmic_bytes_per_launch": int(r["decode_bytes"]),
                 "avg_launch_ms": round(r["decode_ms"], 5)}
 
+    upkeep = measure_upkeep(torch, eb, w, cache, dec, consts[args.rho], frozen, sumT)
+    print(f"[bench] upkeep: {json.dumps(upkeep)}", file=sys.stderr, flush=True)
+
     cpu = None if args.no_cpu else cpu_baseline(w, consts[args.rho], args.rho)
 
     out = {
@@ -308,9 +315,74 @@ def main():
                                "ideal_speedup": round(dense_bytes / v["step_bytes"], 3)}
                   for k, v in sweep.items()},
         "roofline": roofline,
+        "upkeep": upkeep,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def measure_upkeep(torch, eb, w, cache, dec, c, frozen, sumT):
+    """Cache upkeep, timed apart from the step: the bulk statistics build that
+    follows a prefill, single-token appends (which compute the statistics of
+    every block they complete), and the whole per-token loop (append, then
+    threshold, screen and decode) run across block boundaries.  Each is timed
+    over 2 blocks' worth of tokens so block completions are included at their
+    real rate.  Leaves every sequence 4 blocks longer."""
+    B, H, D, bs = w.B, w.H, w.D, w.block
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    s0, e0 = ev(), ev()
+    s0.record()
+    for _ in range(3):
+        eb.build_block_meta(cache)
+    e0.record()
+    torch.cuda.synchronize()
+    meta_ms = s0.elapsed_time(e0) / 3
+    elt = cache.k.element_size()
+    meta_bytes = sumT * H * D * elt + (sumT // bs) * H * (2 * D + 1) * 4
+
+    g = torch.Generator(device="cuda").manual_seed(99)
+    kn = torch.randn((B, H, D), generator=g, device="cuda").to(cache.kv_dtype)
+    vn = torch.randn((B, H, D), generator=g, device="cuda").to(cache.kv_dtype)
+    n = 2 * bs
+    torch.cuda.synchronize()
+    s1, e1 = ev(), ev()
+    s1.record()
+    for _ in range(n):
+        eb.append_kv(cache, kn, vn)
+    e1.record()
+    torch.cuda.synchronize()
+    append_us = s1.elapsed_time(e1) * 1e3 / n
+
+    if frozen:
+        dec.predict(w.q, None, c)
+    s2, e2 = ev(), ev()
+    s2.record()
+    for _ in range(n):
+        eb.append_kv(cache, kn, vn)
+        if not frozen:
+            dec.predict(w.q, w.W, c)
+        dec.screen(w.q)
+        dec.attend(w.q)
+    e2.record()
+    torch.cuda.synchronize()
+    loop_ms = s2.elapsed_time(e2) / n
+    s3, e3 = ev(), ev()
+    s3.record()
+    for _ in range(n):
+        if not frozen:
+            dec.predict(w.q, w.W, c)
+    e3.record()
+    torch.cuda.synchronize()
+    pred_us = s3.elapsed_time(e3) * 1e3 / n
+    return {"meta_build_ms": round(meta_ms, 4),
+            "meta_build_gbs": round(meta_bytes / meta_ms / 1e6, 1),
+            "append_us": round(append_us, 2),
+            "predict_us": round(pred_us, 2) if not frozen else 0.0,
+            "loop_ms_per_token": round(loop_ms, 5),
+            "tokens_timed": n}
 
 
 def cpu_baseline(w, c_gpu, rho):

@@ -15,11 +15,14 @@ namespace eta {
 // the wave covers RPI = 64 / LPR rows.  Each lane accumulates its EPL columns
 // over rows g, g+RPI, ...; the column sums of the RPI row groups are then
 // combined with an xor butterfly.  Row norms are reduced inside the lane group
-// with DPP.  `last_row`, when given, replaces row b-1 (the append path passes
-// the key it has just written, so the block is complete without re-reading).
-// Both the append and the bulk path call this function, so they produce
-// bit-identical statistics.
-template <int D, int DT>
+// with DPP.  When a lane's share of the block is at most NR loads, the rows
+// stay in registers between the mean and the variance pass (K is read from
+// HBM once); larger blocks re-read them.  `last_row`, when given, replaces row
+// b-1 (the append path passes the key it has just written, so the block is
+// complete without re-reading).  Both the append and the bulk path call this
+// function with the same summation order, so they produce bit-identical
+// statistics.
+template <int D, int DT, int NR>
 __device__ __forceinline__ void block_stats_wave(const CacheView& c, int u, int j,
                                                  const void* last_row, int lane) {
   constexpr int EPL = Elt<DT>::kPer16B;
@@ -28,27 +31,48 @@ __device__ __forceinline__ void block_stats_wave(const CacheView& c, int u, int 
   constexpr int RB = D * Elt<DT>::kBytes;  // bytes per key row
   const int g = lane / LPR, li = lane % LPR;
   const char* base = static_cast<const char*>(c.k) + ((size_t)u * c.cap + ((size_t)j << c.log2bs)) * RB;
+  auto row_ptr = [&](int r) {
+    return ((last_row && r == c.bs - 1) ? static_cast<const char*>(last_row)
+                                        : base + (size_t)r * RB) + li * 16;
+  };
+  const int nr = (c.bs + RPI - 1) / RPI;  // loads per lane
+  const bool keep = nr <= NR;             // rows fit in registers
 
+  uint4 rows[NR];
+  if (keep) {
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const int r = i * RPI + g;
+      rows[i] = (i < nr && r < c.bs) ? ld16_nt(row_ptr(r)) : make_uint4(0, 0, 0, 0);
+    }
+  }
   float sum[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) sum[e] = 0.f;
   float best = 0.f;  // largest squared row norm
-  for (int r0 = 0; r0 < c.bs; r0 += RPI) {
-    const int r = r0 + g;
-    float x[EPL];
+  auto first_pass = [&](int r, const uint4& raw) {
     float n2 = 0.f;
     if (r < c.bs) {
-      const char* src = (last_row && r == c.bs - 1) ? static_cast<const char*>(last_row)
-                                                    : base + (size_t)r * RB;
-      widen<DT>(ld16(src + li * 16), x);
+      float x[EPL];
+      widen<DT>(raw, x);
 #pragma unroll
       for (int e = 0; e < EPL; ++e) {
         sum[e] += x[e];
         n2 = fmaf(x[e], x[e], n2);
       }
     }
-    n2 = group_sum<LPR>(n2);
+    n2 = group_sum<LPR>(n2);  // every lane of the wave takes part
     best = fmaxf(best, n2);
+  };
+  if (keep) {
+#pragma unroll
+    for (int i = 0; i < NR; ++i)
+      if (i < nr) first_pass(i * RPI + g, rows[i]);
+  } else {
+    for (int i = 0; i < nr; ++i) {
+      const int r = i * RPI + g;
+      first_pass(r, r < c.bs ? ld16(row_ptr(r)) : make_uint4(0, 0, 0, 0));
+    }
   }
 #pragma unroll
   for (int off = LPR; off < kWave; off <<= 1) {
@@ -63,18 +87,25 @@ __device__ __forceinline__ void block_stats_wave(const CacheView& c, int u, int 
     mean[e] = sum[e] * inv_b;
     ss[e] = 0.f;
   }
-  for (int r0 = 0; r0 < c.bs; r0 += RPI) {
-    const int r = r0 + g;
+  auto second_pass = [&](int r, const uint4& raw) {
     if (r < c.bs) {
-      const char* src = (last_row && r == c.bs - 1) ? static_cast<const char*>(last_row)
-                                                    : base + (size_t)r * RB;
       float x[EPL];
-      widen<DT>(ld16(src + li * 16), x);
+      widen<DT>(raw, x);
 #pragma unroll
       for (int e = 0; e < EPL; ++e) {
         const float dlt = x[e] - mean[e];
         ss[e] = fmaf(dlt, dlt, ss[e]);
       }
+    }
+  };
+  if (keep) {
+#pragma unroll
+    for (int i = 0; i < NR; ++i)
+      if (i < nr) second_pass(i * RPI + g, rows[i]);
+  } else {
+    for (int i = 0; i < nr; ++i) {
+      const int r = i * RPI + g;
+      if (r < c.bs) second_pass(r, ld16(row_ptr(r)));
     }
   }
 #pragma unroll
@@ -93,33 +124,44 @@ __device__ __forceinline__ void block_stats_wave(const CacheView& c, int u, int 
   }
 }
 
+constexpr int kStatRows = 16;  // loads per lane kept in registers (64 VGPRs)
+
 // ---------------------------------------------------------------------------
-// Append: one wavefront per (b, h) stream.
+// Append: one work-group per sequence b, one wavefront per head (heads h,
+// h + waves, ... when there are more heads than waves).  Every wave writes its
+// head's k and v at position T_b and computes the statistics of the block the
+// token completes; after a barrier one thread advances T_b, so the whole
+// append is one launch.
+constexpr int kAppendWaves = 8;
 template <int D, int DT>
-__global__ __launch_bounds__(64) void append_kernel(CacheView c, const void* k_new,
-                                                    const void* v_new, int32_t* overflow) {
+__global__ __launch_bounds__(kAppendWaves * kWave) void append_kernel(CacheView c,
+                                                                      const void* k_new,
+                                                                      const void* v_new,
+                                                                      int32_t* overflow) {
   constexpr int RB = D * Elt<DT>::kBytes;
-  const int u = blockIdx.x, lane = threadIdx.x;
-  const int pos = c.seq_len[u / c.H];
-  if (pos >= c.cap) {
-    if (overflow && lane == 0) *overflow = 1;
+  const int b = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int waves = blockDim.x >> 6;
+  const int pos = c.seq_len[b];
+  if (pos >= c.cap) {  // uniform over the work-group
+    if (overflow && threadIdx.x == 0) *overflow = 1;
     return;
   }
-  const char* kn = static_cast<const char*>(k_new) + (size_t)u * RB;
-  const char* vn = static_cast<const char*>(v_new) + (size_t)u * RB;
-  const size_t off = ((size_t)u * c.cap + pos) * RB;
-  char* kd = static_cast<char*>(const_cast<void*>(c.k)) + off;
-  char* vd = static_cast<char*>(const_cast<void*>(c.v)) + off;
-  for (int p = lane; p < RB / 16; p += kWave) {
-    *reinterpret_cast<uint4*>(kd + p * 16) = ld16(kn + p * 16);
-    *reinterpret_cast<uint4*>(vd + p * 16) = ld16(vn + p * 16);
+  for (int h = wave; h < c.H; h += waves) {
+    const int u = b * c.H + h;
+    const char* kn = static_cast<const char*>(k_new) + (size_t)u * RB;
+    const char* vn = static_cast<const char*>(v_new) + (size_t)u * RB;
+    const size_t off = ((size_t)u * c.cap + pos) * RB;
+    char* kd = static_cast<char*>(const_cast<void*>(c.k)) + off;
+    char* vd = static_cast<char*>(const_cast<void*>(c.v)) + off;
+    for (int p = lane; p < RB / 16; p += kWave) {
+      *reinterpret_cast<uint4*>(kd + p * 16) = ld16(kn + p * 16);
+      *reinterpret_cast<uint4*>(vd + p * 16) = ld16(vn + p * 16);
+    }
+    if (((pos + 1) & (c.bs - 1)) == 0)
+      block_stats_wave<D, DT, kStatRows>(c, u, pos >> c.log2bs, kn, lane);
   }
-  if (((pos + 1) & (c.bs - 1)) == 0) block_stats_wave<D, DT>(c, u, pos >> c.log2bs, kn, lane);
-}
-
-__global__ void bump_len_kernel(int B, int cap, int32_t* seq_len) {
-  const int b = blockIdx.x * blockDim.x + threadIdx.x;
-  if (b < B && seq_len[b] < cap) seq_len[b] += 1;
+  __syncthreads();  // every wave has read T_b
+  if (threadIdx.x == 0) const_cast<int32_t*>(c.seq_len)[b] = pos + 1;
 }
 
 // Bulk statistics: 4 wavefronts per work-group, one block each.
@@ -134,7 +176,7 @@ __global__ __launch_bounds__(256) void block_meta_kernel(CacheView c, int first,
   const int j = first + i;
   const int T = c.seq_len[u / c.H];
   if (j >= (T >> c.log2bs)) return;
-  block_stats_wave<D, DT>(c, u, j, nullptr, lane);
+  block_stats_wave<D, DT, kStatRows>(c, u, j, nullptr, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -208,11 +250,8 @@ __global__ __launch_bounds__(256) void predict_kernel(int H, int D, const float*
 template <int D, int DT>
 static hipError_t append_t(const CacheView& c, const void* kn, const void* vn, int32_t* of,
                            hipStream_t s) {
-  hipLaunchKernelGGL((append_kernel<D, DT>), dim3(c.B * c.H), dim3(64), 0, s, c, kn, vn, of);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bump_len_kernel, dim3(ceil_div(c.B, 256)), dim3(256), 0, s, c.B, c.cap,
-                     const_cast<int32_t*>(c.seq_len));
+  const int waves = c.H < kAppendWaves ? c.H : kAppendWaves;
+  hipLaunchKernelGGL((append_kernel<D, DT>), dim3(c.B), dim3(waves * kWave), 0, s, c, kn, vn, of);
   return hipGetLastError();
 }
 

@@ -83,6 +83,11 @@ def load(path: str | None = None):
     lib.eta_oracle_dense_batch.restype = None
     lib.eta_oracle_calibrate.argtypes = [_i] * 6 + [_p] * 6 + [_d, _d, _d, _p, _p]
     lib.eta_oracle_calibrate.restype = None
+    lib.eta_oracle_gqa_screen_attend_batch.argtypes = (
+        [_i] * 7 + [_p] * 7 + [_p, _p] + [_d, _d, _i, _d] + [_p] * 8)
+    lib.eta_oracle_gqa_screen_attend_batch.restype = None
+    lib.eta_oracle_gqa_dense_batch.argtypes = [_i] * 6 + [_p] * 4 + [_d, _p]
+    lib.eta_oracle_gqa_dense_batch.restype = None
     lib.eta_oracle_threads.argtypes = []
     lib.eta_oracle_threads.restype = _i
     if path is None:
@@ -235,6 +240,50 @@ def screen_attend_batch(q, K, V, seq_len, b, meta, tau, tau_screen, *, z=1.0, sc
                                        _ptr(r["score"]), _ptr(r["active"]), _ptr(r["cnt"]),
                                        _ptr(r["tokens"]), _ptr(r["out"]))
     return r
+
+
+def gqa_screen_attend_batch(q, K, V, seq_len, b, meta, tau, tau_screen, group, *, z=1.0,
+                            scale=None, mode=GATED, beta=5.0, lib=None):
+    """Grouped-query screen and attention: q [B][Hkv*G][d], K/V and statistics
+    per KV head [B][Hkv][...], thresholds [B][Hkv*G] (fp64)."""
+    lib = lib or load()
+    q = _f32(q); K, dt = _kv(K); V, dt2 = _kv(V)
+    assert dt == dt2
+    B, Hkv, cap, d = K.shape
+    G = int(group)
+    Hq = Hkv * G
+    assert q.shape == (B, Hq, d)
+    nbcap = -(-cap // b)
+    if scale is None:
+        scale = float(np.float32(1.0 / np.sqrt(d)))
+    mu, var, M = (np.ascontiguousarray(x, dtype=np.float64) for x in meta)
+    sl = np.ascontiguousarray(seq_len, dtype=np.int32)
+    tau = np.ascontiguousarray(tau, dtype=np.float64).reshape(B, Hq)
+    ts = np.ascontiguousarray(tau_screen, dtype=np.float64).reshape(B, Hq)
+    r = dict(tau=tau, tau_screen=ts, score=np.zeros((B, Hq, nbcap)),
+             active=np.zeros((B, Hq, nbcap), np.uint8), cnt=np.zeros((B, Hq), np.int32),
+             tokens=np.zeros((B, Hq), np.int64), union=np.zeros((B, Hkv, nbcap), np.uint8),
+             union_cnt=np.zeros((B, Hkv), np.int32), union_tokens=np.zeros((B, Hkv), np.int64),
+             out=np.zeros((B, Hq, d)))
+    lib.eta_oracle_gqa_screen_attend_batch(
+        B, Hkv, G, d, b, cap, dt, _ptr(sl), _ptr(q), _ptr(K), _ptr(V), _ptr(mu), _ptr(var),
+        _ptr(M), _ptr(tau), _ptr(ts), float(z), float(scale), int(mode), float(beta),
+        _ptr(r["score"]), _ptr(r["active"]), _ptr(r["cnt"]), _ptr(r["tokens"]), _ptr(r["union"]),
+        _ptr(r["union_cnt"]), _ptr(r["union_tokens"]), _ptr(r["out"]))
+    return r
+
+
+def gqa_dense_batch(q, K, V, seq_len, group, scale=None, lib=None):
+    lib = lib or load()
+    q = _f32(q); K, dt = _kv(K); V, _ = _kv(V)
+    B, Hkv, cap, d = K.shape
+    if scale is None:
+        scale = float(np.float32(1.0 / np.sqrt(d)))
+    sl = np.ascontiguousarray(seq_len, dtype=np.int32)
+    out = np.zeros((B, Hkv * int(group), d))
+    lib.eta_oracle_gqa_dense_batch(B, Hkv, int(group), d, cap, dt, _ptr(sl), _ptr(q), _ptr(K),
+                                   _ptr(V), float(scale), _ptr(out))
+    return out
 
 
 def attend_batch(q, K, V, seq_len, b, active, tau, *, mode=GATED, beta=5.0, scale=None,

@@ -307,6 +307,80 @@ void eta_oracle_dense_batch(int B, int H, int d, int cap, int dtype, const int32
 }
 
 /* ---------------------------------------------------------------------- */
+/* Grouped-query decode (the pages' benchmark shape: several query heads
+ * share one KV head; v2 page, Table 5; summary, Theoretical and Practical
+ * Implications on the GQA-union bandwidth).  Query head h = kv * G + g reads
+ * KV head kv.  Each query head is screened with its own query and threshold
+ * against the KV head's block statistics (Eq. 5), attends only over the
+ * blocks it admits itself (D_head), and a KV block is loaded when any head of
+ * the group admits it (the union, D_union).
+ *   q [B][Hkv*G][d], tau/tau_screen [B][Hkv*G]; K, V, statistics per KV head.
+ * Outputs: score/active [B][Hkv*G][nbcap], cnt/tokens [B][Hkv*G],
+ * union_active [B][Hkv][nbcap], union_cnt/union_tokens [B][Hkv], out
+ * [B][Hkv*G][d]. */
+void eta_oracle_gqa_screen_attend_batch(int B, int Hkv, int G, int d, int b, int cap, int dtype,
+                                        const int32_t* seq_len, const float* q, const void* K,
+                                        const void* V, const double* mu, const double* var,
+                                        const double* maxnorm, const double* tau,
+                                        const double* tau_screen, double z, double scale,
+                                        int mode, double beta, double* score, uint8_t* active,
+                                        int32_t* cnt, int64_t* tokens, uint8_t* union_active,
+                                        int32_t* union_cnt, int64_t* union_tokens, double* out) {
+  int nbcap = (cap + b - 1) / b;
+  int Hq = Hkv * G;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int uq = 0; uq < B * Hq; ++uq) {
+    int bb = uq / Hq, kv = (uq % Hq) / G;
+    size_t ukv = (size_t)bb * Hkv + kv;
+    int T = seq_len[bb];
+    const float* qu = q + (size_t)uq * d;
+    size_t kv_off = ukv * cap * d * elt_bytes(dtype);
+    double* sc = score + (size_t)uq * nbcap;
+    uint8_t* act = active + (size_t)uq * nbcap;
+    for (int j = 0; j < nbcap; ++j) sc[j] = NAN;
+    for (int j = 0; j < T / b; ++j)
+      sc[j] = eta_oracle_block_score(qu, mu + (ukv * nbcap + j) * d, var + (ukv * nbcap + j) * d,
+                                     maxnorm[ukv * nbcap + j], d, z, scale);
+    memset(act, 0, (size_t)nbcap);
+    cnt[uq] = eta_oracle_admit(T, b, sc, tau_screen[uq], act);
+    int64_t tk = 0;
+    for (int s = 0; s < T; ++s) tk += act[s / b];
+    tokens[uq] = tk;
+    eta_oracle_attend(qu, (const char*)K + kv_off, (const char*)V + kv_off, dtype, T, d, b, act,
+                      mode, beta, tau[uq], scale, out + (size_t)uq * d);
+  }
+  for (int u = 0; u < B * Hkv; ++u) {
+    int T = seq_len[u / Hkv];
+    uint8_t* un = union_active + (size_t)u * nbcap;
+    int c = 0;
+    int64_t tk = 0;
+    for (int j = 0; j < nbcap; ++j) {
+      uint8_t on = 0;
+      for (int g = 0; g < G; ++g) on |= active[((size_t)u * G + g) * nbcap + j];
+      un[j] = on;
+      c += on;
+    }
+    for (int s = 0; s < T; ++s) tk += un[s / b];
+    union_cnt[u] = c;
+    union_tokens[u] = tk;
+  }
+}
+
+/* Dense grouped-query decode: every query head over every key of its KV head. */
+void eta_oracle_gqa_dense_batch(int B, int Hkv, int G, int d, int cap, int dtype,
+                                const int32_t* seq_len, const float* q, const void* K,
+                                const void* V, double scale, double* out) {
+  int Hq = Hkv * G;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int uq = 0; uq < B * Hq; ++uq) {
+    int bb = uq / Hq, kv = (uq % Hq) / G;
+    size_t kv_off = ((size_t)bb * Hkv + kv) * cap * d * elt_bytes(dtype);
+    eta_oracle_dense(q + (size_t)uq * d, (const char*)K + kv_off, (const char*)V + kv_off, dtype,
+                     seq_len[bb], d, scale, out + (size_t)uq * d);
+  }
+}
+
+/* ---------------------------------------------------------------------- */
 /* Offline calibration of frozen per-head constants (the pages describe an
  * offline algorithm that freezes per-(layer, head) thresholds but give no
  * steps; this is the plain quantile reading).  For head h, pool over the

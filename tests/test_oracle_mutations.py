@@ -2,7 +2,8 @@
 
 Each case plants one mistake in a copy of oracle/eta_oracle.c (on the CPU),
 builds it, and runs the pin suites (test_oracle_hand_example.py,
-test_oracle_properties.py) against the mutant through ETA_ORACLE_LIB.  Every
+test_oracle_properties.py, test_oracle_gqa.py) against the mutant through
+ETA_ORACLE_LIB.  Every
 mutant must make at least one pin fail; the unmodified source must pass.
 """
 import os
@@ -16,7 +17,8 @@ import oracle
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 PINS = [os.path.join(HERE, "test_oracle_hand_example.py"),
-        os.path.join(HERE, "test_oracle_properties.py")]
+        os.path.join(HERE, "test_oracle_properties.py"),
+        os.path.join(HERE, "test_oracle_gqa.py")]
 
 MUTANTS = {
     "sample_variance": ("var[(size_t)j * d + i] = s / b;", "var[(size_t)j * d + i] = s / (b - 1);"),
@@ -47,6 +49,10 @@ MUTANTS = {
     "calibration_off_by_one": ("c = 0.5 * (x[k - 1] + x[k]);", "c = 0.5 * (x[k] + x[k + 1 < (long long)n ? k + 1 : k]);"),
     "calibration_forced_ignored": ("double want = (rho * total - forced) / b;",
                                    "double want = (rho * total) / b;"),
+    "gqa_wrong_kv_head": ("int bb = uq / Hq, kv = (uq % Hq) / G;",
+                          "int bb = uq / Hq, kv = (uq % Hq) % Hkv;", 2),
+    "gqa_union_counts_first_head": ("for (int g = 0; g < G; ++g) on |= active",
+                                    "for (int g = 0; g < 1; ++g) on |= active"),
 }
 
 

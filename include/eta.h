@@ -17,8 +17,10 @@
  *                                                        (Eq. 3, Fig. 6)
  *
  * plus eta_build_block_meta (statistics of many blocks, e.g. after prefill),
- * eta_dense_decode (the same kernels over every key: plain dense decode) and
- * eta_calibrate_threshold (per-head constants for a target density).
+ * eta_dense_decode (the same kernels over every key: plain dense decode),
+ * eta_calibrate_threshold (per-head constants for a target density) and the
+ * grouped-query forms eta_screen_gqa / eta_decode_gqa / eta_dense_decode_gqa
+ * (several query heads per KV head, one read of each union block).
  *
  * Conventions shared by every call
  *   - Every function returns eta_status; ETA_OK is 0.  All arguments are
@@ -49,7 +51,7 @@
 extern "C" {
 #endif
 
-#define ETA_ABI_VERSION 1
+#define ETA_ABI_VERSION 2
 
 typedef int32_t eta_status;
 enum {
@@ -209,6 +211,68 @@ eta_status eta_calibrate_threshold(const eta_cache* c, int32_t n_sets, const flo
                                    const float* tau0, float z, float scale,
                                    float target_density, void* workspace,
                                    size_t workspace_bytes, float* c_out, void* stream);
+
+/*
+ * Grouped-query attention (thelatestinai.com paper page: Table 5's benchmark
+ * shape of 32 query heads on 4 KV heads, Fig. 9 union loading vs per-head
+ * compute; picx.dev summary, Practical Implications: a block is read when any
+ * head of the group admits it).  The cache holds KV heads: c->heads is the
+ * KV head count H_kv, and query head h = kv * group + g (0 <= g < group)
+ * reads KV head kv.  q is device [batch][H_kv * group][head_dim] float32;
+ * thresholds are device [batch][H_kv * group].  1 <= group <= 16.
+ *
+ * eta_screen_gqa: every query head is screened exactly as eta_screen does
+ * against the statistics of its KV head (Eq. 5, own query and own
+ * tau_screen; the last block is admitted for every head).  Outputs, device:
+ *   head_mask  [batch][H_kv][cap_blocks] uint32: bit g of entry j is set iff
+ *              query head kv * group + g admits block j (entries j < n_b,
+ *              the block count of sequence b; the rest unspecified);
+ *   union_idx  [batch][H_kv][cap_blocks] int32: ascending list of the blocks
+ *              admitted by at least one head of the group (the union), in
+ *              the first union_cnt[b][kv] entries;
+ *   union_cnt  [batch][H_kv] int32;
+ *   density_ctr (optional, two uint64): [0] += admitted tokens summed over
+ *              query heads (D_head numerator), [1] += union tokens summed
+ *              over KV heads (D_union numerator).
+ * Workspace: eta_screen_gqa_workspace_bytes(); no initialisation needed.
+ */
+size_t eta_screen_gqa_workspace_bytes(int32_t batch, int32_t kv_heads, int32_t cap_blocks);
+eta_status eta_screen_gqa(const eta_cache* c, int32_t group, const float* q,
+                          const float* tau_screen, float z, float scale, int32_t* union_idx,
+                          uint32_t* head_mask, int32_t* union_cnt, uint64_t* density_ctr,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Grouped-query block-sparse decode.  Each block of the union list is read
+ * once for its whole group; query head kv * group + g attends over the keys of
+ * the blocks whose head_mask bit g is set, with the logits of eta_decode
+ * (Eq. 3, its own tau_gate; the query's own key is never gated), normalised
+ * over its own admitted set.  Chunks of blocks_per_split union blocks, partial
+ * results per query head, log-sum-exp combine; out is device
+ * [batch][H_kv * group][head_dim] float32, zeros for T_b == 0.
+ * Requires kv_dtype == ETA_DT_BF16: the scores and value sums run on the
+ * matrix cores as bf16 products with float32 accumulation, the query and the
+ * softmax weights each split into two bf16 terms (float32-level accuracy).
+ * 1 <= blocks_per_split <= 2048.
+ * Workspace: eta_decode_gqa_workspace_bytes(); no initialisation needed.
+ */
+size_t eta_decode_gqa_workspace_bytes(int32_t batch, int32_t kv_heads, int32_t group,
+                                      int32_t head_dim, int32_t cap_blocks,
+                                      int32_t blocks_per_split);
+eta_status eta_decode_gqa(const eta_cache* c, int32_t group, const float* q,
+                          const float* tau_gate, const int32_t* union_idx,
+                          const uint32_t* head_mask, const int32_t* union_cnt,
+                          int32_t logit_mode, float beta, float scale, int32_t blocks_per_split,
+                          void* workspace, size_t workspace_bytes, float* out, void* stream);
+
+/*
+ * Grouped-query dense decode: every key of its KV head for every query head,
+ * RAW logits, the same kernels as eta_decode_gqa (the dense GQA baseline).
+ * Workspace as for eta_decode_gqa.
+ */
+eta_status eta_dense_decode_gqa(const eta_cache* c, int32_t group, const float* q, float scale,
+                                int32_t blocks_per_split, void* workspace,
+                                size_t workspace_bytes, float* out, void* stream);
 
 #ifdef __cplusplus
 }

@@ -58,6 +58,16 @@ _SIGS = {
     "eta_calibrate_workspace_bytes": ([c_int32, c_int32, c_int32, c_int32], c_size_t),
     "eta_calibrate_threshold": ([_P, c_int32, c_void_p, c_void_p, c_float, c_float, c_float,
                                  c_void_p, c_size_t, c_void_p, c_void_p], c_int32),
+    "eta_screen_gqa_workspace_bytes": ([c_int32, c_int32, c_int32], c_size_t),
+    "eta_screen_gqa": ([_P, c_int32, c_void_p, c_void_p, c_float, c_float, c_void_p, c_void_p,
+                        c_void_p, c_void_p, c_void_p, c_size_t, c_void_p], c_int32),
+    "eta_decode_gqa_workspace_bytes": ([c_int32, c_int32, c_int32, c_int32, c_int32, c_int32],
+                                       c_size_t),
+    "eta_decode_gqa": ([_P, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
+                        c_float, c_float, c_int32, c_void_p, c_size_t, c_void_p, c_void_p],
+                       c_int32),
+    "eta_dense_decode_gqa": ([_P, c_int32, c_void_p, c_float, c_int32, c_void_p, c_size_t,
+                              c_void_p, c_void_p], c_int32),
 }
 
 _lib = None
@@ -219,6 +229,55 @@ def calibrate_threshold(cache: KVCache, q_sets, tau0, z, scale, target_density, 
            "eta_calibrate_threshold")
 
 
+# Grouped-query attention: the cache holds the KV heads, q and the thresholds
+# hold kv_heads * group query heads (query head kv * group + g reads KV head kv).
+def screen_gqa_workspace_bytes(batch, kv_heads, cap_blocks) -> int:
+    return int(lib().eta_screen_gqa_workspace_bytes(batch, kv_heads, cap_blocks))
+
+
+def screen_gqa(cache: KVCache, group, q, tau_screen, z, scale, union_idx, head_mask, union_cnt,
+               density_ctr, workspace, stream=None):
+    _check(lib().eta_screen_gqa(_ref(cache), int(group), _dev(q, torch.float32, "q"),
+                                _dev(tau_screen, torch.float32, "tau_screen"), float(z),
+                                float(scale), _dev(union_idx, torch.int32, "union_idx"),
+                                _dev(head_mask, torch.int32, "head_mask"),
+                                _dev(union_cnt, torch.int32, "union_cnt"),
+                                _dev(density_ctr, None, "density_ctr"),
+                                _dev(workspace, None, "workspace"),
+                                workspace.numel() * workspace.element_size(), _stream(stream)),
+           "eta_screen_gqa")
+
+
+def decode_gqa_workspace_bytes(batch, kv_heads, group, head_dim, cap_blocks,
+                               blocks_per_split) -> int:
+    return int(lib().eta_decode_gqa_workspace_bytes(batch, kv_heads, group, head_dim, cap_blocks,
+                                                    blocks_per_split))
+
+
+def decode_gqa(cache: KVCache, group, q, tau_gate, union_idx, head_mask, union_cnt, logit_mode,
+               beta, scale, blocks_per_split, workspace, out, stream=None):
+    _check(lib().eta_decode_gqa(_ref(cache), int(group), _dev(q, torch.float32, "q"),
+                                _dev(tau_gate, torch.float32, "tau_gate"),
+                                _dev(union_idx, torch.int32, "union_idx"),
+                                _dev(head_mask, torch.int32, "head_mask"),
+                                _dev(union_cnt, torch.int32, "union_cnt"), int(logit_mode),
+                                float(beta), float(scale), int(blocks_per_split),
+                                _dev(workspace, None, "workspace"),
+                                workspace.numel() * workspace.element_size(),
+                                _dev(out, torch.float32, "out"), _stream(stream)),
+           "eta_decode_gqa")
+
+
+def dense_decode_gqa(cache: KVCache, group, q, scale, blocks_per_split, workspace, out,
+                     stream=None):
+    _check(lib().eta_dense_decode_gqa(_ref(cache), int(group), _dev(q, torch.float32, "q"),
+                                      float(scale), int(blocks_per_split),
+                                      _dev(workspace, None, "workspace"),
+                                      workspace.numel() * workspace.element_size(),
+                                      _dev(out, torch.float32, "out"), _stream(stream)),
+           "eta_dense_decode_gqa")
+
+
 def workspace(nbytes: int, device="cuda") -> torch.Tensor:
     """A caller-owned byte workspace (torch allocation; 256-byte aligned)."""
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
@@ -283,4 +342,60 @@ class Decoder:
 
     def dense(self, q, stream=None):
         dense_decode(self.cache, q, self.scale, self.dense_split, self.decode_ws, self.out, stream)
+        return self.out
+
+
+class GqaDecoder:
+    """Grouped-query decode step with preallocated buffers: predict_tau over
+    the query heads -> screen_gqa (per-head masks, union lists) ->
+    decode_gqa.  ``density_ctr[0]`` accumulates admitted tokens over query
+    heads, ``density_ctr[1]`` union tokens over KV heads."""
+
+    def __init__(self, cache: KVCache, group: int, *, z, scale=None, beta=5.0, a=0.0,
+                 logit_mode=GATED, blocks_per_split=None, dense_blocks_per_split=None):
+        self.cache, self.group = cache, int(group)
+        self.z, self.beta, self.a = float(z), float(beta), float(a)
+        self.scale = float(scale) if scale is not None else float(
+            torch.tensor(1.0 / cache.head_dim ** 0.5, dtype=torch.float32).item())
+        B, Hkv, D, nbc = cache.batch, cache.heads, cache.head_dim, cache.cap_blocks
+        Hq = Hkv * self.group
+        self.mode = logit_mode
+        self.split = int(blocks_per_split or min(2048, auto_split(B * Hkv, nbc, cache.block)))
+        self.dense_split = int(dense_blocks_per_split or
+                               min(2048, auto_split(B * Hkv, nbc, cache.block, dense=True)))
+        dev = cache.k.device
+        self.tau_gate = torch.zeros((B, Hq), dtype=torch.float32, device=dev)
+        self.tau_screen = torch.zeros_like(self.tau_gate)
+        self.union_idx = torch.zeros((B, Hkv, nbc), dtype=torch.int32, device=dev)
+        self.head_mask = torch.zeros((B, Hkv, nbc), dtype=torch.int32, device=dev)
+        self.union_cnt = torch.zeros((B, Hkv), dtype=torch.int32, device=dev)
+        self.density_ctr = torch.zeros((2,), dtype=torch.int64, device=dev)
+        self.screen_ws = workspace(screen_gqa_workspace_bytes(B, Hkv, nbc), dev)
+        self.decode_ws = workspace(decode_gqa_workspace_bytes(
+            B, Hkv, self.group, D, nbc, min(self.split, self.dense_split)), dev)
+        self.out = torch.zeros((B, Hq, D), dtype=torch.float32, device=dev)
+
+    def predict(self, q, W, bias_or_c, stream=None):
+        predict_tau(q, W, bias_or_c, self.a, self.tau_gate, self.tau_screen, stream)
+
+    def screen(self, q, stream=None):
+        screen_gqa(self.cache, self.group, q, self.tau_screen, self.z, self.scale,
+                   self.union_idx, self.head_mask, self.union_cnt, self.density_ctr,
+                   self.screen_ws, stream)
+
+    def attend(self, q, stream=None):
+        decode_gqa(self.cache, self.group, q, self.tau_gate, self.union_idx, self.head_mask,
+                   self.union_cnt, self.mode, self.beta, self.scale, self.split, self.decode_ws,
+                   self.out, stream)
+
+    def step(self, q, W=None, bias_or_c=None, stream=None):
+        if bias_or_c is not None:
+            self.predict(q, W, bias_or_c, stream)
+        self.screen(q, stream)
+        self.attend(q, stream)
+        return self.out
+
+    def dense(self, q, stream=None):
+        dense_decode_gqa(self.cache, self.group, q, self.scale, self.dense_split,
+                         self.decode_ws, self.out, stream)
         return self.out

@@ -332,4 +332,128 @@ eta_status eta_calibrate_threshold(const eta_cache* c, int32_t n_sets, const flo
                     "eta_calibrate_threshold launch");
 }
 
+// ---------------------------------------------------------------------------
+// Grouped-query attention.
+
+size_t eta_screen_gqa_workspace_bytes(int32_t batch, int32_t kv_heads, int32_t cap_blocks) {
+  return eta_screen_workspace_bytes(batch, kv_heads, cap_blocks);
+}
+
+eta_status eta_screen_gqa(const eta_cache* c, int32_t group, const float* q,
+                          const float* tau_screen, float z, float scale, int32_t* union_idx,
+                          uint32_t* head_mask, int32_t* union_cnt, uint64_t* density_ctr,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  eta::CacheView v;
+  if (eta_status s = check_cache(c, &v)) return s;
+  if (group < 1 || group > eta::kMaxGroup)
+    return fail(ETA_ERR_BAD_SHAPE, "group %d outside [1, %d]", group, eta::kMaxGroup);
+  if (bad_float(z) || z < 0.f) return fail(ETA_ERR_BAD_ARG, "z must be >= 0 (or +inf)");
+  if (bad_float(scale) || !(scale > 0.f) || isinf(scale))
+    return fail(ETA_ERR_BAD_ARG, "scale must be finite and > 0");
+  if (empty(v)) return ok();
+  if (!q || !tau_screen || !union_idx || !head_mask || !union_cnt)
+    return fail(ETA_ERR_NULL_PTR, "q/tau_screen/union_idx/head_mask/union_cnt is NULL");
+  const size_t need = eta_screen_gqa_workspace_bytes(v.B, v.H, v.cap_blocks);
+  if (!workspace || workspace_bytes < need)
+    return fail(ETA_ERR_WORKSPACE, "screen workspace %zu bytes < %zu", workspace_bytes, need);
+  if ((long long)eta::ceil_div(v.cap_blocks, 64) * v.B * v.H > kMaxGrid)
+    return fail(ETA_ERR_BAD_SHAPE, "grid too large");
+  return hip_status(eta::launch_screen_gqa(v, group, q, tau_screen, z, scale, union_idx,
+                                           head_mask, union_cnt, density_ctr,
+                                           static_cast<uint64_t*>(workspace),
+                                           (hipStream_t)stream),
+                    "eta_screen_gqa launch");
+}
+
+// GQA decode workspace: [part_m | part_l | part_acc] per query head and chunk.
+static size_t decode_gqa_ws(long long units_q, int D, int cap_blocks, int split) {
+  const long long maxc = (cap_blocks + split - 1) / split;
+  const size_t slots = (size_t)units_q * (size_t)maxc;
+  return align256(slots * 4) * 2 + align256(slots * (size_t)D * 4);
+}
+
+size_t eta_decode_gqa_workspace_bytes(int32_t batch, int32_t kv_heads, int32_t group,
+                                      int32_t head_dim, int32_t cap_blocks,
+                                      int32_t blocks_per_split) {
+  if (batch <= 0 || kv_heads <= 0 || group <= 0 || head_dim <= 0 || cap_blocks <= 0 ||
+      blocks_per_split <= 0)
+    return 256;
+  return decode_gqa_ws((long long)batch * kv_heads * group, head_dim, cap_blocks,
+                       blocks_per_split);
+}
+
+static eta_status decode_gqa_common(const eta_cache* c, int32_t group, const float* q,
+                                    const float* tau_gate, const int32_t* union_idx,
+                                    const uint32_t* head_mask, const int32_t* union_cnt,
+                                    int32_t mode, bool dense, float beta, float scale,
+                                    int32_t split, void* ws, size_t ws_bytes, float* out,
+                                    void* stream) {
+  eta::CacheView v;
+  if (eta_status s = check_cache(c, &v)) return s;
+  if (group < 1 || group > eta::kMaxGroup)
+    return fail(ETA_ERR_BAD_SHAPE, "group %d outside [1, %d]", group, eta::kMaxGroup);
+  if (v.dtype != ETA_DT_BF16)
+    return fail(ETA_ERR_BAD_ARG, "grouped-query decode needs a bf16 cache (kv_dtype %d)",
+                v.dtype);
+  if (mode != ETA_LOGIT_GATED && mode != ETA_LOGIT_RAW)
+    return fail(ETA_ERR_BAD_ARG, "logit_mode %d unknown", mode);
+  if (mode == ETA_LOGIT_GATED && !dense && (bad_float(beta) || !(beta > 0.f) || isinf(beta)))
+    return fail(ETA_ERR_BAD_ARG, "beta must be finite and > 0");
+  if (bad_float(scale) || !(scale > 0.f) || isinf(scale))
+    return fail(ETA_ERR_BAD_ARG, "scale must be finite and > 0");
+  if (split < 1 || split > 2048)
+    return fail(ETA_ERR_BAD_ARG, "blocks_per_split %d outside [1, 2048]", split);
+  if (empty(v)) return ok();
+  if (!q || !out) return fail(ETA_ERR_NULL_PTR, "q/out is NULL");
+  if (!dense && (!union_idx || !head_mask || !union_cnt))
+    return fail(ETA_ERR_NULL_PTR, "union_idx/head_mask/union_cnt is NULL");
+  if (!dense && mode == ETA_LOGIT_GATED && !tau_gate)
+    return fail(ETA_ERR_NULL_PTR, "tau_gate is NULL in GATED mode");
+  const long long units = (long long)v.B * v.H;
+  const int maxc = eta::ceil_div(v.cap_blocks, split);
+  if ((long long)maxc * units > kMaxGrid || units * group > kMaxGrid)
+    return fail(ETA_ERR_BAD_SHAPE, "grid too large");
+  const size_t need = decode_gqa_ws(units * group, v.D, v.cap_blocks, split);
+  if (!ws || ws_bytes < need)
+    return fail(ETA_ERR_WORKSPACE, "decode workspace %zu bytes < %zu", ws_bytes, need);
+  const size_t slots = (size_t)units * group * maxc;
+  char* w = static_cast<char*>(ws);
+  eta::GqaDecode g;
+  g.G = group;
+  g.q = q;
+  g.tau = tau_gate;
+  g.union_idx = union_idx;
+  g.head_mask = head_mask;
+  g.union_cnt = union_cnt;
+  g.mode = dense ? ETA_LOGIT_RAW : mode;
+  g.dense = dense;
+  g.beta = beta;
+  g.scale = scale;
+  g.split = split;
+  g.max_chunks = maxc;
+  g.part_m = reinterpret_cast<float*>(w);
+  g.part_l = reinterpret_cast<float*>(w + align256(slots * 4));
+  g.part_acc = reinterpret_cast<float*>(w + 2 * align256(slots * 4));
+  g.out = out;
+  return hip_status(eta::launch_decode_gqa(v, g, (hipStream_t)stream), "eta_decode_gqa launch");
+}
+
+eta_status eta_decode_gqa(const eta_cache* c, int32_t group, const float* q,
+                          const float* tau_gate, const int32_t* union_idx,
+                          const uint32_t* head_mask, const int32_t* union_cnt,
+                          int32_t logit_mode, float beta, float scale, int32_t blocks_per_split,
+                          void* workspace, size_t workspace_bytes, float* out, void* stream) {
+  return decode_gqa_common(c, group, q, tau_gate, union_idx, head_mask, union_cnt, logit_mode,
+                           false, beta, scale, blocks_per_split, workspace, workspace_bytes, out,
+                           stream);
+}
+
+eta_status eta_dense_decode_gqa(const eta_cache* c, int32_t group, const float* q, float scale,
+                                int32_t blocks_per_split, void* workspace,
+                                size_t workspace_bytes, float* out, void* stream) {
+  return decode_gqa_common(c, group, q, nullptr, nullptr, nullptr, nullptr, ETA_LOGIT_RAW, true,
+                           1.f, scale, blocks_per_split, workspace, workspace_bytes, out,
+                           stream);
+}
+
 }  // extern "C"

@@ -157,6 +157,30 @@ struct DecodeArgs {
 constexpr int kMaxQueueUnits = 8192;
 constexpr long long kQueueAboveGrid = 49152;
 hipError_t launch_decode(const CacheView& c, const DecodeArgs& a, hipStream_t s);
+// Grouped-query attention: KV stream u = b*H + kv serves query heads
+// u*G .. u*G + G - 1 (G <= 16).
+struct GqaDecode {
+  int G;
+  const float* q;          // [B*H*G][D]
+  const float* tau;        // [B*H*G] gate thresholds (GATED)
+  const int32_t* union_idx;  // [B*H][cap_blocks] ascending union lists
+  const uint32_t* head_mask; // [B*H][cap_blocks] bit g: query head g admits block j
+  const int32_t* union_cnt;  // [B*H]
+  int mode;
+  bool dense;
+  float beta, scale;
+  int split, max_chunks;
+  float* part_m;    // [B*H*G][max_chunks]
+  float* part_l;    // [B*H*G][max_chunks]
+  float* part_acc;  // [B*H*G][max_chunks][D]
+  float* out;       // [B*H*G][D]
+};
+constexpr int kMaxGroup = 16;
+hipError_t launch_screen_gqa(const CacheView& c, int G, const float* q, const float* tau_screen,
+                             float z, float scale, int32_t* union_idx, uint32_t* head_mask,
+                             int32_t* union_cnt, uint64_t* ctr, uint64_t* words, hipStream_t s);
+size_t gqa_decode_lds_bytes(int D, int split);
+hipError_t launch_decode_gqa(const CacheView& c, const GqaDecode& g, hipStream_t s);
 hipError_t launch_calibrate(const CacheView& c, int n_sets, const float* q_sets,
                             const float* tau0, float z, float scale, float rho, float* values,
                             float* c_out, hipStream_t s);

@@ -1,0 +1,563 @@
+// kernels_gqa.hip -- grouped-query screen, compaction and decode.
+//
+// Paper: "Elastic Threshold Attention ..." (v2 page, Table 5 benchmark shape:
+// 32 query heads on 4 KV heads; summary page, Implications: a KV block is
+// loaded when any head of its group admits it).  Query head h = kv*G + g
+// reads KV head kv.  Every query head is screened with its own query and
+// threshold against the KV head's block statistics (Eq. 5) and attends only
+// over the blocks it admits itself (Eq. 3 logits); the union of the group's
+// admitted blocks is what is read from HBM, once for the whole group.
+//
+// With G query heads per loaded key row, the scores and the value sums are
+// G x b x d contractions, so the decode runs them on the matrix cores
+// (v_mfma_f32_16x16x32_bf16; the group is padded to 16).  K and V are bf16 as
+// stored; the scaled query and the softmax weights are split into bf16 hi and
+// lo parts (x = hi + lo to about 2^-16 relative), so each product is two
+// MFMAs and the result keeps float32-level accuracy.
+#include "eta_internal.h"
+
+namespace eta {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// Screen: one work-group per 64-block admission word of KV stream u; wave w
+// scores blocks 16 w .. 16 w + 15 of the word (8 lanes per block).  A block's
+// statistics are loaded once and scored against every query head of the
+// group (queries, norms and thresholds staged in LDS).  Writes the per-block
+// head mask (bit g: query head u*G + g admits the block) for every block of
+// the stream and the union admission word.
+template <int D>
+__global__ __launch_bounds__(256) void screen_gqa_kernel(CacheView c, int G, const float* q,
+                                                         const float* tau_screen, float z,
+                                                         float scale, uint32_t* head_mask,
+                                                         uint64_t* words, int words_per_unit) {
+  constexpr int LPB = 8;            // lanes per block
+  constexpr int NL = D / 32;        // float4 loads per lane per statistics row
+  __shared__ float s_q[kMaxGroup][D];
+  __shared__ float s_qn[kMaxGroup];
+  __shared__ float s_ts[kMaxGroup];
+  __shared__ uint32_t s_bits[4];
+  const int units = c.B * c.H;
+  const int u = blockIdx.x % units, wd = blockIdx.x / units;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int T = c.seq_len[u / c.H];
+  const int nb = (T + c.bs - 1) >> c.log2bs;
+  const int nbc = T >> c.log2bs;
+  if ((wd << 6) >= nb) return;  // uniform over the work-group
+  for (int i = threadIdx.x; i < G * D; i += blockDim.x) s_q[i / D][i % D] = q[(size_t)u * G * D + i];
+  if (threadIdx.x < G) s_ts[threadIdx.x] = tau_screen[(size_t)u * G + threadIdx.x];
+  __syncthreads();
+  if (threadIdx.x < G) {
+    float qq = 0.f;
+    for (int i = 0; i < D; ++i) qq = fmaf(s_q[threadIdx.x][i], s_q[threadIdx.x][i], qq);
+    s_qn[threadIdx.x] = sqrtf(qq);
+  }
+  __syncthreads();
+  const bool z_inf = __builtin_isinf(z);
+  const int gi = lane / LPB, li = lane % LPB;
+  const uint32_t all = (G >= 32) ? 0xffffffffu : ((1u << G) - 1u);
+  uint32_t bits = 0;
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int j = (wd << 6) + wave * 16 + it * 8 + gi;
+    const bool scored = j < nbc;
+    const size_t row = ((size_t)u * c.cap_blocks + j) * D;
+    float4 m4[NL], v4[NL];
+#pragma unroll
+    for (int t = 0; t < NL; ++t) {
+      m4[t] = scored ? ld16f_nt(c.mu + row + 32 * t + 4 * li) : make_float4(0, 0, 0, 0);
+      v4[t] = scored ? ld16f_nt(c.var + row + 32 * t + 4 * li) : make_float4(0, 0, 0, 0);
+    }
+    const float M = scored ? c.maxnorm[(size_t)u * c.cap_blocks + j] : 0.f;
+    uint32_t mask = 0;
+    for (int g = 0; g < G; ++g) {
+      float dot = 0.f, mom = 0.f;
+#pragma unroll
+      for (int t = 0; t < NL; ++t) {
+        const float4 qv = *reinterpret_cast<const float4*>(&s_q[g][32 * t + 4 * li]);
+        dot = fmaf(qv.x, m4[t].x, dot);
+        dot = fmaf(qv.y, m4[t].y, dot);
+        dot = fmaf(qv.z, m4[t].z, dot);
+        dot = fmaf(qv.w, m4[t].w, dot);
+        mom = fmaf(qv.x * qv.x, v4[t].x, mom);
+        mom = fmaf(qv.y * qv.y, v4[t].y, mom);
+        mom = fmaf(qv.z * qv.z, v4[t].z, mom);
+        mom = fmaf(qv.w * qv.w, v4[t].w, mom);
+      }
+      dot = group_sum<LPB>(dot);
+      mom = group_sum<LPB>(mom);
+      const float geometric = s_qn[g] * M;
+      const float sc = z_inf ? scale * geometric
+                             : scale * fminf(fmaf(z, sqrtf(mom), dot), geometric);
+      if (scored && sc >= s_ts[g]) mask |= 1u << g;
+    }
+    if (j == nb - 1) mask = all;  // the last block is admitted for every head
+    if (li == 0 && j < nb) head_mask[(size_t)u * c.cap_blocks + j] = mask;
+    const uint64_t bal = __ballot(mask != 0u);
+#pragma unroll
+    for (int g8 = 0; g8 < 8; ++g8)
+      bits |= (uint32_t)((bal >> (g8 * LPB)) & 1ull) << (it * 8 + g8);
+  }
+  if (lane == 0) s_bits[wave] = bits;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint64_t word = (uint64_t)s_bits[0] | ((uint64_t)s_bits[1] << 16) |
+                          ((uint64_t)s_bits[2] << 32) | ((uint64_t)s_bits[3] << 48);
+    words[(size_t)u * words_per_unit + wd] = word;
+  }
+}
+
+// Compaction of the union words into the ascending union list (as for one
+// head per KV head), plus the counters: ctr[0] += admitted tokens summed over
+// the group's query heads, ctr[1] += union tokens.
+__global__ __launch_bounds__(256) void compact_gqa_kernel(CacheView c, const uint64_t* words,
+                                                          int words_per_unit,
+                                                          const uint32_t* head_mask,
+                                                          int32_t* union_idx, int32_t* union_cnt,
+                                                          uint64_t* ctr) {
+  __shared__ int scan[256];
+  __shared__ unsigned long long s_tok[256];
+  const int u = blockIdx.x, t = threadIdx.x;
+  const int T = c.seq_len[u / c.H];
+  const int nb = (T + c.bs - 1) >> c.log2bs;
+  const int nw = (nb + 63) >> 6;
+  const int per = (nw + 255) >> 8;
+  const int w0 = min(t * per, nw), w1 = min(w0 + per, nw);
+  const uint64_t* wu = words + (size_t)u * words_per_unit;
+  const uint32_t* hm = head_mask + (size_t)u * c.cap_blocks;
+  auto word_at = [&](int w) {
+    uint64_t x = wu[w];
+    const int rem = nb - (w << 6);
+    if (rem < 64) x &= (1ull << rem) - 1ull;
+    return x;
+  };
+  int mine = 0;
+  for (int w = w0; w < w1; ++w) mine += __popcll(word_at(w));
+  scan[t] = mine;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const int add = t >= off ? scan[t - off] : 0;
+    __syncthreads();
+    scan[t] += add;
+    __syncthreads();
+  }
+  int pos = scan[t] - mine;
+  const int total = scan[255];
+  const int tail = T - ((nb - 1) << c.log2bs);
+  int32_t* out = union_idx + (size_t)u * c.cap_blocks;
+  unsigned long long head_tokens = 0;
+  for (int w = w0; w < w1; ++w) {
+    uint64_t x = word_at(w);
+    while (x) {
+      const int j = (w << 6) + __ffsll((unsigned long long)x) - 1;
+      out[pos++] = j;
+      head_tokens += (unsigned long long)__popc(hm[j]) * (j == nb - 1 ? tail : c.bs);
+      x &= x - 1ull;
+    }
+  }
+  s_tok[t] = head_tokens;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (t < s) s_tok[t] += s_tok[t + s];
+    __syncthreads();
+  }
+  if (t == 0) {
+    union_cnt[u] = total;
+    if (ctr && total > 0) {
+      atomicAdd(reinterpret_cast<unsigned long long*>(ctr), s_tok[0]);
+      const unsigned long long ut =
+          (unsigned long long)(total - 1) * c.bs + (unsigned long long)tail;
+      atomicAdd(reinterpret_cast<unsigned long long*>(ctr + 1), ut);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Decode.  One work-group (4 waves) per chunk of `split` union blocks of KV
+// stream u; wave w takes 32-key tiles w, w+4, ...  For a tile:
+//   S[16 keys x 16 heads] = K_tile (A: lane l holds key l%16, 8 dims from
+//     8*(l/16)) x Q^T (B: head l%16, same dims), for each 32-dim slab and for
+//     both halves (hi, lo) of the query; result lane l: keys 4*(l/16)+i,
+//     head l%16, for the two 16-key halves of the tile.
+//   Logits per head (own admission, tail, Eq. 3 gate), online softmax per
+//   head (the 4 lanes holding a head agree on its running max).
+//   O[16 heads x 16 dims] += P (A: head l%16, the 8 keys the lane holds) x V
+//     (B: dim l%16, the same 8 keys), V read transposed from the wave's LDS
+//     tile, for each 16-dim slab and both halves of P.
+// The 4 waves' (max, sum, O) are merged through LDS and written as the
+// chunk's partial per query head (or the output for single-chunk streams).
+constexpr int kTileKeys = 32;
+constexpr int kVtStride = kTileKeys + 4;  // bf16 per transposed row (pad: banks, 8-byte reads)
+
+__device__ __forceinline__ __bf16 to_bf16(float x) {
+  // round to nearest even (finite inputs only)
+  uint32_t u = __float_as_uint(x);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return __builtin_bit_cast(__bf16, (uint16_t)(u >> 16));
+}
+__device__ __forceinline__ float from_bf16(__bf16 h) {
+  return __uint_as_float((uint32_t)__builtin_bit_cast(uint16_t, h) << 16);
+}
+
+using GqaArgs = GqaDecode;
+
+__device__ __forceinline__ int gqa_stream(const CacheView& c, const GqaArgs& a, bool dense, int u,
+                                          int* T_out, int* cnt_out) {
+  const int T = c.seq_len[u / c.H];
+  const int nb = T > 0 ? (T + c.bs - 1) >> c.log2bs : 0;
+  const int cnt = dense ? nb : max(0, min(a.union_cnt[u], nb));
+  *T_out = T;
+  *cnt_out = cnt;
+  return (cnt + a.split - 1) / a.split;
+}
+
+template <int D, int MODE, bool DENSE>
+__global__ __launch_bounds__(256) void decode_gqa_kernel(CacheView c, GqaArgs a) {
+  constexpr int NK = D / 32;  // 32-dim slabs of the score product
+  constexpr int NV = D / 16;  // 16-dim slabs of the value product
+  constexpr int RB = D * 2;   // bytes per bf16 key row
+  extern __shared__ __align__(16) char s_raw[];
+  __bf16* s_vt = reinterpret_cast<__bf16*>(s_raw);                   // [4][D][kVtStride]
+  float* s_o = reinterpret_cast<float*>(s_raw);                       // reused: [4][16][D]
+  int* s_list = reinterpret_cast<int*>(s_raw + 4 * D * kVtStride * 2);  // [split]
+  uint32_t* s_mask = reinterpret_cast<uint32_t*>(s_list + a.split);      // [split]
+  __shared__ float s_ml[4][16][2];
+
+  const int u = blockIdx.x / a.max_chunks, k = blockIdx.x % a.max_chunks;
+  int T, cnt;
+  const int nch = gqa_stream(c, a, DENSE, u, &T, &cnt);
+  if (k >= nch) return;
+  const int nb = (T + c.bs - 1) >> c.log2bs;
+  const int first = k * a.split, nblk = min(a.split, cnt - first);
+  const int G = a.G;
+  const uint32_t all = (1u << G) - 1u;
+  for (int i = threadIdx.x; i < nblk; i += blockDim.x) {
+    if constexpr (DENSE) {
+      s_list[i] = first + i;
+      s_mask[i] = all;
+    } else {
+      const int j = a.union_idx[(size_t)u * c.cap_blocks + first + i];
+      s_list[i] = j;
+      s_mask[i] = ((unsigned)j < (unsigned)nb) ? a.head_mask[(size_t)u * c.cap_blocks + j] : 0u;
+    }
+  }
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n = lane & 15, grp = lane >> 4;  // S layout: head n; keys 4*grp + i
+
+  // Query operand (head n, dims 32*kk + 8*grp + i), scaled, split hi + lo.
+  bf16x8 qhi[NK], qlo[NK];
+  {
+    const float* qn = a.q + ((size_t)u * G + (n < G ? n : 0)) * D;
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float x = n < G ? qn[32 * kk + 8 * grp + i] * a.scale : 0.f;
+        const __bf16 h = to_bf16(x);
+        qhi[kk][i] = h;
+        qlo[kk][i] = to_bf16(x - from_bf16(h));
+      }
+  }
+  const float tau_n = (MODE == ETA_LOGIT_GATED && n < G) ? a.tau[(size_t)u * G + n] : 0.f;
+  const float beta = a.beta;
+  const char* kbase = static_cast<const char*>(c.k) + (size_t)u * c.cap * RB;
+  const char* vbase = static_cast<const char*>(c.v) + (size_t)u * c.cap * RB;
+  __bf16* vt = s_vt + wave * D * kVtStride;
+  __syncthreads();  // s_list, s_mask
+
+  floatx4 O[NV];
+#pragma unroll
+  for (int nv = 0; nv < NV; ++nv) O[nv] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float m = -__builtin_inff(), lsum = 0.f;
+
+  const int rows = nblk << c.log2bs;
+  const int ntiles = (rows + kTileKeys - 1) / kTileKeys;
+  auto key_pos = [&](int rr) {  // absolute key position of chunk row rr, or -1
+    if (rr >= rows) return -1;
+    const int j = s_list[rr >> c.log2bs];
+    const int s = (j << c.log2bs) + (rr & (c.bs - 1));
+    return ((unsigned)j >= (unsigned)nb || s >= T) ? -1 : s;
+  };
+  for (int t = wave; t < ntiles; t += 4) {
+    const int r0 = t * kTileKeys;
+    // K operand: two 16-key halves x NK slabs; V: key pair 2*(lane%16)+{0,1},
+    // dims 8*(grp + 4*cc) .. +7 for cc < D/32.
+    uint4 kraw[2][NK];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const int s = key_pos(r0 + 16 * st + n);
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk)
+        kraw[st][kk] = s >= 0 ? ld16_nt(kbase + (size_t)s * RB + (32 * kk + 8 * grp) * 2)
+                              : make_uint4(0, 0, 0, 0);
+    }
+    uint4 vraw[2][NK];
+    {
+      const int s0 = key_pos(r0 + 2 * n), s1 = key_pos(r0 + 2 * n + 1);
+#pragma unroll
+      for (int cc = 0; cc < NK; ++cc) {
+        const int col = 8 * (grp + 4 * cc);
+        vraw[0][cc] = s0 >= 0 ? ld16_nt(vbase + (size_t)s0 * RB + col * 2) : make_uint4(0, 0, 0, 0);
+        vraw[1][cc] = s1 >= 0 ? ld16_nt(vbase + (size_t)s1 * RB + col * 2) : make_uint4(0, 0, 0, 0);
+      }
+    }
+    // Scores.
+    floatx4 S[2];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      S[st] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) {
+        const bf16x8 kv = __builtin_bit_cast(bf16x8, kraw[st][kk]);
+        S[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qhi[kk], S[st], 0, 0, 0);
+        S[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qlo[kk], S[st], 0, 0, 0);
+      }
+    }
+    // V tile -> LDS, transposed: vt[dim][key].
+#pragma unroll
+    for (int cc = 0; cc < NK; ++cc) {
+      const uint32_t* a0 = reinterpret_cast<const uint32_t*>(&vraw[0][cc]);
+      const uint32_t* a1 = reinterpret_cast<const uint32_t*>(&vraw[1][cc]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int col = 8 * (grp + 4 * cc) + 2 * e;
+        // dims col (low halves) and col+1 (high halves) of keys 2n and 2n+1
+        const uint32_t lo = (a0[e] & 0xffffu) | (a1[e] << 16);
+        const uint32_t hi = (a0[e] >> 16) | (a1[e] & 0xffff0000u);
+        *reinterpret_cast<uint32_t*>(vt + col * kVtStride + 2 * n) = lo;
+        *reinterpret_cast<uint32_t*>(vt + (col + 1) * kVtStride + 2 * n) = hi;
+      }
+    }
+    // Logits, masks and the running max of head n.
+    float lg[8];
+    float tmax = -__builtin_inff();
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rr = r0 + 16 * st + 4 * grp + i;
+        const int s = key_pos(rr);
+        bool on = s >= 0 && n < G;
+        if (on) on = (s_mask[rr >> c.log2bs] >> n) & 1u;
+        const float d = S[st][i];
+        float lv = d;
+        if (MODE == ETA_LOGIT_GATED && s != T - 1)
+          lv = d * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-beta * (d - tau_n) *
+                                                                       1.4426950408889634f));
+        lg[4 * st + i] = on ? lv : -__builtin_inff();
+        tmax = fmaxf(tmax, lg[4 * st + i]);
+      }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+    const float mn = fmaxf(m, tmax);
+    const float ms = (mn == -__builtin_inff()) ? 0.f : mn;
+    const float alpha = __builtin_amdgcn_exp2f((m - ms) * 1.4426950408889634f);
+    m = mn;
+    bf16x8 phi, plo;
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float p = __builtin_amdgcn_exp2f((lg[i] - ms) * 1.4426950408889634f);
+      psum += p;
+      const __bf16 h = to_bf16(p);
+      phi[i] = h;
+      plo[i] = to_bf16(p - from_bf16(h));
+    }
+    lsum = lsum * alpha + psum;
+    // O rows are heads 4*grp + i: their rescale factors come from lanes 4*grp + i.
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float al = __shfl(alpha, 4 * grp + i, kWave);
+#pragma unroll
+      for (int nv = 0; nv < NV; ++nv) O[nv][i] *= al;
+    }
+    // Values: B operand = dims 16*nv + n, keys of slots 0-3 (4*grp..) and 4-7 (16+4*grp..).
+    // The tile was written by other lanes of this wave: order the LDS accesses.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int nv = 0; nv < NV; ++nv) {
+      const __bf16* row = vt + (16 * nv + n) * kVtStride;
+      const uint2 v03 = *reinterpret_cast<const uint2*>(row + 4 * grp);
+      const uint2 v47 = *reinterpret_cast<const uint2*>(row + 16 + 4 * grp);
+      const uint4 vv = make_uint4(v03.x, v03.y, v47.x, v47.y);
+      const bf16x8 vb = __builtin_bit_cast(bf16x8, vv);
+      O[nv] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi, vb, O[nv], 0, 0, 0);
+      O[nv] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo, vb, O[nv], 0, 0, 0);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+  // Head n's sum over the 4 lane groups (they share the running max).
+  lsum += __shfl_xor(lsum, 16, kWave);
+  lsum += __shfl_xor(lsum, 32, kWave);
+  __syncthreads();  // every wave is done with its transposed V tile
+  float* so = s_o + wave * 16 * D;
+#pragma unroll
+  for (int nv = 0; nv < NV; ++nv)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) so[(4 * grp + i) * D + 16 * nv + n] = O[nv][i];
+  if (grp == 0) {
+    s_ml[wave][n][0] = m;
+    s_ml[wave][n][1] = lsum;
+  }
+  __syncthreads();
+  // Merge the 4 waves per (head, dim) in a fixed order.
+  for (int e = threadIdx.x; e < G * D; e += blockDim.x) {
+    const int h = e / D, col = e % D;
+    float mm = s_ml[0][h][0], ll = s_ml[0][h][1];
+    float aa = s_o[h * D + col];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) {
+      const float m2 = s_ml[w][h][0], l2 = s_ml[w][h][1], a2 = s_o[(w * 16 + h) * D + col];
+      const float mx = fmaxf(mm, m2);
+      const float ms = (mx == -__builtin_inff()) ? 0.f : mx;
+      const float s1 = __builtin_amdgcn_exp2f((mm - ms) * 1.4426950408889634f);
+      const float s2 = __builtin_amdgcn_exp2f((m2 - ms) * 1.4426950408889634f);
+      ll = ll * s1 + l2 * s2;
+      aa = aa * s1 + a2 * s2;
+      mm = mx;
+    }
+    const size_t uq = (size_t)u * G + h;
+    if (nch == 1) {
+      a.out[uq * D + col] = aa / ll;
+    } else {
+      const size_t slot = uq * a.max_chunks + k;
+      a.part_acc[slot * D + col] = aa;
+      if (col == 0) {
+        a.part_m[slot] = mm;
+        a.part_l[slot] = ll;
+      }
+    }
+  }
+}
+
+// Combine of the chunk partials of every query head (log-sum-exp, one pass,
+// 16 waves, 8 partials in flight per wave, fixed-order wave merge); zero
+// output for empty streams.
+template <int D>
+__global__ __launch_bounds__(1024) void combine_gqa_kernel(CacheView c, GqaArgs a, bool dense) {
+  constexpr int W = 16, INF = 8, CPL = D / kWave;
+  __shared__ float s_acc[W][D];
+  __shared__ float s_ml[W][2];
+  const int uq = blockIdx.x, t = threadIdx.x, wave = t >> 6, lane = t & 63;
+  int T, cnt;
+  const int nch = gqa_stream(c, a, dense, uq / a.G, &T, &cnt);
+  if (nch == 0) {
+    if (t < D) a.out[(size_t)uq * D + t] = 0.f;
+    return;
+  }
+  if (nch == 1) return;  // written by the decode kernel
+  const float* pm = a.part_m + (size_t)uq * a.max_chunks;
+  const float* pl = a.part_l + (size_t)uq * a.max_chunks;
+  const float* pa = a.part_acc + (size_t)uq * a.max_chunks * D + lane * CPL;
+  float m = -__builtin_inff(), l = 0.f, acc[CPL];
+#pragma unroll
+  for (int e = 0; e < CPL; ++e) acc[e] = 0.f;
+  for (int base = wave; base < nch; base += W * INF) {
+    float mc[INF], lc[INF], ac[INF][CPL];
+#pragma unroll
+    for (int i = 0; i < INF; ++i) {
+      const int ch = base + W * i;
+      const bool ok = ch < nch;
+      mc[i] = ok ? pm[ch] : -__builtin_inff();
+      lc[i] = ok ? pl[ch] : 0.f;
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) ac[i][e] = ok ? pa[(size_t)ch * D + e] : 0.f;
+    }
+    float mx = m;
+#pragma unroll
+    for (int i = 0; i < INF; ++i) mx = fmaxf(mx, mc[i]);
+    const float ms = (mx == -__builtin_inff()) ? 0.f : mx;
+    const float alpha = __builtin_amdgcn_exp2f((m - ms) * 1.4426950408889634f);
+    l *= alpha;
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) acc[e] *= alpha;
+#pragma unroll
+    for (int i = 0; i < INF; ++i) {
+      const float wgt = __builtin_amdgcn_exp2f((mc[i] - ms) * 1.4426950408889634f);
+      l = fmaf(wgt, lc[i], l);
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) acc[e] = fmaf(wgt, ac[i][e], acc[e]);
+    }
+    m = mx;
+  }
+#pragma unroll
+  for (int e = 0; e < CPL; ++e) s_acc[wave][lane * CPL + e] = acc[e];
+  if (lane == 0) {
+    s_ml[wave][0] = m;
+    s_ml[wave][1] = l;
+  }
+  __syncthreads();
+  if (t < D) {
+    float mm = s_ml[0][0], ll = s_ml[0][1], aa = s_acc[0][t];
+    for (int w = 1; w < W; ++w) {
+      const float m2 = s_ml[w][0], l2 = s_ml[w][1], a2 = s_acc[w][t];
+      const float mx = fmaxf(mm, m2);
+      const float ms = (mx == -__builtin_inff()) ? 0.f : mx;
+      const float s1 = __builtin_amdgcn_exp2f((mm - ms) * 1.4426950408889634f);
+      const float s2 = __builtin_amdgcn_exp2f((m2 - ms) * 1.4426950408889634f);
+      ll = ll * s1 + l2 * s2;
+      aa = aa * s1 + a2 * s2;
+      mm = mx;
+    }
+    a.out[(size_t)uq * D + t] = aa / ll;
+  }
+}
+
+// ---------------------------------------------------------------------------
+template <int D>
+static hipError_t screen_gqa_t(const CacheView& c, int G, const float* q, const float* ts,
+                               float z, float scale, int32_t* idx, uint32_t* mask, int32_t* cnt,
+                               uint64_t* ctr, uint64_t* words, hipStream_t s) {
+  const int units = c.B * c.H;
+  const int wpu = ceil_div(c.cap_blocks, 64);
+  hipLaunchKernelGGL((screen_gqa_kernel<D>), dim3((unsigned)((long long)wpu * units)), dim3(256),
+                     0, s, c, G, q, ts, z, scale, mask, words, wpu);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(compact_gqa_kernel, dim3(units), dim3(256), 0, s, c, words, wpu, mask, idx,
+                     cnt, ctr);
+  return hipGetLastError();
+}
+
+hipError_t launch_screen_gqa(const CacheView& c, int G, const float* q, const float* ts, float z,
+                             float scale, int32_t* idx, uint32_t* mask, int32_t* cnt,
+                             uint64_t* ctr, uint64_t* words, hipStream_t s) {
+  return c.D == 128 ? screen_gqa_t<128>(c, G, q, ts, z, scale, idx, mask, cnt, ctr, words, s)
+                    : screen_gqa_t<64>(c, G, q, ts, z, scale, idx, mask, cnt, ctr, words, s);
+}
+
+size_t gqa_decode_lds_bytes(int D, int split) {
+  return (size_t)4 * D * kVtStride * 2 + (size_t)split * 8;
+}
+
+template <int D, int MODE, bool DENSE>
+static hipError_t decode_gqa_t(const CacheView& c, const GqaDecode& g, hipStream_t s) {
+  const GqaArgs& a = g;
+  const long long grid = (long long)g.max_chunks * c.B * c.H;
+  hipLaunchKernelGGL((decode_gqa_kernel<D, MODE, DENSE>), dim3((unsigned)grid), dim3(256),
+                     gqa_decode_lds_bytes(D, g.split), s, c, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((combine_gqa_kernel<D>), dim3(c.B * c.H * g.G), dim3(1024), 0, s, c, a,
+                     DENSE);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t decode_gqa_d(const CacheView& c, const GqaDecode& g, hipStream_t s) {
+  if (g.dense) return decode_gqa_t<D, ETA_LOGIT_RAW, true>(c, g, s);
+  if (g.mode == ETA_LOGIT_RAW) return decode_gqa_t<D, ETA_LOGIT_RAW, false>(c, g, s);
+  return decode_gqa_t<D, ETA_LOGIT_GATED, false>(c, g, s);
+}
+
+hipError_t launch_decode_gqa(const CacheView& c, const GqaDecode& g, hipStream_t s) {
+  return c.D == 128 ? decode_gqa_d<128>(c, g, s) : decode_gqa_d<64>(c, g, s);
+}
+
+}  // namespace eta

@@ -21,7 +21,7 @@ from dataclasses import dataclass, field
 import numpy as np
 import torch
 
-# Shapes and generator settings of the five decode workloads.
+# Shapes and generator settings of the decode workloads.
 CONFIGS = {
     # correctness size; fp32 cache; frozen per-head tau ~ U(0.5, 1.5)
     "tiny": dict(B=1, H=4, D=64, T=2048, block=16, z=1.5, kv="f32", tau="frozen",
@@ -41,6 +41,18 @@ CONFIGS = {
     "ragged": dict(B=32, H=16, D=128, T=(8192, 65536), block=16, z=2.0, kv="bf16",
                    tau="frozen_calibrated", rho=0.25, n_cal_sets=2, block_mean="t3",
                    needles=dict(kind="uniform", frac=0.01)),
+    # Grouped-query shapes (32 query heads on 4 KV heads, d=64, b=64).  The
+    # queries of a group share a component (correlation q_corr) and a needle
+    # block is lifted toward one head of its group, so heads admit different
+    # blocks and the union exceeds each head's set.
+    "gqa_tiny": dict(B=2, H=2, G=4, D=64, T=(1000, 3000), block=16, z=1.5, kv="bf16",
+                     tau="frozen", block_mean="normal", q_corr=0.8,
+                     needles=dict(kind="uniform", frac=0.03)),
+    # q_corr 0.97 and a predictor at a quarter of the MHA weight scale give
+    # union densities of about 54%, 38% and 16% at 38%, 25% and 10% per head.
+    "gqa128k": dict(B=32, H=4, G=8, D=64, T=131072, block=64, z=1.0, kv="bf16", tau="dynamic",
+                    rho=(0.38, 0.25, 0.10), block_mean="t3", q_corr=0.97, w_scale=0.25,
+                    needles=dict(kind="uniform", frac=0.01)),
 }
 
 NEEDLE_DELTA = 4.0  # a needle block's mean is lifted by this many logits along q
@@ -50,14 +62,14 @@ NEEDLE_DELTA = 4.0  # a needle block's mean is lifted by this many logits along 
 class Workload:
     name: str
     B: int
-    H: int
+    H: int                           # cache (KV) heads
     D: int
     block: int
     cap: int
     z: float
     kv_dtype: torch.dtype
     seq_len: torch.Tensor            # [B] int32
-    q: torch.Tensor                  # [B][H][D] float32
+    q: torch.Tensor                  # [B][H*G][D] float32
     k: torch.Tensor                  # [B][H][cap][D]
     v: torch.Tensor                  # [B][H][cap][D]
     tau_kind: str                    # "frozen" | "dynamic" | "frozen_calibrated"
@@ -66,10 +78,15 @@ class Workload:
     rho: tuple = ()                  # target densities for calibration
     q_cal: torch.Tensor | None = None      # [n][B][H][D] calibration queries
     needle_blocks: list = field(default_factory=list)  # per (b, h): LongTensor of blocks
+    G: int = 1                       # query heads per KV head (q holds H*G heads)
 
     @property
     def cap_blocks(self) -> int:
         return -(-self.cap // self.block)
+
+    @property
+    def Hq(self) -> int:
+        return self.H * self.G
 
     @property
     def scale(self) -> float:
@@ -111,15 +128,19 @@ def _needles(g, spec, nb, device):
 
 
 def make(name: str, *, seed: int = 1234, device="cpu", T=None, B=None, cap=None, pad="zero",
-         block=None, H=None, kv=None) -> Workload:
-    """Draw the workload `name` (a key of CONFIGS).  T, B, cap, block, H and kv
-    override the configuration's sizes for reduced test cases (T: one length,
+         block=None, H=None, kv=None, D=None, G=None) -> Workload:
+    """Draw the workload `name` (a key of CONFIGS).  T, B, cap, block, H, kv, D
+    and G (grouped-query configurations only) override the configuration's sizes for reduced test cases (T: one length,
     a (lo, hi) uniform range, or a list of per-sequence lengths); `pad` fills the
-    unused cache slots beyond each T_b with zeros or NaN ("nan")."""
+    unused cache slots beyond each T_b with zeros or NaN ("nan").  For a
+    grouped-query configuration, H counts KV heads and q, W and the frozen
+    constants cover the H*G query heads (query head h*G + g reads KV head h)."""
     cfg = dict(CONFIGS[name])
     B = cfg["B"] if B is None else B
     H = cfg["H"] if H is None else H
-    D = cfg["D"]
+    G = cfg.get("G", 1) if G is None else G
+    assert G == 1 or "q_corr" in cfg, "G applies to grouped-query configurations"
+    D = cfg["D"] if D is None else D
     bs = cfg["block"] if block is None else block
     kvname = cfg["kv"] if kv is None else kv
     kv_dtype = torch.float32 if kvname == "f32" else torch.bfloat16
@@ -141,7 +162,13 @@ def make(name: str, *, seed: int = 1234, device="cpu", T=None, B=None, cap=None,
     assert cap >= int(lens.max())
     nbcap = -(-cap // bs)
 
-    q = torch.randn((B, H, D), generator=g, device=device)
+    if G == 1:
+        q = torch.randn((B, H, D), generator=g, device=device)
+    else:
+        shared = torch.randn((B, H, 1, D), generator=g, device=device)
+        own = torch.randn((B, H, G, D), generator=g, device=device)
+        c = cfg["q_corr"]
+        q = (math.sqrt(c) * shared + math.sqrt(1.0 - c) * own).reshape(B, H * G, D)
     spec = cfg["needles"]
     k = torch.empty((B, H, cap, D), dtype=kv_dtype, device=device)
     v = torch.empty((B, H, cap, D), dtype=kv_dtype, device=device)
@@ -160,9 +187,15 @@ def make(name: str, *, seed: int = 1234, device="cpu", T=None, B=None, cap=None,
             if spec["kind"] == "query_mix":
                 if idx.numel():
                     q[b, h] += spec["weight"] * mu[h, idx].mean(0)
-            elif idx.numel():
+            elif idx.numel() and G == 1:
                 qq = q[b, h]
                 mu[h, idx] += NEEDLE_DELTA * math.sqrt(D) * qq / qq.dot(qq)
+            elif idx.numel():
+                # each needle block is lifted toward one query head of the group
+                owner = torch.randint(0, G, (idx.numel(),), generator=g, device=device)
+                qq = q[b, h * G + owner]                       # [n][D]
+                lift = qq / (qq * qq).sum(1, keepdim=True)
+                mu[h, idx] += NEEDLE_DELTA * math.sqrt(D) * lift
         kb = torch.randn((H, cap, D), generator=g, device=device)
         kb += mu.repeat_interleave(bs, dim=1)[:, :cap]
         vb = torch.randn((H, cap, D), generator=g, device=device)
@@ -176,13 +209,16 @@ def make(name: str, *, seed: int = 1234, device="cpu", T=None, B=None, cap=None,
 
     w = Workload(name=name, B=B, H=H, D=D, block=bs, cap=cap, z=cfg["z"], kv_dtype=kv_dtype,
                  seq_len=lens, q=q, k=k, v=v, tau_kind=cfg["tau"],
-                 needle_blocks=needle_blocks)
+                 needle_blocks=needle_blocks, G=G)
+    Hq = H * G
     if cfg["tau"] == "frozen":
-        w.tau_const = 0.5 + torch.rand((H,), generator=g, device=device)
+        w.tau_const = 0.5 + torch.rand((Hq,), generator=g, device=device)
     if cfg["tau"] == "dynamic":
-        wh = torch.randn((H, D), generator=g, device=device) / math.sqrt(D)
-        W = torch.zeros((H * D, H), device=device)
-        for h in range(H):
+        wh = torch.randn((Hq, D), generator=g, device=device) / math.sqrt(D)
+        if "w_scale" in cfg:
+            wh *= cfg["w_scale"]
+        W = torch.zeros((Hq * D, Hq), device=device)
+        for h in range(Hq):
             W[h * D:(h + 1) * D, h] = wh[h]
         w.W = W
     if "rho" in cfg:

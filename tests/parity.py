@@ -253,3 +253,108 @@ def oracle_constants(w: synth.Workload, rho: float, seqs=None, sets=None):
         c, k = oracle.calibrate(qc, sl, w.block, w.cap, meta, z=w.z, scale=w.scale,
                                 rho=float(np.float32(rho)))
     return torch.from_numpy(c.astype(np.float32)), k
+
+
+# ---------------------------------------------------------------------------
+# Grouped-query attention.
+@dataclass
+class GqaGpuResult:
+    tau_gate: np.ndarray
+    tau_screen: np.ndarray
+    union_idx: np.ndarray
+    union_cnt: np.ndarray
+    head_mask: np.ndarray   # [B][Hkv][cap_blocks] uint32 bit patterns
+    density: np.ndarray     # [2]: head tokens, union tokens
+    out: np.ndarray
+    mask: np.ndarray        # [B][Hq][cap_blocks] per-query-head admission
+    union: np.ndarray       # [B][Hkv][cap_blocks] from the union lists
+
+
+def run_gpu_gqa(cache: eb.KVCache, group, q, *, W=None, bias_or_c=None, z, scale,
+                mode=eb.GATED, beta=5.0, a=0.0, split=None, build_meta=True) -> GqaGpuResult:
+    if build_meta:
+        eb.build_block_meta(cache)
+    dec = eb.GqaDecoder(cache, group, z=z, scale=scale, beta=beta, a=a, logit_mode=mode,
+                        blocks_per_split=split)
+    dec.step(q, W, bias_or_c)
+    torch.cuda.synchronize()
+    B, Hkv, nbc = cache.batch, cache.heads, cache.cap_blocks
+    idx = dec.union_idx.cpu().numpy()
+    cnt = dec.union_cnt.cpu().numpy()
+    hm = dec.head_mask.cpu().numpy().view(np.uint32)
+    sl = cache.seq_len.cpu().numpy()
+    union = gpu_mask(idx, cnt, nbc)
+    mask = np.zeros((B, Hkv * group, nbc), np.uint8)
+    for b in range(B):
+        T = int(sl[b])
+        nb = -(-T // cache.block) if T > 0 else 0
+        for kv in range(Hkv):
+            for g in range(group):
+                mask[b, kv * group + g, :nb] = (hm[b, kv, :nb] >> np.uint32(g)) & 1
+    return GqaGpuResult(dec.tau_gate.cpu().numpy(), dec.tau_screen.cpu().numpy(), idx, cnt, hm,
+                        dec.density_ctr.cpu().numpy(), dec.out.cpu().numpy(), mask, union)
+
+
+def union_of(mask: np.ndarray, group: int) -> np.ndarray:
+    B, Hq, nbc = mask.shape
+    return mask.reshape(B, Hq // group, group, nbc).max(axis=2)
+
+
+def tokens_of(mask: np.ndarray, seq_len: np.ndarray, b: int) -> np.ndarray:
+    """Admitted tokens per stream of a block mask (the last block may be partial)."""
+    B, H, nbc = mask.shape
+    out = np.zeros((B, H), np.int64)
+    for bb in range(B):
+        T = int(seq_len[bb])
+        if T == 0:
+            continue
+        per = np.full(nbc, b, np.int64)
+        nb = -(-T // b)
+        per[nb - 1] = T - (nb - 1) * b
+        per[nb:] = 0
+        out[bb] = (mask[bb].astype(np.int64) * per[None]).sum(1)
+    return out
+
+
+def check_gqa(w: synth.Workload, g: GqaGpuResult, *, W, bias_or_c, z, scale, mode, beta=5.0,
+              a=0.0, K=None, V=None, internal_tol=1e-4):
+    """Every stream of a grouped-query step against the oracle.  Besides the
+    output bar of the decode path, the outputs must lie within internal_tol
+    (relative to each head's largest output) of the oracle: the matrix-core
+    products split q and the softmax weights into two bf16 terms, which keeps
+    float32-level accuracy; dropping a term would show up here."""
+    if K is None:
+        K, V = host_kv(w)
+    G = w.G
+    sl = w.seq_len.cpu().numpy().astype(np.int32)
+    q = w.q.cpu().numpy()
+    meta = oracle.meta_batch(K, sl, w.block)
+    Wn = None if W is None else W.cpu().numpy()
+    tau, ts = oracle.predict_tau(q, Wn, bias_or_c.cpu().numpy(), a=a)
+    close(g.tau_gate, tau, 1e-5, "tau_gate")
+    close(g.tau_screen, ts, 1e-5, "tau_screen")
+    r = oracle.gqa_screen_attend_batch(q, K, V, sl, w.block, meta, tau, ts, G, z=z, scale=scale,
+                                       mode=mode, beta=beta)
+    flips, screened = compare_masks(r["active"], r["score"], r["tau_screen"], g.mask, sl, w.block)
+    # the union lists are exactly the OR of the per-head masks, whatever flipped
+    np.testing.assert_array_equal(g.union, union_of(g.mask, G))
+    np.testing.assert_array_equal(g.union_cnt, g.union.sum(2))
+    head_tok = tokens_of(g.mask, sl, w.block)
+    union_tok = tokens_of(g.union, sl, w.block)
+    assert int(g.density[0]) == int(head_tok.sum()), (g.density, head_tok.sum())
+    assert int(g.density[1]) == int(union_tok.sum()), (g.density, union_tok.sum())
+    if flips == 0:
+        np.testing.assert_array_equal(g.union, r["union"])
+        np.testing.assert_array_equal(g.union_cnt, r["union_cnt"])
+        np.testing.assert_array_equal(head_tok, r["tokens"])
+        np.testing.assert_array_equal(union_tok, r["union_tokens"])
+        ref = r["out"]
+    else:
+        ref = oracle.attend_batch(q, np.repeat(K, G, axis=1), np.repeat(V, G, axis=1), sl,
+                                  w.block, g.mask, r["tau"], mode=mode, beta=beta, scale=scale)
+    worst = compare_outputs(g.out, ref, w.kv_dtype)
+    assert worst <= internal_tol, f"grouped-query output rel err {worst:.2e} > {internal_tol:.0e}"
+    tot = max(1, int(sl.sum()))
+    return dict(out_rel=worst, flips=flips, screened=screened,
+                d_head=float(head_tok.sum()) / (tot * w.Hq),
+                d_union=float(union_tok.sum()) / (tot * w.H))

@@ -31,13 +31,13 @@ def declared():
 
 def test_exports_every_declared_symbol(lib):
     names = declared()
-    assert len(names) >= 14
+    assert len(names) >= 19
     for n in names:
         assert hasattr(lib, n), f"{n} declared in include/eta.h but not exported"
 
 
 def test_version_and_strings(lib):
-    assert lib.eta_abi_version() == 1
+    assert lib.eta_abi_version() == 2
     for s, name in [(0, b"ETA_OK"), (1, b"ETA_ERR_NULL_PTR"), (5, b"ETA_ERR_WORKSPACE"),
                     (6, b"ETA_ERR_HIP")]:
         assert lib.eta_status_string(s) == name
@@ -144,6 +144,45 @@ def test_append_validation(lib):
     L = lib
     assert L.eta_append_kv(cache(), None, FAKE, None, None) == eb.ETA_ERR_NULL_PTR
     assert L.eta_append_kv(cache(head_dim=32), FAKE, FAKE, None, None) == eb.ETA_ERR_BAD_SHAPE
+
+
+def test_gqa_validation(lib):
+    L = lib
+    ws_s = L.eta_screen_gqa_workspace_bytes(2, 4, 32)
+    assert ws_s >= 2 * 4 * 8
+    scr = lambda **o: L.eta_screen_gqa(o.get("c", cache()), o.get("g", 8), o.get("q", FAKE),
+                                       FAKE, o.get("z", 1.0), 0.088, FAKE, o.get("mask", FAKE),
+                                       FAKE, None, FAKE, o.get("wsb", ws_s), None)
+    assert scr(g=0) == eb.ETA_ERR_BAD_SHAPE
+    assert scr(g=17) == eb.ETA_ERR_BAD_SHAPE
+    assert "group" in err(L)
+    assert scr(z=-1.0) == eb.ETA_ERR_BAD_ARG
+    assert scr(q=None) == eb.ETA_ERR_NULL_PTR
+    assert scr(mask=None) == eb.ETA_ERR_NULL_PTR
+    assert scr(wsb=ws_s - 1) == eb.ETA_ERR_WORKSPACE
+    assert scr(c=cache(batch=0, k=None, v=None, mu=None, var=None, maxnorm=None,
+                       seq_len=None), q=None) == eb.ETA_OK
+    # partials of every query head: 2 * 4 * 8 heads, 2 chunks, 128 + 2 floats
+    ws = L.eta_decode_gqa_workspace_bytes(2, 4, 8, 128, 32, 16)
+    assert ws >= 2 * 4 * 8 * 2 * (128 + 2) * 4
+    dec = lambda **o: L.eta_decode_gqa(o.get("c", cache()), o.get("g", 8), FAKE,
+                                       o.get("tau", FAKE), o.get("idx", FAKE), o.get("mask", FAKE),
+                                       FAKE, o.get("mode", 0), o.get("beta", 5.0), 0.088,
+                                       o.get("split", 16), FAKE, o.get("wsb", ws), FAKE, None)
+    assert dec(c=cache(kv_dtype=eb.DT_F32)) == eb.ETA_ERR_BAD_ARG
+    assert "bf16" in err(L)
+    assert dec(g=17) == eb.ETA_ERR_BAD_SHAPE
+    assert dec(mode=3) == eb.ETA_ERR_BAD_ARG
+    assert dec(beta=-1.0) == eb.ETA_ERR_BAD_ARG
+    assert dec(split=2049) == eb.ETA_ERR_BAD_ARG
+    assert dec(tau=None) == eb.ETA_ERR_NULL_PTR
+    assert dec(mask=None) == eb.ETA_ERR_NULL_PTR
+    assert dec(wsb=ws - 4) == eb.ETA_ERR_WORKSPACE
+    assert dec(mode=1, tau=None, wsb=ws - 4) == eb.ETA_ERR_WORKSPACE
+    assert L.eta_dense_decode_gqa(cache(), 8, FAKE, 0.088, 16, FAKE, ws - 4, FAKE,
+                                  None) == eb.ETA_ERR_WORKSPACE
+    assert L.eta_dense_decode_gqa(cache(kv_dtype=eb.DT_F32), 8, FAKE, 0.088, 16, FAKE, ws, FAKE,
+                                  None) == eb.ETA_ERR_BAD_ARG
 
 
 def test_binding_refuses_cpu_tensors(lib):

@@ -175,33 +175,86 @@ __global__ __launch_bounds__(256) void compact_gqa_kernel(CacheView c, const uin
 }
 
 // ---------------------------------------------------------------------------
-// Decode.  One work-group (4 waves) per chunk of `split` union blocks of KV
-// stream u; wave w takes 32-key tiles w, w+4, ...  For a tile:
-//   S[16 keys x 16 heads] = K_tile (A: lane l holds key l%16, 8 dims from
-//     8*(l/16)) x Q^T (B: head l%16, same dims), for each 32-dim slab and for
-//     both halves (hi, lo) of the query; result lane l: keys 4*(l/16)+i,
-//     head l%16, for the two 16-key halves of the tile.
-//   Logits per head (own admission, tail, Eq. 3 gate), online softmax per
-//   head (the 4 lanes holding a head agree on its running max).
-//   O[16 heads x 16 dims] += P (A: head l%16, the 8 keys the lane holds) x V
-//     (B: dim l%16, the same 8 keys), V read transposed from the wave's LDS
-//     tile, for each 16-dim slab and both halves of P.
-// The 4 waves' (max, sum, O) are merged through LDS and written as the
+// Decode.  One work-group of W waves (4 for d = 64, 2 for d = 128) per chunk
+// of `split` union blocks of KV stream u; wave w takes the 32-key tiles w,
+// w + W, ...  A tile passes through the wave's own LDS area:
+//   load    coalesced 128-bit reads of whole K and V rows (d/8 lanes per row)
+//           into registers.  The loads of the wave's next tile are issued as
+//           soon as these registers are in LDS, so they overlap the compute of
+//           the current tile at no register cost;
+//   stage   K rows as stored, each row's 16-byte chunks permuted by an XOR
+//           with a function of the key so that the operand reads below hit
+//           distinct LDS banks; V transposed, vt[dim][k] with k = 4 (key % 8)
+//           + key / 8, rows of 18 words, the 8-byte groups of 4 keys permuted
+//           by an XOR with a function of the dim (the same goal, for writes
+//           and reads);
+//   scores  for each 16-key half st: S[16 keys x 16 heads] = K (A operand:
+//           lane l holds key rho(st, l % 16) = 2 ((l%16) / 4) + st +
+//           8 ((l%16) % 4), dims 32 kk + 8 (l / 16) .. + 7) times Q^T (B: head
+//           l % 16, the same dims; q split hi + lo).  Lane l receives head
+//           l % 16 and keys rho(st, 4 (l / 16) + i), i < 4;
+//   softmax per head with a lazily moved reference max; weights split hi + lo;
+//   values  O[16 heads x 16 dims] += P (A: head l % 16, contraction slots
+//           k = 8 (l / 16) + i: by the choice of rho and of the vt order these
+//           are exactly the lane's 8 score keys) times V (B: dim l % 16, the
+//           same slots, one 16-byte read of vt).
+// The W waves' (max, sum, O) are merged through LDS and written as the
 // chunk's partial per query head (or the output for single-chunk streams).
+#ifndef ETA_GQA_PREFETCH
+#define ETA_GQA_PREFETCH 1
+#endif
 constexpr int kTileKeys = 32;
-constexpr int kVtStride = kTileKeys + 4;  // bf16 per transposed row (pad: banks, 8-byte reads)
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazyRaise = 8.f;  // natural-log units
+constexpr int kVtWords = 18;       // 32-bit words per vt row: 32 keys + 8 bytes of padding
 
-__device__ __forceinline__ __bf16 to_bf16(float x) {
-  // round to nearest even (finite inputs only)
-  uint32_t u = __float_as_uint(x);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return __builtin_bit_cast(__bf16, (uint16_t)(u >> 16));
-}
-__device__ __forceinline__ float from_bf16(__bf16 h) {
-  return __uint_as_float((uint32_t)__builtin_bit_cast(uint16_t, h) << 16);
-}
+template <int D>
+struct GqaShape {
+  static constexpr int W = D == 64 ? 4 : 2;        // waves per work-group
+  // d = 64: at most 128 registers per lane, so 4 work-groups (16 waves) fit a
+  // CU; measured 440 vs 516 us at 3 per CU (32 x 128K, 57% union).
+  static constexpr int MinBlocks = D == 64 ? 4 : 1;
+  static constexpr int NK = D / 32;                 // 32-dim slabs (score product)
+  static constexpr int NV = D / 16;                 // 16-dim slabs (value product)
+  static constexpr int RB = D * 2;                  // bytes per bf16 row
+  static constexpr int LPR = D / 8;                 // lanes per row in a coalesced load
+  static constexpr int RPI = 64 / LPR;              // rows per load instruction
+  static constexpr int NI = kTileKeys / RPI;        // load instructions per tile and tensor
+  static constexpr int QPL = 8 / RPI;               // vt key groups per lane
+  static constexpr int KStride = RB;                // staged K row stride, bytes
+  static constexpr int KBytes = kTileKeys * KStride;
+  static constexpr int VBytes = D * kVtWords * 4;
+  static constexpr int WaveBytes = KBytes + VBytes;  // per-wave LDS area
+  static constexpr int MergeBytes = W * 16 * D * 4;
+  static_assert(MergeBytes <= W * WaveBytes, "merge area reuses the staging areas");
+};
 
 using GqaArgs = GqaDecode;
+
+// x where on, zeros elsewhere (component-wise, so it stays in registers).
+__device__ __forceinline__ uint4 keep(const uint4& x, bool on) {
+  const uint32_t m = on ? 0xffffffffu : 0u;
+  return make_uint4(x.x & m, x.y & m, x.z & m, x.w & m);
+}
+
+__device__ __forceinline__ uint32_t word(const uint4& x, int i) {
+  return i == 0 ? x.x : i == 1 ? x.y : i == 2 ? x.z : x.w;
+}
+
+// LDS layout permutations of the staged tiles (chosen for conflict-free
+// 128-bit operand reads of K, 64-bit writes and reads of vt, and cheap K
+// writes): K chunk c of key r is stored at chunk c ^ k_swz(r); the 4-key
+// group g of vt row dim is stored at group g ^ v_swz(dim) (even, so the two
+// groups an operand read takes stay adjacent).
+__device__ __forceinline__ int k_swz(int key) { return ((key >> 3) & 3) ^ (((key >> 1) & 1) << 2); }
+__device__ __forceinline__ int v_swz(int dim) { return 2 * ((dim >> 4) & 3); }
+
+// Orders this wave's LDS writes before its later LDS reads (and vice versa).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
 __device__ __forceinline__ int gqa_stream(const CacheView& c, const GqaArgs& a, bool dense, int u,
                                           int* T_out, int* cnt_out) {
@@ -214,16 +267,15 @@ __device__ __forceinline__ int gqa_stream(const CacheView& c, const GqaArgs& a, 
 }
 
 template <int D, int MODE, bool DENSE>
-__global__ __launch_bounds__(256) void decode_gqa_kernel(CacheView c, GqaArgs a) {
-  constexpr int NK = D / 32;  // 32-dim slabs of the score product
-  constexpr int NV = D / 16;  // 16-dim slabs of the value product
-  constexpr int RB = D * 2;   // bytes per bf16 key row
+__global__ __launch_bounds__(GqaShape<D>::W * 64, GqaShape<D>::MinBlocks) void decode_gqa_kernel(CacheView c, GqaArgs a) {
+  using Sh = GqaShape<D>;
+  constexpr int W = Sh::W, NK = Sh::NK, NV = Sh::NV, RB = Sh::RB;
+  constexpr int LPR = Sh::LPR, RPI = Sh::RPI, NI = Sh::NI, QPL = Sh::QPL;
   extern __shared__ __align__(16) char s_raw[];
-  __bf16* s_vt = reinterpret_cast<__bf16*>(s_raw);                   // [4][D][kVtStride]
-  float* s_o = reinterpret_cast<float*>(s_raw);                       // reused: [4][16][D]
-  int* s_list = reinterpret_cast<int*>(s_raw + 4 * D * kVtStride * 2);  // [split]
-  uint32_t* s_mask = reinterpret_cast<uint32_t*>(s_list + a.split);      // [split]
-  __shared__ float s_ml[4][16][2];
+  float* s_o = reinterpret_cast<float*>(s_raw);                        // merge: [W][16][D]
+  int* s_list = reinterpret_cast<int*>(s_raw + W * Sh::WaveBytes);     // [split]
+  uint32_t* s_mask = reinterpret_cast<uint32_t*>(s_list + a.split);    // [split]
+  __shared__ float s_ml[W][16][2];
 
   const int u = blockIdx.x / a.max_chunks, k = blockIdx.x % a.max_chunks;
   int T, cnt;
@@ -244,27 +296,42 @@ __global__ __launch_bounds__(256) void decode_gqa_kernel(CacheView c, GqaArgs a)
     }
   }
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int n = lane & 15, grp = lane >> 4;  // S layout: head n; keys 4*grp + i
+  const int n = lane & 15, grp = lane >> 4;  // operand layout: row/column n, k group grp
+  char* s_k = s_raw + wave * Sh::WaveBytes;  // staged K tile
+  char* s_v = s_k + Sh::KBytes;              // transposed V tile
 
   // Query operand (head n, dims 32*kk + 8*grp + i), scaled, split hi + lo.
+  // Lanes of padding heads (n >= G) load head G-1 and use zeros.
   bf16x8 qhi[NK], qlo[NK];
   {
-    const float* qn = a.q + ((size_t)u * G + (n < G ? n : 0)) * D;
+    const int hn = min(n, G - 1);
+    const float4* qn =
+        reinterpret_cast<const float4*>(a.q + ((size_t)u * G + hn) * D + 8 * grp);
+    float4 qv[NK][2];
 #pragma unroll
-    for (int kk = 0; kk < NK; ++kk)
+    for (int kk = 0; kk < NK; ++kk) {
+      qv[kk][0] = qn[8 * kk];
+      qv[kk][1] = qn[8 * kk + 1];
+    }
+    const float sc = n < G ? a.scale : 0.f;
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+      const float x8[8] = {qv[kk][0].x, qv[kk][0].y, qv[kk][0].z, qv[kk][0].w,
+                           qv[kk][1].x, qv[kk][1].y, qv[kk][1].z, qv[kk][1].w};
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float x = n < G ? qn[32 * kk + 8 * grp + i] * a.scale : 0.f;
-        const __bf16 h = to_bf16(x);
+        const float x = x8[i] * sc;
+        const __bf16 h = (__bf16)x;
         qhi[kk][i] = h;
-        qlo[kk][i] = to_bf16(x - from_bf16(h));
+        qlo[kk][i] = (__bf16)(x - (float)h);
       }
+    }
   }
-  const float tau_n = (MODE == ETA_LOGIT_GATED && n < G) ? a.tau[(size_t)u * G + n] : 0.f;
-  const float beta = a.beta;
+  const float tau_n = MODE == ETA_LOGIT_GATED ? a.tau[(size_t)u * G + min(n, G - 1)] : 0.f;
+  // Gate of Eq. 3: sigmoid(beta (S - tau)) = 1 / (1 + 2^(S gk1 + gk0)).
+  const float gk1 = -a.beta * kLog2e, gk0 = a.beta * kLog2e * tau_n;
   const char* kbase = static_cast<const char*>(c.k) + (size_t)u * c.cap * RB;
   const char* vbase = static_cast<const char*>(c.v) + (size_t)u * c.cap * RB;
-  __bf16* vt = s_vt + wave * D * kVtStride;
   __syncthreads();  // s_list, s_mask
 
   floatx4 O[NV];
@@ -274,128 +341,162 @@ __global__ __launch_bounds__(256) void decode_gqa_kernel(CacheView c, GqaArgs a)
 
   const int rows = nblk << c.log2bs;
   const int ntiles = (rows + kTileKeys - 1) / kTileKeys;
-  auto key_pos = [&](int rr) {  // absolute key position of chunk row rr, or -1
-    if (rr >= rows) return -1;
-    const int j = s_list[rr >> c.log2bs];
+  // Chunk row rr -> absolute key position, or -1 past the chunk, past the
+  // stream or for an out-of-range list entry.
+  auto key_pos = [&](int rr, int j) {
     const int s = (j << c.log2bs) + (rr & (c.bs - 1));
-    return ((unsigned)j >= (unsigned)nb || s >= T) ? -1 : s;
+    return (rr < rows && (unsigned)j < (unsigned)nb && s < T) ? s : -1;
   };
-  for (int t = wave; t < ntiles; t += 4) {
-    const int r0 = t * kTileKeys;
-    // K operand: two 16-key halves x NK slabs; V: key pair 2*(lane%16)+{0,1},
-    // dims 8*(grp + 4*cc) .. +7 for cc < D/32.
-    uint4 kraw[2][NK];
+  auto slot_of = [&](int rr) { return min(rr >> c.log2bs, nblk - 1); };
+
+  // Coalesced loads of tile t: instruction it reads key it*RPI + lane/LPR,
+  // bytes 16 (lane % LPR) .. +15.  Invalid keys read row 0 of the stream
+  // (always in bounds) and are replaced by zeros.
+  const int ri = lane / LPR, cc = lane % LPR;
+  auto fetch = [&](int t, uint4 (&kr)[NI], uint4 (&vr)[NI]) {
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      const int s = key_pos(r0 + 16 * st + n);
-#pragma unroll
-      for (int kk = 0; kk < NK; ++kk)
-        kraw[st][kk] = s >= 0 ? ld16_nt(kbase + (size_t)s * RB + (32 * kk + 8 * grp) * 2)
-                              : make_uint4(0, 0, 0, 0);
+    for (int it = 0; it < NI; ++it) {
+      const int rr = t * kTileKeys + it * RPI + ri;
+      const int s = key_pos(rr, s_list[slot_of(rr)]);
+      const size_t off = (size_t)max(s, 0) * RB + 16 * cc;
+      const uint4 x = ld16_nt(kbase + off);
+      const uint4 y = ld16_nt(vbase + off);
+      kr[it] = keep(x, s >= 0);
+      vr[it] = keep(y, s >= 0);
     }
-    uint4 vraw[2][NK];
-    {
-      const int s0 = key_pos(r0 + 2 * n), s1 = key_pos(r0 + 2 * n + 1);
+  };
+  // Registers -> LDS.
+  auto stage = [&](const uint4 (&kr)[NI], const uint4 (&vr)[NI]) {
 #pragma unroll
-      for (int cc = 0; cc < NK; ++cc) {
-        const int col = 8 * (grp + 4 * cc);
-        vraw[0][cc] = s0 >= 0 ? ld16_nt(vbase + (size_t)s0 * RB + col * 2) : make_uint4(0, 0, 0, 0);
-        vraw[1][cc] = s1 >= 0 ? ld16_nt(vbase + (size_t)s1 * RB + col * 2) : make_uint4(0, 0, 0, 0);
+    for (int it = 0; it < NI; ++it) {
+      const int key = it * RPI + ri;
+      const int chunk = cc ^ k_swz(key);
+      *reinterpret_cast<uint4*>(s_k + key * Sh::KStride + 16 * chunk) = kr[it];
+    }
+#pragma unroll
+    for (int qi = 0; qi < QPL; ++qi) {
+      const int q = ri + RPI * qi;  // keys q + 8 j sit in instructions qi + QPL j
+#pragma unroll
+      for (int w2 = 0; w2 < 4; ++w2) {
+        const int dim = 8 * cc + 2 * w2;
+        const uint32_t x0 = word(vr[qi], w2), x1 = word(vr[qi + QPL], w2);
+        const uint32_t x2 = word(vr[qi + 2 * QPL], w2), x3 = word(vr[qi + 3 * QPL], w2);
+        // dims `dim` (low halves) and dim + 1 (high halves) of keys q + 8 j
+        const uint2 lo = make_uint2((x0 & 0xffffu) | (x1 << 16), (x2 & 0xffffu) | (x3 << 16));
+        const uint2 hi = make_uint2((x0 >> 16) | (x1 & 0xffff0000u),
+                                    (x2 >> 16) | (x3 & 0xffff0000u));
+        *reinterpret_cast<uint2*>(s_v + (dim * kVtWords + 2 * (q ^ v_swz(dim))) * 4) = lo;
+        *reinterpret_cast<uint2*>(s_v + ((dim + 1) * kVtWords + 2 * (q ^ v_swz(dim + 1))) * 4) =
+            hi;
       }
     }
+  };
+  auto compute = [&](int t) {
+    const int r0 = t * kTileKeys;
     // Scores.
     floatx4 S[2];
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
+      const int key = 2 * (n >> 2) + st + 8 * (n & 3);
+      const char* row = s_k + key * Sh::KStride;
+      const int sw = k_swz(key);
       S[st] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk) {
-        const bf16x8 kv = __builtin_bit_cast(bf16x8, kraw[st][kk]);
+        const uint4 kx = *reinterpret_cast<const uint4*>(row + 16 * ((4 * kk + grp) ^ sw));
+        const bf16x8 kv = __builtin_bit_cast(bf16x8, kx);
         S[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qhi[kk], S[st], 0, 0, 0);
         S[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qlo[kk], S[st], 0, 0, 0);
       }
     }
-    // V tile -> LDS, transposed: vt[dim][key].
-#pragma unroll
-    for (int cc = 0; cc < NK; ++cc) {
-      const uint32_t* a0 = reinterpret_cast<const uint32_t*>(&vraw[0][cc]);
-      const uint32_t* a1 = reinterpret_cast<const uint32_t*>(&vraw[1][cc]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int col = 8 * (grp + 4 * cc) + 2 * e;
-        // dims col (low halves) and col+1 (high halves) of keys 2n and 2n+1
-        const uint32_t lo = (a0[e] & 0xffffu) | (a1[e] << 16);
-        const uint32_t hi = (a0[e] >> 16) | (a1[e] & 0xffff0000u);
-        *reinterpret_cast<uint32_t*>(vt + col * kVtStride + 2 * n) = lo;
-        *reinterpret_cast<uint32_t*>(vt + (col + 1) * kVtStride + 2 * n) = hi;
-      }
-    }
-    // Logits, masks and the running max of head n.
+    // Logits, masks and the running max of head n.  Score i of half st is
+    // key 2 grp + st + 8 i of the tile.
     float lg[8];
     float tmax = -__builtin_inff();
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
+    for (int st = 0; st < 2; ++st) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int rr = r0 + 16 * st + 4 * grp + i;
-        const int s = key_pos(rr);
-        bool on = s >= 0 && n < G;
-        if (on) on = (s_mask[rr >> c.log2bs] >> n) & 1u;
+        const int rr = r0 + 2 * grp + st + 8 * i;
+        const int slot = slot_of(rr);
+        const int s = key_pos(rr, s_list[slot]);
+        const bool on = n < G && s >= 0 && ((s_mask[slot] >> n) & 1u);
         const float d = S[st][i];
         float lv = d;
         if (MODE == ETA_LOGIT_GATED && s != T - 1)
-          lv = d * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-beta * (d - tau_n) *
-                                                                       1.4426950408889634f));
+          lv = d * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(fmaf(d, gk1, gk0)));
         lg[4 * st + i] = on ? lv : -__builtin_inff();
         tmax = fmaxf(tmax, lg[4 * st + i]);
       }
+    }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-    const float mn = fmaxf(m, tmax);
-    const float ms = (mn == -__builtin_inff()) ? 0.f : mn;
-    const float alpha = __builtin_amdgcn_exp2f((m - ms) * 1.4426950408889634f);
-    m = mn;
+    // Lazy rescaling: the reference max m of a head moves only when a tile
+    // raises the head's max above m + kLazyRaise (then every head moves to
+    // its own max, one wave-uniform branch).  Weights relative to m stay
+    // below e^kLazyRaise, well inside float32, and the softmax is unchanged
+    // by the choice of reference.
+    if (__ballot(tmax > m + kLazyRaise) != 0ull) {
+      const float mn = fmaxf(m, tmax);
+      const float alpha =
+          mn == -__builtin_inff() ? 1.f : __builtin_amdgcn_exp2f((m - mn) * kLog2e);
+      lsum *= alpha;
+      // O rows are heads 4*grp + i: their factors come from lanes 4*grp + i.
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float al = __shfl(alpha, 4 * grp + i, kWave);
+#pragma unroll
+        for (int nv = 0; nv < NV; ++nv) O[nv][i] *= al;
+      }
+      m = mn;
+    }
+    const float ms2 = m == -__builtin_inff() ? 0.f : m * kLog2e;
     bf16x8 phi, plo;
     float psum = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float p = __builtin_amdgcn_exp2f((lg[i] - ms) * 1.4426950408889634f);
+      const float p = __builtin_amdgcn_exp2f(fmaf(lg[i], kLog2e, -ms2));
       psum += p;
-      const __bf16 h = to_bf16(p);
+      const __bf16 h = (__bf16)p;
       phi[i] = h;
-      plo[i] = to_bf16(p - from_bf16(h));
+      plo[i] = (__bf16)(p - (float)h);
     }
-    lsum = lsum * alpha + psum;
-    // O rows are heads 4*grp + i: their rescale factors come from lanes 4*grp + i.
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float al = __shfl(alpha, 4 * grp + i, kWave);
-#pragma unroll
-      for (int nv = 0; nv < NV; ++nv) O[nv][i] *= al;
-    }
-    // Values: B operand = dims 16*nv + n, keys of slots 0-3 (4*grp..) and 4-7 (16+4*grp..).
-    // The tile was written by other lanes of this wave: order the LDS accesses.
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    lsum += psum;
+    // Values: B operand = dim 16 nv + n, contraction slots 8 grp .. 8 grp + 7.
 #pragma unroll
     for (int nv = 0; nv < NV; ++nv) {
-      const __bf16* row = vt + (16 * nv + n) * kVtStride;
-      const uint2 v03 = *reinterpret_cast<const uint2*>(row + 4 * grp);
-      const uint2 v47 = *reinterpret_cast<const uint2*>(row + 16 + 4 * grp);
-      const uint4 vv = make_uint4(v03.x, v03.y, v47.x, v47.y);
-      const bf16x8 vb = __builtin_bit_cast(bf16x8, vv);
+      const int dim = 16 * nv + n;
+      const char* vrow = s_v + dim * kVtWords * 4;
+      const uint2 v0 = *reinterpret_cast<const uint2*>(vrow + 8 * ((2 * grp) ^ v_swz(dim)));
+      const uint2 v1 = *reinterpret_cast<const uint2*>(vrow + 8 * ((2 * grp + 1) ^ v_swz(dim)));
+      const bf16x8 vb = __builtin_bit_cast(bf16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
       O[nv] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi, vb, O[nv], 0, 0, 0);
       O[nv] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo, vb, O[nv], 0, 0, 0);
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+
+  {
+    uint4 kr[NI], vr[NI];
+    int t = wave;
+    if (t < ntiles) fetch(t, kr, vr);
+    while (t < ntiles) {
+      stage(kr, vr);
+#if ETA_GQA_PREFETCH
+      if (t + W < ntiles) fetch(t + W, kr, vr);
+#endif
+      wave_lds_sync();
+      compute(t);
+      wave_lds_sync();
+#if !ETA_GQA_PREFETCH
+      if (t + W < ntiles) fetch(t + W, kr, vr);
+#endif
+      t += W;
+    }
   }
-  // Head n's sum over the 4 lane groups (they share the running max).
+  // Head n's sum over the 4 lane groups (they share the reference max).
   lsum += __shfl_xor(lsum, 16, kWave);
   lsum += __shfl_xor(lsum, 32, kWave);
-  __syncthreads();  // every wave is done with its transposed V tile
+  __syncthreads();  // every wave is done with its staging area
   float* so = s_o + wave * 16 * D;
 #pragma unroll
   for (int nv = 0; nv < NV; ++nv)
@@ -406,18 +507,18 @@ __global__ __launch_bounds__(256) void decode_gqa_kernel(CacheView c, GqaArgs a)
     s_ml[wave][n][1] = lsum;
   }
   __syncthreads();
-  // Merge the 4 waves per (head, dim) in a fixed order.
+  // Merge the W waves per (head, dim) in a fixed order.
   for (int e = threadIdx.x; e < G * D; e += blockDim.x) {
     const int h = e / D, col = e % D;
     float mm = s_ml[0][h][0], ll = s_ml[0][h][1];
     float aa = s_o[h * D + col];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) {
+    for (int w = 1; w < W; ++w) {
       const float m2 = s_ml[w][h][0], l2 = s_ml[w][h][1], a2 = s_o[(w * 16 + h) * D + col];
       const float mx = fmaxf(mm, m2);
       const float ms = (mx == -__builtin_inff()) ? 0.f : mx;
-      const float s1 = __builtin_amdgcn_exp2f((mm - ms) * 1.4426950408889634f);
-      const float s2 = __builtin_amdgcn_exp2f((m2 - ms) * 1.4426950408889634f);
+      const float s1 = __builtin_amdgcn_exp2f((mm - ms) * kLog2e);
+      const float s2 = __builtin_amdgcn_exp2f((m2 - ms) * kLog2e);
       ll = ll * s1 + l2 * s2;
       aa = aa * s1 + a2 * s2;
       mm = mx;
@@ -473,13 +574,13 @@ __global__ __launch_bounds__(1024) void combine_gqa_kernel(CacheView c, GqaArgs 
 #pragma unroll
     for (int i = 0; i < INF; ++i) mx = fmaxf(mx, mc[i]);
     const float ms = (mx == -__builtin_inff()) ? 0.f : mx;
-    const float alpha = __builtin_amdgcn_exp2f((m - ms) * 1.4426950408889634f);
+    const float alpha = __builtin_amdgcn_exp2f((m - ms) * kLog2e);
     l *= alpha;
 #pragma unroll
     for (int e = 0; e < CPL; ++e) acc[e] *= alpha;
 #pragma unroll
     for (int i = 0; i < INF; ++i) {
-      const float wgt = __builtin_amdgcn_exp2f((mc[i] - ms) * 1.4426950408889634f);
+      const float wgt = __builtin_amdgcn_exp2f((mc[i] - ms) * kLog2e);
       l = fmaf(wgt, lc[i], l);
 #pragma unroll
       for (int e = 0; e < CPL; ++e) acc[e] = fmaf(wgt, ac[i][e], acc[e]);
@@ -499,8 +600,8 @@ __global__ __launch_bounds__(1024) void combine_gqa_kernel(CacheView c, GqaArgs 
       const float m2 = s_ml[w][0], l2 = s_ml[w][1], a2 = s_acc[w][t];
       const float mx = fmaxf(mm, m2);
       const float ms = (mx == -__builtin_inff()) ? 0.f : mx;
-      const float s1 = __builtin_amdgcn_exp2f((mm - ms) * 1.4426950408889634f);
-      const float s2 = __builtin_amdgcn_exp2f((m2 - ms) * 1.4426950408889634f);
+      const float s1 = __builtin_amdgcn_exp2f((mm - ms) * kLog2e);
+      const float s2 = __builtin_amdgcn_exp2f((m2 - ms) * kLog2e);
       ll = ll * s1 + l2 * s2;
       aa = aa * s1 + a2 * s2;
       mm = mx;
@@ -533,14 +634,17 @@ hipError_t launch_screen_gqa(const CacheView& c, int G, const float* q, const fl
 }
 
 size_t gqa_decode_lds_bytes(int D, int split) {
-  return (size_t)4 * D * kVtStride * 2 + (size_t)split * 8;
+  const size_t stage = D == 128 ? (size_t)GqaShape<128>::W * GqaShape<128>::WaveBytes
+                                : (size_t)GqaShape<64>::W * GqaShape<64>::WaveBytes;
+  return stage + (size_t)split * 8;
 }
 
 template <int D, int MODE, bool DENSE>
 static hipError_t decode_gqa_t(const CacheView& c, const GqaDecode& g, hipStream_t s) {
   const GqaArgs& a = g;
   const long long grid = (long long)g.max_chunks * c.B * c.H;
-  hipLaunchKernelGGL((decode_gqa_kernel<D, MODE, DENSE>), dim3((unsigned)grid), dim3(256),
+  hipLaunchKernelGGL((decode_gqa_kernel<D, MODE, DENSE>), dim3((unsigned)grid),
+                     dim3(GqaShape<D>::W * 64),
                      gqa_decode_lds_bytes(D, g.split), s, c, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

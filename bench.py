@@ -11,7 +11,10 @@ Inputs are resident in HBM before timing starts.
 Printed: one JSON line with dense-equivalent KV tokens/s (sum_b T_b per step
 / step time), the decode kernel's roofline against 8 TB/s, a density sweep
 (10/38/70/100%) with the in-house dense HIP decode at the same shape, and the
-fp64 oracle timed on the host on a bounded sample of the same workload.
+fp64 oracle timed on the host on a bounded sample of the same workload.  A
+grouped-query section follows (32 sequences x 128K, 32 query heads on 4 KV
+heads, d 64, b 64: eta_screen_gqa + eta_decode_gqa against the grouped dense
+decode at 38/25/10% head density).
 """
 from __future__ import annotations
 
@@ -45,6 +48,8 @@ def parse():
     ap.add_argument("--split", type=int, default=0, help="blocks per split (0: auto)")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-gqa", action="store_true",
+                    help="skip the grouped-query section (32 x 128K, 32 query / 4 KV heads)")
     ap.add_argument("--seed", type=int, default=1234)
     ap.add_argument("--copy-reference", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times "
@@ -274,6 +279,9 @@ def main():
     print(f"[bench] upkeep: {json.dumps(upkeep)}", file=sys.stderr, flush=True)
 
     cpu = None if args.no_cpu else cpu_baseline(w, consts[args.rho], args.rho)
+    gqa = None
+    if not args.no_gqa:
+        gqa = gqa_bench(torch, np, eb, synth, args.steps, args.warmup, args.seed)
 
     out = {
         "metric": "dense-equiv KV tokens/s + achieved HBM GB/s (active bytes) at 128K ctx",
@@ -317,6 +325,7 @@ def main():
         "roofline": roofline,
         "upkeep": upkeep,
         "cpu_baseline": cpu,
+        "gqa": gqa,
     }
     print(json.dumps(out), flush=True)
 
@@ -383,6 +392,117 @@ def measure_upkeep(torch, eb, w, cache, dec, c, frozen, sumT):
             "predict_us": round(pred_us, 2) if not frozen else 0.0,
             "loop_ms_per_token": round(loop_ms, 5),
             "tokens_timed": n}
+
+
+def gqa_bench(torch, np, eb, synth, steps, warmup, seed):
+    """Grouped-query decode at the pages' benchmark shape (32 sequences x
+    128K, 32 query heads on 4 KV heads, d 64, b 64, bf16): dynamic Eq. 1
+    thresholds over the query heads with constants calibrated per query head
+    (the library's calibration, one call per head position in the group) to
+    38%, 25% and 10% head density; step = predict + screen_gqa + decode_gqa,
+    graph-captured; the grouped dense decode at the same shape alongside.
+    Decode bytes: union K+V rows, q, head masks and union lists, chunk
+    partials, outputs."""
+    dev = "cuda"
+    w = synth.make("gqa128k", seed=seed, device=dev)
+    B, Hkv, G, D, bs = w.B, w.H, w.G, w.D, w.block
+    Hq = Hkv * G
+    cache = eb.KVCache(B, Hkv, D, bs, w.cap, w.kv_dtype, device=dev, k=w.k, v=w.v)
+    cache.seq_len.copy_(w.seq_len)
+    eb.build_block_meta(cache)
+    sumT = int(w.seq_len.sum().item())
+    dec = eb.GqaDecoder(cache, G, z=w.z, scale=w.scale)
+    tau0 = torch.zeros((B, Hq), device=dev)
+    tmp = torch.zeros_like(tau0)
+    eb.predict_tau(w.q, w.W, torch.zeros(Hq, device=dev), 0.0, tau0, tmp)
+    q4 = w.q.view(B, Hkv, G, D)
+    t4 = tau0.view(B, Hkv, G)
+    cws = eb.workspace(eb.calibrate_workspace_bytes(1, B, Hkv, cache.cap_blocks))
+    res = {}
+    for rho in (0.38, 0.25, 0.10):
+        c = torch.zeros((Hkv, G), device=dev)
+        cg = torch.zeros(Hkv, device=dev)
+        for g in range(G):
+            eb.calibrate_threshold(cache, q4[:, :, g].contiguous()[None],
+                                   t4[:, :, g].contiguous()[None], w.z, w.scale, rho, cws, cg)
+            c[:, g] = cg
+        c = c.reshape(Hq).contiguous()
+
+        def step():
+            dec.predict(w.q, w.W, c)
+            dec.screen(w.q)
+            dec.attend(w.q)
+
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        ctr0 = dec.density_ctr.clone()
+        tscr, tdec = Timer(torch), Timer(torch)
+        for _ in range(steps):
+            dec.predict(w.q, w.W, c)
+            tscr.around(lambda: dec.screen(w.q))
+            tdec.around(lambda: dec.attend(w.q))
+        torch.cuda.synchronize()
+        ctr = ((dec.density_ctr - ctr0) // steps).cpu().numpy()
+        ucnt = dec.union_cnt.cpu().numpy().astype(np.int64)
+        ref = dec.out.clone()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(3):
+            dec.out.zero_()
+            graph.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(dec.out, ref), "graph replay differs from eager decode"
+        for _ in range(warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        a = time.perf_counter()
+        for _ in range(steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - a) * 1e3 / steps
+        del graph
+        union_tok = int(ctr[1])
+        chunks = -(-ucnt // dec.split)
+        part = int((np.where(chunks > 1, chunks, 0) * G * (D + 2) * 4 * 2).sum())
+        dbytes = union_tok * D * 2 * 2 + 2 * B * Hq * D * 4 + int(ucnt.sum()) * 8 + part
+        res[f"{rho:.2f}"] = {
+            "d_head": round(int(ctr[0]) / (sumT * Hq), 4),
+            "d_union": round(union_tok / (sumT * Hkv), 4),
+            "ms": round(ms, 5), "screen_ms": round(tscr.mean_ms(), 5),
+            "decode_ms": round(tdec.mean_ms(), 5),
+            "decode_gbs": round(dbytes / tdec.mean_ms() / 1e6, 1),
+            "tokens_per_s": round(sumT / (ms * 1e-3), 1)}
+        print(f"[bench] gqa rho={rho:.2f}: {json.dumps(res[f'{rho:.2f}'])}", file=sys.stderr,
+              flush=True)
+    graph = torch.cuda.CUDAGraph()
+    dec.dense(w.q)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        dec.dense(w.q)
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    a = time.perf_counter()
+    for _ in range(steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    dense_ms = (time.perf_counter() - a) * 1e3 / steps
+    dense_bytes = sumT * Hkv * D * 2 * 2
+    for v in res.values():
+        v["speedup_vs_dense"] = round(dense_ms / v["ms"], 3)
+    out = {"workload": f"gqa128k: batch {B}, {Hq} query heads on {Hkv} KV heads, head dim {D}, "
+                       f"context {int(w.seq_len.max())}, block {bs}, z {w.z}, bf16 KV, "
+                       "dynamic linear tau",
+           "blocks_per_split": dec.split, "dense_blocks_per_split": dec.dense_split,
+           "dense_ms": round(dense_ms, 5),
+           "dense_gbs": round(dense_bytes / dense_ms / 1e6, 1),
+           "by_head_density": res}
+    print(f"[bench] gqa dense: {dense_ms:.4f} ms", file=sys.stderr, flush=True)
+    del dec, cache, w
+    torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(w, c_gpu, rho):

@@ -345,6 +345,16 @@ class Decoder:
         return self.out
 
 
+def auto_split_gqa(units: int, cap_blocks: int, block: int, dense: bool = False) -> int:
+    """Blocks per chunk of the grouped-query decode: about 1024 keys per chunk
+    (4096 dense), fewer for a small cache so the grid still fills the chip.
+    From sweeps on MI355X at 32 x 128K, 4 KV heads, b = 64: 16 blocks at 57%
+    and 19% union (vs 8 or 32), 64 blocks dense."""
+    if dense:
+        return max(1, min(4096 // block, (units * cap_blocks) // 2048))
+    return max(1, min(1024 // block, (units * cap_blocks) // 1024))
+
+
 class GqaDecoder:
     """Grouped-query decode step with preallocated buffers: predict_tau over
     the query heads -> screen_gqa (per-head masks, union lists) ->
@@ -360,9 +370,9 @@ class GqaDecoder:
         B, Hkv, D, nbc = cache.batch, cache.heads, cache.head_dim, cache.cap_blocks
         Hq = Hkv * self.group
         self.mode = logit_mode
-        self.split = int(blocks_per_split or min(2048, auto_split(B * Hkv, nbc, cache.block)))
+        self.split = int(blocks_per_split or auto_split_gqa(B * Hkv, nbc, cache.block))
         self.dense_split = int(dense_blocks_per_split or
-                               min(2048, auto_split(B * Hkv, nbc, cache.block, dense=True)))
+                               auto_split_gqa(B * Hkv, nbc, cache.block, dense=True))
         dev = cache.k.device
         self.tau_gate = torch.zeros((B, Hq), dtype=torch.float32, device=dev)
         self.tau_screen = torch.zeros_like(self.tau_gate)

@@ -200,9 +200,6 @@ __global__ __launch_bounds__(256) void compact_gqa_kernel(CacheView c, const uin
 //           same slots, one 16-byte read of vt).
 // The W waves' (max, sum, O) are merged through LDS and written as the
 // chunk's partial per query head (or the output for single-chunk streams).
-#ifndef ETA_GQA_PREFETCH
-#define ETA_GQA_PREFETCH 1
-#endif
 constexpr int kTileKeys = 32;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazyRaise = 8.f;  // natural-log units
@@ -211,9 +208,12 @@ constexpr int kVtWords = 18;       // 32-bit words per vt row: 32 keys + 8 bytes
 template <int D>
 struct GqaShape {
   static constexpr int W = D == 64 ? 4 : 2;        // waves per work-group
-  // d = 64: at most 128 registers per lane, so 4 work-groups (16 waves) fit a
-  // CU; measured 440 vs 516 us at 3 per CU (32 x 128K, 57% union).
-  static constexpr int MinBlocks = D == 64 ? 4 : 1;
+  // d = 64: at most 168 registers per lane, 3 work-groups (12 waves) per CU.
+  // The register budget holds the wave's next tile in flight during the
+  // compute of the current one; at 4 per CU (128 registers) it spills.
+  // Measured on 32 x 128K at 57% union: 431 us (3 per CU) vs 448 us (4, with
+  // spills).
+  static constexpr int MinBlocks = D == 64 ? 3 : 1;
   static constexpr int NK = D / 32;                 // 32-dim slabs (score product)
   static constexpr int NV = D / 16;                 // 16-dim slabs (value product)
   static constexpr int RB = D * 2;                  // bytes per bf16 row
@@ -273,8 +273,8 @@ __global__ __launch_bounds__(GqaShape<D>::W * 64, GqaShape<D>::MinBlocks) void d
   constexpr int LPR = Sh::LPR, RPI = Sh::RPI, NI = Sh::NI, QPL = Sh::QPL;
   extern __shared__ __align__(16) char s_raw[];
   float* s_o = reinterpret_cast<float*>(s_raw);                        // merge: [W][16][D]
-  int* s_list = reinterpret_cast<int*>(s_raw + W * Sh::WaveBytes);     // [split]
-  uint32_t* s_mask = reinterpret_cast<uint32_t*>(s_list + a.split);    // [split]
+  // chunk's block list: (block index, head mask) per slot
+  int2* s_blk = reinterpret_cast<int2*>(s_raw + W * Sh::WaveBytes);    // [split]
   __shared__ float s_ml[W][16][2];
 
   const int u = blockIdx.x / a.max_chunks, k = blockIdx.x % a.max_chunks;
@@ -287,12 +287,12 @@ __global__ __launch_bounds__(GqaShape<D>::W * 64, GqaShape<D>::MinBlocks) void d
   const uint32_t all = (1u << G) - 1u;
   for (int i = threadIdx.x; i < nblk; i += blockDim.x) {
     if constexpr (DENSE) {
-      s_list[i] = first + i;
-      s_mask[i] = all;
+      s_blk[i] = make_int2(first + i, (int)all);
     } else {
       const int j = a.union_idx[(size_t)u * c.cap_blocks + first + i];
-      s_list[i] = j;
-      s_mask[i] = ((unsigned)j < (unsigned)nb) ? a.head_mask[(size_t)u * c.cap_blocks + j] : 0u;
+      const uint32_t hm =
+          ((unsigned)j < (unsigned)nb) ? a.head_mask[(size_t)u * c.cap_blocks + j] : 0u;
+      s_blk[i] = make_int2(j, (int)hm);
     }
   }
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -332,7 +332,7 @@ __global__ __launch_bounds__(GqaShape<D>::W * 64, GqaShape<D>::MinBlocks) void d
   const float gk1 = -a.beta * kLog2e, gk0 = a.beta * kLog2e * tau_n;
   const char* kbase = static_cast<const char*>(c.k) + (size_t)u * c.cap * RB;
   const char* vbase = static_cast<const char*>(c.v) + (size_t)u * c.cap * RB;
-  __syncthreads();  // s_list, s_mask
+  __syncthreads();  // s_blk
 
   floatx4 O[NV];
 #pragma unroll
@@ -351,24 +351,29 @@ __global__ __launch_bounds__(GqaShape<D>::W * 64, GqaShape<D>::MinBlocks) void d
 
   // Coalesced loads of tile t: instruction it reads key it*RPI + lane/LPR,
   // bytes 16 (lane % LPR) .. +15.  Invalid keys read row 0 of the stream
-  // (always in bounds) and are replaced by zeros.
+  // (always in bounds) and are zeroed when staged; bit it of `ok` records
+  // validity.  Nothing here waits for the data.
   const int ri = lane / LPR, cc = lane % LPR;
-  auto fetch = [&](int t, uint4 (&kr)[NI], uint4 (&vr)[NI]) {
+  auto fetch = [&](int t, uint4 (&kr)[NI], uint4 (&vr)[NI], uint32_t& ok) {
+    int js[NI];
+#pragma unroll
+    for (int it = 0; it < NI; ++it) js[it] = s_blk[slot_of(t * kTileKeys + it * RPI + ri)].x;
+    ok = 0;
 #pragma unroll
     for (int it = 0; it < NI; ++it) {
-      const int rr = t * kTileKeys + it * RPI + ri;
-      const int s = key_pos(rr, s_list[slot_of(rr)]);
+      const int s = key_pos(t * kTileKeys + it * RPI + ri, js[it]);
       const size_t off = (size_t)max(s, 0) * RB + 16 * cc;
-      const uint4 x = ld16_nt(kbase + off);
-      const uint4 y = ld16_nt(vbase + off);
-      kr[it] = keep(x, s >= 0);
-      vr[it] = keep(y, s >= 0);
+      kr[it] = ld16_nt(kbase + off);
+      vr[it] = ld16_nt(vbase + off);
+      ok |= (s >= 0 ? 1u : 0u) << it;
     }
   };
-  // Registers -> LDS.
-  auto stage = [&](const uint4 (&kr)[NI], const uint4 (&vr)[NI]) {
+  // Registers -> LDS (zeros for invalid keys).
+  auto stage = [&](uint4 (&kr)[NI], uint4 (&vr)[NI], uint32_t ok) {
 #pragma unroll
     for (int it = 0; it < NI; ++it) {
+      kr[it] = keep(kr[it], (ok >> it) & 1u);
+      vr[it] = keep(vr[it], (ok >> it) & 1u);
       const int key = it * RPI + ri;
       const int chunk = cc ^ k_swz(key);
       *reinterpret_cast<uint4*>(s_k + key * Sh::KStride + 16 * chunk) = kr[it];
@@ -413,14 +418,18 @@ __global__ __launch_bounds__(GqaShape<D>::W * 64, GqaShape<D>::MinBlocks) void d
     // key 2 grp + st + 8 i of the tile.
     float lg[8];
     float tmax = -__builtin_inff();
+    int2 blk[2][4];
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) blk[st][i] = s_blk[slot_of(r0 + 2 * grp + st + 8 * i)];
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int rr = r0 + 2 * grp + st + 8 * i;
-        const int slot = slot_of(rr);
-        const int s = key_pos(rr, s_list[slot]);
-        const bool on = n < G && s >= 0 && ((s_mask[slot] >> n) & 1u);
+        const int s = key_pos(rr, blk[st][i].x);
+        const bool on = (s >= 0) & (((uint32_t)blk[st][i].y >> n) & 1u);
         const float d = S[st][i];
         float lv = d;
         if (MODE == ETA_LOGIT_GATED && s != T - 1)
@@ -477,19 +486,15 @@ __global__ __launch_bounds__(GqaShape<D>::W * 64, GqaShape<D>::MinBlocks) void d
 
   {
     uint4 kr[NI], vr[NI];
+    uint32_t ok = 0;
     int t = wave;
-    if (t < ntiles) fetch(t, kr, vr);
+    if (t < ntiles) fetch(t, kr, vr, ok);
     while (t < ntiles) {
-      stage(kr, vr);
-#if ETA_GQA_PREFETCH
-      if (t + W < ntiles) fetch(t + W, kr, vr);
-#endif
+      stage(kr, vr, ok);
+      if (t + W < ntiles) fetch(t + W, kr, vr, ok);
       wave_lds_sync();
       compute(t);
       wave_lds_sync();
-#if !ETA_GQA_PREFETCH
-      if (t + W < ntiles) fetch(t + W, kr, vr);
-#endif
       t += W;
     }
   }

@@ -109,9 +109,12 @@ __global__ __launch_bounds__(256) void screen_gqa_kernel(CacheView c, int G, con
   }
 }
 
-// Compaction of the union words into the ascending union list (as for one
-// head per KV head), plus the counters: ctr[0] += admitted tokens summed over
-// the group's query heads, ctr[1] += union tokens.
+// Compaction of the union words into the ascending union list, plus the
+// counters: ctr[0] += admitted tokens summed over the group's query heads,
+// ctr[1] += union tokens.  Thread t takes a run of bpt consecutive blocks
+// (bpt a power of two <= 64, so a run lies in one word), rounds of 256 runs
+// in ascending order; a work-group scan places each run's entries.  The head
+// masks of the run's admitted blocks are independent loads.
 __global__ __launch_bounds__(256) void compact_gqa_kernel(CacheView c, const uint64_t* words,
                                                           int words_per_unit,
                                                           const uint32_t* head_mask,
@@ -122,36 +125,37 @@ __global__ __launch_bounds__(256) void compact_gqa_kernel(CacheView c, const uin
   const int u = blockIdx.x, t = threadIdx.x;
   const int T = c.seq_len[u / c.H];
   const int nb = (T + c.bs - 1) >> c.log2bs;
-  const int nw = (nb + 63) >> 6;
-  const int per = (nw + 255) >> 8;
-  const int w0 = min(t * per, nw), w1 = min(w0 + per, nw);
   const uint64_t* wu = words + (size_t)u * words_per_unit;
   const uint32_t* hm = head_mask + (size_t)u * c.cap_blocks;
-  auto word_at = [&](int w) {
-    uint64_t x = wu[w];
-    const int rem = nb - (w << 6);
-    if (rem < 64) x &= (1ull << rem) - 1ull;
-    return x;
-  };
-  int mine = 0;
-  for (int w = w0; w < w1; ++w) mine += __popcll(word_at(w));
-  scan[t] = mine;
-  __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {
-    const int add = t >= off ? scan[t - off] : 0;
-    __syncthreads();
-    scan[t] += add;
-    __syncthreads();
-  }
-  int pos = scan[t] - mine;
-  const int total = scan[255];
-  const int tail = T - ((nb - 1) << c.log2bs);
   int32_t* out = union_idx + (size_t)u * c.cap_blocks;
+  const int tail = T - ((nb - 1) << c.log2bs);
+  int bpt = 1;
+  while (bpt < 64 && bpt * 256 < nb) bpt <<= 1;
+  int base_pos = 0;
   unsigned long long head_tokens = 0;
-  for (int w = w0; w < w1; ++w) {
-    uint64_t x = word_at(w);
+  for (int r0 = 0; r0 < nb; r0 += 256 * bpt) {
+    const int b0 = r0 + t * bpt;  // first block of this thread's run
+    uint64_t x = 0;
+    if (b0 < nb) {
+      x = wu[b0 >> 6] >> (b0 & 63);
+      if (bpt < 64) x &= (1ull << bpt) - 1ull;
+      const int rem = nb - b0;
+      if (rem < 64) x &= (1ull << rem) - 1ull;
+    }
+    const int mine = __popcll(x);
+    scan[t] = mine;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+      const int add = t >= off ? scan[t - off] : 0;
+      __syncthreads();
+      scan[t] += add;
+      __syncthreads();
+    }
+    int pos = base_pos + scan[t] - mine;
+    base_pos += scan[255];
+    __syncthreads();  // scan[] is rewritten next round
     while (x) {
-      const int j = (w << 6) + __ffsll((unsigned long long)x) - 1;
+      const int j = b0 + __ffsll((unsigned long long)x) - 1;
       out[pos++] = j;
       head_tokens += (unsigned long long)__popc(hm[j]) * (j == nb - 1 ? tail : c.bs);
       x &= x - 1ull;
@@ -159,11 +163,12 @@ __global__ __launch_bounds__(256) void compact_gqa_kernel(CacheView c, const uin
   }
   s_tok[t] = head_tokens;
   __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (t < s) s_tok[t] += s_tok[t + s];
+  for (int st = 128; st > 0; st >>= 1) {
+    if (t < st) s_tok[t] += s_tok[t + st];
     __syncthreads();
   }
   if (t == 0) {
+    const int total = base_pos;
     union_cnt[u] = total;
     if (ctr && total > 0) {
       atomicAdd(reinterpret_cast<unsigned long long*>(ctr), s_tok[0]);

@@ -32,9 +32,11 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 COUNTERS = os.path.join(ROOT, "profiles", "decode_counters.json")
+GQA_COUNTERS = os.path.join(ROOT, "profiles", "gqa_decode_counters.json")
 # the decode kernels and the host code that picks their launch path
-DECODE_SRC = [os.path.join(ROOT, "long_context_decode_eta_amd", "csrc", f)
-              for f in ("kernels_decode.hip", "eta_api.hip")]
+CSRC = os.path.join(ROOT, "long_context_decode_eta_amd", "csrc")
+DECODE_SRC = [os.path.join(CSRC, f) for f in ("kernels_decode.hip", "eta_api.hip")]
+GQA_SRC = [os.path.join(CSRC, f) for f in ("kernels_gqa.hip", "eta_api.hip")]
 
 
 def parse():
@@ -44,12 +46,18 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="ctx128k",
                     choices=["ctx128k", "ctx32k", "ctx512k", "ragged"])
-    ap.add_argument("--rho", type=float, default=0.38, help="headline admitted density")
+    ap.add_argument("--rho", type=float, default=None,
+                    help="headline admitted density (default: the workload's target, 38%% for "
+                         "the density-swept 128K workload)")
     ap.add_argument("--split", type=int, default=0, help="blocks per split (0: auto)")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-gqa", action="store_true",
                     help="skip the grouped-query section (32 x 128K, 32 query / 4 KV heads)")
+    ap.add_argument("--gqa-only", action="store_true",
+                    help="run only the grouped-query section and print its JSON")
+    ap.add_argument("--gqa-rho", default="0.38,0.25,0.10",
+                    help="head densities of the grouped-query section")
     ap.add_argument("--seed", type=int, default=1234)
     ap.add_argument("--copy-reference", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times "
@@ -87,11 +95,22 @@ class Timer:
         return sum(s.elapsed_time(e) for s, e in self.pairs) / max(1, len(self.pairs))
 
 
-def kernel_hash() -> str:
+def kernel_hash(files=DECODE_SRC) -> str:
     h = hashlib.sha256()
-    for f in DECODE_SRC:
+    for f in files:
         h.update(open(f, "rb").read())
     return h.hexdigest()[:16]
+
+
+def counters_traffic(path, files, workload):
+    """HBM bytes per launch from a committed counter summary, if it was taken
+    on the same kernel sources and workload."""
+    if not os.path.exists(path):
+        return None
+    cj = json.load(open(path))
+    if cj.get("kernel_hash") == kernel_hash(files) and cj.get("workload") == workload:
+        return cj.get("hbm_bytes_per_launch")
+    return None
 
 
 def main():
@@ -110,8 +129,16 @@ def main():
     from long_context_decode_eta_amd import binding as eb
     from long_context_decode_eta_amd import synth
 
+    if args.rho is None:
+        target = synth.CONFIGS[args.workload].get("rho", 0.38)
+        args.rho = target if isinstance(target, float) else 0.38
     dev = "cuda"
     torch.cuda.set_device(0)
+    gqa_rhos = [float(x) for x in args.gqa_rho.split(",")]
+    if args.gqa_only:
+        print(json.dumps(gqa_bench(torch, np, eb, synth, args.steps, args.warmup, args.seed,
+                                   gqa_rhos)), flush=True)
+        return
     t0 = time.time()
     blk = synth.CONFIGS[args.workload]["block"]
     Tmax = synth.CONFIGS[args.workload]["T"]
@@ -264,24 +291,22 @@ def main():
     main = r
     value = sumT / (r["ms"] * 1e-3)
     achieved = r["decode_bytes"] / (r["decode_ms"] * 1e-3) / 1e9
-    traffic = None
-    if os.path.exists(COUNTERS):
-        cj = json.load(open(COUNTERS))
-        if cj.get("kernel_hash") == kernel_hash() and cj.get("workload") == args.workload:
-            traffic = cj.get("hbm_bytes_per_launch")
+    traffic = counters_traffic(COUNTERS, DECODE_SRC, args.workload)
     roofline = {"bound": "hbm", "kernel": "eta_decode (prepare + decode + combine kernels)",
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "algorithmic_bytes_per_launch": int(r["decode_bytes"]),
                 "avg_launch_ms": round(r["decode_ms"], 5)}
 
+    offsets = None if args.no_sweep else offset_sweep(torch, np, eb, w, dec, consts[args.rho],
+                                                       frozen, sumT, args.steps, args.warmup)
     upkeep = measure_upkeep(torch, eb, w, cache, dec, consts[args.rho], frozen, sumT)
     print(f"[bench] upkeep: {json.dumps(upkeep)}", file=sys.stderr, flush=True)
 
     cpu = None if args.no_cpu else cpu_baseline(w, consts[args.rho], args.rho)
     gqa = None
     if not args.no_gqa:
-        gqa = gqa_bench(torch, np, eb, synth, args.steps, args.warmup, args.seed)
+        gqa = gqa_bench(torch, np, eb, synth, args.steps, args.warmup, args.seed, gqa_rhos)
 
     out = {
         "metric": "dense-equiv KV tokens/s + achieved HBM GB/s (active bytes) at 128K ctx",
@@ -323,11 +348,66 @@ def main():
                                "ideal_speedup": round(dense_bytes / v["step_bytes"], 3)}
                   for k, v in sweep.items()},
         "roofline": roofline,
+        "offset_sweep": offsets,
         "upkeep": upkeep,
         "cpu_baseline": cpu,
         "gqa": gqa,
     }
     print(json.dumps(out), flush=True)
+
+
+def offset_sweep(torch, np, eb, w, dec, c, frozen, sumT, steps, warmup):
+    """Threshold-offset sweep on the synthetic workload (a Pareto curve in the
+    manner of the pages' offset tables): per-head constants fixed at the
+    headline density, screening threshold tau - a for several offsets a.  For
+    each a: admitted density, recall of the generator's needle blocks, the
+    output's relative L2 distance to the same gated attention with every block
+    admitted (a = +inf), and the step time (eager, HIP events)."""
+    W = None if frozen else w.W
+    H = w.H
+
+    def step(a):
+        dec.a = a
+        dec.predict(w.q, W, c)
+        dec.screen(w.q)
+        dec.attend(w.q)
+
+    step(math.inf)
+    torch.cuda.synchronize()
+    full = dec.out.clone()
+    out = {}
+    for a in (-1.0, -0.5, 0.0, 0.25, 0.5, 1.0, 2.0):
+        for _ in range(warmup):
+            step(a)
+        torch.cuda.synchronize()
+        ctr0 = int(dec.density_ctr.item())
+        s0 = torch.cuda.Event(enable_timing=True)
+        e0 = torch.cuda.Event(enable_timing=True)
+        s0.record()
+        for _ in range(steps):
+            step(a)
+        e0.record()
+        torch.cuda.synchronize()
+        ms = s0.elapsed_time(e0) / steps
+        toks = (int(dec.density_ctr.item()) - ctr0) // steps
+        idx = dec.active_idx.cpu().numpy()
+        cnt = dec.active_cnt.cpu().numpy()
+        hit = tot = 0
+        for u, nd in enumerate(w.needle_blocks):
+            b, h = divmod(u, H)
+            if nd.numel():
+                sel = idx[b, h, :cnt[b, h]]
+                hit += int(np.isin(nd.cpu().numpy(), sel).sum())
+                tot += int(nd.numel())
+        err = float(torch.linalg.vector_norm(dec.out - full) / torch.linalg.vector_norm(full))
+        out[f"{a:+.2f}"] = {"density": round(toks / (H * sumT), 4),
+                            "needle_recall": round(hit / max(1, tot), 4),
+                            "rel_l2_vs_all_admitted": float(f"{err:.3e}"),
+                            "eager_ms": round(ms, 5)}
+        print(f"[bench] offset a={a:+.2f}: {json.dumps(out[f'{a:+.2f}'])}", file=sys.stderr,
+              flush=True)
+    dec.a = 0.0
+    return out
 
 
 def measure_upkeep(torch, eb, w, cache, dec, c, frozen, sumT):
@@ -394,7 +474,7 @@ def measure_upkeep(torch, eb, w, cache, dec, c, frozen, sumT):
             "tokens_timed": n}
 
 
-def gqa_bench(torch, np, eb, synth, steps, warmup, seed):
+def gqa_bench(torch, np, eb, synth, steps, warmup, seed, rhos=(0.38, 0.25, 0.10)):
     """Grouped-query decode at the pages' benchmark shape (32 sequences x
     128K, 32 query heads on 4 KV heads, d 64, b 64, bf16): dynamic Eq. 1
     thresholds over the query heads with constants calibrated per query head
@@ -419,7 +499,7 @@ def gqa_bench(torch, np, eb, synth, steps, warmup, seed):
     t4 = tau0.view(B, Hkv, G)
     cws = eb.workspace(eb.calibrate_workspace_bytes(1, B, Hkv, cache.cap_blocks))
     res = {}
-    for rho in (0.38, 0.25, 0.10):
+    for rho in rhos:
         c = torch.zeros((Hkv, G), device=dev)
         cg = torch.zeros(Hkv, device=dev)
         for g in range(G):
@@ -468,6 +548,7 @@ def gqa_bench(torch, np, eb, synth, steps, warmup, seed):
         part = int((np.where(chunks > 1, chunks, 0) * G * (D + 2) * 4 * 2).sum())
         dbytes = union_tok * D * 2 * 2 + 2 * B * Hq * D * 4 + int(ucnt.sum()) * 8 + part
         res[f"{rho:.2f}"] = {
+            "decode_bytes": int(dbytes),
             "d_head": round(int(ctr[0]) / (sumT * Hq), 4),
             "d_union": round(union_tok / (sumT * Hkv), 4),
             "ms": round(ms, 5), "screen_ms": round(tscr.mean_ms(), 5),
@@ -492,9 +573,20 @@ def gqa_bench(torch, np, eb, synth, steps, warmup, seed):
     dense_bytes = sumT * Hkv * D * 2 * 2
     for v in res.values():
         v["speedup_vs_dense"] = round(dense_ms / v["ms"], 3)
+    roofline = None
+    if "0.38" in res:
+        r = res["0.38"]
+        ach = r["decode_bytes"] / (r["decode_ms"] * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "kernel": "eta_decode_gqa (decode + combine kernels), 38% head",
+                    "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(ach / HBM_PEAK_GBS, 4),
+                    "traffic": counters_traffic(GQA_COUNTERS, GQA_SRC, "gqa128k"),
+                    "algorithmic_bytes_per_launch": r["decode_bytes"],
+                    "avg_launch_ms": r["decode_ms"]}
     out = {"workload": f"gqa128k: batch {B}, {Hq} query heads on {Hkv} KV heads, head dim {D}, "
                        f"context {int(w.seq_len.max())}, block {bs}, z {w.z}, bf16 KV, "
                        "dynamic linear tau",
+           "roofline": roofline,
            "blocks_per_split": dec.split, "dense_blocks_per_split": dec.dense_split,
            "dense_ms": round(dense_ms, 5),
            "dense_gbs": round(dense_bytes / dense_ms / 1e6, 1),

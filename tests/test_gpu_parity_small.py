@@ -187,3 +187,17 @@ def test_queue_scheduled_decode_path():
         st = check_against_oracle(w, g, cache, W=None, bias_or_c=c, z=w.z, scale=w.scale,
                                   mode=mode)
     note(f"  density {st['density']:.3f} out_rel {st['out_rel']:.2e}")
+
+
+@pytest.mark.parametrize("a", [-0.4, 0.6, math.inf])
+def test_threshold_offset(a):
+    # Screening threshold tau - a (the threshold adjustment), gate at tau.
+    w = to_gpu(synth.make("ctx128k", seed=17, T=(3000, 9000), B=2, H=4, cap=9000))
+    cache = make_cache(w)
+    c = torch.full((4,), 0.9, dtype=torch.float32, device="cuda")
+    g = run_gpu(cache, w.q, W=w.W, bias_or_c=c, z=1.0, scale=w.scale, a=a, split=8)
+    st = check_against_oracle(w, g, cache, W=w.W, bias_or_c=c, z=1.0, scale=w.scale,
+                              mode=eb.GATED, a=a)
+    note(f"  a={a}: density {st['density']:.3f} out_rel {st['out_rel']:.2e}")
+    if a == math.inf:
+        assert st["density"] == 1.0

@@ -180,6 +180,10 @@ def main():
             dec.predict(w.q, None, c)
     torch.cuda.synchronize()
 
+    kv_bytes = 2 * w.k.numel() * w.k.element_size()
+    flush = (torch.empty((512 << 20) // 4, dtype=torch.float32, device=dev)
+             if kv_bytes < (2 << 30) else None)
+
     def run(rho, steps, warmup):
         """Eager steps timed per kernel with HIP events, then the same step
         captured once in a HIP graph (checked bit for bit against the eager
@@ -209,6 +213,21 @@ def main():
         torch.cuda.synchronize()
         eager = time.perf_counter() - a
         toks = (int(dec.density_ctr.item()) - ctr0) // steps
+        # Per-step latency distribution (HIP events around each whole step); for
+        # a cache that could sit in the 256 MB last-level cache, 512 MiB of
+        # scratch is written before every timed step so no step reads KV from it.
+        per_step = []
+        for _ in range(steps):
+            if flush is not None:
+                flush.fill_(1.0)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            step()
+            e1.record()
+            per_step.append((e0, e1))
+        torch.cuda.synchronize()
+        lat = sorted(s0.elapsed_time(s1) for s0, s1 in per_step)
         cnt = dec.active_cnt.cpu().numpy().astype(np.int64)
         ref = dec.out.clone()
 
@@ -229,7 +248,9 @@ def main():
         torch.cuda.synchronize()
         wall = time.perf_counter() - a
         del graph
+        pct = lambda f: lat[min(len(lat) - 1, int(f * (len(lat) - 1) + 0.5))]
         return dict(ms=wall * 1e3 / steps, eager_ms=eager * 1e3 / steps,
+                    step_ms_median=pct(0.5), step_ms_p10=pct(0.1), step_ms_p90=pct(0.9),
                     decode_ms=tdec.mean_ms(), screen_ms=tscr.mean_ms(),
                     density=toks / (H * sumT), tokens=toks, cnt=cnt)
 
@@ -317,6 +338,9 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(r["ms"], 5),
         "eager_ms_per_step": round(r["eager_ms"], 5),
+        "eager_step_ms": {"median": round(r["step_ms_median"], 5),
+                          "p10": round(r["step_ms_p10"], 5), "p90": round(r["step_ms_p90"], 5),
+                          "llc_flushed": flush is not None},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -634,11 +658,33 @@ def cpu_baseline(w, c_gpu, rho):
         reps += 1
         dens = float(r["tokens"].sum()) / (H * int(sl.sum()))
     per = t / reps
+    lib = oracle.load()
+    cores = int(lib.eta_oracle_threads())
+    # the same sample on one thread, for about 3 s
+    lib.eta_oracle_set_threads(1)
+    reps1, t1 = 0, 0.0
+    while t1 < 3.0 and reps1 < 1000:
+        a = time.perf_counter()
+        oracle.step_batch(q, K, V, sl, w.block, meta, Wn, c, z=w.z, scale=w.scale)
+        t1 += time.perf_counter() - a
+        reps1 += 1
+    lib.eta_oracle_set_threads(cores)
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": round(int(sl.sum()) / per, 1), "unit": "tokens/s",
-            "cores": int(oracle.load().eta_oracle_threads()), "kind": "oracle",
+            "cores": cores, "kind": "oracle",
+            "value_1thread": round(int(sl.sum()) / (t1 / reps1), 1),
+            "host": {"nproc": os.cpu_count(), "model": model},
             "sample": f"sequence {b0} of the workload ({H} heads x {int(sl.sum())} keys), "
-                      f"{reps} repetitions of threshold+screen+attention, density {dens:.3f}, "
-                      f"{per * 1e3:.1f} ms per repetition"}
+                      f"{reps} repetitions of threshold+screen+attention on {cores} threads "
+                      f"({per * 1e3:.1f} ms each) and {reps1} on one thread "
+                      f"({t1 / reps1 * 1e3:.1f} ms each), density {dens:.3f}"}
 
 
 if __name__ == "__main__":

@@ -90,6 +90,8 @@ def load(path: str | None = None):
     lib.eta_oracle_gqa_dense_batch.restype = None
     lib.eta_oracle_threads.argtypes = []
     lib.eta_oracle_threads.restype = _i
+    lib.eta_oracle_set_threads.argtypes = [_i]
+    lib.eta_oracle_set_threads.restype = None
     if path is None:
         _lib = lib
     return lib

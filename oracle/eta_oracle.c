@@ -213,6 +213,7 @@ void eta_oracle_dense(const float* q, const void* K, const void* V, int dtype, i
 
 /* Threads an OpenMP region of the batch drivers uses. */
 int eta_oracle_threads(void) { return omp_get_max_threads(); }
+void eta_oracle_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
 
 /* ---------------------------------------------------------------------- */
 /* Batch drivers: the same steps for every (sequence, head) stream, one

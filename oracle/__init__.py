@@ -88,6 +88,8 @@ def load(path: str | None = None):
     lib.eta_oracle_gqa_screen_attend_batch.restype = None
     lib.eta_oracle_gqa_dense_batch.argtypes = [_i] * 6 + [_p] * 4 + [_d, _p]
     lib.eta_oracle_gqa_dense_batch.restype = None
+    lib.eta_oracle_prefill.argtypes = [_i] * 6 + [_p] * 4 + [_d, _d, _p, _p]
+    lib.eta_oracle_prefill.restype = None
     lib.eta_oracle_threads.argtypes = []
     lib.eta_oracle_threads.restype = _i
     lib.eta_oracle_set_threads.argtypes = [_i]
@@ -286,6 +288,27 @@ def gqa_dense_batch(q, K, V, seq_len, group, scale=None, lib=None):
     lib.eta_oracle_gqa_dense_batch(B, Hkv, int(group), d, cap, dt, _ptr(sl), _ptr(q), _ptr(K),
                                    _ptr(V), float(scale), _ptr(out))
     return out
+
+
+def prefill(q, K, V, tau, group=1, *, beta=5.0, scale=None, lib=None):
+    """Gated causal attention forward over whole sequences (Eqs. 2-3) and the
+    per-row density term of Eq. 4.  q [B][H_kv*G][T][d], K/V [B][H_kv][T][d]
+    (all float32, or all bf16 bits as uint16), tau [B][H_kv*G][T].  Returns
+    (out [B][H_q][T][d], dens [B][H_q][T]) in float64."""
+    lib = lib or load()
+    q, dq = _kv(q); K, dt = _kv(K); V, dt2 = _kv(V)
+    assert dq == dt == dt2
+    B, Hkv, T, d = K.shape
+    G = int(group)
+    assert q.shape == (B, Hkv * G, T, d)
+    if scale is None:
+        scale = float(np.float32(1.0 / np.sqrt(d)))
+    tau = np.ascontiguousarray(np.broadcast_to(tau, (B, Hkv * G, T)), dtype=np.float64)
+    out = np.zeros((B, Hkv * G, T, d))
+    dens = np.zeros((B, Hkv * G, T))
+    lib.eta_oracle_prefill(B, Hkv, G, T, d, dt, _ptr(q), _ptr(K), _ptr(V), _ptr(tau), float(beta),
+                           float(scale), _ptr(out), _ptr(dens))
+    return out, dens
 
 
 def attend_batch(q, K, V, seq_len, b, active, tau, *, mode=GATED, beta=5.0, scale=None,

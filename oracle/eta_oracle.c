@@ -382,6 +382,59 @@ void eta_oracle_gqa_dense_batch(int B, int Hkv, int G, int d, int cap, int dtype
 }
 
 /* ---------------------------------------------------------------------- */
+/* Gated causal attention over a whole sequence: the forward pass of the
+ * model's own attention in prefill or training (summary, Methodology 2,
+ * Eqs. 2-3), and the per-row density term of the sparsity loss (Methodology
+ * 3, Eq. 4).  Query head h of sequence b reads KV head h / G.  For query
+ * position t (0-based) and keys s = 0..t:
+ *   S_ts   = scale <q_t, k_s>
+ *   m_ts   = sigmoid(beta (S_ts - tau_t))                      (Eq. 2)
+ *   l_ts   = S_ts for s = t, S_ts m_ts otherwise; causal softmax (Eq. 3)
+ *   out_t  = sum_s softmax(l_t.)_s v_s
+ *   dens_t = (1 / (t + 1)) sum_{s <= t} m_ts   (the inner average of Eq. 4)
+ * The layer's sparsity term is lambda / (H T) sum_h sum_t dens_t.  q, K and
+ * V share one element type; tau is [B][H_q][T]. */
+void eta_oracle_prefill(int B, int Hkv, int G, int T, int d, int dtype, const void* q,
+                        const void* K, const void* V, const double* tau, double beta,
+                        double scale, double* out, double* dens) {
+  int Hq = Hkv * G;
+  size_t eb = elt_bytes(dtype);
+#pragma omp parallel for schedule(dynamic, 1)
+  for (long long row = 0; row < (long long)B * Hq * T; ++row) {
+    int t = (int)(row % T);
+    long long uq = row / T;
+    int bb = (int)(uq / Hq), kv = (int)((uq % Hq) / G);
+    const char* qt = (const char*)q + (size_t)row * d * eb;
+    const char* Ku = (const char*)K + ((size_t)bb * Hkv + kv) * (size_t)T * d * eb;
+    const char* Vu = (const char*)V + ((size_t)bb * Hkv + kv) * (size_t)T * d * eb;
+    double tt = tau[row];
+    double* logit = (double*)malloc(sizeof(double) * (size_t)(t + 1));
+    double top = -INFINITY, msum = 0.0;
+    for (int s = 0; s <= t; ++s) {
+      double S = 0.0;
+      for (int i = 0; i < d; ++i) S += elem(qt, dtype, (size_t)i) * elem(Ku, dtype, (size_t)s * d + i);
+      S *= scale;
+      double m = 1.0 / (1.0 + exp(-beta * (S - tt)));
+      msum += m;
+      double l = (s == t) ? S : S * m;
+      logit[s] = l;
+      if (l > top) top = l;
+    }
+    double* o = out + (size_t)row * d;
+    for (int i = 0; i < d; ++i) o[i] = 0.0;
+    double den = 0.0;
+    for (int s = 0; s <= t; ++s) {
+      double w = exp(logit[s] - top);
+      den += w;
+      for (int i = 0; i < d; ++i) o[i] += w * elem(Vu, dtype, (size_t)s * d + i);
+    }
+    for (int i = 0; i < d; ++i) o[i] /= den;
+    if (dens) dens[row] = msum / (double)(t + 1);
+    free(logit);
+  }
+}
+
+/* ---------------------------------------------------------------------- */
 /* Offline calibration of frozen per-head constants (the pages describe an
  * offline algorithm that freezes per-(layer, head) thresholds but give no
  * steps; this is the plain quantile reading).  For head h, pool over the

@@ -2,7 +2,7 @@
 
 Each case plants one mistake in a copy of oracle/eta_oracle.c (on the CPU),
 builds it, and runs the pin suites (test_oracle_hand_example.py,
-test_oracle_properties.py, test_oracle_gqa.py) against the mutant through
+test_oracle_properties.py, test_oracle_gqa.py, test_oracle_prefill.py) against the mutant through
 ETA_ORACLE_LIB.  Every
 mutant must make at least one pin fail; the unmodified source must pass.
 """
@@ -18,9 +18,16 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 PINS = [os.path.join(HERE, "test_oracle_hand_example.py"),
         os.path.join(HERE, "test_oracle_properties.py"),
-        os.path.join(HERE, "test_oracle_gqa.py")]
+        os.path.join(HERE, "test_oracle_gqa.py"),
+        os.path.join(HERE, "test_oracle_prefill.py")]
 
 MUTANTS = {
+    "prefill_diagonal_gated": ("double l = (s == t) ? S : S * m;", "double l = S * m;"),
+    "prefill_density_over_t": ("dens[row] = msum / (double)(t + 1);",
+                               "dens[row] = msum / (double)(t > 0 ? t : 1);"),
+    "prefill_density_skips_diagonal": ("msum += m;", "if (s != t) msum += m;"),
+    "prefill_wrong_kv_head": ("kv = (int)((uq % Hq) / G);", "kv = (int)((uq % Hq) % Hkv);"),
+    "prefill_key_t_excluded": ("for (int s = 0; s <= t; ++s) {", "for (int s = 0; s < t; ++s) {", 2),
     "sample_variance": ("var[(size_t)j * d + i] = s / b;", "var[(size_t)j * d + i] = s / (b - 1);"),
     "mean_over_d": ("mu[(size_t)j * d + i] = s / b;", "mu[(size_t)j * d + i] = s / d;"),
     "maxnorm_squared": ("double n = sqrt(n2);", "double n = n2;"),

@@ -20,7 +20,9 @@
  * eta_dense_decode (the same kernels over every key: plain dense decode),
  * eta_calibrate_threshold (per-head constants for a target density) and the
  * grouped-query forms eta_screen_gqa / eta_decode_gqa / eta_dense_decode_gqa
- * (several query heads per KV head, one read of each union block).
+ * (several query heads per KV head, one read of each union block), and
+ * eta_gated_prefill (the gated causal attention forward over whole
+ * sequences, with the density term of the sparsity loss).
  *
  * Conventions shared by every call
  *   - Every function returns eta_status; ETA_OK is 0.  All arguments are
@@ -51,7 +53,7 @@
 extern "C" {
 #endif
 
-#define ETA_ABI_VERSION 2
+#define ETA_ABI_VERSION 3
 
 typedef int32_t eta_status;
 enum {
@@ -273,6 +275,29 @@ eta_status eta_decode_gqa(const eta_cache* c, int32_t group, const float* q,
 eta_status eta_dense_decode_gqa(const eta_cache* c, int32_t group, const float* q, float scale,
                                 int32_t blocks_per_split, void* workspace,
                                 size_t workspace_bytes, float* out, void* stream);
+
+/*
+ * Gated causal attention forward over whole sequences: prefill, or the
+ * forward pass of training (picx.dev summary, Methodology 2, Eqs. 2-3; and
+ * Methodology 3, Eq. 4 for `dens`).  Query head h = kv * group + g reads KV
+ * head kv.  For position t (0-based) and keys s <= t, with
+ * S_ts = scale <q_t, k_s> and m_ts = sigmoid(beta (S_ts - tau_t)):
+ *   out_t  = sum_s softmax_s(l_ts) v_s,  l_ts = S_ts m_ts (s < t), S_tt (s = t)
+ *   dens_t = (1 / (t + 1)) sum_{s <= t} m_ts
+ * (Eq. 4's term of the layer is lambda / (H T) sum_h sum_t dens_t.)
+ *   q     device [batch][kv_heads*group][seq_len][head_dim] bf16
+ *   k, v  device [batch][kv_heads][seq_len][head_dim] bf16
+ *   tau   device [batch][kv_heads*group][seq_len] float32 (Eq. 1 per position)
+ *   out   device [batch][kv_heads*group][seq_len][head_dim] float32
+ *   dens  device [batch][kv_heads*group][seq_len] float32, or NULL
+ * head_dim in {64, 128}; beta and scale finite and > 0.  Both products run
+ * on the matrix cores with float32 accumulation; the softmax weights are
+ * split into two bf16 terms.  No workspace.
+ */
+eta_status eta_gated_prefill(int32_t batch, int32_t kv_heads, int32_t group, int32_t seq_len,
+                             int32_t head_dim, const void* q, const void* k, const void* v,
+                             const float* tau, float beta, float scale, float* out, float* dens,
+                             void* stream);
 
 #ifdef __cplusplus
 }

@@ -68,6 +68,9 @@ _SIGS = {
                        c_int32),
     "eta_dense_decode_gqa": ([_P, c_int32, c_void_p, c_float, c_int32, c_void_p, c_size_t,
                               c_void_p, c_void_p], c_int32),
+    "eta_gated_prefill": ([c_int32, c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p,
+                           c_void_p, c_void_p, c_float, c_float, c_void_p, c_void_p, c_void_p],
+                          c_int32),
 }
 
 _lib = None
@@ -276,6 +279,19 @@ def dense_decode_gqa(cache: KVCache, group, q, scale, blocks_per_split, workspac
                                       workspace.numel() * workspace.element_size(),
                                       _dev(out, torch.float32, "out"), _stream(stream)),
            "eta_dense_decode_gqa")
+
+
+def gated_prefill(q, k, v, tau, group, beta, scale, out, dens=None, stream=None):
+    """Gated causal attention forward over whole sequences: q [B][H_kv*G][T][d]
+    bf16, k/v [B][H_kv][T][d] bf16, tau [B][H_kv*G][T] float32 -> out
+    [B][H_kv*G][T][d] float32 and, if given, dens [B][H_kv*G][T] float32."""
+    B, Hkv, T, D = k.shape
+    _check(lib().eta_gated_prefill(B, Hkv, int(group), T, D, _dev(q, torch.bfloat16, "q"),
+                                   _dev(k, torch.bfloat16, "k"), _dev(v, torch.bfloat16, "v"),
+                                   _dev(tau, torch.float32, "tau"), float(beta), float(scale),
+                                   _dev(out, torch.float32, "out"),
+                                   _dev(dens, torch.float32, "dens"), _stream(stream)),
+           "eta_gated_prefill")
 
 
 def workspace(nbytes: int, device="cuda") -> torch.Tensor:

@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libeta.so")
 SOURCES = ["eta_api.hip", "kernels_meta.hip", "kernels_screen.hip", "kernels_decode.hip",
-           "kernels_gqa.hip"]
+           "kernels_gqa.hip", "kernels_prefill.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -456,4 +456,45 @@ eta_status eta_dense_decode_gqa(const eta_cache* c, int32_t group, const float* 
                            stream);
 }
 
+// ---------------------------------------------------------------------------
+// Gated causal attention forward (prefill / training forward).
+
+eta_status eta_gated_prefill(int32_t batch, int32_t kv_heads, int32_t group, int32_t seq_len,
+                             int32_t head_dim, const void* q, const void* k, const void* v,
+                             const float* tau, float beta, float scale, float* out, float* dens,
+                             void* stream) {
+  if (batch < 0 || kv_heads < 0 || group < 1 || seq_len < 0)
+    return fail(ETA_ERR_BAD_SHAPE, "batch %d, kv_heads %d, group %d, seq_len %d", batch,
+                kv_heads, group, seq_len);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(ETA_ERR_BAD_SHAPE, "head_dim %d unsupported (64 or 128)", head_dim);
+  if (bad_float(beta) || !(beta > 0.f) || isinf(beta))
+    return fail(ETA_ERR_BAD_ARG, "beta must be finite and > 0");
+  if (bad_float(scale) || !(scale > 0.f) || isinf(scale))
+    return fail(ETA_ERR_BAD_ARG, "scale must be finite and > 0");
+  if (batch == 0 || kv_heads == 0 || seq_len == 0) return ok();
+  if (!q || !k || !v || !tau || !out) return fail(ETA_ERR_NULL_PTR, "q/k/v/tau/out is NULL");
+  const long long hq = (long long)kv_heads * group;
+  if ((long long)batch * hq * seq_len * head_dim > (1LL << 40))
+    return fail(ETA_ERR_BAD_SHAPE, "problem too large");
+  if ((long long)eta::ceil_div(seq_len, 64) * batch * hq > kMaxGrid)
+    return fail(ETA_ERR_BAD_SHAPE, "grid too large");
+  eta::PrefillArgs a;
+  a.B = batch;
+  a.Hkv = kv_heads;
+  a.G = group;
+  a.Hq = (int)hq;
+  a.T = seq_len;
+  a.D = head_dim;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.tau = tau;
+  a.beta = beta;
+  a.scale = scale;
+  a.out = out;
+  a.dens = dens;
+  return hip_status(eta::launch_prefill(a, (hipStream_t)stream), "eta_gated_prefill launch");
+}
+
 }  // extern "C"

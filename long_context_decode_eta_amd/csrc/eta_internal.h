@@ -109,6 +109,50 @@ __device__ __forceinline__ float group_max(float x) {
 }
 
 // ---------------------------------------------------------------------------
+// Matrix-core tiles (grouped-query decode, gated prefill).  A 32-key tile of K
+// and V passes through LDS: K rows as stored with their 16-byte chunks
+// permuted, V transposed (vt[dim][k], k = 4 (key % 8) + key / 8, rows of
+// kVtWords words), so that v_mfma_f32_16x16x32_bf16 operands are single
+// conflict-free LDS reads.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr int kTileKeys = 32;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazyRaise = 8.f;  // natural-log units
+constexpr int kVtWords = 18;       // 32-bit words per vt row: 32 keys + 8 bytes of padding
+
+// x where on, zeros elsewhere (component-wise, so it stays in registers).
+__device__ __forceinline__ uint4 keep(const uint4& x, bool on) {
+  const uint32_t m = on ? 0xffffffffu : 0u;
+  return make_uint4(x.x & m, x.y & m, x.z & m, x.w & m);
+}
+
+__device__ __forceinline__ uint32_t word(const uint4& x, int i) {
+  return i == 0 ? x.x : i == 1 ? x.y : i == 2 ? x.z : x.w;
+}
+
+// LDS layout permutations of the staged tiles (chosen for conflict-free
+// 128-bit operand reads of K, 64-bit writes and reads of vt, and cheap K
+// writes): K chunk c of key r is stored at chunk c ^ k_swz(r); the 4-key
+// group g of vt row dim is stored at group g ^ v_swz(dim) (even, so the two
+// groups an operand read takes stay adjacent).
+__device__ __forceinline__ int k_swz(int key) { return ((key >> 3) & 3) ^ (((key >> 1) & 1) << 2); }
+__device__ __forceinline__ int v_swz(int dim) { return 2 * ((dim >> 4) & 3); }
+
+// Orders this wave's LDS writes before its later LDS reads (and vice versa).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Score-tile key of operand row r in 16-key half st of a 32-key tile: with
+// this order, the 8 scores a lane receives (keys 2 (l/16) + st + 8 i) are
+// exactly its 8 contraction slots of the value product.
+__device__ __forceinline__ int tile_key(int st, int r) { return 2 * (r >> 2) + st + 8 * (r & 3); }
+
+// ---------------------------------------------------------------------------
 // Device view of the cache (plain values; built on the host per call).
 struct CacheView {
   int B, H, D, bs, log2bs, cap, cap_blocks, dtype;
@@ -181,6 +225,18 @@ hipError_t launch_screen_gqa(const CacheView& c, int G, const float* q, const fl
                              int32_t* union_cnt, uint64_t* ctr, uint64_t* words, hipStream_t s);
 size_t gqa_decode_lds_bytes(int D, int split);
 hipError_t launch_decode_gqa(const CacheView& c, const GqaDecode& g, hipStream_t s);
+// Gated causal attention forward over whole sequences (bf16 q, K, V).
+struct PrefillArgs {
+  int B, Hkv, G, Hq, T, D;
+  const void* q;  // [B][Hq][T][D] bf16
+  const void* k;  // [B][Hkv][T][D] bf16
+  const void* v;
+  const float* tau;  // [B][Hq][T]
+  float beta, scale;
+  float* out;   // [B][Hq][T][D]
+  float* dens;  // [B][Hq][T] or null
+};
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_calibrate(const CacheView& c, int n_sets, const float* q_sets,
                             const float* tau0, float z, float scale, float rho, float* values,
                             float* c_out, hipStream_t s);

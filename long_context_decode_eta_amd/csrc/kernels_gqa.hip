@@ -18,8 +18,6 @@
 
 namespace eta {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------------------
 // Screen: one work-group per 64-block admission word of KV stream u; wave w
@@ -205,10 +203,6 @@ __global__ __launch_bounds__(256) void compact_gqa_kernel(CacheView c, const uin
 //           same slots, one 16-byte read of vt).
 // The W waves' (max, sum, O) are merged through LDS and written as the
 // chunk's partial per query head (or the output for single-chunk streams).
-constexpr int kTileKeys = 32;
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLazyRaise = 8.f;  // natural-log units
-constexpr int kVtWords = 18;       // 32-bit words per vt row: 32 keys + 8 bytes of padding
 
 template <int D>
 struct GqaShape {
@@ -235,31 +229,6 @@ struct GqaShape {
 };
 
 using GqaArgs = GqaDecode;
-
-// x where on, zeros elsewhere (component-wise, so it stays in registers).
-__device__ __forceinline__ uint4 keep(const uint4& x, bool on) {
-  const uint32_t m = on ? 0xffffffffu : 0u;
-  return make_uint4(x.x & m, x.y & m, x.z & m, x.w & m);
-}
-
-__device__ __forceinline__ uint32_t word(const uint4& x, int i) {
-  return i == 0 ? x.x : i == 1 ? x.y : i == 2 ? x.z : x.w;
-}
-
-// LDS layout permutations of the staged tiles (chosen for conflict-free
-// 128-bit operand reads of K, 64-bit writes and reads of vt, and cheap K
-// writes): K chunk c of key r is stored at chunk c ^ k_swz(r); the 4-key
-// group g of vt row dim is stored at group g ^ v_swz(dim) (even, so the two
-// groups an operand read takes stay adjacent).
-__device__ __forceinline__ int k_swz(int key) { return ((key >> 3) & 3) ^ (((key >> 1) & 1) << 2); }
-__device__ __forceinline__ int v_swz(int dim) { return 2 * ((dim >> 4) & 3); }
-
-// Orders this wave's LDS writes before its later LDS reads (and vice versa).
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 __device__ __forceinline__ int gqa_stream(const CacheView& c, const GqaArgs& a, bool dense, int u,
                                           int* T_out, int* cnt_out) {
@@ -407,7 +376,7 @@ __global__ __launch_bounds__(GqaShape<D>::W * 64, GqaShape<D>::MinBlocks) void d
     floatx4 S[2];
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
-      const int key = 2 * (n >> 2) + st + 8 * (n & 3);
+      const int key = tile_key(st, n);
       const char* row = s_k + key * Sh::KStride;
       const int sw = k_swz(key);
       S[st] = floatx4{0.f, 0.f, 0.f, 0.f};

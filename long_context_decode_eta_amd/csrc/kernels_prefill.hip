@@ -1,0 +1,245 @@
+// kernels_prefill.hip -- gated causal attention forward over whole sequences.
+//
+// Paper: "Elastic Threshold Attention ..." (summary page, Methodology 2,
+// Eqs. 2-3: the model's own attention, with every off-diagonal score
+// multiplied by its soft inclusion gate sigmoid(beta (S - tau_t)) before a
+// causal softmax; Methodology 3, Eq. 4: the per-row mean of the gates, whose
+// average over heads and positions is the layer's sparsity term).  This is
+// the forward pass of prefill and training; decode (one query against a
+// cache) is the block-sparse path of the other kernels.
+//
+// One work-group of 4 waves takes 64 consecutive queries of one query head;
+// wave w owns queries t0 + 16 w .. + 15.  The keys 0 .. t0 + 63 are walked in
+// 32-key tiles.  A tile is loaded once for the 4 waves (coalesced 128-bit
+// reads by all 256 threads, the next tile's loads in flight while the
+// current one is computed) and staged in LDS in the layout of the
+// grouped-query decode (K rows chunk-swizzled, V transposed), double
+// buffered, one barrier per tile.  Each wave then computes, on the matrix
+// cores, S^T = K_tile Q_w^T (queries as the 16 columns; q is bf16 as given)
+// and O += P V with the weights split hi + lo, applying the causal mask, the
+// gate and an online softmax per query column in between.
+#include "eta_internal.h"
+
+namespace eta {
+
+constexpr int kPrefillRows = 64;  // queries per work-group
+
+template <int D>
+struct PrefillShape {
+  static constexpr int NK = D / 32;                  // 32-dim slabs of the score product
+  static constexpr int NV = D / 16;                  // 16-dim slabs of the value product
+  static constexpr int RB = D * 2;                   // bytes per bf16 row
+  static constexpr int LPR = D / 8;                  // threads per row in a coalesced load
+  static constexpr int KP = kTileKeys * LPR / 256;   // K loads per thread per tile
+  static constexpr int VT = 8 * LPR;                 // threads loading V (4 keys each)
+  static constexpr int KBytes = kTileKeys * RB;
+  static constexpr int VBytes = D * kVtWords * 4;
+  static constexpr int StageBytes = KBytes + VBytes;
+  static_assert(KP >= 1 && VT <= 256, "tile loads");
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
+  using Sh = PrefillShape<D>;
+  constexpr int NK = Sh::NK, NV = Sh::NV, RB = Sh::RB, LPR = Sh::LPR, KP = Sh::KP;
+  __shared__ __align__(16) char s_stage[2][Sh::StageBytes];
+
+  const int T = a.T;
+  const int units = a.B * a.Hq;
+  const int ntq = ceil_div(T, kPrefillRows);
+  const int tq = ntq - 1 - (int)(blockIdx.x / units);  // longest query tiles first
+  const int uq = blockIdx.x % units;
+  const int b = uq / a.Hq, kvh = (uq % a.Hq) / a.G;
+  const int t0 = tq * kPrefillRows;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, tid = threadIdx.x;
+  const int n = lane & 15, grp = lane >> 4;
+  const int tw = t0 + 16 * wave;  // the wave's first query
+  const int tn = tw + n;          // this lane's query column
+  const char* qbase = static_cast<const char*>(a.q) + (size_t)uq * T * RB;
+  const char* kbase = static_cast<const char*>(a.k) + ((size_t)b * a.Hkv + kvh) * T * RB;
+  const char* vbase = static_cast<const char*>(a.v) + ((size_t)b * a.Hkv + kvh) * T * RB;
+
+  // Query operand: column n = query tn, dims 32 kk + 8 grp .. +7 (rows past
+  // the sequence read the last row and are never written).
+  bf16x8 qb[NK];
+  {
+    const char* qrow = qbase + (size_t)min(tn, T - 1) * RB + 16 * grp;
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) qb[kk] = __builtin_bit_cast(bf16x8, ld16(qrow + 64 * kk));
+  }
+  const float tau_n = a.tau[(size_t)uq * T + min(tn, T - 1)];
+  // Gate of Eq. 2: sigmoid(beta (S - tau)) = 1 / (1 + 2^(S gk1 + gk0)).
+  const float gk1 = -a.beta * kLog2e, gk0 = a.beta * kLog2e * tau_n;
+  const float scale = a.scale;
+
+  const int kend = min(T, t0 + kPrefillRows);  // keys this work-group needs
+  const int ntiles = ceil_div(kend, kTileKeys);
+
+  // Cooperative tile loads: K as (key, 16-byte chunk) pairs, V as 4 keys
+  // q8 + 8 j of one chunk per thread (so vt words pack 4 keys).  Keys past the
+  // sequence read its last row (finite data; causally masked).
+  uint4 kr[KP], vr[4];
+  auto fetch = [&](int j) {
+    const int s0 = j * kTileKeys;
+#pragma unroll
+    for (int p = 0; p < KP; ++p) {
+      const int e = tid + 256 * p;
+      const int s = min(s0 + e / LPR, T - 1);
+      kr[p] = ld16(kbase + (size_t)s * RB + 16 * (e % LPR));
+    }
+    if (tid < Sh::VT) {
+      const int q8 = tid / LPR, ch = tid % LPR;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int s = min(s0 + q8 + 8 * jj, T - 1);
+        vr[jj] = ld16(vbase + (size_t)s * RB + 16 * ch);
+      }
+    }
+  };
+  auto stage = [&](int buf) {
+    char* sk = s_stage[buf];
+    char* sv = sk + Sh::KBytes;
+#pragma unroll
+    for (int p = 0; p < KP; ++p) {
+      const int e = tid + 256 * p;
+      const int key = e / LPR;
+      *reinterpret_cast<uint4*>(sk + key * RB + 16 * ((e % LPR) ^ k_swz(key))) = kr[p];
+    }
+    if (tid < Sh::VT) {
+      const int q8 = tid / LPR, ch = tid % LPR;
+#pragma unroll
+      for (int w2 = 0; w2 < 4; ++w2) {
+        const int dim = 8 * ch + 2 * w2;
+        const uint32_t x0 = word(vr[0], w2), x1 = word(vr[1], w2);
+        const uint32_t x2 = word(vr[2], w2), x3 = word(vr[3], w2);
+        const uint2 lo = make_uint2((x0 & 0xffffu) | (x1 << 16), (x2 & 0xffffu) | (x3 << 16));
+        const uint2 hi = make_uint2((x0 >> 16) | (x1 & 0xffff0000u),
+                                    (x2 >> 16) | (x3 & 0xffff0000u));
+        *reinterpret_cast<uint2*>(sv + (dim * kVtWords + 2 * (q8 ^ v_swz(dim))) * 4) = lo;
+        *reinterpret_cast<uint2*>(sv + ((dim + 1) * kVtWords + 2 * (q8 ^ v_swz(dim + 1))) * 4) =
+            hi;
+      }
+    }
+  };
+
+  floatx4 O[NV];
+#pragma unroll
+  for (int nv = 0; nv < NV; ++nv) O[nv] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float m = -__builtin_inff(), lsum = 0.f, gsum = 0.f;
+
+  auto compute = [&](int j, int buf) {
+    const int s0 = j * kTileKeys;
+    const char* sk = s_stage[buf];
+    const char* sv = sk + Sh::KBytes;
+    floatx4 S[2];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const int key = tile_key(st, n);
+      const char* row = sk + key * RB;
+      const int sw = k_swz(key);
+      S[st] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) {
+        const bf16x8 kv =
+            __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(row + 16 * ((4 * kk + grp) ^ sw)));
+        S[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qb[kk], S[st], 0, 0, 0);
+      }
+    }
+    // Score i of half st is key s0 + 2 grp + st + 8 i against query tn.
+    float lg[8];
+    float tmax = -__builtin_inff();
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int s = s0 + 2 * grp + st + 8 * i;
+        const bool on = s <= tn && tn < T;
+        const float d = S[st][i] * scale;
+        const float g = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(fmaf(d, gk1, gk0)));
+        gsum += on ? g : 0.f;
+        const float lv = s == tn ? d : d * g;
+        lg[4 * st + i] = on ? lv : -__builtin_inff();
+        tmax = fmaxf(tmax, lg[4 * st + i]);
+      }
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+    // Lazy rescaling as in the grouped decode: the reference max of a query
+    // moves only when the tile raises it by more than kLazyRaise.
+    if (__ballot(tmax > m + kLazyRaise) != 0ull) {
+      const float mn = fmaxf(m, tmax);
+      const float alpha =
+          mn == -__builtin_inff() ? 1.f : __builtin_amdgcn_exp2f((m - mn) * kLog2e);
+      lsum *= alpha;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float al = __shfl(alpha, 4 * grp + i, kWave);
+#pragma unroll
+        for (int nv = 0; nv < NV; ++nv) O[nv][i] *= al;
+      }
+      m = mn;
+    }
+    const float ms2 = m == -__builtin_inff() ? 0.f : m * kLog2e;
+    bf16x8 phi, plo;
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(lg[i], kLog2e, -ms2));
+      psum += p;
+      const __bf16 h = (__bf16)p;
+      phi[i] = h;
+      plo[i] = (__bf16)(p - (float)h);
+    }
+    lsum += psum;
+#pragma unroll
+    for (int nv = 0; nv < NV; ++nv) {
+      const int dim = 16 * nv + n;
+      const char* vrow = sv + dim * kVtWords * 4;
+      const uint2 v0 = *reinterpret_cast<const uint2*>(vrow + 8 * ((2 * grp) ^ v_swz(dim)));
+      const uint2 v1 = *reinterpret_cast<const uint2*>(vrow + 8 * ((2 * grp + 1) ^ v_swz(dim)));
+      const bf16x8 vb = __builtin_bit_cast(bf16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
+      O[nv] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi, vb, O[nv], 0, 0, 0);
+      O[nv] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo, vb, O[nv], 0, 0, 0);
+    }
+  };
+
+  fetch(0);
+  stage(0);
+  __syncthreads();
+  for (int j = 0; j < ntiles; ++j) {
+    if (j + 1 < ntiles) fetch(j + 1);
+    // keys of tile j all after this wave's queries (or no query left): skip
+    if (j * kTileKeys <= tw + 15 && tw < T) compute(j, j & 1);
+    if (j + 1 < ntiles) stage((j + 1) & 1);
+    __syncthreads();
+  }
+
+  // Per-query sums over the 4 lane groups of a column.
+  lsum += __shfl_xor(lsum, 16, kWave);
+  lsum += __shfl_xor(lsum, 32, kWave);
+  gsum += __shfl_xor(gsum, 16, kWave);
+  gsum += __shfl_xor(gsum, 32, kWave);
+  // O rows are queries tw + 4 grp + i; their sums sit in lanes 4 grp + i.
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float li = __shfl(lsum, 4 * grp + i, kWave);
+    const int t = tw + 4 * grp + i;
+    if (t < T) {
+      float* orow = a.out + ((size_t)uq * T + t) * D;
+#pragma unroll
+      for (int nv = 0; nv < NV; ++nv) orow[16 * nv + n] = O[nv][i] / li;
+    }
+  }
+  if (a.dens && grp == 0 && tn < T) a.dens[(size_t)uq * T + tn] = gsum / (float)(tn + 1);
+}
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
+  const long long grid = (long long)ceil_div(a.T, kPrefillRows) * a.B * a.Hq;
+  if (a.D == 128)
+    hipLaunchKernelGGL(prefill_kernel<128>, dim3((unsigned)grid), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(prefill_kernel<64>, dim3((unsigned)grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace eta

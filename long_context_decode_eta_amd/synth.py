@@ -229,6 +229,61 @@ def make(name: str, *, seed: int = 1234, device="cpu", T=None, B=None, cap=None,
 
 
 # ---------------------------------------------------------------------------
+# Prefill / training-forward workload: the pages' 1.45B training shape (32
+# query heads on 4 KV heads, d 64, context 2048).  Keys are unit Gaussian plus
+# a per-64-position mean (Student-t(3) x 0.5); the queries of a group share a
+# component; per-position thresholds are drawn directly (tau ~ N(0.5, 0.25^2)
+# in logit units), since the gate takes them as given.  All bf16 except tau.
+PREFILL = dict(B=8, H=4, G=8, D=64, T=2048, q_corr=0.5, tau_mean=0.5, tau_std=0.25)
+
+
+@dataclass
+class PrefillWorkload:
+    B: int
+    H: int          # KV heads
+    G: int
+    D: int
+    T: int
+    q: torch.Tensor    # [B][H*G][T][D] bf16
+    k: torch.Tensor    # [B][H][T][D] bf16
+    v: torch.Tensor    # [B][H][T][D] bf16
+    tau: torch.Tensor  # [B][H*G][T] float32
+
+    @property
+    def Hq(self) -> int:
+        return self.H * self.G
+
+    @property
+    def scale(self) -> float:
+        return float(np.float32(1.0 / math.sqrt(self.D)))
+
+
+def make_prefill(*, seed: int = 1234, device="cpu", B=None, H=None, G=None, D=None,
+                 T=None) -> PrefillWorkload:
+    cfg = dict(PREFILL)
+    B = cfg["B"] if B is None else B
+    H = cfg["H"] if H is None else H
+    G = cfg["G"] if G is None else G
+    D = cfg["D"] if D is None else D
+    T = cfg["T"] if T is None else T
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    c = cfg["q_corr"]
+    shared = torch.randn((B, H, 1, T, D), generator=g, device=device)
+    own = torch.randn((B, H, G, T, D), generator=g, device=device)
+    q = (math.sqrt(c) * shared + math.sqrt(1.0 - c) * own).reshape(B, H * G, T, D)
+    nblk = -(-T // 64)
+    mu = 0.5 * _t3(g, (B, H, nblk, D), device)
+    k = torch.randn((B, H, T, D), generator=g, device=device)
+    k += mu.repeat_interleave(64, dim=2)[:, :, :T]
+    v = torch.randn((B, H, T, D), generator=g, device=device)
+    tau = cfg["tau_mean"] + cfg["tau_std"] * torch.randn((B, H * G, T), generator=g,
+                                                         device=device)
+    return PrefillWorkload(B=B, H=H, G=G, D=D, T=T, q=q.to(torch.bfloat16),
+                           k=k.to(torch.bfloat16), v=v.to(torch.bfloat16), tau=tau)
+
+
+# ---------------------------------------------------------------------------
 def kv_numpy(t: torch.Tensor) -> np.ndarray:
     """A cache tensor as the oracle reads it: float32 array, or the raw
     bfloat16 bit patterns as uint16."""

@@ -31,13 +31,13 @@ def declared():
 
 def test_exports_every_declared_symbol(lib):
     names = declared()
-    assert len(names) >= 19
+    assert len(names) >= 20
     for n in names:
         assert hasattr(lib, n), f"{n} declared in include/eta.h but not exported"
 
 
 def test_version_and_strings(lib):
-    assert lib.eta_abi_version() == 2
+    assert lib.eta_abi_version() == 3
     for s, name in [(0, b"ETA_OK"), (1, b"ETA_ERR_NULL_PTR"), (5, b"ETA_ERR_WORKSPACE"),
                     (6, b"ETA_ERR_HIP")]:
         assert lib.eta_status_string(s) == name
@@ -183,6 +183,23 @@ def test_gqa_validation(lib):
                                   None) == eb.ETA_ERR_WORKSPACE
     assert L.eta_dense_decode_gqa(cache(kv_dtype=eb.DT_F32), 8, FAKE, 0.088, 16, FAKE, ws, FAKE,
                                   None) == eb.ETA_ERR_BAD_ARG
+
+
+def test_prefill_validation(lib):
+    L = lib
+    call = lambda **o: L.eta_gated_prefill(o.get("B", 2), o.get("Hkv", 4), o.get("G", 8),
+                                           o.get("T", 100), o.get("d", 64), o.get("q", FAKE),
+                                           FAKE, FAKE, o.get("tau", FAKE), o.get("beta", 5.0),
+                                           o.get("scale", 0.125), o.get("out", FAKE), None, None)
+    assert call(d=96) == eb.ETA_ERR_BAD_SHAPE
+    assert call(G=0) == eb.ETA_ERR_BAD_SHAPE
+    assert call(T=-1) == eb.ETA_ERR_BAD_SHAPE
+    assert call(beta=0.0) == eb.ETA_ERR_BAD_ARG
+    assert call(scale=float("nan")) == eb.ETA_ERR_BAD_ARG
+    assert call(q=None) == eb.ETA_ERR_NULL_PTR
+    assert call(tau=None) == eb.ETA_ERR_NULL_PTR
+    assert call(out=None) == eb.ETA_ERR_NULL_PTR
+    assert call(T=0, q=None, out=None) == eb.ETA_OK  # empty: nothing launched
 
 
 def test_binding_refuses_cpu_tensors(lib):

@@ -14,7 +14,8 @@ Printed: one JSON line with dense-equivalent KV tokens/s (sum_b T_b per step
 fp64 oracle timed on the host on a bounded sample of the same workload.  A
 grouped-query section follows (32 sequences x 128K, 32 query heads on 4 KV
 heads, d 64, b 64: eta_screen_gqa + eta_decode_gqa against the grouped dense
-decode at 38/25/10% head density).
+decode at 38/25/10% head density) and a gated prefill section (8 x 2048, the
+pages' training shape: eta_gated_prefill against the bf16 matrix-core peak).
 """
 from __future__ import annotations
 
@@ -54,6 +55,10 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-gqa", action="store_true",
                     help="skip the grouped-query section (32 x 128K, 32 query / 4 KV heads)")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the gated prefill section (8 x 2048, 32 query / 4 KV heads)")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="run only the gated prefill section and print its JSON")
     ap.add_argument("--gqa-only", action="store_true",
                     help="run only the grouped-query section and print its JSON")
     ap.add_argument("--gqa-rho", default="0.38,0.25,0.10",
@@ -135,6 +140,10 @@ def main():
     dev = "cuda"
     torch.cuda.set_device(0)
     gqa_rhos = [float(x) for x in args.gqa_rho.split(",")]
+    if args.prefill_only:
+        print(json.dumps(prefill_bench(torch, eb, synth, args.steps, args.warmup, args.seed)),
+              flush=True)
+        return
     if args.gqa_only:
         print(json.dumps(gqa_bench(torch, np, eb, synth, args.steps, args.warmup, args.seed,
                                    gqa_rhos)), flush=True)
@@ -328,6 +337,9 @@ def main():
     gqa = None
     if not args.no_gqa:
         gqa = gqa_bench(torch, np, eb, synth, args.steps, args.warmup, args.seed, gqa_rhos)
+    prefill = None
+    if not args.no_prefill:
+        prefill = prefill_bench(torch, eb, synth, args.steps, args.warmup, args.seed)
 
     out = {
         "metric": "dense-equiv KV tokens/s + achieved HBM GB/s (active bytes) at 128K ctx",
@@ -376,6 +388,7 @@ def main():
         "upkeep": upkeep,
         "cpu_baseline": cpu,
         "gqa": gqa,
+        "prefill": prefill,
     }
     print(json.dumps(out), flush=True)
 
@@ -619,6 +632,59 @@ def gqa_bench(torch, np, eb, synth, steps, warmup, seed, rhos=(0.38, 0.25, 0.10)
     del dec, cache, w
     torch.cuda.empty_cache()
     return out
+
+
+MFMA_BF16_PEAK_TFS = 2500.0
+
+
+def prefill_bench(torch, eb, synth, steps, warmup, seed):
+    """Gated causal attention forward at the pages' training shape (8 x 2048,
+    32 query heads on 4 KV heads, d 64, bf16): one eta_gated_prefill call per
+    step, graph-captured and checked against eager.  Algorithmic flops: 4 d
+    per (query, causal key) pair (the score and value products)."""
+    w = synth.make_prefill(seed=seed, device="cuda")
+    out = torch.zeros((w.B, w.Hq, w.T, w.D), device="cuda")
+    dens = torch.zeros((w.B, w.Hq, w.T), device="cuda")
+
+    def step():
+        eb.gated_prefill(w.q, w.k, w.v, w.tau, w.G, 5.0, w.scale, out, dens)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = Timer(torch)
+    for _ in range(steps):
+        ev.around(step)
+    torch.cuda.synchronize()
+    ref = out.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(3):
+        out.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), "graph replay differs from eager prefill"
+    a = time.perf_counter()
+    for _ in range(steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - a) * 1e3 / steps
+    del graph
+    pairs = w.B * w.Hq * w.T * (w.T + 1) // 2
+    flops = 4 * w.D * pairs
+    tfs = flops / (ev.mean_ms() * 1e-3) / 1e12
+    res = {"workload": f"prefill: batch {w.B}, {w.Hq} query heads on {w.H} KV heads, head dim "
+                       f"{w.D}, context {w.T}, bf16 q/k/v, beta 5",
+           "ms": round(ms, 5), "kernel_ms": round(ev.mean_ms(), 5),
+           "tokens_per_s": round(w.B * w.T / (ms * 1e-3), 1),
+           "mean_density": round(float(dens.mean()), 4),
+           "roofline": {"bound": "mfma", "achieved": round(tfs, 1),
+                        "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+                        "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4), "traffic": None,
+                        "algorithmic_flops_per_launch": int(flops)}}
+    print(f"[bench] prefill: {json.dumps(res)}", file=sys.stderr, flush=True)
+    return res
 
 
 def cpu_baseline(w, c_gpu, rho):

@@ -24,6 +24,11 @@ namespace eta {
 
 constexpr int kPrefillRows = 64;  // queries per work-group
 
+template <bool B>
+struct MaskTag {
+  static constexpr bool value = B;
+};
+
 template <int D>
 struct PrefillShape {
   static constexpr int NK = D / 32;                  // 32-dim slabs of the score product
@@ -127,7 +132,10 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   for (int nv = 0; nv < NV; ++nv) O[nv] = floatx4{0.f, 0.f, 0.f, 0.f};
   float m = -__builtin_inff(), lsum = 0.f, gsum = 0.f;
 
-  auto compute = [&](int j, int buf) {
+  // MASK: the tile holds the diagonal or keys past some query (or the wave has
+  // queries past the sequence); otherwise every key precedes every query.
+  auto compute = [&](int j, int buf, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const int s0 = j * kTileKeys;
     const char* sk = s_stage[buf];
     const char* sv = sk + Sh::KBytes;
@@ -152,13 +160,18 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     for (int st = 0; st < 2; ++st) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int s = s0 + 2 * grp + st + 8 * i;
-        const bool on = s <= tn && tn < T;
         const float d = S[st][i] * scale;
         const float g = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(fmaf(d, gk1, gk0)));
-        gsum += on ? g : 0.f;
-        const float lv = s == tn ? d : d * g;
-        lg[4 * st + i] = on ? lv : -__builtin_inff();
+        if constexpr (MASK) {
+          const int s = s0 + 2 * grp + st + 8 * i;
+          const bool on = s <= tn && tn < T;
+          gsum += on ? g : 0.f;
+          const float lv = s == tn ? d : d * g;
+          lg[4 * st + i] = on ? lv : -__builtin_inff();
+        } else {
+          gsum += g;
+          lg[4 * st + i] = d * g;
+        }
         tmax = fmaxf(tmax, lg[4 * st + i]);
       }
     }
@@ -209,7 +222,12 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   for (int j = 0; j < ntiles; ++j) {
     if (j + 1 < ntiles) fetch(j + 1);
     // keys of tile j all after this wave's queries (or no query left): skip
-    if (j * kTileKeys <= tw + 15 && tw < T) compute(j, j & 1);
+    if (j * kTileKeys <= tw + 15 && tw < T) {
+      if (j * kTileKeys + kTileKeys - 1 < tw && tw + 15 < T)
+        compute(j, j & 1, MaskTag<false>{});
+      else
+        compute(j, j & 1, MaskTag<true>{});
+    }
     if (j + 1 < ntiles) stage((j + 1) & 1);
     __syncthreads();
   }

@@ -369,7 +369,11 @@ __global__ __launch_bounds__(kCombWaves * kWave) void combine_kernel(CacheView c
   const int u = blockIdx.x;
   int T, cnt;
   const int nch = stream_chunks(c, a, u, &T, &cnt);
-  if (nch <= 1) return;  // no chunk (zeros from the prepare kernel) or a single chunk
+  if (nch == 0) {  // empty stream: zeros
+    for (int i = threadIdx.x; i < D; i += blockDim.x) a.out[(size_t)u * D + i] = 0.f;
+    return;
+  }
+  if (nch == 1) return;  // written by the decode kernel
   combine_stream<D>(a, u, nch, s_acc, s_ml);
 }
 
@@ -379,9 +383,10 @@ static hipError_t decode_t(const CacheView& c, const DecodeArgs& a, hipStream_t 
   const int units = c.B * c.H;
   const size_t list_bytes = DENSE ? 0 : (size_t)a.split * 4;
   hipError_t e;
-  hipLaunchKernelGGL((decode_prepare_kernel<D>), dim3(1), dim3(1024), 0, s, c, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
   if (a.use_queue) {
+    // chunk table and queue counter for the persistent grid
+    hipLaunchKernelGGL((decode_prepare_kernel<D>), dim3(1), dim3(1024), 0, s, c, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     const size_t lds = (size_t)(units + 1) * 4 + list_bytes;
     hipLaunchKernelGGL((decode_queue_kernel<D, DT, MODE, DENSE>), dim3(a.queue_grid), dim3(256),
                        lds, s, c, a);

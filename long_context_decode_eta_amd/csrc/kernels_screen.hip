@@ -158,7 +158,7 @@ __global__ __launch_bounds__(256) void screen_kernel(CacheView c, const float* q
 }
 
 // Compaction: one work-group per stream turns the admission words into the
-// ascending index list.  Thread t owns a contiguous run of words, so an
+// ascending index list.  Each thread owns a contiguous run of blocks, so an
 // exclusive scan of per-thread popcounts gives every thread its output offset
 // and the list comes out ascending with no sorting.
 __global__ __launch_bounds__(256) void compact_kernel(CacheView c, const uint64_t* words,
@@ -168,38 +168,41 @@ __global__ __launch_bounds__(256) void compact_kernel(CacheView c, const uint64_
   const int u = blockIdx.x, t = threadIdx.x;
   const int T = c.seq_len[u / c.H];
   const int nb = (T + c.bs - 1) >> c.log2bs;
-  const int nw = (nb + 63) >> 6;
-  const int per = (nw + 255) >> 8;
-  const int w0 = min(t * per, nw), w1 = min(w0 + per, nw);
   const uint64_t* wu = words + (size_t)u * words_per_unit;
-  auto word_at = [&](int w) {
-    uint64_t x = wu[w];
-    const int rem = nb - (w << 6);
-    if (rem < 64) x &= (1ull << rem) - 1ull;
-    return x;
-  };
-  int mine = 0;
-  for (int w = w0; w < w1; ++w) mine += __popcll(word_at(w));
-  scan[t] = mine;
-  __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {  // Hillis-Steele inclusive scan
-    const int add = t >= off ? scan[t - off] : 0;
-    __syncthreads();
-    scan[t] += add;
-    __syncthreads();
-  }
-  int pos = scan[t] - mine;
-  const int total = scan[255];
   int32_t* out = active_idx + (size_t)u * c.cap_blocks;
-  for (int w = w0; w < w1; ++w) {
-    uint64_t x = word_at(w);
+  // Thread t takes a run of bpt consecutive blocks (bpt a power of two <= 64,
+  // so a run lies in one word); rounds of 256 runs in ascending order.
+  int bpt = 1;
+  while (bpt < 64 && bpt * 256 < nb) bpt <<= 1;
+  int base_pos = 0;
+  for (int r0 = 0; r0 < nb; r0 += 256 * bpt) {
+    const int b0 = r0 + t * bpt;
+    uint64_t x = 0;
+    if (b0 < nb) {
+      x = wu[b0 >> 6] >> (b0 & 63);
+      if (bpt < 64) x &= (1ull << bpt) - 1ull;
+      const int rem = nb - b0;
+      if (rem < 64) x &= (1ull << rem) - 1ull;
+    }
+    const int mine = __popcll(x);
+    scan[t] = mine;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {  // Hillis-Steele inclusive scan
+      const int add = t >= off ? scan[t - off] : 0;
+      __syncthreads();
+      scan[t] += add;
+      __syncthreads();
+    }
+    int pos = base_pos + scan[t] - mine;
+    base_pos += scan[255];
+    __syncthreads();  // scan[] is rewritten next round
     while (x) {
-      const int bit = __ffsll((unsigned long long)x) - 1;
-      out[pos++] = (w << 6) + bit;
+      out[pos++] = b0 + __ffsll((unsigned long long)x) - 1;
       x &= x - 1ull;
     }
   }
   if (t == 0) {
+    const int total = base_pos;
     active_cnt[u] = total;
     if (ctr && total > 0) {
       const unsigned long long tokens =

@@ -12,9 +12,9 @@
 // wave w owns queries t0 + 16 w .. + 15.  The keys 0 .. t0 + 63 are walked in
 // 32-key tiles.  A tile is loaded once for the 4 waves (coalesced 128-bit
 // reads by all 256 threads, the next tile's loads in flight while the
-// current one is computed) and staged in LDS in the layout of the
-// grouped-query decode (K rows chunk-swizzled, V transposed), double
-// buffered, one barrier per tile.  Each wave then computes, on the matrix
+// current one is computed) and staged in LDS as rows (chunk-swizzled),
+// double buffered, one barrier per tile; the value product reads V with the
+// transposing LDS read.  Each wave then computes, on the matrix
 // cores, S^T = K_tile Q_w^T (queries as the 16 columns; q is bf16 as given)
 // and O += P V with the weights split hi + lo, applying the causal mask, the
 // gate and an online softmax per query column in between.
@@ -23,6 +23,20 @@
 namespace eta {
 
 constexpr int kPrefillRows = 64;  // queries per work-group
+
+// Chunk swizzle of staged V rows: the four rows one transposing read takes
+// (keys 2 g + h + 8 j, j = 0..3) land their 32 bytes in distinct banks.
+__device__ __forceinline__ int vrow_swz(int key) { return 2 * ((key >> 3) & 3); }
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane l receives element
+// l % 4 of the 8-byte pieces addressed by lanes 4 j + (l % 16) / 4, j = 0..3
+// (measured lane layout on gfx950).  Returned as raw 64 bits.
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 tr_read(const char* p) {
+  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+  const bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
+  return __builtin_bit_cast(uint2, v);
+}
 
 template <bool B>
 struct MaskTag {
@@ -35,12 +49,11 @@ struct PrefillShape {
   static constexpr int NV = D / 16;                  // 16-dim slabs of the value product
   static constexpr int RB = D * 2;                   // bytes per bf16 row
   static constexpr int LPR = D / 8;                  // threads per row in a coalesced load
-  static constexpr int KP = kTileKeys * LPR / 256;   // K loads per thread per tile
-  static constexpr int VT = 8 * LPR;                 // threads loading V (4 keys each)
+  static constexpr int KP = kTileKeys * LPR / 256;   // K (and V) loads per thread per tile
   static constexpr int KBytes = kTileKeys * RB;
-  static constexpr int VBytes = D * kVtWords * 4;
+  static constexpr int VBytes = kTileKeys * RB;
   static constexpr int StageBytes = KBytes + VBytes;
-  static_assert(KP >= 1 && VT <= 256, "tile loads");
+  static_assert(KP >= 1, "tile loads");
 };
 
 template <int D>
@@ -73,32 +86,30 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     for (int kk = 0; kk < NK; ++kk) qb[kk] = __builtin_bit_cast(bf16x8, ld16(qrow + 64 * kk));
   }
   const float tau_n = a.tau[(size_t)uq * T + min(tn, T - 1)];
-  // Gate of Eq. 2: sigmoid(beta (S - tau)) = 1 / (1 + 2^(S gk1 + gk0)).
-  const float gk1 = -a.beta * kLog2e, gk0 = a.beta * kLog2e * tau_n;
-  const float scale = a.scale;
+  // Gate of Eq. 2: sigmoid(beta (scale r - tau)) = 1 / (1 + 2^(r gk1 + gk0)).
+  // Scores stay unscaled (raw dot products r) through the softmax: the logit is
+  // scale * r * gate, so scale is folded into the exponent constants and the
+  // lazy-rescale step (scale > 0 keeps every max and comparison).
+  const float gk1 = -a.beta * kLog2e * a.scale, gk0 = a.beta * kLog2e * tau_n;
+  const float sl2 = a.scale * kLog2e;
+  const float lazy_raw = kLazyRaise / a.scale;
 
   const int kend = min(T, t0 + kPrefillRows);  // keys this work-group needs
   const int ntiles = ceil_div(kend, kTileKeys);
 
-  // Cooperative tile loads: K as (key, 16-byte chunk) pairs, V as 4 keys
-  // q8 + 8 j of one chunk per thread (so vt words pack 4 keys).  Keys past the
-  // sequence read its last row (finite data; causally masked).
-  uint4 kr[KP], vr[4];
+  // Cooperative tile loads: K and V as (key, 16-byte chunk) pairs, D/8
+  // threads per row.  Keys past the sequence read its last row (finite data;
+  // causally masked).  Both are staged as rows; V's value-product operand is
+  // taken with the transposing LDS read, so no thread repacks V.
+  uint4 kr[KP], vr[KP];
   auto fetch = [&](int j) {
     const int s0 = j * kTileKeys;
 #pragma unroll
     for (int p = 0; p < KP; ++p) {
       const int e = tid + 256 * p;
-      const int s = min(s0 + e / LPR, T - 1);
-      kr[p] = ld16(kbase + (size_t)s * RB + 16 * (e % LPR));
-    }
-    if (tid < Sh::VT) {
-      const int q8 = tid / LPR, ch = tid % LPR;
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int s = min(s0 + q8 + 8 * jj, T - 1);
-        vr[jj] = ld16(vbase + (size_t)s * RB + 16 * ch);
-      }
+      const size_t off = (size_t)min(s0 + e / LPR, T - 1) * RB + 16 * (e % LPR);
+      kr[p] = ld16(kbase + off);
+      vr[p] = ld16(vbase + off);
     }
   };
   auto stage = [&](int buf) {
@@ -109,21 +120,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
       const int e = tid + 256 * p;
       const int key = e / LPR;
       *reinterpret_cast<uint4*>(sk + key * RB + 16 * ((e % LPR) ^ k_swz(key))) = kr[p];
-    }
-    if (tid < Sh::VT) {
-      const int q8 = tid / LPR, ch = tid % LPR;
-#pragma unroll
-      for (int w2 = 0; w2 < 4; ++w2) {
-        const int dim = 8 * ch + 2 * w2;
-        const uint32_t x0 = word(vr[0], w2), x1 = word(vr[1], w2);
-        const uint32_t x2 = word(vr[2], w2), x3 = word(vr[3], w2);
-        const uint2 lo = make_uint2((x0 & 0xffffu) | (x1 << 16), (x2 & 0xffffu) | (x3 << 16));
-        const uint2 hi = make_uint2((x0 >> 16) | (x1 & 0xffff0000u),
-                                    (x2 >> 16) | (x3 & 0xffff0000u));
-        *reinterpret_cast<uint2*>(sv + (dim * kVtWords + 2 * (q8 ^ v_swz(dim))) * 4) = lo;
-        *reinterpret_cast<uint2*>(sv + ((dim + 1) * kVtWords + 2 * (q8 ^ v_swz(dim + 1))) * 4) =
-            hi;
-      }
+      *reinterpret_cast<uint4*>(sv + key * RB + 16 * ((e % LPR) ^ vrow_swz(key))) = vr[p];
     }
   };
 
@@ -160,7 +157,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     for (int st = 0; st < 2; ++st) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float d = S[st][i] * scale;
+        const float d = S[st][i];
         const float g = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(fmaf(d, gk1, gk0)));
         if constexpr (MASK) {
           const int s = s0 + 2 * grp + st + 8 * i;
@@ -179,10 +176,10 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
     // Lazy rescaling as in the grouped decode: the reference max of a query
     // moves only when the tile raises it by more than kLazyRaise.
-    if (__ballot(tmax > m + kLazyRaise) != 0ull) {
+    if (__ballot(tmax > m + lazy_raw) != 0ull) {
       const float mn = fmaxf(m, tmax);
       const float alpha =
-          mn == -__builtin_inff() ? 1.f : __builtin_amdgcn_exp2f((m - mn) * kLog2e);
+          mn == -__builtin_inff() ? 1.f : __builtin_amdgcn_exp2f((m - mn) * sl2);
       lsum *= alpha;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -192,24 +189,30 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
       }
       m = mn;
     }
-    const float ms2 = m == -__builtin_inff() ? 0.f : m * kLog2e;
+    const float ms2 = m == -__builtin_inff() ? 0.f : m * sl2;
     bf16x8 phi, plo;
     float psum = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float p = __builtin_amdgcn_exp2f(fmaf(lg[i], kLog2e, -ms2));
+      const float p = __builtin_amdgcn_exp2f(fmaf(lg[i], sl2, -ms2));
       psum += p;
       const __bf16 h = (__bf16)p;
       phi[i] = h;
       plo[i] = (__bf16)(p - (float)h);
     }
     lsum += psum;
+    // Value operand (dim 16 nv + n, slots 8 grp + 4 h + j) by two transposing
+    // reads: lane L of group g supplies row tile_key(h, 4 g + (L%16)/4), dims
+    // 16 nv + 4 ((L%16) % 4) .. +3, and lane l receives element l % 4 of the
+    // rows supplied by lanes 16 g + 4 j + (l%16)/4, j = 0..3.
+    const int trow0 = tile_key(0, 4 * grp + ((lane & 15) >> 2));
+    const int trow1 = tile_key(1, 4 * grp + ((lane & 15) >> 2));
+    const int tr4 = lane & 3;
 #pragma unroll
     for (int nv = 0; nv < NV; ++nv) {
-      const int dim = 16 * nv + n;
-      const char* vrow = sv + dim * kVtWords * 4;
-      const uint2 v0 = *reinterpret_cast<const uint2*>(vrow + 8 * ((2 * grp) ^ v_swz(dim)));
-      const uint2 v1 = *reinterpret_cast<const uint2*>(vrow + 8 * ((2 * grp + 1) ^ v_swz(dim)));
+      const int c = 2 * nv + (tr4 >> 1);
+      const uint2 v0 = tr_read(sv + trow0 * RB + 16 * (c ^ vrow_swz(trow0)) + 8 * (tr4 & 1));
+      const uint2 v1 = tr_read(sv + trow1 * RB + 16 * (c ^ vrow_swz(trow1)) + 8 * (tr4 & 1));
       const bf16x8 vb = __builtin_bit_cast(bf16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
       O[nv] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi, vb, O[nv], 0, 0, 0);
       O[nv] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo, vb, O[nv], 0, 0, 0);

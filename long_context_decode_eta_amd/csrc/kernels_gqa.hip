@@ -44,45 +44,67 @@ __global__ __launch_bounds__(256) void screen_gqa_kernel(CacheView c, int G, con
   const int nb = (T + c.bs - 1) >> c.log2bs;
   const int nbc = T >> c.log2bs;
   if ((wd << 6) >= nb) return;  // uniform over the work-group
+  const int gi = lane / LPB, li = lane % LPB;
+  // The word's statistics are requested first, so their latency overlaps the
+  // staging of the queries below.
+  float4 m4[2][NL], v4[2][NL];
+  float Ms[2];
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int j = (wd << 6) + wave * 16 + it * 8 + gi;
+    const bool scored = j < nbc;
+    const size_t row = ((size_t)u * c.cap_blocks + j) * D;
+#pragma unroll
+    for (int t = 0; t < NL; ++t) {
+      m4[it][t] = scored ? ld16f_nt(c.mu + row + 32 * t + 4 * li) : make_float4(0, 0, 0, 0);
+      v4[it][t] = scored ? ld16f_nt(c.var + row + 32 * t + 4 * li) : make_float4(0, 0, 0, 0);
+    }
+    Ms[it] = scored ? c.maxnorm[(size_t)u * c.cap_blocks + j] : 0.f;
+  }
   for (int i = threadIdx.x; i < G * D; i += blockDim.x) s_q[i / D][i % D] = q[(size_t)u * G * D + i];
   if (threadIdx.x < G) s_ts[threadIdx.x] = tau_screen[(size_t)u * G + threadIdx.x];
   __syncthreads();
-  if (threadIdx.x < G) {
+  // ||q|| per head, 8 lanes per head summing in the same order as the
+  // one-head-per-KV-head screen (so G = 1 reproduces it bit for bit).
+  {
+    const int hg = wave * 8 + gi;
     float qq = 0.f;
-    for (int i = 0; i < D; ++i) qq = fmaf(s_q[threadIdx.x][i], s_q[threadIdx.x][i], qq);
-    s_qn[threadIdx.x] = sqrtf(qq);
+    if (hg < G) {
+#pragma unroll
+      for (int t = 0; t < NL; ++t) {
+        const float4 v = *reinterpret_cast<const float4*>(&s_q[hg][32 * t + 4 * li]);
+        qq = fmaf(v.x, v.x, qq);
+        qq = fmaf(v.y, v.y, qq);
+        qq = fmaf(v.z, v.z, qq);
+        qq = fmaf(v.w, v.w, qq);
+      }
+    }
+    qq = group_sum<LPB>(qq);
+    if (hg < G && li == 0) s_qn[hg] = sqrtf(qq);
   }
   __syncthreads();
   const bool z_inf = __builtin_isinf(z);
-  const int gi = lane / LPB, li = lane % LPB;
   const uint32_t all = (G >= 32) ? 0xffffffffu : ((1u << G) - 1u);
   uint32_t bits = 0;
 #pragma unroll
   for (int it = 0; it < 2; ++it) {
     const int j = (wd << 6) + wave * 16 + it * 8 + gi;
     const bool scored = j < nbc;
-    const size_t row = ((size_t)u * c.cap_blocks + j) * D;
-    float4 m4[NL], v4[NL];
-#pragma unroll
-    for (int t = 0; t < NL; ++t) {
-      m4[t] = scored ? ld16f_nt(c.mu + row + 32 * t + 4 * li) : make_float4(0, 0, 0, 0);
-      v4[t] = scored ? ld16f_nt(c.var + row + 32 * t + 4 * li) : make_float4(0, 0, 0, 0);
-    }
-    const float M = scored ? c.maxnorm[(size_t)u * c.cap_blocks + j] : 0.f;
+    const float M = Ms[it];
     uint32_t mask = 0;
     for (int g = 0; g < G; ++g) {
       float dot = 0.f, mom = 0.f;
 #pragma unroll
       for (int t = 0; t < NL; ++t) {
         const float4 qv = *reinterpret_cast<const float4*>(&s_q[g][32 * t + 4 * li]);
-        dot = fmaf(qv.x, m4[t].x, dot);
-        dot = fmaf(qv.y, m4[t].y, dot);
-        dot = fmaf(qv.z, m4[t].z, dot);
-        dot = fmaf(qv.w, m4[t].w, dot);
-        mom = fmaf(qv.x * qv.x, v4[t].x, mom);
-        mom = fmaf(qv.y * qv.y, v4[t].y, mom);
-        mom = fmaf(qv.z * qv.z, v4[t].z, mom);
-        mom = fmaf(qv.w * qv.w, v4[t].w, mom);
+        dot = fmaf(qv.x, m4[it][t].x, dot);
+        dot = fmaf(qv.y, m4[it][t].y, dot);
+        dot = fmaf(qv.z, m4[it][t].z, dot);
+        dot = fmaf(qv.w, m4[it][t].w, dot);
+        mom = fmaf(qv.x * qv.x, v4[it][t].x, mom);
+        mom = fmaf(qv.y * qv.y, v4[it][t].y, mom);
+        mom = fmaf(qv.z * qv.z, v4[it][t].z, mom);
+        mom = fmaf(qv.w * qv.w, v4[it][t].w, mom);
       }
       dot = group_sum<LPB>(dot);
       mom = group_sum<LPB>(mom);

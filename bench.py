@@ -322,7 +322,7 @@ def main():
     value = sumT / (r["ms"] * 1e-3)
     achieved = r["decode_bytes"] / (r["decode_ms"] * 1e-3) / 1e9
     traffic = counters_traffic(COUNTERS, DECODE_SRC, args.workload)
-    roofline = {"bound": "hbm", "kernel": "eta_decode (prepare + decode + combine kernels)",
+    roofline = {"bound": "hbm", "kernel": "eta_decode (decode + combine kernels)",
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "algorithmic_bytes_per_launch": int(r["decode_bytes"]),

@@ -228,3 +228,14 @@ def test_gqa_full_size_sampled_streams():
          f"flips {flips}/{screened}")
     assert 0.3 < d_head < 0.46 and d_head < d_union < 0.8
     assert not np.isnan(g.out).any()
+
+
+def test_gqa_compaction_over_several_rounds():
+    # 70000 keys in blocks of 4 (17500 blocks): several compaction rounds.
+    w = to_gpu(synth.make("gqa_tiny", seed=24, T=[70000], B=1, H=1, cap=70001, block=4))
+    cache = make_cache(w)
+    c = torch.linspace(0.8, 1.4, w.Hq, device="cuda")
+    g = run_gpu_gqa(cache, w.G, w.q, bias_or_c=c, z=w.z, scale=w.scale, split=128)
+    assert cache.cap_blocks > 256 * 64
+    st = check_gqa(w, g, W=None, bias_or_c=c, z=w.z, scale=w.scale, mode=eb.GATED)
+    note(f"  D_head {st['d_head']:.3f} D_union {st['d_union']:.3f} out_rel {st['out_rel']:.2e}")

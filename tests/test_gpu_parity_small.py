@@ -201,3 +201,16 @@ def test_threshold_offset(a):
     note(f"  a={a}: density {st['density']:.3f} out_rel {st['out_rel']:.2e}")
     if a == math.inf:
         assert st["density"] == 1.0
+
+
+def test_compaction_over_several_rounds():
+    # 70000 keys in blocks of 4: 17500 blocks, more than one round of 256
+    # runs of 64 blocks in the compaction.
+    w = to_gpu(synth.make("ctx128k", seed=23, T=70000, B=1, H=2, cap=70001, block=4))
+    cache = make_cache(w)
+    c = torch.tensor([0.7, 1.1], device="cuda")
+    g = run_gpu(cache, w.q, W=w.W, bias_or_c=c, z=1.0, scale=w.scale, split=64)
+    assert cache.cap_blocks > 256 * 64
+    st = check_against_oracle(w, g, cache, W=w.W, bias_or_c=c, z=1.0, scale=w.scale,
+                              mode=eb.GATED)
+    note(f"  density {st['density']:.3f} out_rel {st['out_rel']:.2e}")

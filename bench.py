@@ -649,6 +649,9 @@ def prefill_bench(torch, eb, synth, steps, warmup, seed):
     def step():
         eb.gated_prefill(w.q, w.k, w.v, w.tau, w.G, 5.0, w.scale, out, dens)
 
+    # Clocks settle only after some tens of milliseconds of matrix-core work:
+    # at least 100 warm-up launches (about 40 ms) before each timed loop.
+    warmup = max(warmup, 100)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -665,6 +668,9 @@ def prefill_bench(torch, eb, synth, steps, warmup, seed):
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, ref), "graph replay differs from eager prefill"
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
     a = time.perf_counter()
     for _ in range(steps):
         graph.replay()

@@ -79,6 +79,42 @@ constexpr int kQuadXor2 = 0x4E;    // quad_perm [2,3,0,1]
 constexpr int kRowMirror = 0x140;  // lane i <-> 15-i within a row of 16
 constexpr int kHalfMirror = 0x141; // lane i <-> 7-i within each half row
 
+// Split two non-negative floats into bf16 hi + lo pairs (hi rounded to
+// nearest, lo the rounded remainder): hi + lo carries 16 significant bits,
+// so a product with bf16 operands summed in float32 keeps float32-level
+// accuracy.  One packed conversion per pair; the hi halves widen back by a
+// shift and a mask.  Element 0 sits in the low 16 bits of each result.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float float2x __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void split_hi_lo(float a, float b, uint32_t& hi, uint32_t& lo) {
+  hi = __builtin_bit_cast(uint32_t, __builtin_convertvector((float2x){a, b}, bf16x2));
+  const float2x rest = {a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xFFFF0000u)};
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(rest, bf16x2));
+}
+
+// Pairs of 16-lane rows on the VALU (gfx950 permlane swaps).  Called with
+// the lane's own value as both operands, v_permlane16_swap returns in every
+// lane the values of the even and of the odd row of the pair (r, r ^ 1), and
+// v_permlane32_swap those of the halves (h, h ^ 1) -- measured lane layout.
+// One add or max of the two results then reduces over lanes l and l ^ 16
+// (l ^ 32), in the same operand order in both lanes, with no LDS round trip.
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 template <int N>
 __device__ __forceinline__ float group_sum(float x) {
   static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16 || N == 32 || N == 64, "group");
@@ -89,8 +125,8 @@ __device__ __forceinline__ float group_sum(float x) {
     x += dpp<kRowMirror>(x);
     x += dpp<kHalfMirror>(x);
   }
-  if constexpr (N >= 32) x += __shfl_xor(x, 16, kWave);
-  if constexpr (N >= 64) x += __shfl_xor(x, 32, kWave);
+  if constexpr (N >= 32) x = sum_xor16(x);
+  if constexpr (N >= 64) x = sum_xor32(x);
   return x;
 }
 
@@ -103,8 +139,8 @@ __device__ __forceinline__ float group_max(float x) {
     x = fmaxf(x, dpp<kRowMirror>(x));
     x = fmaxf(x, dpp<kHalfMirror>(x));
   }
-  if constexpr (N >= 32) x = fmaxf(x, __shfl_xor(x, 16, kWave));
-  if constexpr (N >= 64) x = fmaxf(x, __shfl_xor(x, 32, kWave));
+  if constexpr (N >= 32) x = max_xor16(x);
+  if constexpr (N >= 64) x = max_xor32(x);
   return x;
 }
 

@@ -456,17 +456,18 @@ __global__ __launch_bounds__(GqaShape<D>::W * 64, GqaShape<D>::MinBlocks) void d
       m = mn;
     }
     const float ms2 = m == -__builtin_inff() ? 0.f : m * kLog2e;
-    bf16x8 phi, plo;
-    float psum = 0.f;
+    float pw[8], psum = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float p = __builtin_amdgcn_exp2f(fmaf(lg[i], kLog2e, -ms2));
-      psum += p;
-      const __bf16 h = (__bf16)p;
-      phi[i] = h;
-      plo[i] = (__bf16)(p - (float)h);
+      pw[i] = __builtin_amdgcn_exp2f(fmaf(lg[i], kLog2e, -ms2));
+      psum += pw[i];
     }
     lsum += psum;
+    uint32_t ph[4], pl[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) split_hi_lo(pw[2 * i], pw[2 * i + 1], ph[i], pl[i]);
+    const bf16x8 phi = __builtin_bit_cast(bf16x8, make_uint4(ph[0], ph[1], ph[2], ph[3]));
+    const bf16x8 plo = __builtin_bit_cast(bf16x8, make_uint4(pl[0], pl[1], pl[2], pl[3]));
     // Values: B operand = dim 16 nv + n, contraction slots 8 grp .. 8 grp + 7.
 #pragma unroll
     for (int nv = 0; nv < NV; ++nv) {

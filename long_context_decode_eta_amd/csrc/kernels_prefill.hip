@@ -42,6 +42,10 @@ template <bool B>
 struct MaskTag {
   static constexpr bool value = B;
 };
+template <int I>
+struct BufTag {
+  static constexpr int value = I;
+};
 
 template <int D>
 struct PrefillShape {
@@ -107,13 +111,13 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int p = 0; p < KP; ++p) {
       const int e = tid + 256 * p;
-      const size_t off = (size_t)min(s0 + e / LPR, T - 1) * RB + 16 * (e % LPR);
+      const uint32_t off = (uint32_t)min(s0 + e / LPR, T - 1) * RB + 16 * (e % LPR);
       kr[p] = ld16(kbase + off);
       vr[p] = ld16(vbase + off);
     }
   };
-  auto stage = [&](int buf) {
-    char* sk = s_stage[buf];
+  auto stage = [&](auto buf_tag) {
+    char* sk = s_stage[decltype(buf_tag)::value];
     char* sv = sk + Sh::KBytes;
 #pragma unroll
     for (int p = 0; p < KP; ++p) {
@@ -124,17 +128,24 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     }
   };
 
-  floatx4 O[NV];
+  // O accumulates P V; L accumulates P 1 (every column of the ones operand),
+  // so the softmax denominators of rows 4 grp + i come out of the matrix
+  // cores in O's own layout, summed from the same hi + lo weights.
+  floatx4 O[NV], L = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int nv = 0; nv < NV; ++nv) O[nv] = floatx4{0.f, 0.f, 0.f, 0.f};
-  float m = -__builtin_inff(), lsum = 0.f, gsum = 0.f;
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u,
+                                                             0x3F803F80u));
+  // m: reference max (raw score units) of the lane's query column; ms2 its
+  // exponent offset m * scale * log2(e), 0 while the column is empty.
+  float m = -__builtin_inff(), ms2 = 0.f, gsum = 0.f;
 
   // MASK: the tile holds the diagonal or keys past some query (or the wave has
   // queries past the sequence); otherwise every key precedes every query.
-  auto compute = [&](int j, int buf, auto mask_tag) {
+  auto compute = [&](int j, auto buf_tag, auto mask_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
     const int s0 = j * kTileKeys;
-    const char* sk = s_stage[buf];
+    const char* sk = s_stage[decltype(buf_tag)::value];
     const char* sv = sk + Sh::KBytes;
     floatx4 S[2];
 #pragma unroll
@@ -172,35 +183,35 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
         tmax = fmaxf(tmax, lg[4 * st + i]);
       }
     }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
     // Lazy rescaling as in the grouped decode: the reference max of a query
-    // moves only when the tile raises it by more than kLazyRaise.
+    // moves only when the tile raises it by more than kLazyRaise.  m is the
+    // same in the 4 lane groups of a column, so some lane's own max passes
+    // m + lazy_raw exactly when some column's max does; the column maxima are
+    // formed only then.
     if (__ballot(tmax > m + lazy_raw) != 0ull) {
+      tmax = max_xor32(max_xor16(tmax));
       const float mn = fmaxf(m, tmax);
       const float alpha =
           mn == -__builtin_inff() ? 1.f : __builtin_amdgcn_exp2f((m - mn) * sl2);
-      lsum *= alpha;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float al = __shfl(alpha, 4 * grp + i, kWave);
+        L[i] *= al;
 #pragma unroll
         for (int nv = 0; nv < NV; ++nv) O[nv][i] *= al;
       }
       m = mn;
+      ms2 = m == -__builtin_inff() ? 0.f : m * sl2;
     }
-    const float ms2 = m == -__builtin_inff() ? 0.f : m * sl2;
-    bf16x8 phi, plo;
-    float psum = 0.f;
+    uint32_t ph[4], pl[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float p = __builtin_amdgcn_exp2f(fmaf(lg[i], sl2, -ms2));
-      psum += p;
-      const __bf16 h = (__bf16)p;
-      phi[i] = h;
-      plo[i] = (__bf16)(p - (float)h);
-    }
-    lsum += psum;
+    for (int i = 0; i < 4; ++i)
+      split_hi_lo(__builtin_amdgcn_exp2f(fmaf(lg[2 * i], sl2, -ms2)),
+                  __builtin_amdgcn_exp2f(fmaf(lg[2 * i + 1], sl2, -ms2)), ph[i], pl[i]);
+    const bf16x8 phi = __builtin_bit_cast(bf16x8, make_uint4(ph[0], ph[1], ph[2], ph[3]));
+    const bf16x8 plo = __builtin_bit_cast(bf16x8, make_uint4(pl[0], pl[1], pl[2], pl[3]));
+    L = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi, ones, L, 0, 0, 0);
+    L = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo, ones, L, 0, 0, 0);
     // Value operand (dim 16 nv + n, slots 8 grp + 4 h + j) by two transposing
     // reads: lane L of group g supplies row tile_key(h, 4 g + (L%16)/4), dims
     // 16 nv + 4 ((L%16) % 4) .. +3, and lane l receives element l % 4 of the
@@ -219,31 +230,37 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     }
   };
 
-  fetch(0);
-  stage(0);
-  __syncthreads();
-  for (int j = 0; j < ntiles; ++j) {
-    if (j + 1 < ntiles) fetch(j + 1);
+  // Tile j sits in buffer j & 1; the loop is unrolled by two so that the
+  // buffer, and with it every LDS address, is a per-lane constant plus an
+  // immediate offset.
+  auto step = [&](int j, auto buf_tag) {
+    constexpr int BUF = decltype(buf_tag)::value;
+    const bool more = j + 1 < ntiles;
+    if (more) fetch(j + 1);
     // keys of tile j all after this wave's queries (or no query left): skip
     if (j * kTileKeys <= tw + 15 && tw < T) {
       if (j * kTileKeys + kTileKeys - 1 < tw && tw + 15 < T)
-        compute(j, j & 1, MaskTag<false>{});
+        compute(j, buf_tag, MaskTag<false>{});
       else
-        compute(j, j & 1, MaskTag<true>{});
+        compute(j, buf_tag, MaskTag<true>{});
     }
-    if (j + 1 < ntiles) stage((j + 1) & 1);
+    if (more) stage(BufTag<BUF ^ 1>{});
     __syncthreads();
+  };
+  fetch(0);
+  stage(BufTag<0>{});
+  __syncthreads();
+  for (int j = 0; j < ntiles; j += 2) {
+    step(j, BufTag<0>{});
+    if (j + 1 < ntiles) step(j + 1, BufTag<1>{});
   }
 
-  // Per-query sums over the 4 lane groups of a column.
-  lsum += __shfl_xor(lsum, 16, kWave);
-  lsum += __shfl_xor(lsum, 32, kWave);
-  gsum += __shfl_xor(gsum, 16, kWave);
-  gsum += __shfl_xor(gsum, 32, kWave);
-  // O rows are queries tw + 4 grp + i; their sums sit in lanes 4 grp + i.
+  // Gate sums of a query column over its 4 lane groups.
+  gsum = sum_xor32(sum_xor16(gsum));
+  // O and L rows are queries tw + 4 grp + i.
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float li = __shfl(lsum, 4 * grp + i, kWave);
+    const float li = L[i];
     const int t = tw + 4 * grp + i;
     if (t < T) {
       float* orow = a.out + ((size_t)uq * T + t) * D;

@@ -301,15 +301,16 @@ def workspace(nbytes: int, device="cuda") -> torch.Tensor:
 
 # ---------------------------------------------------------------------------
 def auto_split(units: int, cap_blocks: int, block: int, dense: bool = False) -> int:
-    """Blocks per split-K chunk.  Big enough to amortise a chunk's fixed cost
-    (list staging, merge, partial write): up to 512 keys per chunk (2048 for
-    the dense baseline, whose chunks are contiguous); smaller for a small cache
-    so that it still yields enough chunks to fill the chip
-    (units*cap_blocks/1024, or /2048 dense).  Chosen from sweeps on MI355X
-    over the 32K..512K workloads (e.g. 32K x 16 heads, b=64: 8 blocks)."""
+    """blocks_per_split.  Sparse decode: the balanced kernel uses
+    min(waves, ceil(N / split)) waves for N admitted blocks, so up to 512 keys
+    per wave share keeps big jobs on every wave, and a small cache gets a
+    smaller value (units*cap_blocks/4096) so that it still spreads over enough
+    waves (32K x 16 heads, b=64: 2 blocks).  Dense baseline: chunks of up to
+    2048 keys (units*cap_blocks/2048 for a small cache).  Chosen from sweeps
+    on MI355X over the 32K..512K workloads."""
     if dense:
         return max(1, min(2048 // block, (units * cap_blocks) // 2048))
-    return max(1, min(512 // block, (units * cap_blocks) // 1024))
+    return max(1, min(512 // block, (units * cap_blocks) // 4096))
 
 
 class Decoder:

@@ -87,15 +87,6 @@ eta_status hip_status(hipError_t e, const char* what) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Decode workspace: [queue counter | chunk_start[units+1] | part_m | part_l |
-// part_acc], each 256-byte aligned.
-size_t decode_ws(long long units, int D, int cap_blocks, int split) {
-  const long long maxc = (cap_blocks + split - 1) / split;
-  const size_t slots = (size_t)units * (size_t)maxc;
-  return 256 + align256((size_t)(units + 1) * 4) + align256(slots * 4) * 2 +
-         align256(slots * (size_t)D * 4);
-}
-
 // Compute units of the current device (a device property, cached per device).
 int device_cus() {
   static int cached[64] = {0};
@@ -111,6 +102,26 @@ int device_cus() {
   return cached[dev];
 }
 
+// Partial slots: one per possible chunk of the flat grid, and for the
+// balanced decode one per wave plus one per stream (its slots w + u).
+size_t decode_slots(long long units, int cap_blocks, int split) {
+  const long long maxc = (cap_blocks + split - 1) / split;
+  const long long flow = 4LL * device_cus() * eta::kFlowWGsPerCU + units;
+  return (size_t)(units * maxc > flow ? units * maxc : flow);
+}
+
+// Decode workspace: [queue counter, balanced-decode total at byte 64 |
+// chunk_start or stream offsets [units+1] | part_m | part_l | part_acc], each
+// 256-byte aligned.
+size_t decode_ws(long long units, int D, int cap_blocks, int split) {
+  const size_t slots = decode_slots(units, cap_blocks, split);
+  return 256 + align256((size_t)(units + 1) * 4) + align256(slots * 4) * 2 +
+         align256(slots * (size_t)D * 4);
+}
+
+#ifndef ETA_DECODE_FLOW
+#define ETA_DECODE_FLOW 1
+#endif
 #ifndef ETA_QUEUE_WGS_PER_CU
 #define ETA_QUEUE_WGS_PER_CU 8
 #endif
@@ -247,7 +258,7 @@ static eta_status decode_common(const eta_cache* c, const float* q, const float*
   const size_t need = decode_ws(units, v.D, v.cap_blocks, split);
   if (!ws || ws_bytes < need)
     return fail(ETA_ERR_WORKSPACE, "decode workspace %zu bytes < %zu", ws_bytes, need);
-  const size_t slots = (size_t)units * maxc;
+  const size_t slots = decode_slots(units, v.cap_blocks, split);
   char* w = static_cast<char*>(ws);
   const size_t off_start = 256;
   const size_t off_parts = off_start + align256((size_t)(units + 1) * 4);
@@ -281,6 +292,13 @@ static eta_status decode_common(const eta_cache* c, const float* q, const float*
   a.queue = reinterpret_cast<int*>(w);
   a.chunk_start = reinterpret_cast<int*>(w + off_start);
   a.queue_grid = device_cus() * ETA_QUEUE_WGS_PER_CU;
+  // Sparse decode runs balanced (equal ranges of all admitted blocks per
+  // wave) whenever its stream offsets fit in LDS.
+  a.use_flow = !dense && units <= eta::kMaxFlowUnits &&
+               units * (long long)v.cap_blocks < 0x7fffffffLL && ETA_DECODE_FLOW;
+  a.flow_grid = device_cus() * eta::kFlowWGsPerCU;
+  a.flow_start = a.chunk_start;
+  a.flow_info = reinterpret_cast<int*>(w + 64);
   return hip_status(eta::launch_decode(v, a, (hipStream_t)stream), "eta_decode launch");
 }
 

@@ -92,6 +92,18 @@ __device__ __forceinline__ void split_hi_lo(float a, float b, uint32_t& hi, uint
   lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(rest, bf16x2));
 }
 
+// Chunk k of stream u in a flat grid of max_chunks work-groups per stream.
+// Work-groups are dealt to the 8 XCDs round-robin by blockIdx, so with the
+// plain order u * max_chunks + k and max_chunks a multiple of 8, chunk k of
+// every stream lands on XCD k % 8 and the XCDs holding the low chunk numbers
+// carry the streams' remainders (a stream with 13 chunks puts 2 on XCDs 0-4
+// and 1 on XCDs 5-7).  Rotating each stream's chunks by u % 8 spreads the
+// remainders over all XCDs; a stream's work-groups stay together.
+__device__ __forceinline__ int rotated_chunk(int r, int u, int max_chunks) {
+  const int k = r - (u & 7) % max_chunks;
+  return k < 0 ? k + max_chunks : k;
+}
+
 // Pairs of 16-lane rows on the VALU (gfx950 permlane swaps).  Called with
 // the lane's own value as both operands, v_permlane16_swap returns in every
 // lane the values of the even and of the odd row of the pair (r, r ^ 1), and
@@ -231,7 +243,16 @@ struct DecodeArgs {
   int* chunk_start;  // [B*H + 1] chunk offsets of the queue kernel
   bool use_queue;    // queue kernel (else one work-group per possible chunk)
   int queue_grid;    // work-groups of the queue kernel
+  bool use_flow;     // balanced decode: equal ranges of all admitted blocks per wave
+  int flow_grid;     // work-groups of the balanced decode (4 waves each)
+  int* flow_start;   // [B*H + 1] admitted-block offsets, written by the balanced decode
+  int* flow_info;    // [1] total admitted blocks N
 };
+// Work-groups per compute unit of the balanced decode (its occupancy: all
+// of them are resident at once) and the stream count up to which it is used
+// (its offsets live in LDS).
+constexpr int kFlowWGsPerCU = 3;
+constexpr int kMaxFlowUnits = 8191;
 // Streams up to which the queue kernel can be used (its chunk table lives in
 // LDS), and the flat-grid size above which it is.
 constexpr int kMaxQueueUnits = 8192;

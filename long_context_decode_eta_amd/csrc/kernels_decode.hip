@@ -44,6 +44,77 @@ __device__ __forceinline__ void merge_state(float& m, float& l, float* a, float 
   m = mn;
 }
 
+// Running softmax state of one lane group over the rows it has folded in:
+// reference max m, sum l of e^(logit - m), and the e^(logit - m)-weighted sum
+// of its EPL value columns.
+template <int EPL>
+struct RowState {
+  float m, l, acc[EPL];
+  __device__ __forceinline__ void reset() {
+    m = -__builtin_inff();
+    l = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+  }
+};
+
+// Fold one loaded tile into st: NI rows per lane group, row i holding key
+// sp[i] (-1: no key) with its K and V chunks kr[i], vr[i].  Logits follow
+// Eq. 3 in GATED mode (the query's own key T - 1 ungated), raw otherwise.
+template <int D, int DT, int MODE, int NI>
+__device__ __forceinline__ void fold_tile(RowState<Elt<DT>::kPer16B>& st, const uint4* kr,
+                                          const uint4* vr, const int* sp, const float* qs,
+                                          float tau, float beta, int T) {
+  constexpr int EPL = Elt<DT>::kPer16B;
+  constexpr int LPR = D / EPL;
+  float lg[NI];
+  float tmax = -__builtin_inff();
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    float x[EPL];
+    widen<DT>(kr[i], x);
+    float d = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) d = fmaf(qs[e], x[e], d);
+    d = group_sum<LPR>(d);
+    float lv = d;
+    if (MODE == ETA_LOGIT_GATED && sp[i] != T - 1)
+      lv = d * __builtin_amdgcn_rcpf(1.f + fexp(-beta * (d - tau)));
+    lg[i] = sp[i] >= 0 ? lv : -__builtin_inff();
+    tmax = fmaxf(tmax, lg[i]);
+  }
+  const float mn = fmaxf(st.m, tmax);
+  const float ms = (mn == -__builtin_inff()) ? 0.f : mn;
+  const float alpha = fexp(st.m - ms);
+  st.l *= alpha;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) st.acc[e] *= alpha;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const float p = fexp(lg[i] - ms);
+    st.l += p;
+    float y[EPL];
+    widen<DT>(vr[i], y);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) st.acc[e] = fmaf(p, y[e], st.acc[e]);
+  }
+  st.m = mn;
+}
+
+// Merge the RPI row groups of a wave (xor butterfly: partners end equal).
+template <int EPL, int LPR>
+__device__ __forceinline__ void merge_groups(RowState<EPL>& st) {
+#pragma unroll
+  for (int off = LPR; off < kWave; off <<= 1) {
+    const float m2 = __shfl_xor(st.m, off, kWave);
+    const float l2 = __shfl_xor(st.l, off, kWave);
+    float a2[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) a2[e] = __shfl_xor(st.acc[e], off, kWave);
+    merge_state<EPL>(st.m, st.l, st.acc, m2, l2, a2);
+  }
+}
+
 // Attention of one chunk (chunk k of stream u) by the whole work-group.  The
 // chunk's block indices are first staged in LDS (s_list), so no key or value
 // load ever waits on an index load.  Writes the final output when the chunk is
@@ -79,9 +150,8 @@ __device__ __forceinline__ void chunk_attend(const CacheView& c, const DecodeArg
   const char* vb = static_cast<const char*>(c.v) + (size_t)u * c.cap * RB + li * 16;
   __syncthreads();
 
-  float m = -__builtin_inff(), l = 0.f, acc[EPL];
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+  RowState<EPL> st;
+  st.reset();
 
   const int rows = nblk << c.log2bs;
   const int ntiles = (rows + NI * RPI - 1) / (NI * RPI);
@@ -109,40 +179,8 @@ __device__ __forceinline__ void chunk_attend(const CacheView& c, const DecodeArg
       }
     }
   };
-  // Fold one loaded tile into the running (m, l, acc).
   auto consume = [&](const uint4* kr, const uint4* vr, const int* sp) {
-    float lg[NI];
-    float tmax = -__builtin_inff();
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      float x[EPL];
-      widen<DT>(kr[i], x);
-      float d = 0.f;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) d = fmaf(qs[e], x[e], d);
-      d = group_sum<LPR>(d);
-      float lv = d;
-      if (MODE == ETA_LOGIT_GATED && sp[i] != T - 1)
-        lv = d * __builtin_amdgcn_rcpf(1.f + fexp(-beta * (d - tau)));
-      lg[i] = sp[i] >= 0 ? lv : -__builtin_inff();
-      tmax = fmaxf(tmax, lg[i]);
-    }
-    const float mn = fmaxf(m, tmax);
-    const float ms = (mn == -__builtin_inff()) ? 0.f : mn;
-    const float alpha = fexp(m - ms);
-    l *= alpha;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] *= alpha;
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const float p = fexp(lg[i] - ms);
-      l += p;
-      float y[EPL];
-      widen<DT>(vr[i], y);
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[e] = fmaf(p, y[e], acc[e]);
-    }
-    m = mn;
+    fold_tile<D, DT, MODE, NI>(st, kr, vr, sp, qs, tau, beta, T);
   };
 
   // Two register buffers: the loads of a wave's next tile are in flight while
@@ -158,22 +196,13 @@ __device__ __forceinline__ void chunk_attend(const CacheView& c, const DecodeArg
     if (has_b) consume(kq, vq, sq);
   }
 
-  // Merge the RPI row groups of the wave (xor butterfly: partners end equal).
-#pragma unroll
-  for (int off = LPR; off < kWave; off <<= 1) {
-    const float m2 = __shfl_xor(m, off, kWave);
-    const float l2 = __shfl_xor(l, off, kWave);
-    float a2[EPL];
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) a2[e] = __shfl_xor(acc[e], off, kWave);
-    merge_state<EPL>(m, l, acc, m2, l2, a2);
-  }
+  merge_groups<EPL, LPR>(st);
   if (g == 0) {
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) s_acc[wave][li * EPL + e] = acc[e];
+    for (int e = 0; e < EPL; ++e) s_acc[wave][li * EPL + e] = st.acc[e];
     if (li == 0) {
-      s_ml[wave][0] = m;
-      s_ml[wave][1] = l;
+      s_ml[wave][0] = st.m;
+      s_ml[wave][1] = st.l;
     }
   }
   __syncthreads();
@@ -209,7 +238,8 @@ __device__ __forceinline__ int stream_chunks(const CacheView& c, const DecodeArg
   return (cnt + a.split - 1) / a.split;
 }
 
-// Log-sum-exp merge of the nch chunk partials of stream u into out[u], by the
+// Log-sum-exp merge of the nch partials in slots slot0 .. slot0 + nch - 1 into
+// out[u], by the
 // whole work-group of kCombWaves waves: wave w folds chunks w, w+kCombWaves,
 // ... into a running (max, sum, weighted V) in one pass with kInflight chunks
 // loaded before any is used; lane i owns columns [i*CPL, i*CPL+CPL).  The wave
@@ -217,13 +247,13 @@ __device__ __forceinline__ int stream_chunks(const CacheView& c, const DecodeArg
 constexpr int kInflight = 8;
 constexpr int kCombWaves = 16;
 template <int D>
-__device__ void combine_stream(const DecodeArgs& a, int u, int nch, float (*s_acc)[D],
-                               float (*s_ml)[2]) {
+__device__ void combine_slots(const DecodeArgs& a, int u, size_t slot0, int nch,
+                              float (*s_acc)[D], float (*s_ml)[2]) {
   constexpr int CPL = D / kWave;
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
-  const float* pm = a.part_m + (size_t)u * a.max_chunks;
-  const float* pl = a.part_l + (size_t)u * a.max_chunks;
-  const float* pa = a.part_acc + (size_t)u * a.max_chunks * D + lane * CPL;
+  const float* pm = a.part_m + slot0;
+  const float* pl = a.part_l + slot0;
+  const float* pa = a.part_acc + slot0 * D + lane * CPL;
   float m = -__builtin_inff(), l = 0.f, acc[CPL];
 #pragma unroll
   for (int e = 0; e < CPL; ++e) acc[e] = 0.f;
@@ -345,16 +375,18 @@ __global__ __launch_bounds__(256) void decode_queue_kernel(CacheView c, DecodeAr
   }
 }
 
-// Flat-grid decode for very many streams: one work-group per possible chunk,
-// blockIdx.x = u * max_chunks + k (a stream's chunks are dispatched together,
-// which measured faster than chunk-major order); work-groups past a stream's
-// last chunk exit.
+// Flat-grid decode: one work-group per possible chunk, blockIdx.x =
+// u * max_chunks + (k + u % 8) mod max_chunks (a stream's chunks are
+// dispatched together, which measured faster than chunk-major order, and are
+// rotated so that every XCD gets an even share of them); work-groups past a
+// stream's last chunk exit.
 template <int D, int DT, int MODE, bool DENSE>
 __global__ __launch_bounds__(256) void decode_grid_kernel(CacheView c, DecodeArgs a) {
   extern __shared__ int s_list[];
   __shared__ float s_acc[4][D];
   __shared__ float s_ml[4][2];
-  const int u = blockIdx.x / a.max_chunks, k = blockIdx.x % a.max_chunks;
+  const int u = blockIdx.x / a.max_chunks;
+  const int k = rotated_chunk(blockIdx.x % a.max_chunks, u, a.max_chunks);
   int T, cnt;
   const int nch = stream_chunks(c, a, u, &T, &cnt);
   if (k >= nch) return;
@@ -374,7 +406,208 @@ __global__ __launch_bounds__(kCombWaves * kWave) void combine_kernel(CacheView c
     return;
   }
   if (nch == 1) return;  // written by the decode kernel
-  combine_stream<D>(a, u, nch, s_acc, s_ml);
+  combine_slots<D>(a, u, (size_t)u * a.max_chunks, nch, s_acc, s_ml);
+}
+
+// ---------------------------------------------------------------------------
+// Balanced sparse decode.  The admitted lists of all streams, concatenated in
+// stream order, hold N blocks (exclusive prefix sums start[u]).  Each of
+// min(waves, ceil(N / blocks_per_split)) waves takes an equal contiguous range
+// of that concatenation (small jobs use fewer waves), walks it with its
+// own two-deep load pipeline (no wave waits for another and no work-group
+// restarts per chunk), and writes one partial per stream segment it covers
+// into slot w + u: along the concatenation the wave index and the stream
+// index both only grow and every new segment advances one of them, so the
+// slots are distinct.  The combine merges, per stream, the slots of the waves
+// that cover it.
+
+// Admitted blocks of stream u, clamped to the blocks the stream holds.
+__device__ __forceinline__ int stream_blocks(const CacheView& c, const DecodeArgs& a, int u) {
+  const int T = c.seq_len[u / c.H];
+  const int nb = T > 0 ? (T + c.bs - 1) >> c.log2bs : 0;
+  return max(0, min(a.active_cnt[u], nb));
+}
+
+// The N admitted blocks in wn equal ranges, wn = min(waves, ceil(N / split)),
+// range w = [lo(w), lo(w + 1)), all non-empty as wn <= N.
+struct FlowPlan {
+  int N, wn;
+  __device__ FlowPlan(int n, int waves, int split)
+      : N(n), wn(n == 0 ? 0 : min(waves, ceil_div(n, split))) {}
+  __device__ int lo(int w) const { return (int)((long long)w * N / wn); }
+  // The range holding position p < N.
+  __device__ int range_of(int p) const {
+    int w = (int)((long long)p * wn / N);
+    while (w + 1 < wn && lo(w + 1) <= p) ++w;
+    return w;
+  }
+};
+
+template <int D, int DT, int MODE>
+__global__ __launch_bounds__(256, kFlowWGsPerCU) void decode_flow_kernel(CacheView c, DecodeArgs a) {
+  constexpr int EPL = Elt<DT>::kPer16B;
+  constexpr int LPR = D / EPL;
+  constexpr int RPI = kWave / LPR;
+  constexpr int NI = (kRows / RPI) > 0 ? (kRows / RPI) : 1;
+  constexpr int RB = D * Elt<DT>::kBytes;
+  extern __shared__ int s_start[];  // [units + 1]
+  __shared__ int s_wsum[4];
+  const int units = c.B * c.H;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int g = lane / LPR, li = lane % LPR;
+  const int waves = gridDim.x * 4;
+
+  // Exclusive prefix sums of the admitted counts, every work-group for itself:
+  // thread t sums its run of ceil(units / 256) streams, the runs are scanned
+  // across the work-group, then written back as offsets.
+  {
+    const int per = (units + 255) / 256;
+    const int u0 = min(units, tid * per), u1 = min(units, u0 + per);
+    int sum = 0;
+    for (int u = u0; u < u1; ++u) {
+      const int n = stream_blocks(c, a, u);
+      s_start[u] = n;
+      sum += n;
+    }
+    int incl = sum;  // inclusive scan over the wave
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int y = __shfl_up(incl, off, kWave);
+      if (lane >= off) incl += y;
+    }
+    if (lane == kWave - 1) s_wsum[wave] = incl;
+    __syncthreads();
+    int off = incl - sum;
+    for (int w = 0; w < wave; ++w) off += s_wsum[w];
+    for (int u = u0; u < u1; ++u) {
+      const int n = s_start[u];
+      s_start[u] = off;
+      off += n;
+    }
+    if (tid == 255) s_start[units] = off;
+    __syncthreads();
+  }
+  const FlowPlan plan(s_start[units], waves, a.split);
+  if (blockIdx.x == 0) {  // for the combine
+    for (int u = tid; u <= units; u += 256) a.flow_start[u] = s_start[u];
+    if (tid == 0) a.flow_info[0] = plan.N;
+  }
+  const int w = blockIdx.x * 4 + wave;
+  if (w >= plan.wn) return;  // waves are independent from here on
+
+  // Attention of the wave over positions [p, pend) of the concatenation,
+  // one partial per stream segment, into slot slot_base + u.
+  auto walk = [&](int p, const int pend, const size_t slot_base) {
+    int u = 0;  // the last stream with start[u] <= p (so start[u + 1] > p)
+    {
+      int hi = units - 1;
+      while (u < hi) {
+        const int mid = (u + hi + 1) >> 1;
+        if (s_start[mid] <= p) u = mid; else hi = mid - 1;
+      }
+    }
+    while (p < pend) {
+      const int base = s_start[u];
+      const int i0 = p - base, i1 = min(pend, s_start[u + 1]) - base;  // local blocks
+      const int T = c.seq_len[u / c.H];
+      const int nb = (T + c.bs - 1) >> c.log2bs;
+      const int32_t* list = a.active_idx + (size_t)u * c.cap_blocks + i0;
+      const int nblk = i1 - i0;
+      float qs[EPL];
+      {
+        const float* qu = a.q + (size_t)u * D + li * EPL;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) qs[e] = qu[e] * a.scale;
+      }
+      const float tau = (MODE == ETA_LOGIT_GATED) ? a.tau[u] : 0.f;
+      const char* kb = static_cast<const char*>(c.k) + (size_t)u * c.cap * RB + li * 16;
+      const char* vb = static_cast<const char*>(c.v) + (size_t)u * c.cap * RB + li * 16;
+
+      // Block indices, 64 per register: lane x holds entry bb + x of lst0 and
+      // bb + 64 + x of lst1; the window moves on by 64 once a tile starts past
+      // its first half, and the new second half is loaded then, long before use.
+      int bb = 0;
+      int lst0 = lane < nblk ? list[lane] : -1;
+      int lst1 = 64 + lane < nblk ? list[64 + lane] : -1;
+      const int rows = nblk << c.log2bs;
+      const int ntiles = (rows + kRows - 1) / kRows;
+
+      auto fetch = [&](int t, uint4* kr, uint4* vr, int* sp) {
+        const int first_blk = (t * kRows) >> c.log2bs;
+        if (first_blk >= bb + 64) {  // wave-uniform
+          lst0 = lst1;
+          bb += 64;
+          lst1 = bb + 64 + lane < nblk ? list[bb + 64 + lane] : -1;
+        }
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          const int rr = t * kRows + i * RPI + g;  // row within the segment
+          // Every lane takes part in the shuffles (a lane whose own row is past
+          // the segment may still hold the entry another lane needs).
+          const int o = (rr >> c.log2bs) - bb;  // 0 .. 127
+          const int j0 = __shfl(lst0, o & 63, kWave), j1 = __shfl(lst1, o & 63, kWave);
+          const int j = o < 64 ? j0 : j1;
+          // The list is trusted only as far as it stays inside the stream.
+          int s = rr < rows && (unsigned)j < (unsigned)nb ? (j << c.log2bs) + (rr & (c.bs - 1)) : -1;
+          if (s >= T) s = -1;
+          sp[i] = s;
+          if (s >= 0) {
+            kr[i] = ld16_nt(kb + (size_t)s * RB);
+            vr[i] = ld16_nt(vb + (size_t)s * RB);
+          } else {
+            kr[i] = make_uint4(0, 0, 0, 0);
+            vr[i] = make_uint4(0, 0, 0, 0);
+          }
+        }
+      };
+
+      RowState<EPL> st;
+      st.reset();
+      uint4 ka[NI], va[NI], kq[NI], vq[NI];
+      int sa[NI], sq[NI];
+      fetch(0, ka, va, sa);
+      for (int t = 0; t < ntiles; t += 2) {
+        const bool has_b = t + 1 < ntiles;
+        if (has_b) fetch(t + 1, kq, vq, sq);
+        fold_tile<D, DT, MODE, NI>(st, ka, va, sa, qs, tau, a.beta, T);
+        if (t + 2 < ntiles) fetch(t + 2, ka, va, sa);
+        if (has_b) fold_tile<D, DT, MODE, NI>(st, kq, vq, sq, qs, tau, a.beta, T);
+      }
+      merge_groups<EPL, LPR>(st);
+      const size_t slot = slot_base + u;
+      if (g == 0) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) a.part_acc[slot * D + li * EPL + e] = st.acc[e];
+        if (li == 0) {
+          a.part_m[slot] = st.m;
+          a.part_l[slot] = st.l;
+        }
+      }
+      p = base + i1;
+      if (p < pend)  // next non-empty stream
+        do ++u; while (s_start[u + 1] <= p);
+    }
+  };
+
+  walk(plan.lo(w), plan.lo(w + 1), (size_t)w);
+}
+
+// Combine of the balanced decode: one work-group per stream, merging the
+// slots of the ranges that cover the stream's positions [p0, p1).
+template <int D>
+__global__ __launch_bounds__(kCombWaves * kWave) void combine_flow_kernel(CacheView c,
+                                                                          DecodeArgs a) {
+  __shared__ float s_acc[kCombWaves][D];
+  __shared__ float s_ml[kCombWaves][2];
+  const int u = blockIdx.x;
+  const int p0 = a.flow_start[u], p1 = a.flow_start[u + 1];
+  if (p1 <= p0) {  // empty stream: zeros
+    for (int i = threadIdx.x; i < D; i += blockDim.x) a.out[(size_t)u * D + i] = 0.f;
+    return;
+  }
+  const FlowPlan plan(a.flow_info[0], a.flow_grid * 4, a.split);
+  const int wf = plan.range_of(p0), wl = plan.range_of(p1 - 1);
+  combine_slots<D>(a, u, (size_t)wf + u, wl - wf + 1, s_acc, s_ml);
 }
 
 // ---------------------------------------------------------------------------
@@ -383,6 +616,16 @@ static hipError_t decode_t(const CacheView& c, const DecodeArgs& a, hipStream_t 
   const int units = c.B * c.H;
   const size_t list_bytes = DENSE ? 0 : (size_t)a.split * 4;
   hipError_t e;
+  if constexpr (!DENSE) {
+    if (a.use_flow) {
+      hipLaunchKernelGGL((decode_flow_kernel<D, DT, MODE>), dim3(a.flow_grid), dim3(256),
+                         (size_t)(units + 1) * 4, s, c, a);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      hipLaunchKernelGGL((combine_flow_kernel<D>), dim3(units), dim3(kCombWaves * kWave), 0, s,
+                         c, a);
+      return hipGetLastError();
+    }
+  }
   if (a.use_queue) {
     // chunk table and queue counter for the persistent grid
     hipLaunchKernelGGL((decode_prepare_kernel<D>), dim3(1), dim3(1024), 0, s, c, a);

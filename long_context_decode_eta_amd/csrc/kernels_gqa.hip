@@ -273,7 +273,8 @@ __global__ __launch_bounds__(GqaShape<D>::W * 64, GqaShape<D>::MinBlocks) void d
   int2* s_blk = reinterpret_cast<int2*>(s_raw + W * Sh::WaveBytes);    // [split]
   __shared__ float s_ml[W][16][2];
 
-  const int u = blockIdx.x / a.max_chunks, k = blockIdx.x % a.max_chunks;
+  const int u = blockIdx.x / a.max_chunks;
+  const int k = rotated_chunk(blockIdx.x % a.max_chunks, u, a.max_chunks);
   int T, cnt;
   const int nch = gqa_stream(c, a, DENSE, u, &T, &cnt);
   if (k >= nch) return;

@@ -1,7 +1,8 @@
 """A decode step captured in a HIP graph reproduces the eager step exactly.
 
-The step (threshold, screen, decode with its prepare and combine kernels)
-records no memset: every counter it needs is reset by its own prepare kernel.
+The step (threshold, screen, decode and combine kernels) records no memset:
+every buffer a kernel reads was written earlier in the same step (the density
+counter only accumulates), and the decode keeps no state between calls.
 The graph is replayed several times with eager work and synchronisations in
 between, and every replay is compared bit for bit with the eager result.
 """

@@ -4,7 +4,9 @@ Runs the HIP path (libeta.so) through its C ABI.  Cases: the hand example
 (b=4, T=16, zero-padded to d=64), the tiny fp32 workload (B=1, H=4, d=64,
 T=2048, b=16, z=1.5, frozen tau), ragged lengths with NaN-filled unused slots
 for every block size and head size, threshold extremes, split-size
-invariance, determinism, the threshold predictor and the dense baseline.
+invariance, determinism, the threshold predictor, the dense baseline, many
+short streams, and more streams than the balanced decode handles (queue and
+flat-grid scheduling).
 """
 import json
 import math
@@ -175,9 +177,9 @@ def test_dense_decode(kv):
     compare_outputs(out.cpu().numpy(), ref, w.kv_dtype, "dense")
 
 
-def test_queue_scheduled_decode_path():
-    # 1024 streams with one block per chunk: the flat grid would hold
-    # 1024 x 256 work-groups, so eta_decode takes chunks from its work queue.
+def test_balanced_decode_many_short_streams():
+    # 1024 streams of 1..4096 tokens with one block per wave share: waves that
+    # span several streams and streams that span many waves.
     w = to_gpu(synth.make("ragged", seed=13, T=(1, 4096), B=64, H=16, cap=4096, pad="nan"))
     cache = make_cache(w)
     assert w.B * w.H * cache.cap_blocks > 49152
@@ -186,6 +188,22 @@ def test_queue_scheduled_decode_path():
         g = run_gpu(cache, w.q, bias_or_c=c, z=w.z, scale=w.scale, mode=mode, split=1)
         st = check_against_oracle(w, g, cache, W=None, bias_or_c=c, z=w.z, scale=w.scale,
                                   mode=mode)
+    note(f"  density {st['density']:.3f} out_rel {st['out_rel']:.2e}")
+
+
+@pytest.mark.parametrize("split", [1, 8])
+def test_more_streams_than_the_balanced_decode_holds(split):
+    # 8192 streams: more than the balanced decode keeps offsets for, so
+    # eta_decode schedules chunks instead -- from its work queue when the flat
+    # grid would be mostly empty (8192 x 8 work-groups at one block per
+    # chunk), else on the flat grid (8192 x 1).
+    w = to_gpu(synth.make("ragged", seed=19, T=(1, 128), B=512, H=16, D=64, cap=128, pad="nan"))
+    cache = make_cache(w)
+    assert w.B * w.H > 8191
+    c = torch.linspace(1.0, 2.0, 16, device="cuda")
+    g = run_gpu(cache, w.q, bias_or_c=c, z=w.z, scale=w.scale, split=split)
+    st = check_against_oracle(w, g, cache, W=None, bias_or_c=c, z=w.z, scale=w.scale,
+                              mode=eb.GATED)
     note(f"  density {st['density']:.3f} out_rel {st['out_rel']:.2e}")
 
 

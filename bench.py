@@ -36,8 +36,8 @@ COUNTERS = os.path.join(ROOT, "profiles", "decode_counters.json")
 GQA_COUNTERS = os.path.join(ROOT, "profiles", "gqa_decode_counters.json")
 # the decode kernels and the host code that picks their launch path
 CSRC = os.path.join(ROOT, "long_context_decode_eta_amd", "csrc")
-DECODE_SRC = [os.path.join(CSRC, f) for f in ("kernels_decode.hip", "eta_api.hip")]
-GQA_SRC = [os.path.join(CSRC, f) for f in ("kernels_gqa.hip", "eta_api.hip")]
+DECODE_SRC = [os.path.join(CSRC, f) for f in ("kernels_decode.hip", "eta_api.hip", "eta_internal.h")]
+GQA_SRC = [os.path.join(CSRC, f) for f in ("kernels_gqa.hip", "eta_api.hip", "eta_internal.h")]
 
 
 def parse():

@@ -163,10 +163,14 @@ eta_status eta_screen(const eta_cache* c, const float* q, const float* tau_scree
 /*
  * Block-sparse decode (Theoretical Foundation: attention restricted to the
  * admitted set, normalised over it; Methodology 2, Eq. 3 for the logits;
- * Fig. 6: only admitted blocks are loaded, online softmax).  For each (b, h)
- * the admitted list is cut into chunks of blocks_per_split blocks; each chunk
- * produces a partial (max, sum, weighted V) and one combine pass merges them
- * by log-sum-exp into out [batch][heads][head_dim] float32 (device).
+ * Fig. 6: only admitted blocks are loaded, online softmax).  The admitted
+ * lists of all streams, taken in (b, h) order, are cut into equal contiguous
+ * ranges, min(waves on the device, ceil(N / blocks_per_split)) of them for N
+ * admitted blocks, one per wavefront; every (range, stream) piece produces a
+ * partial (max, sum, weighted V) and one combine pass merges each stream's
+ * partials by log-sum-exp into out [batch][heads][head_dim] float32 (device).
+ * Above 8191 streams the per-stream lists are cut into chunks of
+ * blocks_per_split blocks instead, one work-group each.
  * Logits, with S_s = scale <q, k_s>:
  *   ETA_LOGIT_GATED  l_s = S_s sigmoid(beta (S_s - tau_gate[b][h])) for
  *                    s != T_b - 1, and l_{T_b-1} = S_{T_b-1} (the query's own
@@ -186,8 +190,9 @@ eta_status eta_decode(const eta_cache* c, const float* q, const float* tau_gate,
 
 /*
  * Dense decode over every key of every stream (Theoretical Foundation, dense
- * form): the same split/combine kernels with all blocks admitted and RAW
- * logits.  The in-house dense baseline.  Workspace as for eta_decode.
+ * form): chunks of blocks_per_split consecutive blocks per stream, one
+ * work-group each, with RAW logits and the same log-sum-exp combine.  The
+ * in-house dense baseline.  Workspace as for eta_decode.
  */
 eta_status eta_dense_decode(const eta_cache* c, const float* q, float scale,
                             int32_t blocks_per_split, void* workspace, size_t workspace_bytes,

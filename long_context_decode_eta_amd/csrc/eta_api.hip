@@ -106,7 +106,8 @@ int device_cus() {
 // balanced decode one per wave plus one per stream (its slots w + u).
 size_t decode_slots(long long units, int cap_blocks, int split) {
   const long long maxc = (cap_blocks + split - 1) / split;
-  const long long flow = 4LL * device_cus() * eta::kFlowWGsPerCU + units;
+  const long long flow =
+      (long long)(eta::kFlowThreads / 64) * device_cus() * eta::kFlowWGsPerCU + units;
   return (size_t)(units * maxc > flow ? units * maxc : flow);
 }
 
@@ -119,9 +120,6 @@ size_t decode_ws(long long units, int D, int cap_blocks, int split) {
          align256(slots * (size_t)D * 4);
 }
 
-#ifndef ETA_DECODE_FLOW
-#define ETA_DECODE_FLOW 1
-#endif
 #ifndef ETA_QUEUE_WGS_PER_CU
 #define ETA_QUEUE_WGS_PER_CU 8
 #endif
@@ -295,7 +293,7 @@ static eta_status decode_common(const eta_cache* c, const float* q, const float*
   // Sparse decode runs balanced (equal ranges of all admitted blocks per
   // wave) whenever its stream offsets fit in LDS.
   a.use_flow = !dense && units <= eta::kMaxFlowUnits &&
-               units * (long long)v.cap_blocks < 0x7fffffffLL && ETA_DECODE_FLOW;
+               units * (long long)v.cap_blocks < 0x7fffffffLL;
   a.flow_grid = device_cus() * eta::kFlowWGsPerCU;
   a.flow_start = a.chunk_start;
   a.flow_info = reinterpret_cast<int*>(w + 64);

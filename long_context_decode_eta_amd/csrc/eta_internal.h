@@ -244,14 +244,15 @@ struct DecodeArgs {
   bool use_queue;    // queue kernel (else one work-group per possible chunk)
   int queue_grid;    // work-groups of the queue kernel
   bool use_flow;     // balanced decode: equal ranges of all admitted blocks per wave
-  int flow_grid;     // work-groups of the balanced decode (4 waves each)
+  int flow_grid;     // work-groups of the balanced decode (kFlowThreads each)
   int* flow_start;   // [B*H + 1] admitted-block offsets, written by the balanced decode
   int* flow_info;    // [1] total admitted blocks N
 };
-// Work-groups per compute unit of the balanced decode (its occupancy: all
-// of them are resident at once) and the stream count up to which it is used
-// (its offsets live in LDS).
-constexpr int kFlowWGsPerCU = 3;
+// Work-group size and work-groups per compute unit of the balanced decode
+// (3 waves per SIMD, its occupancy: all of them are resident at once) and the
+// stream count up to which it is used (its offsets live in LDS).
+constexpr int kFlowThreads = 256;
+constexpr int kFlowWGsPerCU = 3 * 256 / kFlowThreads;
 constexpr int kMaxFlowUnits = 8191;
 // Streams up to which the queue kernel can be used (its chunk table lives in
 // LDS), and the flat-grid size above which it is.

@@ -444,24 +444,25 @@ struct FlowPlan {
 };
 
 template <int D, int DT, int MODE>
-__global__ __launch_bounds__(256, kFlowWGsPerCU) void decode_flow_kernel(CacheView c, DecodeArgs a) {
+__global__ __launch_bounds__(kFlowThreads, 3) void decode_flow_kernel(CacheView c, DecodeArgs a) {
   constexpr int EPL = Elt<DT>::kPer16B;
   constexpr int LPR = D / EPL;
   constexpr int RPI = kWave / LPR;
   constexpr int NI = (kRows / RPI) > 0 ? (kRows / RPI) : 1;
   constexpr int RB = D * Elt<DT>::kBytes;
   extern __shared__ int s_start[];  // [units + 1]
-  __shared__ int s_wsum[4];
+  constexpr int NW = kFlowThreads / kWave;  // waves per work-group
+  __shared__ int s_wsum[NW];
   const int units = c.B * c.H;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g = lane / LPR, li = lane % LPR;
-  const int waves = gridDim.x * 4;
+  const int waves = gridDim.x * NW;
 
   // Exclusive prefix sums of the admitted counts, every work-group for itself:
   // thread t sums its run of ceil(units / 256) streams, the runs are scanned
   // across the work-group, then written back as offsets.
   {
-    const int per = (units + 255) / 256;
+    const int per = (units + kFlowThreads - 1) / kFlowThreads;
     const int u0 = min(units, tid * per), u1 = min(units, u0 + per);
     int sum = 0;
     for (int u = u0; u < u1; ++u) {
@@ -484,15 +485,15 @@ __global__ __launch_bounds__(256, kFlowWGsPerCU) void decode_flow_kernel(CacheVi
       s_start[u] = off;
       off += n;
     }
-    if (tid == 255) s_start[units] = off;
+    if (tid == kFlowThreads - 1) s_start[units] = off;
     __syncthreads();
   }
   const FlowPlan plan(s_start[units], waves, a.split);
   if (blockIdx.x == 0) {  // for the combine
-    for (int u = tid; u <= units; u += 256) a.flow_start[u] = s_start[u];
+    for (int u = tid; u <= units; u += kFlowThreads) a.flow_start[u] = s_start[u];
     if (tid == 0) a.flow_info[0] = plan.N;
   }
-  const int w = blockIdx.x * 4 + wave;
+  const int w = blockIdx.x * NW + wave;
   if (w >= plan.wn) return;  // waves are independent from here on
 
   // Attention of the wave over positions [p, pend) of the concatenation,
@@ -605,7 +606,7 @@ __global__ __launch_bounds__(kCombWaves * kWave) void combine_flow_kernel(CacheV
     for (int i = threadIdx.x; i < D; i += blockDim.x) a.out[(size_t)u * D + i] = 0.f;
     return;
   }
-  const FlowPlan plan(a.flow_info[0], a.flow_grid * 4, a.split);
+  const FlowPlan plan(a.flow_info[0], a.flow_grid * (kFlowThreads / kWave), a.split);
   const int wf = plan.range_of(p0), wl = plan.range_of(p1 - 1);
   combine_slots<D>(a, u, (size_t)wf + u, wl - wf + 1, s_acc, s_ml);
 }
@@ -618,7 +619,7 @@ static hipError_t decode_t(const CacheView& c, const DecodeArgs& a, hipStream_t 
   hipError_t e;
   if constexpr (!DENSE) {
     if (a.use_flow) {
-      hipLaunchKernelGGL((decode_flow_kernel<D, DT, MODE>), dim3(a.flow_grid), dim3(256),
+      hipLaunchKernelGGL((decode_flow_kernel<D, DT, MODE>), dim3(a.flow_grid), dim3(kFlowThreads),
                          (size_t)(units + 1) * 4, s, c, a);
       if ((e = hipGetLastError()) != hipSuccess) return e;
       hipLaunchKernelGGL((combine_flow_kernel<D>), dim3(units), dim3(kCombWaves * kWave), 0, s,

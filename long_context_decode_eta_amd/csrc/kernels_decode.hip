@@ -8,15 +8,20 @@
 // from HBM and folded into an online softmax (Fig. 6).  Dense mode walks every
 // block with raw logits (plain decode attention, the in-house baseline).
 //
-// Work decomposition: the admitted list of stream u is cut into chunks of
-// `split` blocks; one work-group of 4 waves handles one chunk, and a combine
-// kernel merges the partials of every multi-chunk stream (log-sum-exp).  The chunk's
-// rows are cut into tiles of kRows rows; wave w takes tiles w, w+4, ...  A key
-// row of D elements is read by LPR lanes with one 128-bit load each (bf16,
-// D=128: 16 lanes), so one load instruction of a wave covers RPI = 64/LPR rows
-// and a tile is NI = kRows/RPI loads of K plus NI loads of V per lane, all
-// issued before any arithmetic.  Each lane group keeps its own running (max,
-// sum, weighted V) over its rows; groups, then waves, are merged at the end.
+// Work decomposition.  Sparse decode (decode_flow_kernel): the admitted lists
+// of all streams, concatenated, are cut into one equal range per wave; each
+// wave walks its range alone and writes a partial per stream it touches, and a
+// combine kernel merges each stream's partials (log-sum-exp).  Dense decode,
+// and sparse decode over more streams than the balanced kernel holds, cut each
+// stream into chunks of `split` blocks, one work-group of 4 waves per chunk
+// (wave w takes the chunk's tiles w, w+4, ...), merged the same way.  Either
+// way rows are handled in tiles of kRows rows: a key row of D elements is read
+// by LPR lanes with one 128-bit load each (bf16, D=128: 16 lanes), so one load
+// instruction of a wave covers RPI = 64/LPR rows and a tile is NI = kRows/RPI
+// loads of K plus NI loads of V per lane, all issued before any arithmetic,
+// the next tile's loads in flight while the current one is folded in.  Each
+// lane group keeps its own running (max, sum, weighted V) over its rows; the
+// groups are merged at the end of a range or chunk.
 #include "eta_internal.h"
 
 namespace eta {

@@ -11,7 +11,25 @@
 
 #include "eta_internal.h"
 
+namespace eta {
+// Compute units of the current device (a device property, cached per device).
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+}  // namespace eta
+
 namespace {
+using eta::device_cus;
 
 thread_local char g_err[512] = "";
 
@@ -87,20 +105,6 @@ eta_status hip_status(hipError_t e, const char* what) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Compute units of the current device (a device property, cached per device).
-int device_cus() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        n <= 0)
-      n = 256;
-    cached[dev] = n;
-  }
-  return cached[dev];
-}
 
 // Partial slots: one per possible chunk of the flat grid, and for the
 // balanced decode one per wave plus one per stream (its slots w + u).
@@ -381,11 +385,22 @@ eta_status eta_screen_gqa(const eta_cache* c, int32_t group, const float* q,
                     "eta_screen_gqa launch");
 }
 
-// GQA decode workspace: [part_m | part_l | part_acc] per query head and chunk.
-static size_t decode_gqa_ws(long long units_q, int D, int cap_blocks, int split) {
+// GQA decode workspace: [balanced-decode total (256 B) | stream offsets
+// [units+1] | part_m | part_l | part_acc], each 256-byte aligned.  Partial
+// slots: one per query head and chunk of the flat grid; for the balanced
+// decode one per query head and (wave, stream) slot, with at most
+// kMaxFlowWavesPerCU waves per compute unit.
+static size_t decode_gqa_slots(long long units, int group, int cap_blocks, int split) {
   const long long maxc = (cap_blocks + split - 1) / split;
-  const size_t slots = (size_t)units_q * (size_t)maxc;
-  return align256(slots * 4) * 2 + align256(slots * (size_t)D * 4);
+  const long long grid = units * group * maxc;
+  const long long flow = ((long long)eta::kMaxFlowWavesPerCU * device_cus() + units) * group;
+  return (size_t)(grid > flow ? grid : flow);
+}
+
+static size_t decode_gqa_ws(long long units, int group, int D, int cap_blocks, int split) {
+  const size_t slots = decode_gqa_slots(units, group, cap_blocks, split);
+  return 256 + align256((size_t)(units + 1) * 4) + align256(slots * 4) * 2 +
+         align256(slots * (size_t)D * 4);
 }
 
 size_t eta_decode_gqa_workspace_bytes(int32_t batch, int32_t kv_heads, int32_t group,
@@ -394,7 +409,7 @@ size_t eta_decode_gqa_workspace_bytes(int32_t batch, int32_t kv_heads, int32_t g
   if (batch <= 0 || kv_heads <= 0 || group <= 0 || head_dim <= 0 || cap_blocks <= 0 ||
       blocks_per_split <= 0)
     return 256;
-  return decode_gqa_ws((long long)batch * kv_heads * group, head_dim, cap_blocks,
+  return decode_gqa_ws((long long)batch * kv_heads, group, head_dim, cap_blocks,
                        blocks_per_split);
 }
 
@@ -429,11 +444,12 @@ static eta_status decode_gqa_common(const eta_cache* c, int32_t group, const flo
   const int maxc = eta::ceil_div(v.cap_blocks, split);
   if ((long long)maxc * units > kMaxGrid || units * group > kMaxGrid)
     return fail(ETA_ERR_BAD_SHAPE, "grid too large");
-  const size_t need = decode_gqa_ws(units * group, v.D, v.cap_blocks, split);
+  const size_t need = decode_gqa_ws(units, group, v.D, v.cap_blocks, split);
   if (!ws || ws_bytes < need)
     return fail(ETA_ERR_WORKSPACE, "decode workspace %zu bytes < %zu", ws_bytes, need);
-  const size_t slots = (size_t)units * group * maxc;
+  const size_t slots = decode_gqa_slots(units, group, v.cap_blocks, split);
   char* w = static_cast<char*>(ws);
+  const size_t off_parts = 256 + align256((size_t)(units + 1) * 4);
   eta::GqaDecode g;
   g.G = group;
   g.q = q;
@@ -447,10 +463,17 @@ static eta_status decode_gqa_common(const eta_cache* c, int32_t group, const flo
   g.scale = scale;
   g.split = split;
   g.max_chunks = maxc;
-  g.part_m = reinterpret_cast<float*>(w);
-  g.part_l = reinterpret_cast<float*>(w + align256(slots * 4));
-  g.part_acc = reinterpret_cast<float*>(w + 2 * align256(slots * 4));
+  g.part_m = reinterpret_cast<float*>(w + off_parts);
+  g.part_l = reinterpret_cast<float*>(w + off_parts + align256(slots * 4));
+  g.part_acc = reinterpret_cast<float*>(w + off_parts + 2 * align256(slots * 4));
   g.out = out;
+  // Sparse grouped decode at d = 64 runs balanced (equal ranges of all union
+  // blocks per wave) whenever its stream offsets fit in LDS.
+  g.use_flow = !dense && v.D == 64 && units <= eta::kMaxGqaFlowUnits &&
+               units * (long long)v.cap_blocks < 0x7fffffffLL;
+  g.flow_grid = 0;
+  g.flow_start = reinterpret_cast<int*>(w + 256);
+  g.flow_info = reinterpret_cast<int*>(w);
   return hip_status(eta::launch_decode_gqa(v, g, (hipStream_t)stream), "eta_decode_gqa launch");
 }
 

@@ -195,6 +195,20 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Chunk swizzle of staged V rows: the four rows one transposing read takes
+// (keys 2 g + h + 8 j, j = 0..3) land their 32 bytes in distinct banks.
+__device__ __forceinline__ int vrow_swz(int key) { return 2 * ((key >> 3) & 3); }
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane l receives element
+// l % 4 of the 8-byte pieces addressed by lanes 4 j + (l % 16) / 4, j = 0..3
+// (measured lane layout on gfx950).  Returned as raw 64 bits.
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 tr_read(const char* p) {
+  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+  const bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
+  return __builtin_bit_cast(uint2, v);
+}
+
 // Score-tile key of operand row r in 16-key half st of a 32-key tile: with
 // this order, the 8 scores a lane receives (keys 2 (l/16) + st + 8 i) are
 // exactly its 8 contraction slots of the value product.
@@ -213,6 +227,21 @@ struct CacheView {
 };
 
 __host__ __device__ constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// The N admitted (or union) blocks of a balanced decode in wn equal ranges, wn = min(waves, ceil(N / split)),
+// range w = [lo(w), lo(w + 1)), all non-empty as wn <= N.
+struct FlowPlan {
+  int N, wn;
+  __device__ FlowPlan(int n, int waves, int split)
+      : N(n), wn(n == 0 ? 0 : min(waves, ceil_div(n, split))) {}
+  __device__ int lo(int w) const { return (int)((long long)w * N / wn); }
+  // The range holding position p < N.
+  __device__ int range_of(int p) const {
+    int w = (int)((long long)p * wn / N);
+    while (w + 1 < wn && lo(w + 1) <= p) ++w;
+    return w;
+  }
+};
 
 // ---------------------------------------------------------------------------
 // Launchers (defined in the kernel translation units).  Each returns the
@@ -276,8 +305,18 @@ struct GqaDecode {
   float* part_l;    // [B*H*G][max_chunks]
   float* part_acc;  // [B*H*G][max_chunks][D]
   float* out;       // [B*H*G][D]
+  bool use_flow;    // balanced decode: an equal range of all union blocks per wave
+  int flow_grid;    // its one-wave work-groups (set at launch)
+  int* flow_start;  // [B*H + 1] union-block offsets, written by the balanced decode
+  int* flow_info;   // [1] total union blocks N
 };
 constexpr int kMaxGroup = 16;
+// Resident one-wave work-groups per compute unit of the balanced grouped
+// decode are at most this many (8 waves per SIMD); it bounds its partial
+// slots.  The stream count up to which it is used (offsets in LDS).
+constexpr int kMaxFlowWavesPerCU = 32;
+constexpr int kMaxGqaFlowUnits = 6143;
+int device_cus();
 hipError_t launch_screen_gqa(const CacheView& c, int G, const float* q, const float* tau_screen,
                              float z, float scale, int32_t* union_idx, uint32_t* head_mask,
                              int32_t* union_cnt, uint64_t* ctr, uint64_t* words, hipStream_t s);

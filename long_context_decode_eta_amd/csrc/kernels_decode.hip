@@ -433,21 +433,6 @@ __device__ __forceinline__ int stream_blocks(const CacheView& c, const DecodeArg
   return max(0, min(a.active_cnt[u], nb));
 }
 
-// The N admitted blocks in wn equal ranges, wn = min(waves, ceil(N / split)),
-// range w = [lo(w), lo(w + 1)), all non-empty as wn <= N.
-struct FlowPlan {
-  int N, wn;
-  __device__ FlowPlan(int n, int waves, int split)
-      : N(n), wn(n == 0 ? 0 : min(waves, ceil_div(n, split))) {}
-  __device__ int lo(int w) const { return (int)((long long)w * N / wn); }
-  // The range holding position p < N.
-  __device__ int range_of(int p) const {
-    int w = (int)((long long)p * wn / N);
-    while (w + 1 < wn && lo(w + 1) <= p) ++w;
-    return w;
-  }
-};
-
 template <int D, int DT, int MODE>
 __global__ __launch_bounds__(kFlowThreads, 3) void decode_flow_kernel(CacheView c, DecodeArgs a) {
   constexpr int EPL = Elt<DT>::kPer16B;

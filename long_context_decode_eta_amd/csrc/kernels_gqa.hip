@@ -614,6 +614,393 @@ __global__ __launch_bounds__(1024) void combine_gqa_kernel(CacheView c, GqaArgs 
 }
 
 // ---------------------------------------------------------------------------
+// Balanced grouped decode (d = 64).  As the per-head balanced decode does with
+// the admitted lists, the union lists of all KV streams, concatenated in
+// stream order, are cut into equal contiguous ranges, one per wave; a
+// work-group is one wave and holds no state shared with others.  The wave
+// walks its range in 32-key tiles: coalesced 128-bit loads of whole K and V
+// rows into registers (the next tile's loads in flight while the current one
+// is computed), staged as rows in the wave's LDS area (K chunk-swizzled for
+// the score operand, V for the transposing read of the value operand).  Keys
+// that are not to be read (past the range, the stream, or an out-of-range
+// list entry) load the stream's row 0 instead -- finite data -- and are masked
+// out of the softmax, so their weights are exactly zero.  Scores and values of
+// all G heads run on the matrix cores as in the chunked kernel; the partial
+// of (stream segment, head g) goes to slot (w + u) * G + g.  Measured on
+// 32 x 128K, 38% head density: about 6% faster than the chunked kernel.
+template <int D>
+struct GqaFlowShape {
+  static constexpr int NK = D / 32;             // 32-dim slabs (score product)
+  static constexpr int NV = D / 16;             // 16-dim slabs (value product)
+  static constexpr int RB = D * 2;              // bytes per bf16 row
+  static constexpr int LPR = D / 8;             // lanes per row of a load
+  static constexpr int RPI = 64 / LPR;          // rows per load instruction
+  static constexpr int NI = kTileKeys / RPI;    // load instructions per tile and tensor
+  static constexpr int TB = kTileKeys * RB;     // one tensor's tile, bytes
+  static constexpr int StageBytes = 2 * TB;     // K rows | V rows
+};
+
+template <int D, int MODE>
+__global__ __launch_bounds__(64) void decode_gqa_flow_kernel(CacheView c, GqaArgs a) {
+  using Sh = GqaFlowShape<D>;
+  constexpr int NK = Sh::NK, NV = Sh::NV, RB = Sh::RB, LPR = Sh::LPR, RPI = Sh::RPI;
+  constexpr int NI = Sh::NI, TB = Sh::TB;
+  __shared__ __align__(16) char s_stage[Sh::StageBytes];
+  extern __shared__ int s_start[];  // [units + 1]
+  const int units = c.B * c.H, lane = threadIdx.x, G = a.G;
+  // Exclusive prefix sums of the union counts: lane x sums a run of
+  // ceil(units / 64) streams, the runs are scanned across the wave.
+  {
+    const int per = (units + 63) / 64;
+    const int u0 = min(units, lane * per), u1 = min(units, u0 + per);
+    int sum = 0;
+    for (int u = u0; u < u1; ++u) {
+      int T, cnt;
+      gqa_stream(c, a, false, u, &T, &cnt);
+      s_start[u] = cnt;
+      sum += cnt;
+    }
+    int incl = sum;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int y = __shfl_up(incl, off, kWave);
+      if (lane >= off) incl += y;
+    }
+    int off = incl - sum;
+    for (int u = u0; u < u1; ++u) {
+      const int n = s_start[u];
+      s_start[u] = off;
+      off += n;
+    }
+    if (lane == kWave - 1) s_start[units] = off;
+    __syncthreads();
+  }
+  const FlowPlan plan(s_start[units], gridDim.x, a.split);
+  if (blockIdx.x == 0) {  // for the combine
+    for (int u = lane; u <= units; u += kWave) a.flow_start[u] = s_start[u];
+    if (lane == 0) a.flow_info[0] = plan.N;
+  }
+  const int w = blockIdx.x;
+  if (w >= plan.wn) return;
+  const int n = lane & 15, grp = lane >> 4;  // operand layout: row/column n, k group grp
+  const int ri = lane / LPR, cc = lane % LPR;  // load layout: row ri, 16-byte chunk cc
+  const bool whole = c.bs >= kTileKeys;      // every tile lies inside one block
+  const float gk1 = -a.beta * kLog2e;
+  // Value-operand rows of the transposing read (as in the prefill kernel).
+  const int trow0 = tile_key(0, 4 * grp + ((lane & 15) >> 2));
+  const int trow1 = tile_key(1, 4 * grp + ((lane & 15) >> 2));
+  const int tr4 = lane & 3;
+
+  int p = plan.lo(w);
+  const int pend = plan.lo(w + 1);
+  int u = 0;  // the last stream with start[u] <= p (so start[u + 1] > p)
+  {
+    int hi = units - 1;
+    while (u < hi) {
+      const int mid = (u + hi + 1) >> 1;
+      if (s_start[mid] <= p) u = mid; else hi = mid - 1;
+    }
+  }
+  while (p < pend) {
+    const int base = s_start[u];
+    const int i0 = p - base, i1 = min(pend, s_start[u + 1]) - base;  // local blocks
+    const int nblk = i1 - i0;
+    const int T = c.seq_len[u / c.H];
+    const int nb = (T + c.bs - 1) >> c.log2bs;
+    const int32_t* list = a.union_idx + (size_t)u * c.cap_blocks + i0;
+    const uint32_t* hmask = a.head_mask + (size_t)u * c.cap_blocks;
+    const char* kbase = static_cast<const char*>(c.k) + (size_t)u * c.cap * RB;
+    const char* vbase = static_cast<const char*>(c.v) + (size_t)u * c.cap * RB;
+    // Query operand (head n, dims 32 kk + 8 grp + i), scaled, split hi + lo.
+    // Lanes of padding heads (n >= G) load head G-1 and use zeros.
+    bf16x8 qhi[NK], qlo[NK];
+    {
+      const int hn = min(n, G - 1);
+      const float4* qn =
+          reinterpret_cast<const float4*>(a.q + ((size_t)u * G + hn) * D + 8 * grp);
+      const float sc = n < G ? a.scale : 0.f;
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) {
+        const float4 x0 = qn[8 * kk], x1 = qn[8 * kk + 1];
+        const float x8[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float x = x8[i] * sc;
+          const __bf16 h = (__bf16)x;
+          qhi[kk][i] = h;
+          qlo[kk][i] = (__bf16)(x - (float)h);
+        }
+      }
+    }
+    const float tau_n = MODE == ETA_LOGIT_GATED ? a.tau[(size_t)u * G + min(n, G - 1)] : 0.f;
+    // Gate of Eq. 3: sigmoid(beta (S - tau)) = 1 / (1 + 2^(S gk1 + gk0)).
+    const float gk0 = a.beta * kLog2e * tau_n;
+    // Block indices and head masks, 64 per register: lane x holds entry
+    // bb + x in (lst0, hm0) and bb + 64 + x in (lst1, hm1).  The window moves
+    // on by 64 when a tile about to be loaded reaches past it; the tile still
+    // to be computed then lies inside the new window.
+    int bb = 0, lst0, lst1;
+    uint32_t hm0, hm1;
+    auto load_entry = [&](int x, int& j, uint32_t& hm) {
+      j = x < nblk ? list[x] : -1;
+      hm = (unsigned)j < (unsigned)nb ? hmask[j] : 0u;
+    };
+    load_entry(lane, lst0, hm0);
+    load_entry(64 + lane, lst1, hm1);
+    // (block index, head mask) of segment row rr; every lane takes part.
+    auto entry = [&](int rr, int& j, uint32_t& hm) {
+      const int o = (rr >> c.log2bs) - bb;
+      if (whole) {  // the same entry for every lane
+        const int ou = __builtin_amdgcn_readfirstlane(o);
+        const int src0 = ou < 64 ? lst0 : lst1;
+        const int src1 = (int)(ou < 64 ? hm0 : hm1);
+        j = __builtin_amdgcn_readlane(src0, ou & 63);
+        hm = (uint32_t)__builtin_amdgcn_readlane(src1, ou & 63);
+      } else {
+        const int j0 = __shfl(lst0, o & 63, kWave), j1 = __shfl(lst1, o & 63, kWave);
+        const int h0 = __shfl((int)hm0, o & 63, kWave), h1 = __shfl((int)hm1, o & 63, kWave);
+        j = o < 64 ? j0 : j1;
+        hm = (uint32_t)(o < 64 ? h0 : h1);
+      }
+    };
+    const int rows = nblk << c.log2bs;
+    const int ntiles = (rows + kTileKeys - 1) / kTileKeys;
+    // Segment row rr -> absolute key position, or -1.
+    auto key_pos = [&](int rr, int j) {
+      const bool ok = rr < rows && (unsigned)j < (unsigned)nb;
+      const int s = ok ? (j << c.log2bs) + (rr & (c.bs - 1)) : -1;
+      return s < T ? s : -1;
+    };
+    // Coalesced loads of tile t: instruction it reads row it*RPI + ri, bytes
+    // 16 cc .. 16 cc + 15, of K and of V.  Nothing here waits for the data.
+    auto fetch = [&](int t, uint4 (&kr)[NI], uint4 (&vr)[NI]) {
+      const int last = min(((t + 1) * kTileKeys - 1) >> c.log2bs, nblk - 1);
+      if (last >= bb + 128) {  // wave-uniform; once per 64 blocks
+        lst0 = lst1;
+        hm0 = hm1;
+        bb += 64;
+        load_entry(bb + 64 + lane, lst1, hm1);
+      }
+#pragma unroll
+      for (int it = 0; it < NI; ++it) {
+        const int key = it * RPI + ri;
+        const int rr = t * kTileKeys + key;
+        int j;
+        uint32_t hm;
+        entry(rr, j, hm);
+        const size_t row = (size_t)max(key_pos(rr, j), 0) * RB + 16 * cc;
+        kr[it] = ld16_nt(kbase + row);
+        vr[it] = ld16_nt(vbase + row);
+      }
+    };
+    // Registers -> LDS rows (chunk slot cc ^ swizzle).
+    auto stage = [&](const uint4 (&kr)[NI], const uint4 (&vr)[NI]) {
+#pragma unroll
+      for (int it = 0; it < NI; ++it) {
+        const int key = it * RPI + ri;
+        *reinterpret_cast<uint4*>(s_stage + key * RB + 16 * (cc ^ k_swz(key))) = kr[it];
+        *reinterpret_cast<uint4*>(s_stage + TB + key * RB + 16 * (cc ^ vrow_swz(key))) = vr[it];
+      }
+    };
+    floatx4 O[NV];
+#pragma unroll
+    for (int nv = 0; nv < NV; ++nv) O[nv] = floatx4{0.f, 0.f, 0.f, 0.f};
+    float m = -__builtin_inff(), lsum = 0.f;
+    auto compute = [&](int t) {
+      const char* sk = s_stage;
+      const char* sv = s_stage + TB;
+      const int r0 = t * kTileKeys;
+      floatx4 S[2];
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const int key = tile_key(st, n);
+        const char* row = sk + key * RB;
+        const int sw = k_swz(key);
+        S[st] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) {
+          const bf16x8 kv = __builtin_bit_cast(
+              bf16x8, *reinterpret_cast<const uint4*>(row + 16 * ((4 * kk + grp) ^ sw)));
+          S[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qhi[kk], S[st], 0, 0, 0);
+          S[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qlo[kk], S[st], 0, 0, 0);
+        }
+      }
+      // Logits, masks and the running max of head n.  Score i of half st is
+      // key 2 grp + st + 8 i of the tile.
+      float lg[8];
+      float tmax = -__builtin_inff();
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int rr = r0 + 2 * grp + st + 8 * i;
+          int j;
+          uint32_t hm;
+          entry(rr, j, hm);
+          const int s = key_pos(rr, j);
+          const bool on = (s >= 0) & ((hm >> n) & 1u);
+          const float d = S[st][i];
+          float lv = d;
+          if (MODE == ETA_LOGIT_GATED && s != T - 1)
+            lv = d * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(fmaf(d, gk1, gk0)));
+          lg[4 * st + i] = on ? lv : -__builtin_inff();
+          tmax = fmaxf(tmax, lg[4 * st + i]);
+        }
+      }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+      // Lazy rescaling, as in the chunked kernel.
+      if (__ballot(tmax > m + kLazyRaise) != 0ull) {
+        const float mn = fmaxf(m, tmax);
+        const float alpha =
+            mn == -__builtin_inff() ? 1.f : __builtin_amdgcn_exp2f((m - mn) * kLog2e);
+        lsum *= alpha;
+        // O rows are heads 4*grp + i: their factors come from lanes 4*grp + i.
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float al = __shfl(alpha, 4 * grp + i, kWave);
+#pragma unroll
+          for (int nv = 0; nv < NV; ++nv) O[nv][i] *= al;
+        }
+        m = mn;
+      }
+      const float ms2 = m == -__builtin_inff() ? 0.f : m * kLog2e;
+      float pw[8], psum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        pw[i] = __builtin_amdgcn_exp2f(fmaf(lg[i], kLog2e, -ms2));
+        psum += pw[i];
+      }
+      lsum += psum;
+      uint32_t ph[4], pl[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) split_hi_lo(pw[2 * i], pw[2 * i + 1], ph[i], pl[i]);
+      const bf16x8 phi = __builtin_bit_cast(bf16x8, make_uint4(ph[0], ph[1], ph[2], ph[3]));
+      const bf16x8 plo = __builtin_bit_cast(bf16x8, make_uint4(pl[0], pl[1], pl[2], pl[3]));
+      // Value operand (dim 16 nv + n, slots 8 grp + 4 h + j) by two
+      // transposing reads of the staged V rows.
+#pragma unroll
+      for (int nv = 0; nv < NV; ++nv) {
+        const int cidx = 2 * nv + (tr4 >> 1);
+        const uint2 v0 = tr_read(sv + trow0 * RB + 16 * (cidx ^ vrow_swz(trow0)) + 8 * (tr4 & 1));
+        const uint2 v1 = tr_read(sv + trow1 * RB + 16 * (cidx ^ vrow_swz(trow1)) + 8 * (tr4 & 1));
+        const bf16x8 vb = __builtin_bit_cast(bf16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
+        O[nv] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi, vb, O[nv], 0, 0, 0);
+        O[nv] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo, vb, O[nv], 0, 0, 0);
+      }
+    };
+    // The next tile's loads are issued once the current one is staged, so
+    // they are in flight during its compute.
+    uint4 kr[NI], vr[NI];
+    fetch(0, kr, vr);
+    for (int t = 0; t < ntiles; ++t) {
+      stage(kr, vr);
+      if (t + 1 < ntiles) fetch(t + 1, kr, vr);
+      wave_lds_sync();
+      compute(t);
+      wave_lds_sync();
+    }
+    // Head n's sum over the 4 lane groups (they share the reference max).
+    lsum += __shfl_xor(lsum, 16, kWave);
+    lsum += __shfl_xor(lsum, 32, kWave);
+    const size_t slot = ((size_t)w + u) * G;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = 4 * grp + i;
+      if (h < G) {
+#pragma unroll
+        for (int nv = 0; nv < NV; ++nv) a.part_acc[(slot + h) * D + 16 * nv + n] = O[nv][i];
+      }
+    }
+    if (grp == 0 && n < G) {
+      a.part_m[slot + n] = m;
+      a.part_l[slot + n] = lsum;
+    }
+    p = base + i1;
+    if (p < pend)  // next non-empty stream
+      do ++u; while (s_start[u + 1] <= p);
+  }
+}
+
+// Combine of the balanced grouped decode: one work-group per query head; its
+// partials sit in slots (w + u) * G + g for the ranges w that cover stream u
+// (log-sum-exp in one pass, 16 waves, 8 partials in flight per wave,
+// fixed-order wave merge); zeros for empty streams.
+template <int D>
+__global__ __launch_bounds__(1024) void combine_gqa_flow_kernel(CacheView c, GqaArgs a) {
+  constexpr int W = 16, INF = 8, CPL = D / kWave;
+  __shared__ float s_acc[W][D];
+  __shared__ float s_ml[W][2];
+  const int uq = blockIdx.x, G = a.G, u = uq / G, g = uq % G;
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+  const int p0 = a.flow_start[u], p1 = a.flow_start[u + 1];
+  if (p1 <= p0) {
+    if (t < D) a.out[(size_t)uq * D + t] = 0.f;
+    return;
+  }
+  const FlowPlan plan(a.flow_info[0], a.flow_grid, a.split);
+  const int wf = plan.range_of(p0), wl = plan.range_of(p1 - 1);
+  const int nch = wl - wf + 1;
+  const size_t slot0 = ((size_t)wf + u) * G + g;
+  const float* pm = a.part_m + slot0;
+  const float* pl = a.part_l + slot0;
+  const float* pa = a.part_acc + slot0 * D + lane * CPL;
+  float m = -__builtin_inff(), l = 0.f, acc[CPL];
+#pragma unroll
+  for (int e = 0; e < CPL; ++e) acc[e] = 0.f;
+  for (int base = wave; base < nch; base += W * INF) {
+    float mc[INF], lc[INF], ac[INF][CPL];
+#pragma unroll
+    for (int i = 0; i < INF; ++i) {
+      const int ch = base + W * i;
+      const bool ok = ch < nch;
+      const size_t o = (size_t)ch * G;
+      mc[i] = ok ? pm[o] : -__builtin_inff();
+      lc[i] = ok ? pl[o] : 0.f;
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) ac[i][e] = ok ? pa[o * D + e] : 0.f;
+    }
+    float mx = m;
+#pragma unroll
+    for (int i = 0; i < INF; ++i) mx = fmaxf(mx, mc[i]);
+    const float ms = (mx == -__builtin_inff()) ? 0.f : mx;
+    const float alpha = __builtin_amdgcn_exp2f((m - ms) * kLog2e);
+    l *= alpha;
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) acc[e] *= alpha;
+#pragma unroll
+    for (int i = 0; i < INF; ++i) {
+      const float wgt = __builtin_amdgcn_exp2f((mc[i] - ms) * kLog2e);
+      l = fmaf(wgt, lc[i], l);
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) acc[e] = fmaf(wgt, ac[i][e], acc[e]);
+    }
+    m = mx;
+  }
+#pragma unroll
+  for (int e = 0; e < CPL; ++e) s_acc[wave][lane * CPL + e] = acc[e];
+  if (lane == 0) {
+    s_ml[wave][0] = m;
+    s_ml[wave][1] = l;
+  }
+  __syncthreads();
+  if (t < D) {
+    float mm = s_ml[0][0], ll = s_ml[0][1], aa = s_acc[0][t];
+    for (int w2 = 1; w2 < W; ++w2) {
+      const float m2 = s_ml[w2][0], l2 = s_ml[w2][1], a2 = s_acc[w2][t];
+      const float mx = fmaxf(mm, m2);
+      const float ms = (mx == -__builtin_inff()) ? 0.f : mx;
+      const float s1 = __builtin_amdgcn_exp2f((mm - ms) * kLog2e);
+      const float s2 = __builtin_amdgcn_exp2f((m2 - ms) * kLog2e);
+      ll = ll * s1 + l2 * s2;
+      aa = aa * s1 + a2 * s2;
+      mm = mx;
+    }
+    a.out[(size_t)uq * D + t] = aa / ll;
+  }
+}
+
+// ---------------------------------------------------------------------------
 template <int D>
 static hipError_t screen_gqa_t(const CacheView& c, int G, const float* q, const float* ts,
                                float z, float scale, int32_t* idx, uint32_t* mask, int32_t* cnt,
@@ -642,9 +1029,36 @@ size_t gqa_decode_lds_bytes(int D, int split) {
   return stage + (size_t)split * 8;
 }
 
+// Work-groups of the balanced grouped decode: as many as are resident at once
+// (one wave each; registers and LDS set the count).
+template <int D, int MODE>
+static int gqa_flow_grid(int units) {
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &per_cu, reinterpret_cast<const void*>(decode_gqa_flow_kernel<D, MODE>), 64,
+          (size_t)(units + 1) * 4) != hipSuccess ||
+      per_cu < 1)
+    per_cu = 1;
+  return device_cus() * min(per_cu, kMaxFlowWavesPerCU);
+}
+
 template <int D, int MODE, bool DENSE>
 static hipError_t decode_gqa_t(const CacheView& c, const GqaDecode& g, hipStream_t s) {
   const GqaArgs& a = g;
+  const int units = c.B * c.H;
+  if constexpr (!DENSE && D == 64) {
+    if (g.use_flow) {
+      GqaArgs f = g;
+      f.flow_grid = gqa_flow_grid<D, MODE>(units);
+      hipLaunchKernelGGL((decode_gqa_flow_kernel<D, MODE>), dim3(f.flow_grid), dim3(64),
+                         (size_t)(units + 1) * 4, s, c, f);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((combine_gqa_flow_kernel<D>), dim3(units * g.G), dim3(1024), 0, s, c,
+                         f);
+      return hipGetLastError();
+    }
+  }
   const long long grid = (long long)g.max_chunks * c.B * c.H;
   hipLaunchKernelGGL((decode_gqa_kernel<D, MODE, DENSE>), dim3((unsigned)grid),
                      dim3(GqaShape<D>::W * 64),

@@ -24,20 +24,6 @@ namespace eta {
 
 constexpr int kPrefillRows = 64;  // queries per work-group
 
-// Chunk swizzle of staged V rows: the four rows one transposing read takes
-// (keys 2 g + h + 8 j, j = 0..3) land their 32 bytes in distinct banks.
-__device__ __forceinline__ int vrow_swz(int key) { return 2 * ((key >> 3) & 3); }
-
-// ds_read_b64_tr_b16: within each group of 16 lanes, lane l receives element
-// l % 4 of the 8-byte pieces addressed by lanes 4 j + (l % 16) / 4, j = 0..3
-// (measured lane layout on gfx950).  Returned as raw 64 bits.
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ uint2 tr_read(const char* p) {
-  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-  const bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
-  return __builtin_bit_cast(uint2, v);
-}
-
 template <bool B>
 struct MaskTag {
   static constexpr bool value = B;

@@ -65,6 +65,20 @@ def test_gqa_ragged_edges(G, D, block):
     note(f"  D_head {st['d_head']:.3f} D_union {st['d_union']:.3f} out_rel {st['out_rel']:.2e}")
 
 
+def test_gqa_more_streams_than_the_balanced_decode_holds():
+    # 6400 KV streams of 1..64 tokens: more than the balanced grouped decode
+    # keeps offsets for, so eta_decode_gqa runs its chunked kernel instead.
+    w = synth.make("gqa_tiny", seed=23, T=(1, 64), B=1600, H=4, cap=64, pad="nan", block=16,
+                   D=64, G=2)
+    to_gpu(w)
+    cache = make_cache(w)
+    assert w.B * w.H > 6143
+    c = torch.linspace(0.2, 1.4, w.Hq, device="cuda")
+    g = run_gpu_gqa(cache, w.G, w.q, bias_or_c=c, z=1.0, scale=w.scale, mode=eb.GATED, split=2)
+    st = check_gqa(w, g, W=None, bias_or_c=c, z=1.0, scale=w.scale, mode=eb.GATED)
+    note(f"  D_head {st['d_head']:.3f} D_union {st['d_union']:.3f} out_rel {st['out_rel']:.2e}")
+
+
 @pytest.mark.parametrize("tau", [math.inf, -math.inf])
 def test_gqa_threshold_extremes(tau):
     w = to_gpu(synth.make("gqa_tiny", seed=5, T=(100, 3000), B=3, cap=3000, block=32))

@@ -923,12 +923,12 @@ __global__ __launch_bounds__(64) void decode_gqa_flow_kernel(CacheView c, GqaArg
 }
 
 // Combine of the balanced grouped decode: one work-group per query head; its
-// partials sit in slots (w + u) * G + g for the ranges w that cover stream u
-// (log-sum-exp in one pass, 16 waves, 8 partials in flight per wave,
-// fixed-order wave merge); zeros for empty streams.
+// partials sit in slots (w + u) * G + g for the ranges w that cover stream u,
+// a few tens at most (log-sum-exp in one pass, 4 waves, 4 partials in flight
+// per wave, fixed-order wave merge); zeros for empty streams.
 template <int D>
-__global__ __launch_bounds__(1024) void combine_gqa_flow_kernel(CacheView c, GqaArgs a) {
-  constexpr int W = 16, INF = 8, CPL = D / kWave;
+__global__ __launch_bounds__(256) void combine_gqa_flow_kernel(CacheView c, GqaArgs a) {
+  constexpr int W = 4, INF = 4, CPL = D / kWave;
   __shared__ float s_acc[W][D];
   __shared__ float s_ml[W][2];
   const int uq = blockIdx.x, G = a.G, u = uq / G, g = uq % G;
@@ -1054,7 +1054,7 @@ static hipError_t decode_gqa_t(const CacheView& c, const GqaDecode& g, hipStream
                          (size_t)(units + 1) * 4, s, c, f);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((combine_gqa_flow_kernel<D>), dim3(units * g.G), dim3(1024), 0, s, c,
+      hipLaunchKernelGGL((combine_gqa_flow_kernel<D>), dim3(units * g.G), dim3(256), 0, s, c,
                          f);
       return hipGetLastError();
     }

@@ -619,7 +619,7 @@ def gqa_bench(torch, np, eb, synth, steps, warmup, seed, rhos=(0.38, 0.25, 0.10)
     if "0.38" in res:
         r = res["0.38"]
         ach = r["decode_bytes"] / (r["decode_ms"] * 1e-3) / 1e9
-        roofline = {"bound": "hbm", "kernel": "eta_decode_gqa (decode + combine kernels), 38% head",
+        roofline = {"bound": "hbm", "kernel": "eta_decode_gqa (balanced decode + combine kernels), 38% head",
                     "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(ach / HBM_PEAK_GBS, 4),
                     "traffic": counters_traffic(GQA_COUNTERS, GQA_SRC, "gqa128k"),

@@ -254,8 +254,12 @@ eta_status eta_screen_gqa(const eta_cache* c, int32_t group, const float* q,
  * once for its whole group; query head kv * group + g attends over the keys of
  * the blocks whose head_mask bit g is set, with the logits of eta_decode
  * (Eq. 3, its own tau_gate; the query's own key is never gated), normalised
- * over its own admitted set.  Chunks of blocks_per_split union blocks, partial
- * results per query head, log-sum-exp combine; out is device
+ * over its own admitted set.  At head_dim 64 with at most 6143 KV streams
+ * the union blocks of all streams, taken in order, are cut into
+ * min(resident waves, ceil(N / blocks_per_split)) equal ranges, one per wave
+ * (N = total union blocks); otherwise into chunks of blocks_per_split union
+ * blocks of one stream.  Partial results per query head, log-sum-exp combine;
+ * out is device
  * [batch][H_kv * group][head_dim] float32, zeros for T_b == 0.
  * Requires kv_dtype == ETA_DT_BF16: the scores and value sums run on the
  * matrix cores as bf16 products with float32 accumulation, the query and the

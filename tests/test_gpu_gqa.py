@@ -48,7 +48,7 @@ def test_gqa_tiny(mode, split):
 LENS = [0, 1, 15, 16, 17, 700, 1024, 2053]
 
 
-@pytest.mark.parametrize("G", [1, 2, 8, 16])
+@pytest.mark.parametrize("G", [1, 2, 3, 8, 16])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("block", [4, 16, 64, 128])
 def test_gqa_ragged_edges(G, D, block):

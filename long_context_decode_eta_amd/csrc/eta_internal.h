@@ -199,6 +199,26 @@ __device__ __forceinline__ void wave_lds_sync() {
 // (keys 2 g + h + 8 j, j = 0..3) land their 32 bytes in distinct banks.
 __device__ __forceinline__ int vrow_swz(int key) { return 2 * ((key >> 3) & 3); }
 
+// Tiles of 32 rows of D bf16 staged as rows (K with the chunk swizzle
+// tile_kswz, V with vrow_swz) and read as MFMA operands (K by 128-bit reads,
+// V by the transposing read).  The LDS of gfx950 has 64 four-byte banks and
+// serves a 128-bit read 16 lanes at a time and a 64-bit read 32 lanes at a
+// time (measured: the bank-conflict counter follows this model exactly).
+// With 128-byte rows (D = 64) the row's parity picks the bank half, and the
+// rows one pass reads all have the same parity, so row r is stored at
+// tile_row(r) = r ^ bit 1 of r, which puts half of each pass in either half;
+// the K swizzle then takes bit 2 of the key, so the chunks within a half are
+// distinct.  Conflict-free for the staging writes and both operand reads.
+// 256-byte rows (D = 128) keep the plain order and k_swz.
+template <int D>
+__device__ __forceinline__ int tile_row(int key) {
+  return D == 64 ? key ^ ((key >> 1) & 1) : key;
+}
+template <int D>
+__device__ __forceinline__ int tile_kswz(int key) {
+  return D == 64 ? (((key >> 3) & 3) ^ (((key >> 2) & 1) << 2)) : k_swz(key);
+}
+
 // ds_read_b64_tr_b16: within each group of 16 lanes, lane l receives element
 // l % 4 of the 8-byte pieces addressed by lanes 4 j + (l % 16) / 4, j = 0..3
 // (measured lane layout on gfx950).  Returned as raw 64 bits.

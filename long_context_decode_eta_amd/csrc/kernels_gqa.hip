@@ -798,8 +798,9 @@ __global__ __launch_bounds__(64) void decode_gqa_flow_kernel(CacheView c, GqaArg
 #pragma unroll
       for (int it = 0; it < NI; ++it) {
         const int key = it * RPI + ri;
-        *reinterpret_cast<uint4*>(s_stage + key * RB + 16 * (cc ^ k_swz(key))) = kr[it];
-        *reinterpret_cast<uint4*>(s_stage + TB + key * RB + 16 * (cc ^ vrow_swz(key))) = vr[it];
+        const int row = tile_row<D>(key) * RB;
+        *reinterpret_cast<uint4*>(s_stage + row + 16 * (cc ^ tile_kswz<D>(key))) = kr[it];
+        *reinterpret_cast<uint4*>(s_stage + TB + row + 16 * (cc ^ vrow_swz(key))) = vr[it];
       }
     };
     floatx4 O[NV];
@@ -814,8 +815,8 @@ __global__ __launch_bounds__(64) void decode_gqa_flow_kernel(CacheView c, GqaArg
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         const int key = tile_key(st, n);
-        const char* row = sk + key * RB;
-        const int sw = k_swz(key);
+        const char* row = sk + tile_row<D>(key) * RB;
+        const int sw = tile_kswz<D>(key);
         S[st] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < NK; ++kk) {
@@ -882,8 +883,10 @@ __global__ __launch_bounds__(64) void decode_gqa_flow_kernel(CacheView c, GqaArg
 #pragma unroll
       for (int nv = 0; nv < NV; ++nv) {
         const int cidx = 2 * nv + (tr4 >> 1);
-        const uint2 v0 = tr_read(sv + trow0 * RB + 16 * (cidx ^ vrow_swz(trow0)) + 8 * (tr4 & 1));
-        const uint2 v1 = tr_read(sv + trow1 * RB + 16 * (cidx ^ vrow_swz(trow1)) + 8 * (tr4 & 1));
+        const uint2 v0 = tr_read(sv + tile_row<D>(trow0) * RB + 16 * (cidx ^ vrow_swz(trow0)) +
+                                 8 * (tr4 & 1));
+        const uint2 v1 = tr_read(sv + tile_row<D>(trow1) * RB + 16 * (cidx ^ vrow_swz(trow1)) +
+                                 8 * (tr4 & 1));
         const bf16x8 vb = __builtin_bit_cast(bf16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
         O[nv] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi, vb, O[nv], 0, 0, 0);
         O[nv] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo, vb, O[nv], 0, 0, 0);

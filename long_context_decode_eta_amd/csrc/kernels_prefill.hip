@@ -109,8 +109,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     for (int p = 0; p < KP; ++p) {
       const int e = tid + 256 * p;
       const int key = e / LPR;
-      *reinterpret_cast<uint4*>(sk + key * RB + 16 * ((e % LPR) ^ k_swz(key))) = kr[p];
-      *reinterpret_cast<uint4*>(sv + key * RB + 16 * ((e % LPR) ^ vrow_swz(key))) = vr[p];
+      const int row = tile_row<D>(key) * RB;
+      *reinterpret_cast<uint4*>(sk + row + 16 * ((e % LPR) ^ tile_kswz<D>(key))) = kr[p];
+      *reinterpret_cast<uint4*>(sv + row + 16 * ((e % LPR) ^ vrow_swz(key))) = vr[p];
     }
   };
 
@@ -137,8 +138,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       const int key = tile_key(st, n);
-      const char* row = sk + key * RB;
-      const int sw = k_swz(key);
+      const char* row = sk + tile_row<D>(key) * RB;
+      const int sw = tile_kswz<D>(key);
       S[st] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk) {
@@ -208,8 +209,10 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int nv = 0; nv < NV; ++nv) {
       const int c = 2 * nv + (tr4 >> 1);
-      const uint2 v0 = tr_read(sv + trow0 * RB + 16 * (c ^ vrow_swz(trow0)) + 8 * (tr4 & 1));
-      const uint2 v1 = tr_read(sv + trow1 * RB + 16 * (c ^ vrow_swz(trow1)) + 8 * (tr4 & 1));
+      const uint2 v0 =
+          tr_read(sv + tile_row<D>(trow0) * RB + 16 * (c ^ vrow_swz(trow0)) + 8 * (tr4 & 1));
+      const uint2 v1 =
+          tr_read(sv + tile_row<D>(trow1) * RB + 16 * (c ^ vrow_swz(trow1)) + 8 * (tr4 & 1));
       const bf16x8 vb = __builtin_bit_cast(bf16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
       O[nv] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi, vb, O[nv], 0, 0, 0);
       O[nv] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo, vb, O[nv], 0, 0, 0);

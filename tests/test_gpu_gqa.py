@@ -45,6 +45,17 @@ def test_gqa_tiny(mode, split):
     assert 0.0 < st["d_head"] < st["d_union"] < 1.0
 
 
+@pytest.mark.parametrize("z", [0.0, math.inf])
+def test_gqa_moment_weight(z):
+    w = to_gpu(synth.make("gqa_tiny", seed=22))
+    cache = make_cache(w)
+    c = w.tau_const
+    g = run_gpu_gqa(cache, w.G, w.q, bias_or_c=c, z=z, scale=w.scale, split=4)
+    st = check_gqa(w, g, W=None, bias_or_c=c, z=z, scale=w.scale, mode=eb.GATED)
+    note(f"  z {z} D_head {st['d_head']:.3f} D_union {st['d_union']:.3f} out_rel {st['out_rel']:.2e}")
+    assert 0.0 < st["d_head"] <= st["d_union"] <= 1.0
+
+
 LENS = [0, 1, 15, 16, 17, 700, 1024, 2053]
 
 

@@ -72,6 +72,19 @@ def test_tiny_workload(mode, split):
     assert 0.0 < st["density"] < 1.0
 
 
+@pytest.mark.parametrize("z", [0.0, 0.5, 3.0, math.inf])
+def test_moment_weight(z):
+    # z = 0 keeps only <q, mu> (capped by the ceiling), z = inf only the ceiling;
+    # the masks move with z and must follow the oracle at each.
+    w = to_gpu(synth.make("tiny", seed=77))
+    cache = make_cache(w)
+    g = run_gpu(cache, w.q, bias_or_c=w.tau_const, z=z, scale=w.scale, split=5)
+    st = check_against_oracle(w, g, cache, W=None, bias_or_c=w.tau_const, z=z, scale=w.scale,
+                              mode=eb.GATED)
+    note(f"  z {z} density {st['density']:.3f} out_rel {st['out_rel']:.2e} flips {st['flips']}")
+    assert 0.0 < st["density"] <= 1.0
+
+
 LENS = [0, 1, 3, 127, 128, 129, 700, 1024]
 
 

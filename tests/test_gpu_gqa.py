@@ -56,6 +56,16 @@ def test_gqa_moment_weight(z):
     assert 0.0 < st["d_head"] <= st["d_union"] <= 1.0
 
 
+@pytest.mark.parametrize("beta", [0.25, 50.0])
+def test_gqa_gate_steepness(beta):
+    w = to_gpu(synth.make("gqa_tiny", seed=23))
+    cache = make_cache(w)
+    c = w.tau_const
+    g = run_gpu_gqa(cache, w.G, w.q, bias_or_c=c, z=w.z, scale=w.scale, beta=beta, split=4)
+    st = check_gqa(w, g, W=None, bias_or_c=c, z=w.z, scale=w.scale, mode=eb.GATED, beta=beta)
+    note(f"  beta {beta} out_rel {st['out_rel']:.2e}")
+
+
 LENS = [0, 1, 15, 16, 17, 700, 1024, 2053]
 
 

@@ -85,6 +85,17 @@ def test_moment_weight(z):
     assert 0.0 < st["density"] <= 1.0
 
 
+@pytest.mark.parametrize("beta", [0.25, 50.0])
+def test_gate_steepness(beta):
+    # A soft gate (beta 0.25) and a nearly hard one (beta 50) around tau.
+    w = to_gpu(synth.make("tiny", seed=78))
+    cache = make_cache(w)
+    g = run_gpu(cache, w.q, bias_or_c=w.tau_const, z=w.z, scale=w.scale, beta=beta, split=3)
+    st = check_against_oracle(w, g, cache, W=None, bias_or_c=w.tau_const, z=w.z,
+                              scale=w.scale, mode=eb.GATED, beta=beta)
+    note(f"  beta {beta} out_rel {st['out_rel']:.2e}")
+
+
 LENS = [0, 1, 3, 127, 128, 129, 700, 1024]
 
 

@@ -68,6 +68,17 @@ def test_prefill_small(D, G, T):
     note(f"  out rel {worst:.2e}, dens abs {derr:.2e}, mean dens {o_dens.mean():.3f}")
 
 
+@pytest.mark.parametrize("beta", [0.25, 50.0])
+def test_prefill_gate_steepness(beta):
+    w = synth.make_prefill(seed=31, B=2, H=2, G=4, D=64, T=150)
+    g_out, g_dens = run_gpu(w, beta=beta)
+    o_out, o_dens = oracle.prefill(synth.kv_numpy(w.q), synth.kv_numpy(w.k),
+                                   synth.kv_numpy(w.v), w.tau.numpy(), 4, beta=beta,
+                                   scale=w.scale)
+    worst, derr = compare(g_out, g_dens, o_out, o_dens)
+    note(f"  beta {beta}: out rel {worst:.2e}, dens abs {derr:.2e}, mean dens {o_dens.mean():.3f}")
+
+
 @pytest.mark.parametrize("tau", [math.inf, -math.inf])
 def test_prefill_threshold_extremes(tau):
     w = synth.make_prefill(seed=3, B=1, H=2, G=2, D=64, T=150)

@@ -86,6 +86,16 @@ def test_gqa_ragged_edges(G, D, block):
     note(f"  D_head {st['d_head']:.3f} D_union {st['d_union']:.3f} out_rel {st['out_rel']:.2e}")
 
 
+def test_gqa_balanced_decode_at_its_stream_limit():
+    # 6143 KV streams, the most the balanced grouped decode keeps offsets for.
+    w = to_gpu(synth.make("gqa_tiny", seed=31, T=(1, 64), B=6143, H=1, G=2, cap=64, block=16))
+    cache = make_cache(w)
+    c = torch.tensor([0.8, 1.2], device="cuda")
+    g = run_gpu_gqa(cache, 2, w.q, bias_or_c=c, z=w.z, scale=w.scale, split=2)
+    st = check_gqa(w, g, W=None, bias_or_c=c, z=w.z, scale=w.scale, mode=eb.GATED)
+    note(f"  D_head {st['d_head']:.3f} D_union {st['d_union']:.3f} out_rel {st['out_rel']:.2e}")
+
+
 def test_gqa_more_streams_than_the_balanced_decode_holds():
     # 6400 KV streams of 1..64 tokens: more than the balanced grouped decode
     # keeps offsets for, so eta_decode_gqa runs its chunked kernel instead.

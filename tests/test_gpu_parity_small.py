@@ -215,6 +215,19 @@ def test_balanced_decode_many_short_streams():
     note(f"  density {st['density']:.3f} out_rel {st['out_rel']:.2e}")
 
 
+def test_balanced_decode_at_its_stream_limit():
+    # 8191 streams, the most the balanced decode keeps offsets for (32 KiB of
+    # LDS per work-group): it still runs, and every stream matches the oracle.
+    w = to_gpu(synth.make("ragged", seed=29, T=(1, 64), B=8191, H=1, D=64, cap=64, block=16,
+                          pad="nan"))
+    cache = make_cache(w)
+    c = torch.full((1,), 1.2, device="cuda")
+    g = run_gpu(cache, w.q, bias_or_c=c, z=w.z, scale=w.scale, split=2)
+    st = check_against_oracle(w, g, cache, W=None, bias_or_c=c, z=w.z, scale=w.scale,
+                              mode=eb.GATED)
+    note(f"  density {st['density']:.3f} out_rel {st['out_rel']:.2e}")
+
+
 @pytest.mark.parametrize("split", [1, 8])
 def test_more_streams_than_the_balanced_decode_holds(split):
     # 8192 streams: more than the balanced decode keeps offsets for, so

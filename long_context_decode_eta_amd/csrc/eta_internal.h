@@ -142,20 +142,6 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
-template <int N>
-__device__ __forceinline__ float group_max(float x) {
-  if constexpr (N >= 2) x = fmaxf(x, dpp<kQuadXor1>(x));
-  if constexpr (N >= 4) x = fmaxf(x, dpp<kQuadXor2>(x));
-  if constexpr (N == 8) x = fmaxf(x, dpp<kHalfMirror>(x));
-  if constexpr (N >= 16) {
-    x = fmaxf(x, dpp<kRowMirror>(x));
-    x = fmaxf(x, dpp<kHalfMirror>(x));
-  }
-  if constexpr (N >= 32) x = max_xor16(x);
-  if constexpr (N >= 64) x = max_xor32(x);
-  return x;
-}
-
 // ---------------------------------------------------------------------------
 // Matrix-core tiles (grouped-query decode, gated prefill).  A 32-key tile of K
 // and V passes through LDS: K rows as stored with their 16-byte chunks

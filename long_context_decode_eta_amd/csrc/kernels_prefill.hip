@@ -8,11 +8,12 @@
 // the forward pass of prefill and training; decode (one query against a
 // cache) is the block-sparse path of the other kernels.
 //
-// One work-group of 4 waves takes 64 consecutive queries of one query head;
-// wave w owns queries t0 + 16 w .. + 15.  The keys 0 .. t0 + 63 are walked in
-// 32-key tiles.  A tile is loaded once for the 4 waves (coalesced 128-bit
-// reads by all 256 threads, the next tile's loads in flight while the
-// current one is computed) and staged in LDS as rows (chunk-swizzled),
+// One work-group of 8 waves (d 64) or 4 waves (d 128) takes 16 consecutive
+// queries of one query head per wave; wave w owns queries t0 + 16 w .. + 15.
+// The keys 0 .. t0 + rows - 1 are walked in 32-key tiles.  A tile is loaded
+// once for all waves (coalesced 128-bit reads by 256 threads, the next
+// tile's loads in flight while the current one is computed) and staged in
+// LDS as rows (chunk-swizzled),
 // double buffered, one barrier per tile; the value product reads V with the
 // transposing LDS read.  Each wave then computes, on the matrix
 // cores, S^T = K_tile Q_w^T (queries as the 16 columns; q is bf16 as given)
@@ -22,7 +23,6 @@
 
 namespace eta {
 
-constexpr int kPrefillRows = 64;  // queries per work-group
 
 template <bool B>
 struct MaskTag {
@@ -39,7 +39,11 @@ struct PrefillShape {
   static constexpr int NV = D / 16;                  // 16-dim slabs of the value product
   static constexpr int RB = D * 2;                   // bytes per bf16 row
   static constexpr int LPR = D / 8;                  // threads per row in a coalesced load
-  static constexpr int KP = kTileKeys * LPR / 256;   // K (and V) loads per thread per tile
+  // Queries per work-group (16 per wave): 128 at d 64, so each staged K/V tile
+  // serves 8 waves; 64 at d 128, whose registers leave room for fewer waves.
+  static constexpr int Rows = D == 64 ? 128 : 64;
+  static constexpr int Threads = Rows / 16 * 64;
+  static constexpr int KP = kTileKeys * LPR / 256;   // K (and V) loads per loading thread per tile
   static constexpr int KBytes = kTileKeys * RB;
   static constexpr int VBytes = kTileKeys * RB;
   static constexpr int StageBytes = KBytes + VBytes;
@@ -47,18 +51,18 @@ struct PrefillShape {
 };
 
 template <int D>
-__global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(PrefillShape<D>::Threads) void prefill_kernel(PrefillArgs a) {
   using Sh = PrefillShape<D>;
   constexpr int NK = Sh::NK, NV = Sh::NV, RB = Sh::RB, LPR = Sh::LPR, KP = Sh::KP;
   __shared__ __align__(16) char s_stage[2][Sh::StageBytes];
 
   const int T = a.T;
   const int units = a.B * a.Hq;
-  const int ntq = ceil_div(T, kPrefillRows);
+  const int ntq = ceil_div(T, Sh::Rows);
   const int tq = ntq - 1 - (int)(blockIdx.x / units);  // longest query tiles first
   const int uq = blockIdx.x % units;
   const int b = uq / a.Hq, kvh = (uq % a.Hq) / a.G;
-  const int t0 = tq * kPrefillRows;
+  const int t0 = tq * Sh::Rows;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, tid = threadIdx.x;
   const int n = lane & 15, grp = lane >> 4;
   const int tw = t0 + 16 * wave;  // the wave's first query
@@ -84,7 +88,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   const float sl2 = a.scale * kLog2e;
   const float lazy_raw = kLazyRaise / a.scale;
 
-  const int kend = min(T, t0 + kPrefillRows);  // keys this work-group needs
+  const int kend = min(T, t0 + Sh::Rows);  // keys this work-group needs
   const int ntiles = ceil_div(kend, kTileKeys);
 
   // Cooperative tile loads: K and V as (key, 16-byte chunk) pairs, D/8
@@ -92,7 +96,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   // causally masked).  Both are staged as rows; V's value-product operand is
   // taken with the transposing LDS read, so no thread repacks V.
   uint4 kr[KP], vr[KP];
+  // The first 256 threads load and stage each tile.
   auto fetch = [&](int j) {
+    if (Sh::Threads > 256 && tid >= 256) return;
     const int s0 = j * kTileKeys;
 #pragma unroll
     for (int p = 0; p < KP; ++p) {
@@ -103,6 +109,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     }
   };
   auto stage = [&](auto buf_tag) {
+    if (Sh::Threads > 256 && tid >= 256) return;
     char* sk = s_stage[decltype(buf_tag)::value];
     char* sv = sk + Sh::KBytes;
 #pragma unroll
@@ -260,13 +267,16 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   if (a.dens && grp == 0 && tn < T) a.dens[(size_t)uq * T + tn] = gsum / (float)(tn + 1);
 }
 
-hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
-  const long long grid = (long long)ceil_div(a.T, kPrefillRows) * a.B * a.Hq;
-  if (a.D == 128)
-    hipLaunchKernelGGL(prefill_kernel<128>, dim3((unsigned)grid), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(prefill_kernel<64>, dim3((unsigned)grid), dim3(256), 0, s, a);
+template <int D>
+static hipError_t prefill_t(const PrefillArgs& a, hipStream_t s) {
+  using Sh = PrefillShape<D>;
+  const long long grid = (long long)ceil_div(a.T, Sh::Rows) * a.B * a.Hq;
+  hipLaunchKernelGGL(prefill_kernel<D>, dim3((unsigned)grid), dim3(Sh::Threads), 0, s, a);
   return hipGetLastError();
+}
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
+  return a.D == 128 ? prefill_t<128>(a, s) : prefill_t<64>(a, s);
 }
 
 }  // namespace eta

@@ -8,15 +8,16 @@
 // the forward pass of prefill and training; decode (one query against a
 // cache) is the block-sparse path of the other kernels.
 //
-// One work-group of 8 waves (d 64) or 4 waves (d 128) takes 16 consecutive
-// queries of one query head per wave; wave w owns queries t0 + 16 w .. + 15.
-// The keys 0 .. t0 + rows - 1 are walked in 32-key tiles.  A tile is loaded
-// once for all waves (coalesced 128-bit reads by 256 threads, the next
-// tile's loads in flight while the current one is computed) and staged in
-// LDS as rows (chunk-swizzled),
-// double buffered, one barrier per tile; the value product reads V with the
-// transposing LDS read.  Each wave then computes, on the matrix
-// cores, S^T = K_tile Q_w^T (queries as the 16 columns; q is bf16 as given)
+// One work-group of 8 waves (d 64) or 4 waves (d 128) takes the query heads
+// of one KV head that share its K and V: with hw of them per work-group
+// (8 at the pages' group of 8), wave w serves head w % hw at queries
+// t0 + 16 (w / hw) .. + 15.  The keys 0 .. t0 + rows - 1 are walked in 32-key
+// tiles.  A tile is loaded once for all waves (coalesced 128-bit reads by 256
+// threads, the next tile's loads in flight while the current one is
+// computed) and staged in LDS as rows (chunk-swizzled), double buffered, one
+// barrier per tile; the value product reads V with the transposing LDS read.
+// Each wave then computes, on the matrix cores, S^T = K_tile Q_w^T (queries
+// as the 16 columns; q is bf16 as given)
 // and O += P V with the weights split hi + lo, applying the causal mask, the
 // gate and an online softmax per query column in between.
 #include "eta_internal.h"
@@ -39,10 +40,10 @@ struct PrefillShape {
   static constexpr int NV = D / 16;                  // 16-dim slabs of the value product
   static constexpr int RB = D * 2;                   // bytes per bf16 row
   static constexpr int LPR = D / 8;                  // threads per row in a coalesced load
-  // Queries per work-group (16 per wave): 128 at d 64, so each staged K/V tile
-  // serves 8 waves; 64 at d 128, whose registers leave room for fewer waves.
-  static constexpr int Rows = D == 64 ? 128 : 64;
-  static constexpr int Threads = Rows / 16 * 64;
+  // Waves per work-group (16 queries each): 8 at d 64, so each staged K/V
+  // tile serves 8 waves; 4 at d 128, whose registers leave room for fewer.
+  static constexpr int NW = D == 64 ? 8 : 4;
+  static constexpr int Threads = NW * 64;
   static constexpr int KP = kTileKeys * LPR / 256;   // K (and V) loads per loading thread per tile
   static constexpr int KBytes = kTileKeys * RB;
   static constexpr int VBytes = kTileKeys * RB;
@@ -50,22 +51,35 @@ struct PrefillShape {
   static_assert(KP >= 1, "tile loads");
 };
 
+// Query heads per work-group: the largest power of two up to the wave count
+// that divides the group, so that the waves of a work-group are hw query
+// heads of one KV head (all reading the same K and V) times nw / hw
+// consecutive 16-query subtiles.
+__host__ __device__ inline int prefill_heads(int nw, int group) {
+  int h = nw;
+  while (h > 1 && group % h != 0) h >>= 1;
+  return h;
+}
+
 template <int D>
 __global__ __launch_bounds__(PrefillShape<D>::Threads) void prefill_kernel(PrefillArgs a) {
   using Sh = PrefillShape<D>;
   constexpr int NK = Sh::NK, NV = Sh::NV, RB = Sh::RB, LPR = Sh::LPR, KP = Sh::KP;
   __shared__ __align__(16) char s_stage[2][Sh::StageBytes];
 
-  const int T = a.T;
-  const int units = a.B * a.Hq;
-  const int ntq = ceil_div(T, Sh::Rows);
+  const int T = a.T, G = a.G;
+  const int hw = prefill_heads(Sh::NW, G), hblocks = G / hw;
+  const int rows = 16 * (Sh::NW / hw);  // query positions per work-group
+  const int units = a.B * a.Hkv * hblocks;
+  const int ntq = ceil_div(T, rows);
   const int tq = ntq - 1 - (int)(blockIdx.x / units);  // longest query tiles first
-  const int uq = blockIdx.x % units;
-  const int b = uq / a.Hq, kvh = (uq % a.Hq) / a.G;
-  const int t0 = tq * Sh::Rows;
+  const int ug = blockIdx.x % units;
+  const int b = ug / (a.Hkv * hblocks), kvh = (ug / hblocks) % a.Hkv, hb = ug % hblocks;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, tid = threadIdx.x;
+  const int uq = (b * a.Hkv + kvh) * G + hb * hw + wave % hw;  // the wave's query head
+  const int t0 = tq * rows;
   const int n = lane & 15, grp = lane >> 4;
-  const int tw = t0 + 16 * wave;  // the wave's first query
+  const int tw = t0 + 16 * (wave / hw);  // the wave's first query
   const int tn = tw + n;          // this lane's query column
   const char* qbase = static_cast<const char*>(a.q) + (size_t)uq * T * RB;
   const char* kbase = static_cast<const char*>(a.k) + ((size_t)b * a.Hkv + kvh) * T * RB;
@@ -88,7 +102,7 @@ __global__ __launch_bounds__(PrefillShape<D>::Threads) void prefill_kernel(Prefi
   const float sl2 = a.scale * kLog2e;
   const float lazy_raw = kLazyRaise / a.scale;
 
-  const int kend = min(T, t0 + Sh::Rows);  // keys this work-group needs
+  const int kend = min(T, t0 + rows);  // keys this work-group needs
   const int ntiles = ceil_div(kend, kTileKeys);
 
   // Cooperative tile loads: K and V as (key, 16-byte chunk) pairs, D/8
@@ -270,7 +284,9 @@ __global__ __launch_bounds__(PrefillShape<D>::Threads) void prefill_kernel(Prefi
 template <int D>
 static hipError_t prefill_t(const PrefillArgs& a, hipStream_t s) {
   using Sh = PrefillShape<D>;
-  const long long grid = (long long)ceil_div(a.T, Sh::Rows) * a.B * a.Hq;
+  const int hw = prefill_heads(Sh::NW, a.G);
+  const long long grid =
+      (long long)ceil_div(a.T, 16 * (Sh::NW / hw)) * a.B * a.Hkv * (a.G / hw);
   hipLaunchKernelGGL(prefill_kernel<D>, dim3((unsigned)grid), dim3(Sh::Threads), 0, s, a);
   return hipGetLastError();
 }

@@ -56,7 +56,7 @@ def compare(g_out, g_dens, o_out, o_dens):
 
 
 @pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("G", [1, 4])
+@pytest.mark.parametrize("G", [1, 3, 4, 8, 16])
 @pytest.mark.parametrize("T", [1, 31, 63, 64, 65, 127, 128, 129, 200])
 def test_prefill_small(D, G, T):
     w = synth.make_prefill(seed=T + G + D, B=2, H=2, G=G, D=D, T=T)

@@ -34,71 +34,81 @@ struct BufTag {
   static constexpr int value = I;
 };
 
-template <int D>
+// HPW query heads per wave (2 at d 64 when the group is even: the wave reads
+// each staged K/V tile from LDS once for both), 16 query positions each.
+template <int D, int HPW>
 struct PrefillShape {
   static constexpr int NK = D / 32;                  // 32-dim slabs of the score product
   static constexpr int NV = D / 16;                  // 16-dim slabs of the value product
   static constexpr int RB = D * 2;                   // bytes per bf16 row
   static constexpr int LPR = D / 8;                  // threads per row in a coalesced load
-  // Waves per work-group (16 queries each): 8 at d 64, so each staged K/V
-  // tile serves 8 waves; 4 at d 128, whose registers leave room for fewer.
-  static constexpr int NW = D == 64 ? 8 : 4;
+  // (head, 16-query subtile) slots per work-group: 8 at d 64, so each staged
+  // K/V tile serves 8 of them; 4 at d 128, whose registers leave room for
+  // fewer waves.
+  static constexpr int Slots = D == 64 ? 8 : 4;
+  static constexpr int NW = Slots / HPW;            // waves per work-group
   static constexpr int Threads = NW * 64;
   static constexpr int KP = kTileKeys * LPR / 256;   // K (and V) loads per loading thread per tile
   static constexpr int KBytes = kTileKeys * RB;
   static constexpr int VBytes = kTileKeys * RB;
   static constexpr int StageBytes = KBytes + VBytes;
   static_assert(KP >= 1, "tile loads");
+  static_assert(Threads >= 256, "the first 256 threads load each tile");
 };
 
-// Query heads per work-group: the largest power of two up to the wave count
-// that divides the group, so that the waves of a work-group are hw query
-// heads of one KV head (all reading the same K and V) times nw / hw
-// consecutive 16-query subtiles.
-__host__ __device__ inline int prefill_heads(int nw, int group) {
-  int h = nw;
+// Query heads per work-group: the largest power of two up to the slot count
+// that divides the group, so that the slots of a work-group are hw query
+// heads of one KV head (all reading the same K and V) times slots / hw
+// consecutive 16-query subtiles.  Slot s is head s % hw, subtile s / hw.
+__host__ __device__ inline int prefill_heads(int slots, int group) {
+  int h = slots;
   while (h > 1 && group % h != 0) h >>= 1;
   return h;
 }
 
-template <int D>
-__global__ __launch_bounds__(PrefillShape<D>::Threads) void prefill_kernel(PrefillArgs a) {
-  using Sh = PrefillShape<D>;
+template <int D, int HPW>
+__global__ __launch_bounds__((PrefillShape<D, HPW>::Threads)) void prefill_kernel(PrefillArgs a) {
+  using Sh = PrefillShape<D, HPW>;
   constexpr int NK = Sh::NK, NV = Sh::NV, RB = Sh::RB, LPR = Sh::LPR, KP = Sh::KP;
   __shared__ __align__(16) char s_stage[2][Sh::StageBytes];
 
   const int T = a.T, G = a.G;
-  const int hw = prefill_heads(Sh::NW, G), hblocks = G / hw;
-  const int rows = 16 * (Sh::NW / hw);  // query positions per work-group
+  const int hw = prefill_heads(Sh::Slots, G), hblocks = G / hw;
+  const int rows = 16 * (Sh::Slots / hw);  // query positions per work-group
   const int units = a.B * a.Hkv * hblocks;
   const int ntq = ceil_div(T, rows);
   const int tq = ntq - 1 - (int)(blockIdx.x / units);  // longest query tiles first
   const int ug = blockIdx.x % units;
   const int b = ug / (a.Hkv * hblocks), kvh = (ug / hblocks) % a.Hkv, hb = ug % hblocks;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, tid = threadIdx.x;
-  const int uq = (b * a.Hkv + kvh) * G + hb * hw + wave % hw;  // the wave's query head
+  // The wave's slots HPW w .. HPW w + HPW - 1: consecutive heads (hw is a
+  // multiple of HPW), one subtile.
+  const int slot = HPW * wave;
+  const int uq0 = (b * a.Hkv + kvh) * G + hb * hw + slot % hw;  // the wave's first query head
   const int t0 = tq * rows;
   const int n = lane & 15, grp = lane >> 4;
-  const int tw = t0 + 16 * (wave / hw);  // the wave's first query
-  const int tn = tw + n;          // this lane's query column
-  const char* qbase = static_cast<const char*>(a.q) + (size_t)uq * T * RB;
+  const int tw = t0 + 16 * (slot / hw);  // the wave's first query
+  const int tn = tw + n;                 // this lane's query column
   const char* kbase = static_cast<const char*>(a.k) + ((size_t)b * a.Hkv + kvh) * T * RB;
   const char* vbase = static_cast<const char*>(a.v) + ((size_t)b * a.Hkv + kvh) * T * RB;
 
-  // Query operand: column n = query tn, dims 32 kk + 8 grp .. +7 (rows past
+  // Query operands: column n = query tn, dims 32 kk + 8 grp .. +7 (rows past
   // the sequence read the last row and are never written).
-  bf16x8 qb[NK];
-  {
-    const char* qrow = qbase + (size_t)min(tn, T - 1) * RB + 16 * grp;
-#pragma unroll
-    for (int kk = 0; kk < NK; ++kk) qb[kk] = __builtin_bit_cast(bf16x8, ld16(qrow + 64 * kk));
-  }
-  const float tau_n = a.tau[(size_t)uq * T + min(tn, T - 1)];
   // Gate of Eq. 2: sigmoid(beta (scale r - tau)) = 1 / (1 + 2^(r gk1 + gk0)).
   // Scores stay unscaled (raw dot products r) through the softmax: the logit is
   // scale * r * gate, so scale is folded into the exponent constants and the
   // lazy-rescale step (scale > 0 keeps every max and comparison).
-  const float gk1 = -a.beta * kLog2e * a.scale, gk0 = a.beta * kLog2e * tau_n;
+  bf16x8 qb[HPW][NK];
+  float gk0[HPW];
+  const float gk1 = -a.beta * kLog2e * a.scale;
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) {
+    const size_t pos = (size_t)(uq0 + hh) * T + min(tn, T - 1);
+    const char* qrow = static_cast<const char*>(a.q) + pos * RB + 16 * grp;
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) qb[hh][kk] = __builtin_bit_cast(bf16x8, ld16(qrow + 64 * kk));
+    gk0[hh] = a.beta * kLog2e * a.tau[pos];
+  }
   const float sl2 = a.scale * kLog2e;
   const float lazy_raw = kLazyRaise / a.scale;
 
@@ -106,11 +116,11 @@ __global__ __launch_bounds__(PrefillShape<D>::Threads) void prefill_kernel(Prefi
   const int ntiles = ceil_div(kend, kTileKeys);
 
   // Cooperative tile loads: K and V as (key, 16-byte chunk) pairs, D/8
-  // threads per row.  Keys past the sequence read its last row (finite data;
-  // causally masked).  Both are staged as rows; V's value-product operand is
-  // taken with the transposing LDS read, so no thread repacks V.
+  // threads per row, by the first 256 threads.  Keys past the sequence read
+  // its last row (finite data; causally masked).  Both are staged as rows;
+  // V's value-product operand is taken with the transposing LDS read, so no
+  // thread repacks V.
   uint4 kr[KP], vr[KP];
-  // The first 256 threads load and stage each tile.
   auto fetch = [&](int j) {
     if (Sh::Threads > 256 && tid >= 256) return;
     const int s0 = j * kTileKeys;
@@ -139,14 +149,24 @@ __global__ __launch_bounds__(PrefillShape<D>::Threads) void prefill_kernel(Prefi
   // O accumulates P V; L accumulates P 1 (every column of the ones operand),
   // so the softmax denominators of rows 4 grp + i come out of the matrix
   // cores in O's own layout, summed from the same hi + lo weights.
-  floatx4 O[NV], L = floatx4{0.f, 0.f, 0.f, 0.f};
+  floatx4 O[HPW][NV], L[HPW];
 #pragma unroll
-  for (int nv = 0; nv < NV; ++nv) O[nv] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int hh = 0; hh < HPW; ++hh) {
+    L[hh] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int nv = 0; nv < NV; ++nv) O[hh][nv] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
   const bf16x8 ones = __builtin_bit_cast(bf16x8, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u,
                                                              0x3F803F80u));
   // m: reference max (raw score units) of the lane's query column; ms2 its
   // exponent offset m * scale * log2(e), 0 while the column is empty.
-  float m = -__builtin_inff(), ms2 = 0.f, gsum = 0.f;
+  float m[HPW], ms2[HPW], gsum[HPW];
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) {
+    m[hh] = -__builtin_inff();
+    ms2[hh] = 0.f;
+    gsum[hh] = 0.f;
+  }
 
   // MASK: the tile holds the diagonal or keys past some query (or the wave has
   // queries past the sequence); otherwise every key precedes every query.
@@ -155,75 +175,84 @@ __global__ __launch_bounds__(PrefillShape<D>::Threads) void prefill_kernel(Prefi
     const int s0 = j * kTileKeys;
     const char* sk = s_stage[decltype(buf_tag)::value];
     const char* sv = sk + Sh::KBytes;
-    floatx4 S[2];
+    // Each K operand read serves every head of the wave.
+    floatx4 S[HPW][2];
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       const int key = tile_key(st, n);
       const char* row = sk + tile_row<D>(key) * RB;
       const int sw = tile_kswz<D>(key);
-      S[st] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int hh = 0; hh < HPW; ++hh) S[hh][st] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk) {
         const bf16x8 kv =
             __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(row + 16 * ((4 * kk + grp) ^ sw)));
-        S[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qb[kk], S[st], 0, 0, 0);
+#pragma unroll
+        for (int hh = 0; hh < HPW; ++hh)
+          S[hh][st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qb[hh][kk], S[hh][st], 0, 0, 0);
       }
     }
-    // Score i of half st is key s0 + 2 grp + st + 8 i against query tn.
-    float lg[8];
-    float tmax = -__builtin_inff();
+    bf16x8 phi[HPW], plo[HPW];
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
+    for (int hh = 0; hh < HPW; ++hh) {
+      // Score i of half st is key s0 + 2 grp + st + 8 i against query tn.
+      float lg[8];
+      float tmax = -__builtin_inff();
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float d = S[st][i];
-        const float g = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(fmaf(d, gk1, gk0)));
-        if constexpr (MASK) {
-          const int s = s0 + 2 * grp + st + 8 * i;
-          const bool on = s <= tn && tn < T;
-          gsum += on ? g : 0.f;
-          const float lv = s == tn ? d : d * g;
-          lg[4 * st + i] = on ? lv : -__builtin_inff();
-        } else {
-          gsum += g;
-          lg[4 * st + i] = d * g;
+      for (int st = 0; st < 2; ++st) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float d = S[hh][st][i];
+          const float g = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(fmaf(d, gk1, gk0[hh])));
+          if constexpr (MASK) {
+            const int s = s0 + 2 * grp + st + 8 * i;
+            const bool on = s <= tn && tn < T;
+            gsum[hh] += on ? g : 0.f;
+            const float lv = s == tn ? d : d * g;
+            lg[4 * st + i] = on ? lv : -__builtin_inff();
+          } else {
+            gsum[hh] += g;
+            lg[4 * st + i] = d * g;
+          }
+          tmax = fmaxf(tmax, lg[4 * st + i]);
         }
-        tmax = fmaxf(tmax, lg[4 * st + i]);
       }
-    }
-    // Lazy rescaling as in the grouped decode: the reference max of a query
-    // moves only when the tile raises it by more than kLazyRaise.  m is the
-    // same in the 4 lane groups of a column, so some lane's own max passes
-    // m + lazy_raw exactly when some column's max does; the column maxima are
-    // formed only then.
-    if (__ballot(tmax > m + lazy_raw) != 0ull) {
-      tmax = max_xor32(max_xor16(tmax));
-      const float mn = fmaxf(m, tmax);
-      const float alpha =
-          mn == -__builtin_inff() ? 1.f : __builtin_amdgcn_exp2f((m - mn) * sl2);
+      // Lazy rescaling as in the grouped decode: the reference max of a query
+      // moves only when the tile raises it by more than kLazyRaise.  m is the
+      // same in the 4 lane groups of a column, so some lane's own max passes
+      // m + lazy_raw exactly when some column's max does; the column maxima
+      // are formed only then.
+      if (__ballot(tmax > m[hh] + lazy_raw) != 0ull) {
+        tmax = max_xor32(max_xor16(tmax));
+        const float mn = fmaxf(m[hh], tmax);
+        const float alpha =
+            mn == -__builtin_inff() ? 1.f : __builtin_amdgcn_exp2f((m[hh] - mn) * sl2);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float al = __shfl(alpha, 4 * grp + i, kWave);
-        L[i] *= al;
+        for (int i = 0; i < 4; ++i) {
+          const float al = __shfl(alpha, 4 * grp + i, kWave);
+          L[hh][i] *= al;
 #pragma unroll
-        for (int nv = 0; nv < NV; ++nv) O[nv][i] *= al;
+          for (int nv = 0; nv < NV; ++nv) O[hh][nv][i] *= al;
+        }
+        m[hh] = mn;
+        ms2[hh] = m[hh] == -__builtin_inff() ? 0.f : m[hh] * sl2;
       }
-      m = mn;
-      ms2 = m == -__builtin_inff() ? 0.f : m * sl2;
-    }
-    uint32_t ph[4], pl[4];
+      uint32_t ph[4], pl[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      split_hi_lo(__builtin_amdgcn_exp2f(fmaf(lg[2 * i], sl2, -ms2)),
-                  __builtin_amdgcn_exp2f(fmaf(lg[2 * i + 1], sl2, -ms2)), ph[i], pl[i]);
-    const bf16x8 phi = __builtin_bit_cast(bf16x8, make_uint4(ph[0], ph[1], ph[2], ph[3]));
-    const bf16x8 plo = __builtin_bit_cast(bf16x8, make_uint4(pl[0], pl[1], pl[2], pl[3]));
-    L = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi, ones, L, 0, 0, 0);
-    L = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo, ones, L, 0, 0, 0);
+      for (int i = 0; i < 4; ++i)
+        split_hi_lo(__builtin_amdgcn_exp2f(fmaf(lg[2 * i], sl2, -ms2[hh])),
+                    __builtin_amdgcn_exp2f(fmaf(lg[2 * i + 1], sl2, -ms2[hh])), ph[i], pl[i]);
+      phi[hh] = __builtin_bit_cast(bf16x8, make_uint4(ph[0], ph[1], ph[2], ph[3]));
+      plo[hh] = __builtin_bit_cast(bf16x8, make_uint4(pl[0], pl[1], pl[2], pl[3]));
+      L[hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi[hh], ones, L[hh], 0, 0, 0);
+      L[hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo[hh], ones, L[hh], 0, 0, 0);
+    }
     // Value operand (dim 16 nv + n, slots 8 grp + 4 h + j) by two transposing
-    // reads: lane L of group g supplies row tile_key(h, 4 g + (L%16)/4), dims
-    // 16 nv + 4 ((L%16) % 4) .. +3, and lane l receives element l % 4 of the
-    // rows supplied by lanes 16 g + 4 j + (l%16)/4, j = 0..3.
+    // reads, each serving every head of the wave: lane L of group g supplies
+    // row tile_key(h, 4 g + (L%16)/4), dims 16 nv + 4 ((L%16) % 4) .. +3, and
+    // lane l receives element l % 4 of the rows supplied by lanes
+    // 16 g + 4 j + (l%16)/4, j = 0..3.
     const int trow0 = tile_key(0, 4 * grp + ((lane & 15) >> 2));
     const int trow1 = tile_key(1, 4 * grp + ((lane & 15) >> 2));
     const int tr4 = lane & 3;
@@ -235,8 +264,11 @@ __global__ __launch_bounds__(PrefillShape<D>::Threads) void prefill_kernel(Prefi
       const uint2 v1 =
           tr_read(sv + tile_row<D>(trow1) * RB + 16 * (c ^ vrow_swz(trow1)) + 8 * (tr4 & 1));
       const bf16x8 vb = __builtin_bit_cast(bf16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
-      O[nv] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi, vb, O[nv], 0, 0, 0);
-      O[nv] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo, vb, O[nv], 0, 0, 0);
+#pragma unroll
+      for (int hh = 0; hh < HPW; ++hh) {
+        O[hh][nv] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi[hh], vb, O[hh][nv], 0, 0, 0);
+        O[hh][nv] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo[hh], vb, O[hh][nv], 0, 0, 0);
+      }
     }
   };
 
@@ -265,34 +297,39 @@ __global__ __launch_bounds__(PrefillShape<D>::Threads) void prefill_kernel(Prefi
     if (j + 1 < ntiles) step(j + 1, BufTag<1>{});
   }
 
-  // Gate sums of a query column over its 4 lane groups.
-  gsum = sum_xor32(sum_xor16(gsum));
-  // O and L rows are queries tw + 4 grp + i.
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float li = L[i];
-    const int t = tw + 4 * grp + i;
-    if (t < T) {
-      float* orow = a.out + ((size_t)uq * T + t) * D;
+  for (int hh = 0; hh < HPW; ++hh) {
+    const int uq = uq0 + hh;
+    // Gate sums of a query column over its 4 lane groups.
+    const float gs = sum_xor32(sum_xor16(gsum[hh]));
+    // O and L rows are queries tw + 4 grp + i.
 #pragma unroll
-      for (int nv = 0; nv < NV; ++nv) orow[16 * nv + n] = O[nv][i] / li;
+    for (int i = 0; i < 4; ++i) {
+      const float li = L[hh][i];
+      const int t = tw + 4 * grp + i;
+      if (t < T) {
+        float* orow = a.out + ((size_t)uq * T + t) * D;
+#pragma unroll
+        for (int nv = 0; nv < NV; ++nv) orow[16 * nv + n] = O[hh][nv][i] / li;
+      }
     }
+    if (a.dens && grp == 0 && tn < T) a.dens[(size_t)uq * T + tn] = gs / (float)(tn + 1);
   }
-  if (a.dens && grp == 0 && tn < T) a.dens[(size_t)uq * T + tn] = gsum / (float)(tn + 1);
 }
 
-template <int D>
+template <int D, int HPW>
 static hipError_t prefill_t(const PrefillArgs& a, hipStream_t s) {
-  using Sh = PrefillShape<D>;
-  const int hw = prefill_heads(Sh::NW, a.G);
+  using Sh = PrefillShape<D, HPW>;
+  const int hw = prefill_heads(Sh::Slots, a.G);
   const long long grid =
-      (long long)ceil_div(a.T, 16 * (Sh::NW / hw)) * a.B * a.Hkv * (a.G / hw);
-  hipLaunchKernelGGL(prefill_kernel<D>, dim3((unsigned)grid), dim3(Sh::Threads), 0, s, a);
+      (long long)ceil_div(a.T, 16 * (Sh::Slots / hw)) * a.B * a.Hkv * (a.G / hw);
+  hipLaunchKernelGGL((prefill_kernel<D, HPW>), dim3((unsigned)grid), dim3(Sh::Threads), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
-  return a.D == 128 ? prefill_t<128>(a, s) : prefill_t<64>(a, s);
+  if (a.D == 128) return prefill_t<128, 1>(a, s);
+  return a.G % 2 == 0 ? prefill_t<64, 2>(a, s) : prefill_t<64, 1>(a, s);
 }
 
 }  // namespace eta

@@ -107,9 +107,13 @@ int32_t eta_cache_blocks(const eta_cache* c);
  * [batch][heads][head_dim], kv_dtype) are written at position T_b, and when
  * T_b + 1 is a multiple of `block` the statistics of that now-complete block
  * are computed (Methodology 4).  Then T_b += 1.
- * A sequence already at cap_tokens is left unchanged and, when `overflow`
- * (device int32, optional) is not NULL, *overflow is set to 1; the flag is
- * never cleared by the library.
+ * `overflow` (device int32, required) reports the capacity error: T_b is
+ * only known on the device, so it cannot be checked on the host.  A sequence
+ * already at cap_tokens is left unchanged (its token is not written and T_b
+ * keeps its value) and *overflow is set to 1; the flag is never cleared by
+ * the library.  After a flagged append the caller must not screen or decode
+ * that step: the query's own key (Eq. 3's never-gated diagonal) is missing.
+ * overflow == NULL (for a non-empty cache) returns ETA_ERR_NULL_PTR.
  */
 eta_status eta_append_kv(const eta_cache* c, const void* k_new, const void* v_new,
                          int32_t* overflow, void* stream);
@@ -299,7 +303,8 @@ eta_status eta_dense_decode_gqa(const eta_cache* c, int32_t group, const float* 
  *   tau   device [batch][kv_heads*group][seq_len] float32 (Eq. 1 per position)
  *   out   device [batch][kv_heads*group][seq_len][head_dim] float32
  *   dens  device [batch][kv_heads*group][seq_len] float32, or NULL
- * head_dim in {64, 128}; beta and scale finite and > 0.  Both products run
+ * head_dim in {64, 128}; beta and scale finite and > 0; one K/V stream holds
+ * fewer than 2^32 bytes (seq_len * head_dim * 2 < 2^32, else ETA_ERR_BAD_SHAPE).  Both products run
  * on the matrix cores with float32 accumulation; the softmax weights are
  * split into two bf16 terms.  No workspace.
  */

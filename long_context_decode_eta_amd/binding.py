@@ -136,6 +136,8 @@ class KVCache:
         self.maxnorm = torch.zeros((batch, heads, self.cap_blocks), dtype=torch.float32,
                                    device=device)
         self.seq_len = torch.zeros((batch,), dtype=torch.int32, device=device)
+        # set to 1 by an append to a full sequence (never cleared by the library)
+        self.overflow = torch.zeros((1,), dtype=torch.int32, device=device)
 
     def struct(self) -> EtaCacheStruct:
         dt = {torch.float32: DT_F32, torch.bfloat16: DT_BF16}[self.kv_dtype]
@@ -153,6 +155,11 @@ def _ref(cache: KVCache):
 
 # ---------------------------------------------------------------------------
 def append_kv(cache: KVCache, k_new, v_new, overflow=None, stream=None):
+    """Append one token per sequence.  The capacity flag is required by the C
+    call; without an explicit one the cache's own ``cache.overflow`` is used.
+    A flagged sequence keeps its length, so its step must not be decoded."""
+    if overflow is None:
+        overflow = cache.overflow
     _check(lib().eta_append_kv(_ref(cache), _dev(k_new, cache.kv_dtype, "k_new"),
                                _dev(v_new, cache.kv_dtype, "v_new"),
                                _dev(overflow, torch.int32, "overflow"), _stream(stream)),

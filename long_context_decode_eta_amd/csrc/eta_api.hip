@@ -162,6 +162,11 @@ eta_status eta_append_kv(const eta_cache* c, const void* k_new, const void* v_ne
   if (eta_status s = check_cache(c, &v)) return s;
   if (empty(v)) return ok();
   if (!k_new || !v_new) return fail(ETA_ERR_NULL_PTR, "k_new/v_new is NULL");
+  // T_b lives on the device, so a full sequence can only be reported there:
+  // the flag is required, so that a dropped token cannot go unnoticed.
+  if (!overflow)
+    return fail(ETA_ERR_NULL_PTR, "overflow flag is NULL (required: it reports an append to a "
+                                  "full sequence)");
   return hip_status(eta::launch_append(v, k_new, v_new, overflow, (hipStream_t)stream),
                     "eta_append_kv launch");
 }
@@ -516,6 +521,10 @@ eta_status eta_gated_prefill(int32_t batch, int32_t kv_heads, int32_t group, int
   const long long hq = (long long)kv_heads * group;
   if ((long long)batch * hq * seq_len * head_dim > (1LL << 40))
     return fail(ETA_ERR_BAD_SHAPE, "problem too large");
+  // The kernel addresses rows within one K/V stream with 32-bit byte offsets.
+  if ((long long)seq_len * head_dim * 2 >= (1LL << 32))
+    return fail(ETA_ERR_BAD_SHAPE, "seq_len %d too long: one K/V stream must hold < 2^32 bytes",
+                seq_len);
   if ((long long)eta::ceil_div(seq_len, 64) * batch * hq > kMaxGrid)
     return fail(ETA_ERR_BAD_SHAPE, "grid too large");
   eta::PrefillArgs a;

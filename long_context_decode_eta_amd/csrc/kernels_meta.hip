@@ -143,7 +143,7 @@ __global__ __launch_bounds__(kAppendWaves * kWave) void append_kernel(CacheView 
   const int waves = blockDim.x >> 6;
   const int pos = c.seq_len[b];
   if (pos >= c.cap) {  // uniform over the work-group
-    if (overflow && threadIdx.x == 0) *overflow = 1;
+    if (threadIdx.x == 0) *overflow = 1;
     return;
   }
   for (int h = wave; h < c.H; h += waves) {

@@ -8,7 +8,13 @@ Bars (from the decode path's statement):
   - outputs, per (sequence, head): max|o_gpu - o_ref| <= tol * max|o_ref|,
     tol = 1e-5 for a float32 cache and 2e-2 for a bfloat16 cache, with o_ref
     evaluated by the oracle on the GPU's mask when allowed near-tie flips
-    occurred.
+    occurred;
+  - in addition, per (sequence, head), the same ratio must stay within
+    INTERNAL_TOL = 1e-5 for the one-query-per-KV-head decode whatever the
+    cache dtype: both sides read the same stored bits and differ only in
+    float32 vs float64 accumulation, so a dropped low-weight partial or a
+    bf16 intermediate (errors of 1e-3 and more) fails here although it would
+    pass the bf16 bar.  The grouped-query decode passes its own internal bar.
 """
 from __future__ import annotations
 
@@ -25,6 +31,7 @@ from long_context_decode_eta_amd import synth
 OUT_TOL = {torch.float32: 1e-5, torch.bfloat16: 2e-2}
 BAND_REL = 1e-5
 MAX_FLIP_FRAC = 1e-3
+INTERNAL_TOL = 1e-5
 
 
 def note(msg: str) -> None:
@@ -132,8 +139,10 @@ def compare_masks(o_active, o_score, o_tau_screen, g_mask, seq_len, b):
     return flips, screened
 
 
-def compare_outputs(g_out, o_out, kv_dtype, what="out"):
-    tol = OUT_TOL[kv_dtype]
+def compare_outputs(g_out, o_out, kv_dtype, what="out", internal=INTERNAL_TOL):
+    """Per (sequence, head) relative error against the output bar of the
+    cache dtype and against the internal bar; returns the worst ratio."""
+    tol = min(OUT_TOL[kv_dtype], internal)
     worst = 0.0
     B, H, _ = g_out.shape
     for bb in range(B):
@@ -234,25 +243,30 @@ def check_units(w: synth.Workload, g: GpuResult, units, *, W, bias_or_c, z, scal
     return worst, flips, screened
 
 
-def oracle_constants(w: synth.Workload, rho: float, seqs=None, sets=None):
+def oracle_constants(w: synth.Workload, rho, seqs=None, sets=None):
     """Per-head constants for a target density from the oracle's calibration,
     pooled over the sequences `seqs` (default: all).  Dynamic workloads pool
     x = score - qbar W (the timed query); frozen-calibrated ones pool the
-    calibration query sets."""
+    calibration query sets.  `rho` may be a list: then a list of results,
+    with the statistics computed once."""
     seqs = list(range(w.B)) if seqs is None else list(seqs)
     K = synth.kv_numpy(w.k[seqs])
     sl = w.seq_len.cpu().numpy()[seqs].astype(np.int32)
     meta = oracle.meta_batch(K, sl, w.block)
-    if w.W is not None:
-        q = w.q.cpu().numpy()[seqs]
-        tau0, _ = oracle.predict_tau(q, w.W.cpu().numpy(), np.zeros(w.H, np.float32))
-        c, k = oracle.calibrate(q[None], sl, w.block, w.cap, meta, tau0=tau0[None], z=w.z,
-                                scale=w.scale, rho=float(np.float32(rho)))
-    else:
-        qc = w.q_cal.cpu().numpy()[:, seqs]
-        c, k = oracle.calibrate(qc, sl, w.block, w.cap, meta, z=w.z, scale=w.scale,
-                                rho=float(np.float32(rho)))
-    return torch.from_numpy(c.astype(np.float32)), k
+    del K
+    res = []
+    for r in (rho if isinstance(rho, (list, tuple)) else [rho]):
+        if w.W is not None:
+            q = w.q.cpu().numpy()[seqs]
+            tau0, _ = oracle.predict_tau(q, w.W.cpu().numpy(), np.zeros(w.H, np.float32))
+            c, k = oracle.calibrate(q[None], sl, w.block, w.cap, meta, tau0=tau0[None], z=w.z,
+                                    scale=w.scale, rho=float(np.float32(r)))
+        else:
+            qc = w.q_cal.cpu().numpy()[:, seqs]
+            c, k = oracle.calibrate(qc, sl, w.block, w.cap, meta, z=w.z, scale=w.scale,
+                                    rho=float(np.float32(r)))
+        res.append((torch.from_numpy(c.astype(np.float32)), k))
+    return res if isinstance(rho, (list, tuple)) else res[0]
 
 
 # ---------------------------------------------------------------------------
@@ -352,8 +366,7 @@ def check_gqa(w: synth.Workload, g: GqaGpuResult, *, W, bias_or_c, z, scale, mod
     else:
         ref = oracle.attend_batch(q, np.repeat(K, G, axis=1), np.repeat(V, G, axis=1), sl,
                                   w.block, g.mask, r["tau"], mode=mode, beta=beta, scale=scale)
-    worst = compare_outputs(g.out, ref, w.kv_dtype)
-    assert worst <= internal_tol, f"grouped-query output rel err {worst:.2e} > {internal_tol:.0e}"
+    worst = compare_outputs(g.out, ref, w.kv_dtype, internal=internal_tol)
     tot = max(1, int(sl.sum()))
     return dict(out_rel=worst, flips=flips, screened=screened,
                 d_head=float(head_tok.sum()) / (tot * w.Hq),

@@ -144,6 +144,10 @@ def test_append_validation(lib):
     L = lib
     assert L.eta_append_kv(cache(), None, FAKE, None, None) == eb.ETA_ERR_NULL_PTR
     assert L.eta_append_kv(cache(head_dim=32), FAKE, FAKE, None, None) == eb.ETA_ERR_BAD_SHAPE
+    # the capacity flag is required: without it an append to a full sequence
+    # could drop its token unseen
+    assert L.eta_append_kv(cache(), FAKE, FAKE, None, None) == eb.ETA_ERR_NULL_PTR
+    assert "overflow" in err(L)
 
 
 def test_gqa_validation(lib):
@@ -200,6 +204,10 @@ def test_prefill_validation(lib):
     assert call(tau=None) == eb.ETA_ERR_NULL_PTR
     assert call(out=None) == eb.ETA_ERR_NULL_PTR
     assert call(T=0, q=None, out=None) == eb.ETA_OK  # empty: nothing launched
+    # rows of one K/V stream are addressed with 32-bit byte offsets
+    assert call(B=1, Hkv=1, G=1, T=1 << 24, d=128) == eb.ETA_ERR_BAD_SHAPE
+    assert "2^32" in err(L)
+    assert call(B=1, Hkv=1, G=1, T=1 << 25, d=64) == eb.ETA_ERR_BAD_SHAPE
 
 
 def test_binding_refuses_cpu_tensors(lib):

@@ -84,6 +84,12 @@ def test_append_at_capacity_flags_and_leaves_cache():
     assert cache.seq_len.cpu().tolist() == [64, 41]
     assert torch.equal(cache.k[0].view(torch.int16), k0[0].view(torch.int16))
     assert torch.all(cache.k[1, :, 40] == 1)
+    # without an explicit flag the binding passes the cache's own
+    assert cache.overflow.item() == 0
+    eb.append_kv(cache, kn, kn)
+    torch.cuda.synchronize()
+    assert cache.overflow.item() == 1
+    assert cache.seq_len.cpu().tolist() == [64, 42]
 
 
 @pytest.mark.parametrize("rho", [0.0, 0.05, 0.25, 0.6, 1.0])

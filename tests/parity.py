@@ -243,6 +243,18 @@ def check_units(w: synth.Workload, g: GpuResult, units, *, W, bias_or_c, z, scal
     return worst, flips, screened
 
 
+def meta_of_sequences(w: synth.Workload, seqs):
+    """The oracle's block statistics of the sequences `seqs`, computed one
+    sequence at a time (bounded host memory at full size) and stacked."""
+    parts = []
+    for b in seqs:
+        K = synth.kv_numpy(w.k[b:b + 1])
+        parts.append(oracle.meta_batch(K, w.seq_len.cpu().numpy()[b:b + 1].astype(np.int32),
+                                       w.block))
+        del K
+    return tuple(np.concatenate([p[i] for p in parts], axis=0) for i in range(3))
+
+
 def oracle_constants(w: synth.Workload, rho, seqs=None, sets=None):
     """Per-head constants for a target density from the oracle's calibration,
     pooled over the sequences `seqs` (default: all).  Dynamic workloads pool
@@ -250,10 +262,8 @@ def oracle_constants(w: synth.Workload, rho, seqs=None, sets=None):
     calibration query sets.  `rho` may be a list: then a list of results,
     with the statistics computed once."""
     seqs = list(range(w.B)) if seqs is None else list(seqs)
-    K = synth.kv_numpy(w.k[seqs])
     sl = w.seq_len.cpu().numpy()[seqs].astype(np.int32)
-    meta = oracle.meta_batch(K, sl, w.block)
-    del K
+    meta = meta_of_sequences(w, seqs)
     res = []
     for r in (rho if isinstance(rho, (list, tuple)) else [rho]):
         if w.W is not None:

@@ -193,6 +193,24 @@ eta_status eta_decode(const eta_cache* c, const float* q, const float* tau_gate,
                       size_t workspace_bytes, float* out, void* stream);
 
 /*
+ * eta_decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): no
+ * workspace argument, the same kernels and the same results as eta_decode.
+ * Its scratch is a static device array of 8 MiB that every device the
+ * library runs on holds until the process ends; that covers every call on
+ * the balanced path (at most 8191 streams, head_dim <= 128).  A call that
+ * would need more (more streams: the chunk grid keeps a partial per possible
+ * chunk) returns ETA_ERR_CAPACITY and launches nothing.  All such calls on
+ * one device share that array, so calls that overlap in time on one device
+ * (two streams, two host threads) race: the caller serialises them.  Nothing
+ * in the array needs clearing between calls.
+ */
+eta_status eta_decode_noalloc(const eta_cache* c, const float* q, const float* tau_gate,
+                              const int32_t* active_idx, const int32_t* active_cnt,
+                              int32_t logit_mode, float beta, float scale,
+                              int32_t blocks_per_split, float* out, void* stream);
+
+/*
  * Dense decode over every key of every stream (Theoretical Foundation, dense
  * form): chunks of blocks_per_split consecutive blocks per stream, one
  * work-group each, with RAW logits and the same log-sum-exp combine.  The

@@ -53,6 +53,8 @@ _SIGS = {
     "eta_decode_workspace_bytes": ([c_int32, c_int32, c_int32, c_int32, c_int32], c_size_t),
     "eta_decode": ([_P, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_float, c_float,
                     c_int32, c_void_p, c_size_t, c_void_p, c_void_p], c_int32),
+    "eta_decode_noalloc": ([_P, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_float,
+                            c_float, c_int32, c_void_p, c_void_p], c_int32),
     "eta_dense_decode": ([_P, c_void_p, c_float, c_int32, c_void_p, c_size_t, c_void_p,
                           c_void_p], c_int32),
     "eta_calibrate_workspace_bytes": ([c_int32, c_int32, c_int32, c_int32], c_size_t),
@@ -213,6 +215,19 @@ def decode(cache: KVCache, q, tau_gate, active_idx, active_cnt, logit_mode, beta
                             workspace.numel() * workspace.element_size(),
                             _dev(out, torch.float32, "out"), _stream(stream)),
            "eta_decode")
+
+
+def decode_noalloc(cache: KVCache, q, tau_gate, active_idx, active_cnt, logit_mode, beta, scale,
+                   blocks_per_split, out, stream=None):
+    """eta_decode on the library's static device scratch (no workspace)."""
+    _check(lib().eta_decode_noalloc(_ref(cache), _dev(q, torch.float32, "q"),
+                                    _dev(tau_gate, torch.float32, "tau_gate"),
+                                    _dev(active_idx, torch.int32, "active_idx"),
+                                    _dev(active_cnt, torch.int32, "active_cnt"),
+                                    int(logit_mode), float(beta), float(scale),
+                                    int(blocks_per_split), _dev(out, torch.float32, "out"),
+                                    _stream(stream)),
+           "eta_decode_noalloc")
 
 
 def dense_decode(cache: KVCache, q, scale, blocks_per_split, workspace, out, stream=None):

@@ -9,6 +9,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "eta_internal.h"
 
 namespace eta {
@@ -106,22 +108,30 @@ eta_status hip_status(hipError_t e, const char* what) {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 
-// Partial slots: one per possible chunk of the flat grid, and for the
-// balanced decode one per wave plus one per stream (its slots w + u).
+// Partial slots.  The balanced decode needs one per wave plus one per stream
+// (its slots w + u); the flat grid one per possible chunk.
+size_t flow_slots(long long units) {
+  return (size_t)((long long)(eta::kFlowThreads / 64) * device_cus() * eta::kFlowWGsPerCU + units);
+}
+size_t grid_slots(long long units, int cap_blocks, int split) {
+  return (size_t)(units * ((cap_blocks + split - 1) / split));
+}
+// Enough for either path (the size query: one workspace serves the sparse and
+// the dense decode of a cache).
 size_t decode_slots(long long units, int cap_blocks, int split) {
-  const long long maxc = (cap_blocks + split - 1) / split;
-  const long long flow =
-      (long long)(eta::kFlowThreads / 64) * device_cus() * eta::kFlowWGsPerCU + units;
-  return (size_t)(units * maxc > flow ? units * maxc : flow);
+  const size_t f = flow_slots(units), g = grid_slots(units, cap_blocks, split);
+  return f > g ? f : g;
 }
 
 // Decode workspace: [queue counter, balanced-decode total at byte 64 |
 // chunk_start or stream offsets [units+1] | part_m | part_l | part_acc], each
 // 256-byte aligned.
-size_t decode_ws(long long units, int D, int cap_blocks, int split) {
-  const size_t slots = decode_slots(units, cap_blocks, split);
+size_t decode_ws_slots(long long units, int D, size_t slots) {
   return 256 + align256((size_t)(units + 1) * 4) + align256(slots * 4) * 2 +
          align256(slots * (size_t)D * 4);
+}
+size_t decode_ws(long long units, int D, int cap_blocks, int split) {
+  return decode_ws_slots(units, D, decode_slots(units, cap_blocks, split));
 }
 
 #ifndef ETA_QUEUE_WGS_PER_CU
@@ -131,6 +141,43 @@ size_t decode_ws(long long units, int D, int cap_blocks, int split) {
 bool bad_float(float x) { return x != x; }
 
 }  // namespace
+
+// ---------------------------------------------------------------------------
+// Decode without allocation: the workspace is a file-scope device array of
+// kScratchBytes, one copy per device, shared by every such call on it.  Its
+// address is looked up once per device (with that device current) and kept;
+// the array's name is only a host-side stand-in and is never passed to a
+// kernel.  The decode needs no part of it cleared: the kernels of one call
+// write every counter and offset before reading it.
+
+namespace {
+constexpr size_t kScratchBytes = (size_t)8 << 20;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+static eta_status static_scratch(void** ptr, size_t* bytes) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(ETA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(ETA_ERR_HIP, "device %d outside the %d devices with a scratch slot", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(ETA_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  *bytes = kScratchBytes;
+  return ETA_OK;
+}
 
 extern "C" {
 
@@ -239,6 +286,11 @@ size_t eta_decode_workspace_bytes(int32_t batch, int32_t heads, int32_t head_dim
   return decode_ws((long long)batch * heads, head_dim, cap_blocks, blocks_per_split);
 }
 
+// ws == kStaticScratch: the library's own scratch (eta_decode_noalloc), looked
+// up only once the arguments are valid.
+static char kStaticScratchTag;
+static void* const kStaticScratch = &kStaticScratchTag;
+
 static eta_status decode_common(const eta_cache* c, const float* q, const float* tau_gate,
                                 const int32_t* active_idx, const int32_t* active_cnt,
                                 int32_t mode, bool dense, float beta, float scale, int32_t split,
@@ -262,10 +314,25 @@ static eta_status decode_common(const eta_cache* c, const float* q, const float*
   const long long units = (long long)v.B * v.H;
   const int maxc = eta::ceil_div(v.cap_blocks, split);
   if ((long long)maxc * units > kMaxGrid) return fail(ETA_ERR_BAD_SHAPE, "grid too large");
-  const size_t need = decode_ws(units, v.D, v.cap_blocks, split);
-  if (!ws || ws_bytes < need)
-    return fail(ETA_ERR_WORKSPACE, "decode workspace %zu bytes < %zu", ws_bytes, need);
-  const size_t slots = decode_slots(units, v.cap_blocks, split);
+  // Sparse decode runs balanced (equal ranges of all admitted blocks per
+  // wave) whenever its stream offsets fit in LDS.
+  const bool flow = !dense && units <= eta::kMaxFlowUnits &&
+                    units * (long long)v.cap_blocks < 0x7fffffffLL;
+  // A caller's workspace must be as large as the size query says (enough for
+  // either path); the static scratch only needs what this call's path uses.
+  const size_t slots = flow ? flow_slots(units) : grid_slots(units, v.cap_blocks, split);
+  if (ws == kStaticScratch) {
+    const size_t need = decode_ws_slots(units, v.D, slots);
+    if (need > ws_bytes)
+      return fail(ETA_ERR_CAPACITY,
+                  "this decode needs %zu bytes of scratch; the static scratch holds %zu "
+                  "(use eta_decode with a workspace)", need, ws_bytes);
+    if (eta_status s = static_scratch(&ws, &ws_bytes)) return s;
+  } else {
+    const size_t need = decode_ws(units, v.D, v.cap_blocks, split);
+    if (!ws || ws_bytes < need)
+      return fail(ETA_ERR_WORKSPACE, "decode workspace %zu bytes < %zu", ws_bytes, need);
+  }
   char* w = static_cast<char*>(ws);
   const size_t off_start = 256;
   const size_t off_parts = off_start + align256((size_t)(units + 1) * 4);
@@ -299,10 +366,7 @@ static eta_status decode_common(const eta_cache* c, const float* q, const float*
   a.queue = reinterpret_cast<int*>(w);
   a.chunk_start = reinterpret_cast<int*>(w + off_start);
   a.queue_grid = device_cus() * ETA_QUEUE_WGS_PER_CU;
-  // Sparse decode runs balanced (equal ranges of all admitted blocks per
-  // wave) whenever its stream offsets fit in LDS.
-  a.use_flow = !dense && units <= eta::kMaxFlowUnits &&
-               units * (long long)v.cap_blocks < 0x7fffffffLL;
+  a.use_flow = flow;
   a.flow_grid = device_cus() * eta::kFlowWGsPerCU;
   a.flow_start = a.chunk_start;
   a.flow_info = reinterpret_cast<int*>(w + 64);
@@ -315,6 +379,14 @@ eta_status eta_decode(const eta_cache* c, const float* q, const float* tau_gate,
                       size_t workspace_bytes, float* out, void* stream) {
   return decode_common(c, q, tau_gate, active_idx, active_cnt, logit_mode, false, beta, scale,
                        blocks_per_split, workspace, workspace_bytes, out, stream);
+}
+
+eta_status eta_decode_noalloc(const eta_cache* c, const float* q, const float* tau_gate,
+                              const int32_t* active_idx, const int32_t* active_cnt,
+                              int32_t logit_mode, float beta, float scale,
+                              int32_t blocks_per_split, float* out, void* stream) {
+  return decode_common(c, q, tau_gate, active_idx, active_cnt, logit_mode, false, beta, scale,
+                       blocks_per_split, kStaticScratch, kScratchBytes, out, stream);
 }
 
 eta_status eta_dense_decode(const eta_cache* c, const float* q, float scale,

@@ -124,6 +124,24 @@ def test_decode_validation(lib):
     assert L.eta_dense_decode(cache(), FAKE, -1.0, 16, FAKE, ws, FAKE, None) == eb.ETA_ERR_BAD_ARG
 
 
+def test_decode_noalloc_validation(lib):
+    L = lib
+    args = lambda **o: [o.get("c", cache()), FAKE, o.get("tau", FAKE), FAKE, FAKE,
+                        o.get("mode", 0), 5.0, 0.088, o.get("split", 16), o.get("out", FAKE),
+                        None]
+    assert L.eta_decode_noalloc(*args(split=0)) == eb.ETA_ERR_BAD_ARG
+    assert L.eta_decode_noalloc(*args(tau=None)) == eb.ETA_ERR_NULL_PTR
+    assert L.eta_decode_noalloc(*args(out=None)) == eb.ETA_ERR_NULL_PTR
+    assert L.eta_decode_noalloc(*args(c=cache(batch=0, k=None, v=None, mu=None, var=None,
+                                                maxnorm=None, seq_len=None))) == eb.ETA_OK
+    # 8192 streams take the chunk grid: one partial per possible chunk (16 per
+    # stream here) is 64 MiB, beyond the 8 MiB static scratch; refused on the
+    # host, before any HIP call.
+    big = cache(batch=8192, heads=1, head_dim=128, block=4, cap_tokens=64)
+    assert L.eta_decode_noalloc(*args(c=big, split=1)) == eb.ETA_ERR_CAPACITY
+    assert "scratch" in err(L)
+
+
 def test_predict_and_calibrate_validation(lib):
     L = lib
     assert L.eta_predict_tau(2, 300, 128, FAKE, FAKE, FAKE, 0.0, FAKE, FAKE, None) == eb.ETA_ERR_BAD_SHAPE

@@ -12,7 +12,10 @@ Printed: one JSON line with dense-equivalent KV tokens/s (sum_b T_b per step
 / step time), the decode kernel's roofline against 8 TB/s, a density sweep
 (10/38/70/100%) with the in-house dense HIP decode at the same shape, and the
 fp64 oracle timed on the host on a bounded sample of the same workload.  A
-grouped-query section follows (32 sequences x 128K, 32 query heads on 4 KV
+`configs` section times the other decode workloads the same way (512K single
+sequence, the ragged batch of 32 with frozen calibrated thresholds, 32K
+single sequence), each with its dense decode, speedup, ideal speedup and
+roofline.  A grouped-query section follows (32 sequences x 128K, 32 query heads on 4 KV
 heads, d 64, b 64: eta_screen_gqa + eta_decode_gqa against the grouped dense
 decode at 38/25/10% head density) and a gated prefill section (8 x 2048, the
 pages' training shape: eta_gated_prefill against the bf16 matrix-core peak).
@@ -63,7 +66,16 @@ def parse():
                     help="run only the grouped-query section and print its JSON")
     ap.add_argument("--gqa-rho", default="0.38,0.25,0.10",
                     help="head densities of the grouped-query section")
+    ap.add_argument("--configs", default="ctx512k,ragged,ctx32k",
+                    help="other decode workloads timed after the headline one ('none': skip)")
     ap.add_argument("--seed", type=int, default=1234)
+    ap.add_argument("--summarize-counters", nargs=4, default=None,
+                    metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="turn rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE and "
+                         "WRITE_SIZE of a bench run, then of --copy-reference 1024) into the "
+                         "per-launch HBM bytes of --workload's decode call, stored in "
+                         "profiles/decode_counters.json (or gqa_decode_counters.json with "
+                         "--gqa-only) with the hash of the kernel sources")
     ap.add_argument("--copy-reference", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times "
                          "(reference dispatches for calibrating HBM byte counters)")
@@ -79,6 +91,44 @@ def copy_reference(mib: int) -> None:
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_reference_bytes": n, "dispatches": 5}), flush=True)
+
+
+def graph_call_ms(torch, fn, steps, warmup, flush=None):
+    """Mean duration of one call of `fn` (one or more kernel launches) on the
+    current stream (the stream the library launches on).  Without `flush`:
+    the call captured alone in a HIP graph and replayed `steps` times back to
+    back between two HIP events, so no host launch gap enters the figure.
+    With `flush` (a cache that could sit in the 256 MB last-level cache): the
+    buffer is overwritten before every call and events bracket each call
+    alone (the host has queued the call while the flush runs)."""
+    if flush is not None:
+        for _ in range(warmup):
+            fn()
+        pairs = []
+        for _ in range(steps):
+            flush.fill_(1.0)
+            s = torch.cuda.Event(enable_timing=True)
+            e = torch.cuda.Event(enable_timing=True)
+            s.record()
+            fn()
+            e.record()
+            pairs.append((s, e))
+        torch.cuda.synchronize()
+        return sum(s.elapsed_time(e) for s, e in pairs) / steps
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    for _ in range(warmup):
+        g.replay()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(steps):
+        g.replay()
+    e.record()
+    torch.cuda.synchronize()
+    del g
+    return s.elapsed_time(e) / steps
 
 
 class Timer:
@@ -109,100 +159,153 @@ def kernel_hash(files=DECODE_SRC) -> str:
 
 def counters_traffic(path, files, workload):
     """HBM bytes per launch from a committed counter summary, if it was taken
-    on the same kernel sources and workload."""
+    on the same kernel sources (and this workload)."""
     if not os.path.exists(path):
         return None
     cj = json.load(open(path))
-    if cj.get("kernel_hash") == kernel_hash(files) and cj.get("workload") == workload:
-        return cj.get("hbm_bytes_per_launch")
-    return None
+    if cj.get("kernel_hash") != kernel_hash(files):
+        return None
+    return cj.get("workloads", {}).get(workload, {}).get("hbm_bytes_per_launch")
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the decode path runs on a single GPU; see the sharding notes in the design).",
-              file=sys.stderr)
-        sys.exit(2)
-    if args.copy_reference:
-        copy_reference(args.copy_reference)
-        return
-    import numpy as np
-    import torch
+def _counter_rows(path):
+    """(kernel name, counter, value per dispatch) rows of a rocprofv3
+    counter_collection.csv, summed per dispatch."""
+    import csv
+    per = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            key = (r["Dispatch_Id"], r["Kernel_Name"], r["Counter_Name"])
+            per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    return [(k[1], k[2], v) for k, v in per.items()]
 
-    from long_context_decode_eta_amd import binding as eb
-    from long_context_decode_eta_amd import synth
 
-    if args.rho is None:
-        target = synth.CONFIGS[args.workload].get("rho", 0.38)
-        args.rho = target if isinstance(target, float) else 0.38
-    dev = "cuda"
-    torch.cuda.set_device(0)
-    gqa_rhos = [float(x) for x in args.gqa_rho.split(",")]
-    if args.prefill_only:
-        print(json.dumps(prefill_bench(torch, eb, synth, args.steps, args.warmup, args.seed)),
-              flush=True)
-        return
-    if args.gqa_only:
-        print(json.dumps(gqa_bench(torch, np, eb, synth, args.steps, args.warmup, args.seed,
-                                   gqa_rhos)), flush=True)
-        return
-    t0 = time.time()
-    blk = synth.CONFIGS[args.workload]["block"]
-    Tmax = synth.CONFIGS[args.workload]["T"]
-    Tmax = Tmax[1] if isinstance(Tmax, tuple) else Tmax
-    # room for the appends of the upkeep measurement (4 blocks per stream)
-    w = synth.make(args.workload, seed=args.seed, device=dev, cap=Tmax + 4 * blk)
-    B, H, D, bs = w.B, w.H, w.D, w.block
-    cache = eb.KVCache(B, H, D, bs, w.cap, w.kv_dtype, device=dev, k=w.k, v=w.v)
-    cache.seq_len.copy_(w.seq_len)
-    eb.build_block_meta(cache)
-    sl = w.seq_len.cpu().numpy().astype(np.int64)
-    sumT = int(sl.sum())
-    dec = eb.Decoder(cache, z=w.z, scale=w.scale, blocks_per_split=args.split or None)
-    split = dec.split
-    print(f"[bench] workload {args.workload}: B={B} H={H} D={D} b={bs} sumT={sumT} "
-          f"split={split} dense split={dec.dense_split} ({time.time() - t0:.1f}s setup)",
-          file=sys.stderr, flush=True)
-    W = w.W
-    # Per-head constants for each target density, from the library's calibration.
-    if w.tau_kind == "dynamic":
-        tau0 = torch.zeros((B, H), device=dev)
-        tmp = torch.zeros_like(tau0)
-        eb.predict_tau(w.q, W, torch.zeros(H, device=dev), 0.0, tau0, tmp)
-        qs, t0s = w.q[None].contiguous(), tau0[None].contiguous()
-    else:
-        qs, t0s = w.q_cal.contiguous(), None
-    cws = eb.workspace(eb.calibrate_workspace_bytes(qs.shape[0], B, H, cache.cap_blocks))
-    rhos = sorted(set([args.rho] + ([] if args.no_sweep else [0.10, 0.38, 0.70, 1.0])))
-    consts = {}
-    for rho in rhos:
-        c = torch.zeros(H, device=dev)
-        eb.calibrate_threshold(cache, qs, t0s, w.z, w.scale, rho, cws, c)
-        consts[rho] = c
-    del cws
-    frozen = W is None
-    if frozen:
-        # frozen constants: no predictor in the timed step; tau is the broadcast
-        def set_tau(c):
-            dec.predict(w.q, None, c)
-    torch.cuda.synchronize()
+def summarize_counters(args):
+    """Per-launch HBM bytes of the decode call of one workload from four
+    counter runs: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of a bench run,
+    each scaled by what the same counter reads for a plain 1 GiB device copy."""
+    fetch, write, cfetch, cwrite = args.summarize_counters
+    ref_bytes = 1 << 30
 
-    kv_bytes = 2 * w.k.numel() * w.k.element_size()
-    flush = (torch.empty((512 << 20) // 4, dtype=torch.float32, device=dev)
-             if kv_bytes < (2 << 30) else None)
+    def mean_of(rows, counter, pred):
+        vals = [v for k, c, v in rows if c == counter and pred(k)]
+        return sum(vals) / len(vals) if vals else 0.0, len(vals)
 
-    def run(rho, steps, warmup):
+    is_copy = lambda k: "copyBuffer" in k or "copy" in k.lower()
+    cf, _ = mean_of(_counter_rows(cfetch), "FETCH_SIZE", is_copy)
+    cw, _ = mean_of(_counter_rows(cwrite), "WRITE_SIZE", is_copy)
+    f_factor = ref_bytes / (cf * 1024.0)
+    w_factor = ref_bytes / (cw * 1024.0)
+    gqa = args.gqa_only
+    parts = (("decode_gqa_flow_kernel", "combine_gqa_flow_kernel") if gqa else
+             ("decode_flow_kernel", "combine_flow_kernel"))
+    frows, wrows = _counter_rows(fetch), _counter_rows(write)
+    table = []
+    total = 0.0
+    for kname in sorted({k for k, c, v in frows} | {k for k, c, v in wrows}):
+        short = kname.split("(")[0].replace("void ", "")
+        f, nf = mean_of(frows, "FETCH_SIZE", lambda k: k == kname)
+        w, nw = mean_of(wrows, "WRITE_SIZE", lambda k: k == kname)
+        rd, wr = f * 1024.0 * f_factor, w * 1024.0 * w_factor
+        table.append((short, max(nf, nw), f, w, rd, wr))
+        # the sparse decode call: balanced decode + combine (not the dense
+        # instantiation, whose template arguments end in ", true>")
+        if any(p in short for p in parts) and not short.endswith("true>"):
+            total += rd + wr
+    workload = "gqa128k" if gqa else args.workload
+    path = GQA_COUNTERS if gqa else COUNTERS
+    cj = json.load(open(path)) if os.path.exists(path) else {}
+    files = GQA_SRC if gqa else DECODE_SRC
+    if cj.get("kernel_hash") != kernel_hash(files):
+        cj = {}
+    cj["kernel_hash"] = kernel_hash(files)
+    cj["fetch_factor"], cj["write_factor"] = f_factor, w_factor
+    cj.setdefault("workloads", {})[workload] = {
+        "hbm_bytes_per_launch": int(round(total)),
+        "note": f"{' + '.join(parts)} per {'eta_decode_gqa' if gqa else 'eta_decode'} call; "
+                "FETCH_SIZE and WRITE_SIZE scaled by a 1 GiB device copy"}
+    with open(path, "w") as f:
+        json.dump(cj, f, indent=1)
+    print(f"copy reference: FETCH_SIZE x {f_factor:.4f}, WRITE_SIZE x {w_factor:.4f}")
+    print("| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled read MB | "
+          "scaled write MB |")
+    print("|---|---|---|---|---|---|")
+    for short, n, f, w, rd, wr in table:
+        print(f"| `{short}` | {n} | {f:.1f} | {w:.1f} | {rd / 1e6:.1f} | {wr / 1e6:.1f} |")
+    print(f"decode call ({workload}): {total / 1e9:.4f} GB of HBM traffic per call "
+          f"(kernel hash {cj['kernel_hash']})")
+class DecodeBench:
+    """One decode workload resident on the GPU: cache, statistics, per-head
+    constants from the library's calibration for each target density, and the
+    step (threshold, screen, decode) timed eagerly per kernel and as a HIP
+    graph, beside the in-house dense decode at the same shape."""
+
+    def __init__(self, torch, np, eb, synth, name, seed, split=0, cap_extra_blocks=0):
+        self.torch, self.np, self.eb, self.name = torch, np, eb, name
+        dev = "cuda"
+        t0 = time.time()
+        blk = synth.CONFIGS[name]["block"]
+        Tmax = synth.CONFIGS[name]["T"]
+        Tmax = Tmax[1] if isinstance(Tmax, tuple) else Tmax
+        w = synth.make(name, seed=seed, device=dev, cap=Tmax + cap_extra_blocks * blk)
+        self.w = w
+        B, H, D, bs = w.B, w.H, w.D, w.block
+        self.cache = eb.KVCache(B, H, D, bs, w.cap, w.kv_dtype, device=dev, k=w.k, v=w.v)
+        self.cache.seq_len.copy_(w.seq_len)
+        eb.build_block_meta(self.cache)
+        self.sl = w.seq_len.cpu().numpy().astype(np.int64)
+        self.sumT = int(self.sl.sum())
+        self.dec = eb.Decoder(self.cache, z=w.z, scale=w.scale, blocks_per_split=split or None)
+        self.split = self.dec.split
+        self.frozen = w.W is None
+        self.elt = 2 if w.kv_dtype == torch.bfloat16 else 4
+        self.consts = {}
+        kv_bytes = 2 * w.k.numel() * w.k.element_size()
+        # a cache that could sit in the 256 MB last-level cache is flushed
+        # (512 MiB written) before every step of the latency distribution
+        self.flush = (torch.empty((512 << 20) // 4, dtype=torch.float32, device=dev)
+                      if kv_bytes < (2 << 30) else None)
+        nbc = self.sl // bs
+        self.meta_bytes = int(H * (nbc * (2 * D + 1) * 4).sum())
+        self.dense_bytes = self.sumT * H * D * 2 * self.elt
+        print(f"[bench] workload {name}: B={B} H={H} D={D} b={bs} sumT={self.sumT} "
+              f"split={self.split} dense split={self.dec.dense_split} "
+              f"({time.time() - t0:.1f}s setup)", file=sys.stderr, flush=True)
+
+    def calibrate(self, rhos):
+        """Per-head constants for each target density (eta_calibrate_threshold;
+        dynamic thresholds pool score - qbar W over the timed query, frozen
+        ones pool the workload's calibration queries)."""
+        torch, eb, w = self.torch, self.eb, self.w
+        B, H = w.B, w.H
+        if not self.frozen:
+            tau0 = torch.zeros((B, H), device="cuda")
+            tmp = torch.zeros_like(tau0)
+            eb.predict_tau(w.q, w.W, torch.zeros(H, device="cuda"), 0.0, tau0, tmp)
+            qs, t0s = w.q[None].contiguous(), tau0[None].contiguous()
+        else:
+            qs, t0s = w.q_cal.contiguous(), None
+        cws = eb.workspace(eb.calibrate_workspace_bytes(qs.shape[0], B, H,
+                                                        self.cache.cap_blocks))
+        for rho in rhos:
+            c = torch.zeros(H, device="cuda")
+            eb.calibrate_threshold(self.cache, qs, t0s, w.z, w.scale, rho, cws, c)
+            self.consts[rho] = c
+        del cws
+        torch.cuda.synchronize()
+
+    def run(self, rho, steps, warmup):
         """Eager steps timed per kernel with HIP events, then the same step
         captured once in a HIP graph (checked bit for bit against the eager
         output) and timed over `steps` replays."""
-        c = consts[rho]
-        if frozen:
-            set_tau(c)
+        torch, np, w, dec = self.torch, self.np, self.w, self.dec
+        c = self.consts[rho]
+        W = w.W
+        if self.frozen:  # no predictor in the timed step: tau is the constants
+            dec.predict(w.q, None, c)
 
         def step():
-            if not frozen:
+            if not self.frozen:
                 dec.predict(w.q, W, c)
             dec.screen(w.q)
             dec.attend(w.q)
@@ -215,20 +318,17 @@ def main():
         torch.cuda.synchronize()
         a = time.perf_counter()
         for _ in range(steps):
-            if not frozen:
+            if not self.frozen:
                 dec.predict(w.q, W, c)
             tscr.around(lambda: dec.screen(w.q))
             tdec.around(lambda: dec.attend(w.q))
         torch.cuda.synchronize()
         eager = time.perf_counter() - a
         toks = (int(dec.density_ctr.item()) - ctr0) // steps
-        # Per-step latency distribution (HIP events around each whole step); for
-        # a cache that could sit in the 256 MB last-level cache, 512 MiB of
-        # scratch is written before every timed step so no step reads KV from it.
         per_step = []
         for _ in range(steps):
-            if flush is not None:
-                flush.fill_(1.0)
+            if self.flush is not None:
+                self.flush.fill_(1.0)
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record()
@@ -257,15 +357,28 @@ def main():
         torch.cuda.synchronize()
         wall = time.perf_counter() - a
         del graph
+        # The decode call (balanced decode + combine kernels) and the screen
+        # call (screen + compaction), each replayed alone as a graph.
+        decode_ms = graph_call_ms(torch, lambda: dec.attend(w.q), steps, warmup, self.flush)
+        screen_ms = graph_call_ms(torch, lambda: dec.screen(w.q), steps, warmup, self.flush)
         pct = lambda f: lat[min(len(lat) - 1, int(f * (len(lat) - 1) + 0.5))]
-        return dict(ms=wall * 1e3 / steps, eager_ms=eager * 1e3 / steps,
-                    step_ms_median=pct(0.5), step_ms_p10=pct(0.1), step_ms_p90=pct(0.9),
-                    decode_ms=tdec.mean_ms(), screen_ms=tscr.mean_ms(),
-                    density=toks / (H * sumT), tokens=toks, cnt=cnt)
+        r = dict(ms=wall * 1e3 / steps, eager_ms=eager * 1e3 / steps,
+                 step_ms_median=pct(0.5), step_ms_p10=pct(0.1), step_ms_p90=pct(0.9),
+                 decode_ms=decode_ms, screen_ms=screen_ms,
+                 eager_decode_ms=tdec.mean_ms(), eager_screen_ms=tscr.mean_ms(),
+                 density=toks / (w.H * self.sumT), tokens=toks, cnt=cnt)
+        r["decode_bytes"] = self.decode_bytes(r)
+        r["step_bytes"] = self.step_bytes(r)
+        print(f"[bench] {self.name} rho={rho:.2f}: density {r['density']:.4f} step "
+              f"{r['ms']:.4f} ms (eager {r['eager_ms']:.4f}; screen {r['screen_ms']:.4f}, "
+              f"decode {r['decode_ms']:.4f}) {r['step_bytes'] / r['ms'] / 1e6:.0f} GB/s",
+              file=sys.stderr, flush=True)
+        return r
 
-    def run_dense(steps, warmup):
+    def run_dense(self, steps, warmup):
         """The in-house dense decode at the same shape, captured in a HIP graph
         like the sparse step."""
+        torch, dec, w = self.torch, self.dec, self.w
         graph = torch.cuda.CUDAGraph()
         dec.dense(w.q)
         torch.cuda.synchronize()
@@ -278,67 +391,155 @@ def main():
         for _ in range(steps):
             graph.replay()
         torch.cuda.synchronize()
-        return (time.perf_counter() - a) * 1e3 / steps
+        ms = (time.perf_counter() - a) * 1e3 / steps
+        print(f"[bench] {self.name} dense: {ms:.4f} ms ({self.dense_bytes / ms / 1e6:.0f} GB/s)",
+              file=sys.stderr, flush=True)
+        return ms
 
-    elt = 2 if w.kv_dtype == torch.bfloat16 else 4
-    nbc = sl // bs
-    meta_bytes = int(H * (nbc * (2 * D + 1) * 4).sum())
-
-    def decode_bytes(r):
-        # algorithmic bytes of one eta_decode call: admitted K+V, q, the active
-        # list, partial (m, l, acc) write + read for multi-chunk streams, output
-        chunks = -(-r["cnt"] // split)
+    def decode_bytes(self, r):
+        """Algorithmic bytes of one eta_decode call: admitted K+V, q, the
+        active lists, partials (m, l, acc) written and read for streams split
+        over several ranges, output."""
+        np, w = self.np, self.w
+        B, H, D = w.B, w.H, w.D
+        chunks = -(-r["cnt"] // self.split)
         part = int((np.where(chunks > 1, chunks, 0) * (D + 2) * 4 * 2).sum())
-        return r["tokens"] * D * 2 * elt + B * H * D * 4 * 2 + int(r["cnt"].sum()) * 4 + part
+        return (r["tokens"] * D * 2 * self.elt + B * H * D * 4 * 2 + int(r["cnt"].sum()) * 4 +
+                part)
 
-    def step_bytes(r):
-        pred = 0 if frozen else B * H * D * 4 + H * D * H * 4 + 2 * B * H * 4
-        screen = meta_bytes + B * H * D * 4 + int(r["cnt"].sum()) * 4 + B * H * 4
-        return pred + screen + decode_bytes(r)
+    def step_bytes(self, r):
+        w = self.w
+        B, H, D = w.B, w.H, w.D
+        pred = 0 if self.frozen else B * H * D * 4 + H * D * H * 4 + 2 * B * H * 4
+        screen = self.meta_bytes + B * H * D * 4 + int(r["cnt"].sum()) * 4 + B * H * 4
+        return pred + screen + r["decode_bytes"]
 
-    sweep = {}
-    main = None
-    for rho in rhos:
-        r = run(rho, args.steps, args.warmup)
-        r["step_bytes"] = step_bytes(r)
-        r["decode_bytes"] = decode_bytes(r)
-        sweep[rho] = r
-        print(f"[bench] rho={rho:.2f}: density {r['density']:.4f} step {r['ms']:.4f} ms "
-              f"(eager {r['eager_ms']:.4f}; screen {r['screen_ms']:.4f}, "
-              f"decode {r['decode_ms']:.4f}) "
-              f"{r['step_bytes'] / r['ms'] / 1e6:.0f} GB/s", file=sys.stderr, flush=True)
-        if rho == args.rho:
-            main = r
-    dense_ms = run_dense(args.steps, args.warmup)
-    dense_bytes = sumT * H * D * 2 * elt
-    print(f"[bench] dense: {dense_ms:.4f} ms ({dense_bytes / dense_ms / 1e6:.0f} GB/s)",
-          file=sys.stderr, flush=True)
-
-    # Headline run: exactly `steps` timed steps at the headline density.
-    r = run(args.rho, args.steps, args.warmup)
-    r["step_bytes"] = step_bytes(r)
-    r["decode_bytes"] = decode_bytes(r)
-    main = r
-    value = sumT / (r["ms"] * 1e-3)
-    achieved = r["decode_bytes"] / (r["decode_ms"] * 1e-3) / 1e9
-    traffic = counters_traffic(COUNTERS, DECODE_SRC, args.workload)
-    # The measured streaming peak beside the spec: the dense decode reads every
-    # K and V byte of the same cache in long contiguous runs.
-    stream_gbs = dense_bytes / dense_ms / 1e6
-    roofline = {"bound": "hbm", "kernel": "eta_decode (balanced decode + combine kernels)",
+    def roofline(self, r, dense_ms):
+        achieved = r["decode_bytes"] / (r["decode_ms"] * 1e-3) / 1e9
+        stream_gbs = self.dense_bytes / dense_ms / 1e6
+        return {"bound": "hbm", "kernel": "eta_decode (balanced decode + combine kernels)",
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": counters_traffic(COUNTERS, DECODE_SRC, self.name),
                 "algorithmic_bytes_per_launch": int(r["decode_bytes"]),
                 "avg_launch_ms": round(r["decode_ms"], 5),
                 "measured_stream_gbs": round(stream_gbs, 1),
                 "frac_of_measured_stream": round(achieved / stream_gbs, 4)}
 
-    offsets = None if args.no_sweep else offset_sweep(torch, np, eb, w, dec, consts[args.rho],
-                                                       frozen, sumT, args.steps, args.warmup)
-    upkeep = measure_upkeep(torch, eb, w, cache, dec, consts[args.rho], frozen, sumT)
+    def summary(self, r, dense_ms):
+        return {"density": round(r["density"], 4), "ms": round(r["ms"], 5),
+                "eager_ms": round(r["eager_ms"], 5),
+                "tokens_per_s": round(self.sumT / (r["ms"] * 1e-3), 1),
+                "step_gbs": round(r["step_bytes"] / r["ms"] / 1e6, 1),
+                "decode_gbs": round(r["decode_bytes"] / r["decode_ms"] / 1e6, 1),
+                "screen_ms": round(r["screen_ms"], 5),
+                "decode_ms": round(r["decode_ms"], 5),
+                "speedup_vs_dense": round(dense_ms / r["ms"], 3),
+                "ideal_speedup": round(self.dense_bytes / r["step_bytes"], 3)}
+
+    def describe(self, rho):
+        w, sl = self.w, self.sl
+        return (f"{self.name}: batch {w.B}, {w.H} heads, head dim {w.D}, context "
+                f"{int(sl.min()) if sl.min() != sl.max() else int(sl.max())}"
+                f"{'..' + str(int(sl.max())) if sl.min() != sl.max() else ''} "
+                f"(sum {self.sumT}), block {w.block}, z {w.z}, "
+                f"{'bf16' if self.elt == 2 else 'fp32'} KV, "
+                f"{'frozen calibrated' if self.frozen else 'dynamic linear'} tau at "
+                f"{rho:.0%} target density")
+
+    def release(self):
+        self.dec = self.cache = self.w = self.flush = None
+        self.consts = {}
+        self.torch.cuda.empty_cache()
+
+
+def config_bench(torch, np, eb, synth, name, steps, warmup, seed):
+    """One more decode workload at its target density: the step, the dense
+    decode, speedup against the ideal (the ratio of algorithmic bytes) and the
+    decode call's roofline."""
+    target = synth.CONFIGS[name].get("rho", 0.38)
+    rho = target if isinstance(target, float) else 0.38
+    b = DecodeBench(torch, np, eb, synth, name, seed)
+    b.calibrate([rho])
+    r = b.run(rho, steps, warmup)
+    dense_ms = b.run_dense(steps, warmup)
+    out = {"workload": b.describe(rho), **b.summary(r, dense_ms),
+           "dense_ms": round(dense_ms, 5), "blocks_per_split": b.split,
+           "dense_blocks_per_split": b.dec.dense_split,
+           "step_ms_median": round(r["step_ms_median"], 5),
+           "step_ms_p10": round(r["step_ms_p10"], 5), "step_ms_p90": round(r["step_ms_p90"], 5),
+           "llc_flushed": b.flush is not None,
+           "roofline": b.roofline(r, dense_ms)}
+    b.release()
+    return out
+
+
+def main():
+    args = parse()
+    if args.summarize_counters:
+        summarize_counters(args)
+        return
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the decode path runs on a single GPU; see the sharding notes in the design).",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.copy_reference:
+        copy_reference(args.copy_reference)
+        return
+    import numpy as np
+    import torch
+
+    from long_context_decode_eta_amd import binding as eb
+    from long_context_decode_eta_amd import synth
+
+    if args.rho is None:
+        target = synth.CONFIGS[args.workload].get("rho", 0.38)
+        args.rho = target if isinstance(target, float) else 0.38
+    torch.cuda.set_device(0)
+    gqa_rhos = [float(x) for x in args.gqa_rho.split(",")]
+    if args.prefill_only:
+        print(json.dumps(prefill_bench(torch, eb, synth, args.steps, args.warmup, args.seed)),
+              flush=True)
+        return
+    if args.gqa_only:
+        print(json.dumps(gqa_bench(torch, np, eb, synth, args.steps, args.warmup, args.seed,
+                                   gqa_rhos)), flush=True)
+        return
+    # room for the appends of the upkeep measurement (4 blocks per stream)
+    hb = DecodeBench(torch, np, eb, synth, args.workload, args.seed, split=args.split,
+                     cap_extra_blocks=4)
+    w, dec, sumT = hb.w, hb.dec, hb.sumT
+    B, H, D, bs = w.B, w.H, w.D, w.block
+    rhos = sorted(set([args.rho] + ([] if args.no_sweep else [0.10, 0.38, 0.70, 1.0])))
+    hb.calibrate(rhos)
+
+    sweep = {rho: hb.run(rho, args.steps, args.warmup) for rho in rhos}
+    dense_ms = hb.run_dense(args.steps, args.warmup)
+
+    # Headline run: exactly `steps` timed steps at the headline density.
+    r = hb.run(args.rho, args.steps, args.warmup)
+    value = sumT / (r["ms"] * 1e-3)
+    roofline = hb.roofline(r, dense_ms)
+
+    offsets = None if args.no_sweep else offset_sweep(torch, np, eb, w, dec, hb.consts[args.rho],
+                                                       hb.frozen, sumT, args.steps, args.warmup)
+    upkeep = measure_upkeep(torch, eb, w, hb.cache, dec, hb.consts[args.rho], hb.frozen, sumT)
     print(f"[bench] upkeep: {json.dumps(upkeep)}", file=sys.stderr, flush=True)
 
-    cpu = None if args.no_cpu else cpu_baseline(w, consts[args.rho], args.rho)
+    cpu = None if args.no_cpu else cpu_baseline(w, hb.consts[args.rho], args.rho)
+    describe = hb.describe(args.rho)
+    elt, sl, split, dense_split = hb.elt, hb.sl, hb.split, dec.dense_split
+    llc_flushed = hb.flush is not None
+    sweep_out = {f"{k:.2f}": hb.summary(v, dense_ms) for k, v in sweep.items()}
+    hb.release()
+    del w, dec
+
+    configs = {}
+    if args.configs != "none":
+        for name in [x for x in args.configs.split(",") if x and x != args.workload]:
+            configs[name] = config_bench(torch, np, eb, synth, name, args.steps, args.warmup,
+                                         args.seed)
     gqa = None
     if not args.no_gqa:
         gqa = gqa_bench(torch, np, eb, synth, args.steps, args.warmup, args.seed, gqa_rhos)
@@ -357,38 +558,27 @@ def main():
         "eager_ms_per_step": round(r["eager_ms"], 5),
         "eager_step_ms": {"median": round(r["step_ms_median"], 5),
                           "p10": round(r["step_ms_p10"], 5), "p90": round(r["step_ms_p90"], 5),
-                          "llc_flushed": flush is not None},
+                          "llc_flushed": llc_flushed},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": f"{args.workload}: batch {B}, {H} heads, head dim {D}, "
-                        f"context {int(sl.max())} (sum {sumT}), block {bs}, z {w.z}, "
-                        f"{'bf16' if elt == 2 else 'fp32'} KV, "
-                        f"{'frozen calibrated' if frozen else 'dynamic linear'} tau at "
-                        f"{args.rho:.0%} target density",
+            "workload": describe,
             "global_batch": B, "seq_len": int(sl.max()), "parallelism": "single GPU",
             "kv_dtype": "bf16" if elt == 2 else "f32", "blocks_per_split": split,
-            "dense_blocks_per_split": dec.dense_split,
+            "dense_blocks_per_split": dense_split,
         },
         "density": round(r["density"], 4),
         "step_hbm_gbs": round(r["step_bytes"] / r["ms"] / 1e6, 1),
         "step_roofline_frac": round(r["step_bytes"] / r["ms"] / 1e6 / HBM_PEAK_GBS, 4),
         "dense_ms": round(dense_ms, 5),
         "speedup_vs_dense": round(dense_ms / r["ms"], 3),
-        "sweep": {f"{k:.2f}": {"density": round(v["density"], 4), "ms": round(v["ms"], 5),
-                               "eager_ms": round(v["eager_ms"], 5),
-                               "tokens_per_s": round(sumT / (v["ms"] * 1e-3), 1),
-                               "step_gbs": round(v["step_bytes"] / v["ms"] / 1e6, 1),
-                               "decode_gbs": round(v["decode_bytes"] / v["decode_ms"] / 1e6, 1),
-                               "screen_ms": round(v["screen_ms"], 5),
-                               "decode_ms": round(v["decode_ms"], 5),
-                               "speedup_vs_dense": round(dense_ms / v["ms"], 3),
-                               "ideal_speedup": round(dense_bytes / v["step_bytes"], 3)}
-                  for k, v in sweep.items()},
+        "ideal_speedup": round(hb.dense_bytes / r["step_bytes"], 3),
+        "sweep": sweep_out,
         "roofline": roofline,
+        "configs": configs,
         "offset_sweep": offsets,
         "upkeep": upkeep,
         "cpu_baseline": cpu,
@@ -585,6 +775,8 @@ def gqa_bench(torch, np, eb, synth, steps, warmup, seed, rhos=(0.38, 0.25, 0.10)
         torch.cuda.synchronize()
         ms = (time.perf_counter() - a) * 1e3 / steps
         del graph
+        decode_ms = graph_call_ms(torch, lambda: dec.attend(w.q), steps, warmup)
+        screen_ms = graph_call_ms(torch, lambda: dec.screen(w.q), steps, warmup)
         union_tok = int(ctr[1])
         chunks = -(-ucnt // dec.split)
         part = int((np.where(chunks > 1, chunks, 0) * G * (D + 2) * 4 * 2).sum())
@@ -593,9 +785,11 @@ def gqa_bench(torch, np, eb, synth, steps, warmup, seed, rhos=(0.38, 0.25, 0.10)
             "decode_bytes": int(dbytes),
             "d_head": round(int(ctr[0]) / (sumT * Hq), 4),
             "d_union": round(union_tok / (sumT * Hkv), 4),
-            "ms": round(ms, 5), "screen_ms": round(tscr.mean_ms(), 5),
-            "decode_ms": round(tdec.mean_ms(), 5),
-            "decode_gbs": round(dbytes / tdec.mean_ms() / 1e6, 1),
+            "ms": round(ms, 5), "screen_ms": round(screen_ms, 5),
+            "decode_ms": round(decode_ms, 5),
+            "eager_screen_ms": round(tscr.mean_ms(), 5),
+            "eager_decode_ms": round(tdec.mean_ms(), 5),
+            "decode_gbs": round(dbytes / decode_ms / 1e6, 1),
             "tokens_per_s": round(sumT / (ms * 1e-3), 1)}
         print(f"[bench] gqa rho={rho:.2f}: {json.dumps(res[f'{rho:.2f}'])}", file=sys.stderr,
               flush=True)

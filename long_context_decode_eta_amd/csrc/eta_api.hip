@@ -432,8 +432,11 @@ eta_status eta_calibrate_threshold(const eta_cache* c, int32_t n_sets, const flo
 // ---------------------------------------------------------------------------
 // Grouped-query attention.
 
+// Grouped screen workspace: the union admission words (8 bytes per 64 blocks)
+// followed by each word's admitted head tokens (4 bytes).
 size_t eta_screen_gqa_workspace_bytes(int32_t batch, int32_t kv_heads, int32_t cap_blocks) {
-  return eta_screen_workspace_bytes(batch, kv_heads, cap_blocks);
+  if (batch <= 0 || kv_heads <= 0 || cap_blocks <= 0) return 256;
+  return align256((size_t)batch * kv_heads * (size_t)eta::ceil_div(cap_blocks, 64) * 12);
 }
 
 eta_status eta_screen_gqa(const eta_cache* c, int32_t group, const float* q,

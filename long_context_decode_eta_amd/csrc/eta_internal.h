@@ -142,6 +142,33 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// Exclusive prefix sum of v over a work-group of NW waves (every thread
+// calls it): an inclusive scan within each wave by shuffles, then the wave
+// totals from LDS (s_w holds NW ints).  *total receives the sum over the
+// work-group.  Two barriers; s_w may be reused after the call.
+template <int NW>
+__device__ __forceinline__ int wg_exclusive_scan(int v, int* s_w, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int y = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += y;
+  }
+  if (lane == kWave - 1) s_w[wave] = incl;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int x = s_w[w];
+    base += w < wave ? x : 0;
+    tot += x;
+  }
+  __syncthreads();
+  *total = tot;
+  return base + incl - v;
+}
+
 // ---------------------------------------------------------------------------
 // Matrix-core tiles (grouped-query decode, gated prefill).  A 32-key tile of K
 // and V passes through LDS: K rows as stored with their 16-byte chunks

@@ -21,22 +21,61 @@ namespace eta {
 
 // ---------------------------------------------------------------------------
 // Screen: one work-group per 64-block admission word of KV stream u; wave w
-// scores blocks 16 w .. 16 w + 15 of the word (8 lanes per block).  A block's
-// statistics are loaded once and scored against every query head of the
-// group (queries, norms and thresholds staged in LDS).  Writes the per-block
-// head mask (bit g: query head u*G + g admits the block) for every block of
-// the stream and the union admission word.
-template <int D>
+// scores blocks 16 w .. 16 w + 15 of the word in two steps of 8 blocks, 8
+// lanes per block.  A block's statistics are loaded once and scored against
+// every query head of the group: each lane forms the partial dot products
+// q_g . mu and (q_g * q_g) . var over its 8 dims for all NH head slots (NH = 8
+// for groups up to 8, 16 up to 16; queries and their squares staged in LDS,
+// zero past the group), and an exchange butterfly over the 8 lanes of the
+// block (partners l ^ 1, l ^ 2, l ^ 4) leaves lane l with the complete sums
+// of NH / 8 heads: at each step a lane keeps half of its values and adds its
+// partner's copy of them.  The additions pair the same partial sums as
+// group_sum<8> (whose last partner, the half-row mirror l ^ 7, holds the same
+// sum as l ^ 4 with its operands commuted), so each head's sums are
+// bit-identical to the one-query-per-KV-head screen's.  Each head is then scored once (Eq. 5) instead of
+// on all 8 lanes.  Writes the per-block head mask (bit g: query head u*G + g
+// admits the block) for every block of the stream, the union admission word,
+// and the word's admitted head tokens (for the D_head counter).
+
+// Keep half of the N values of x (the upper half when `upper`), adding the
+// copy held by the partner lane: lane ^ 1 or lane ^ 2 by a DPP quad
+// permutation (CTRL), lane ^ 4 by ds_swizzle (CTRL = 0: and-mask 31, xor 4).
+constexpr int kSwizzleXor4 = 0x101F;
+template <int N, int CTRL>
+__device__ __forceinline__ void fold_half_dpp(float* x, bool upper) {
+#pragma unroll
+  for (int i = 0; i < N / 2; ++i) {
+    const float send = upper ? x[i] : x[N / 2 + i];
+    const float keep = upper ? x[N / 2 + i] : x[i];
+    const float other =
+        CTRL ? dpp<CTRL>(send)
+             : __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(send), kSwizzleXor4));
+    x[i] = keep + other;
+  }
+}
+
+// Head slot of the first value lane li (0..7) holds after the butterfly:
+// step k keeps the half selected by bit k of li, so bits 0, 1, 2 of li pick
+// the head's top three bits in that order.
+__device__ __forceinline__ int rev3(int li) {
+  return ((li & 1) << 2) | (li & 2) | ((li >> 2) & 1);
+}
+
+template <int D, int NH>
 __global__ __launch_bounds__(256) void screen_gqa_kernel(CacheView c, int G, const float* q,
                                                          const float* tau_screen, float z,
                                                          float scale, uint32_t* head_mask,
-                                                         uint64_t* words, int words_per_unit) {
+                                                         uint64_t* words, uint32_t* word_tokens,
+                                                         int words_per_unit) {
   constexpr int LPB = 8;            // lanes per block
   constexpr int NL = D / 32;        // float4 loads per lane per statistics row
-  __shared__ float s_q[kMaxGroup][D];
-  __shared__ float s_qn[kMaxGroup];
-  __shared__ float s_ts[kMaxGroup];
+  constexpr int PER = NH / 8;       // heads per lane after the butterfly
+  __shared__ __align__(16) float s_q[NH][D];
+  __shared__ __align__(16) float s_q2[NH][D];
+  __shared__ float s_qn[NH];
+  __shared__ float s_ts[NH];
   __shared__ uint32_t s_bits[4];
+  __shared__ uint32_t s_tok[4];
   const int units = c.B * c.H;
   const int u = blockIdx.x % units, wd = blockIdx.x / units;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -61,15 +100,21 @@ __global__ __launch_bounds__(256) void screen_gqa_kernel(CacheView c, int G, con
     }
     Ms[it] = scored ? c.maxnorm[(size_t)u * c.cap_blocks + j] : 0.f;
   }
-  for (int i = threadIdx.x; i < G * D; i += blockDim.x) s_q[i / D][i % D] = q[(size_t)u * G * D + i];
-  if (threadIdx.x < G) s_ts[threadIdx.x] = tau_screen[(size_t)u * G + threadIdx.x];
+  for (int i = threadIdx.x; i < NH * D; i += blockDim.x) {
+    const int g = i / D;
+    const float x = g < G ? q[(size_t)u * G * D + i] : 0.f;
+    s_q[g][i % D] = x;
+    s_q2[g][i % D] = x * x;
+  }
+  if (threadIdx.x < NH) s_ts[threadIdx.x] = threadIdx.x < G ? tau_screen[(size_t)u * G + threadIdx.x] : 0.f;
   __syncthreads();
   // ||q|| per head, 8 lanes per head summing in the same order as the
   // one-head-per-KV-head screen (so G = 1 reproduces it bit for bit).
-  {
-    const int hg = wave * 8 + gi;
+#pragma unroll
+  for (int h8 = 0; h8 < NH; h8 += 32) {
+    const int hg = h8 + wave * 8 + gi;
     float qq = 0.f;
-    if (hg < G) {
+    if (hg < NH) {
 #pragma unroll
       for (int t = 0; t < NL; ++t) {
         const float4 v = *reinterpret_cast<const float4*>(&s_q[hg][32 * t + 4 * li]);
@@ -80,79 +125,108 @@ __global__ __launch_bounds__(256) void screen_gqa_kernel(CacheView c, int G, con
       }
     }
     qq = group_sum<LPB>(qq);
-    if (hg < G && li == 0) s_qn[hg] = sqrtf(qq);
+    if (hg < NH && li == 0) s_qn[hg] = sqrtf(qq);
   }
   __syncthreads();
   const bool z_inf = __builtin_isinf(z);
-  const uint32_t all = (G >= 32) ? 0xffffffffu : ((1u << G) - 1u);
-  uint32_t bits = 0;
+  const int tail = T - ((nb - 1) << c.log2bs);
+  uint32_t bits = 0, tokens = 0;
 #pragma unroll
   for (int it = 0; it < 2; ++it) {
     const int j = (wd << 6) + wave * 16 + it * 8 + gi;
     const bool scored = j < nbc;
-    const float M = Ms[it];
-    uint32_t mask = 0;
-    for (int g = 0; g < G; ++g) {
+    // v[2 g] = q_g . mu, v[2 g + 1] = (q_g * q_g) . var over this lane's dims
+    float v[2 * NH];
+#pragma unroll
+    for (int g = 0; g < NH; ++g) {
       float dot = 0.f, mom = 0.f;
 #pragma unroll
       for (int t = 0; t < NL; ++t) {
         const float4 qv = *reinterpret_cast<const float4*>(&s_q[g][32 * t + 4 * li]);
+        const float4 q2 = *reinterpret_cast<const float4*>(&s_q2[g][32 * t + 4 * li]);
         dot = fmaf(qv.x, m4[it][t].x, dot);
         dot = fmaf(qv.y, m4[it][t].y, dot);
         dot = fmaf(qv.z, m4[it][t].z, dot);
         dot = fmaf(qv.w, m4[it][t].w, dot);
-        mom = fmaf(qv.x * qv.x, v4[it][t].x, mom);
-        mom = fmaf(qv.y * qv.y, v4[it][t].y, mom);
-        mom = fmaf(qv.z * qv.z, v4[it][t].z, mom);
-        mom = fmaf(qv.w * qv.w, v4[it][t].w, mom);
+        mom = fmaf(q2.x, v4[it][t].x, mom);
+        mom = fmaf(q2.y, v4[it][t].y, mom);
+        mom = fmaf(q2.z, v4[it][t].z, mom);
+        mom = fmaf(q2.w, v4[it][t].w, mom);
       }
-      dot = group_sum<LPB>(dot);
-      mom = group_sum<LPB>(mom);
-      const float geometric = s_qn[g] * M;
-      const float sc = z_inf ? scale * geometric
-                             : scale * fminf(fmaf(z, sqrtf(mom), dot), geometric);
-      if (scored && sc >= s_ts[g]) mask |= 1u << g;
+      v[2 * g] = dot;
+      v[2 * g + 1] = mom;
     }
-    if (j == nb - 1) mask = all;  // the last block is admitted for every head
+    fold_half_dpp<2 * NH, kQuadXor1>(v, li & 1);
+    fold_half_dpp<NH, kQuadXor2>(v, li & 2);
+    fold_half_dpp<NH / 2, 0>(v, li & 4);
+    // This lane now holds heads PER * rev3(li) + e, e < PER: (v[2e], v[2e+1]).
+    uint32_t mine = 0;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int g = PER * rev3(li) + e;
+      const float geometric = s_qn[g] * Ms[it];
+      const float sc = z_inf ? scale * geometric
+                             : scale * fminf(fmaf(z, sqrtf(v[2 * e + 1]), v[2 * e]), geometric);
+      if (g < G && scored && sc >= s_ts[g]) mine |= 1u << g;
+    }
+    // OR of the block's 8 lanes (disjoint head bits).
+    mine |= __shfl_xor(mine, 1, kWave);
+    mine |= __shfl_xor(mine, 2, kWave);
+    mine |= __shfl_xor(mine, 4, kWave);
+    const uint32_t all = (G >= 32) ? 0xffffffffu : ((1u << G) - 1u);
+    const uint32_t mask = (j == nb - 1) ? all : mine;  // the last block: every head
     if (li == 0 && j < nb) head_mask[(size_t)u * c.cap_blocks + j] = mask;
+    if (li == 0 && j < nb)
+      tokens += (uint32_t)__popc(mask) * (uint32_t)(j == nb - 1 ? tail : c.bs);
     const uint64_t bal = __ballot(mask != 0u);
 #pragma unroll
     for (int g8 = 0; g8 < 8; ++g8)
       bits |= (uint32_t)((bal >> (g8 * LPB)) & 1ull) << (it * 8 + g8);
   }
-  if (lane == 0) s_bits[wave] = bits;
+  // Head tokens of the wave: lanes 0, 8, ..., 56 hold their blocks' counts.
+  tokens += __shfl_xor(tokens, 8, kWave);
+  tokens += __shfl_xor(tokens, 16, kWave);
+  tokens += __shfl_xor(tokens, 32, kWave);
+  if (lane == 0) {
+    s_bits[wave] = bits;
+    s_tok[wave] = tokens;
+  }
   __syncthreads();
   if (threadIdx.x == 0) {
     const uint64_t word = (uint64_t)s_bits[0] | ((uint64_t)s_bits[1] << 16) |
                           ((uint64_t)s_bits[2] << 32) | ((uint64_t)s_bits[3] << 48);
     words[(size_t)u * words_per_unit + wd] = word;
+    word_tokens[(size_t)u * words_per_unit + wd] = s_tok[0] + s_tok[1] + s_tok[2] + s_tok[3];
   }
 }
 
 // Compaction of the union words into the ascending union list, plus the
-// counters: ctr[0] += admitted tokens summed over the group's query heads,
-// ctr[1] += union tokens.  Thread t takes a run of bpt consecutive blocks
-// (bpt a power of two <= 64, so a run lies in one word), rounds of 256 runs
-// in ascending order; a work-group scan places each run's entries.  The head
-// masks of the run's admitted blocks are independent loads.
+// counters: ctr[0] += admitted tokens summed over the group's query heads
+// (the screen's per-word counts), ctr[1] += union tokens.  Thread t takes a
+// run of bpt consecutive blocks (bpt a power of two <= 64, so a run lies in
+// one word), rounds of 256 runs in ascending order; a work-group scan places
+// each run's entries.
 __global__ __launch_bounds__(256) void compact_gqa_kernel(CacheView c, const uint64_t* words,
+                                                          const uint32_t* word_tokens,
                                                           int words_per_unit,
-                                                          const uint32_t* head_mask,
                                                           int32_t* union_idx, int32_t* union_cnt,
                                                           uint64_t* ctr) {
-  __shared__ int scan[256];
-  __shared__ unsigned long long s_tok[256];
+  __shared__ int s_w[4];
+  __shared__ unsigned long long s_tok[4];
   const int u = blockIdx.x, t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
   const int T = c.seq_len[u / c.H];
   const int nb = (T + c.bs - 1) >> c.log2bs;
+  const int nw = (nb + 63) >> 6;
   const uint64_t* wu = words + (size_t)u * words_per_unit;
-  const uint32_t* hm = head_mask + (size_t)u * c.cap_blocks;
   int32_t* out = union_idx + (size_t)u * c.cap_blocks;
   const int tail = T - ((nb - 1) << c.log2bs);
+  // head tokens: the screen's per-word counts, summed in a fixed order
+  unsigned long long head_tokens = 0;
+  for (int i = t; i < nw; i += 256) head_tokens += word_tokens[(size_t)u * words_per_unit + i];
   int bpt = 1;
   while (bpt < 64 && bpt * 256 < nb) bpt <<= 1;
   int base_pos = 0;
-  unsigned long long head_tokens = 0;
   for (int r0 = 0; r0 < nb; r0 += 256 * bpt) {
     const int b0 = r0 + t * bpt;  // first block of this thread's run
     uint64_t x = 0;
@@ -162,36 +236,24 @@ __global__ __launch_bounds__(256) void compact_gqa_kernel(CacheView c, const uin
       const int rem = nb - b0;
       if (rem < 64) x &= (1ull << rem) - 1ull;
     }
-    const int mine = __popcll(x);
-    scan[t] = mine;
-    __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {
-      const int add = t >= off ? scan[t - off] : 0;
-      __syncthreads();
-      scan[t] += add;
-      __syncthreads();
-    }
-    int pos = base_pos + scan[t] - mine;
-    base_pos += scan[255];
-    __syncthreads();  // scan[] is rewritten next round
+    int round_total;
+    int pos = base_pos + wg_exclusive_scan<4>(__popcll(x), s_w, &round_total);
+    base_pos += round_total;
     while (x) {
-      const int j = b0 + __ffsll((unsigned long long)x) - 1;
-      out[pos++] = j;
-      head_tokens += (unsigned long long)__popc(hm[j]) * (j == nb - 1 ? tail : c.bs);
+      out[pos++] = b0 + __ffsll((unsigned long long)x) - 1;
       x &= x - 1ull;
     }
   }
-  s_tok[t] = head_tokens;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) head_tokens += __shfl_xor(head_tokens, off, kWave);
+  if (lane == 0) s_tok[wave] = head_tokens;
   __syncthreads();
-  for (int st = 128; st > 0; st >>= 1) {
-    if (t < st) s_tok[t] += s_tok[t + st];
-    __syncthreads();
-  }
   if (t == 0) {
     const int total = base_pos;
     union_cnt[u] = total;
     if (ctr && total > 0) {
-      atomicAdd(reinterpret_cast<unsigned long long*>(ctr), s_tok[0]);
+      atomicAdd(reinterpret_cast<unsigned long long*>(ctr),
+                (s_tok[0] + s_tok[1]) + (s_tok[2] + s_tok[3]));
       const unsigned long long ut =
           (unsigned long long)(total - 1) * c.bs + (unsigned long long)tail;
       atomicAdd(reinterpret_cast<unsigned long long*>(ctr + 1), ut);
@@ -1010,11 +1072,18 @@ static hipError_t screen_gqa_t(const CacheView& c, int G, const float* q, const 
                                uint64_t* ctr, uint64_t* words, hipStream_t s) {
   const int units = c.B * c.H;
   const int wpu = ceil_div(c.cap_blocks, 64);
-  hipLaunchKernelGGL((screen_gqa_kernel<D>), dim3((unsigned)((long long)wpu * units)), dim3(256),
-                     0, s, c, G, q, ts, z, scale, mask, words, wpu);
+  // per-word head-token counts follow the words in the workspace
+  uint32_t* wtok = reinterpret_cast<uint32_t*>(words + (size_t)units * wpu);
+  const dim3 grid((unsigned)((long long)wpu * units));
+  if (G <= 8)
+    hipLaunchKernelGGL((screen_gqa_kernel<D, 8>), grid, dim3(256), 0, s, c, G, q, ts, z, scale,
+                       mask, words, wtok, wpu);
+  else
+    hipLaunchKernelGGL((screen_gqa_kernel<D, 16>), grid, dim3(256), 0, s, c, G, q, ts, z, scale,
+                       mask, words, wtok, wpu);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(compact_gqa_kernel, dim3(units), dim3(256), 0, s, c, words, wpu, mask, idx,
+  hipLaunchKernelGGL(compact_gqa_kernel, dim3(units), dim3(256), 0, s, c, words, wtok, wpu, idx,
                      cnt, ctr);
   return hipGetLastError();
 }

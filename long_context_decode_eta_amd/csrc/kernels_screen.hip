@@ -164,7 +164,7 @@ __global__ __launch_bounds__(256) void screen_kernel(CacheView c, const float* q
 __global__ __launch_bounds__(256) void compact_kernel(CacheView c, const uint64_t* words,
                                                       int words_per_unit, int32_t* active_idx,
                                                       int32_t* active_cnt, uint64_t* ctr) {
-  __shared__ int scan[256];
+  __shared__ int s_w[4];
   const int u = blockIdx.x, t = threadIdx.x;
   const int T = c.seq_len[u / c.H];
   const int nb = (T + c.bs - 1) >> c.log2bs;
@@ -184,18 +184,9 @@ __global__ __launch_bounds__(256) void compact_kernel(CacheView c, const uint64_
       const int rem = nb - b0;
       if (rem < 64) x &= (1ull << rem) - 1ull;
     }
-    const int mine = __popcll(x);
-    scan[t] = mine;
-    __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {  // Hillis-Steele inclusive scan
-      const int add = t >= off ? scan[t - off] : 0;
-      __syncthreads();
-      scan[t] += add;
-      __syncthreads();
-    }
-    int pos = base_pos + scan[t] - mine;
-    base_pos += scan[255];
-    __syncthreads();  // scan[] is rewritten next round
+    int round_total;
+    int pos = base_pos + wg_exclusive_scan<4>(__popcll(x), s_w, &round_total);
+    base_pos += round_total;
     while (x) {
       out[pos++] = b0 + __ffsll((unsigned long long)x) - 1;
       x &= x - 1ull;

@@ -41,6 +41,14 @@ GQA_COUNTERS = os.path.join(ROOT, "profiles", "gqa_decode_counters.json")
 CSRC = os.path.join(ROOT, "long_context_decode_eta_amd", "csrc")
 DECODE_SRC = [os.path.join(CSRC, f) for f in ("kernels_decode.hip", "eta_api.hip", "eta_internal.h")]
 GQA_SRC = [os.path.join(CSRC, f) for f in ("kernels_gqa.hip", "eta_api.hip", "eta_internal.h")]
+PREFILL_COUNTERS = os.path.join(ROOT, "profiles", "prefill_counters.json")
+PREFILL_SRC = [os.path.join(CSRC, f) for f in ("kernels_prefill.hip", "eta_api.hip",
+                                                "eta_internal.h")]
+# Vector-ALU issue ceiling of the chip: the fp32 vector peak (157.3 TFLOP/s,
+# 256 CUs x 4 SIMDs at 2.4 GHz) is 78.6e12 FMA lane-ops/s, i.e. 1.229e12
+# wave64 instructions per second (one every 2 cycles per SIMD).  A
+# transcendental (v_exp_f32, v_rcp_f32) is charged two issue slots.
+VALU_WAVE_INSTR_PER_S = 157.3e12 / 2 / 64
 
 
 def parse():
@@ -69,6 +77,13 @@ def parse():
     ap.add_argument("--configs", default="ctx512k,ragged,ctx32k",
                     help="other decode workloads timed after the headline one ('none': skip)")
     ap.add_argument("--seed", type=int, default=1234)
+    ap.add_argument("--summarize-prefill-counters", nargs=5, default=None,
+                    metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV",
+                             "SQ_CSV"),
+                    help="turn rocprofv3 counter csv files of a --prefill-only run (FETCH_SIZE, "
+                         "WRITE_SIZE, the 1 GiB copy's FETCH_SIZE and WRITE_SIZE, and a pass "
+                         "with SQ_INSTS_VALU, SQ_INSTS_VALU_TRANS_F32, SQ_INSTS_MFMA, "
+                         "SQ_VALU_MFMA_BUSY_CYCLES) into profiles/prefill_counters.json")
     ap.add_argument("--summarize-counters", nargs=4, default=None,
                     metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="turn rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE and "
@@ -178,6 +193,36 @@ def _counter_rows(path):
             key = (r["Dispatch_Id"], r["Kernel_Name"], r["Counter_Name"])
             per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
     return [(k[1], k[2], v) for k, v in per.items()]
+
+
+def summarize_prefill_counters(args):
+    """Per-launch HBM bytes and vector/matrix instruction counts of the
+    prefill kernel, stored with the hash of its sources."""
+    fetch, write, cfetch, cwrite, sq = args.summarize_prefill_counters
+    ref_bytes = 1 << 30
+
+    def mean_of(rows, counter, pred):
+        vals = [v for k, c, v in rows if c == counter and pred(k)]
+        return sum(vals) / len(vals) if vals else 0.0
+
+    is_copy = lambda k: "copyBuffer" in k or "copy" in k.lower()
+    is_pf = lambda k: "prefill_kernel" in k
+    f_factor = ref_bytes / (mean_of(_counter_rows(cfetch), "FETCH_SIZE", is_copy) * 1024.0)
+    w_factor = ref_bytes / (mean_of(_counter_rows(cwrite), "WRITE_SIZE", is_copy) * 1024.0)
+    f = mean_of(_counter_rows(fetch), "FETCH_SIZE", is_pf)
+    w = mean_of(_counter_rows(write), "WRITE_SIZE", is_pf)
+    sqrows = _counter_rows(sq)
+    per = {c: mean_of(sqrows, c, is_pf) for c in
+           ("SQ_INSTS_VALU", "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES",
+            "SQ_WAVES", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES", "SQ_ACTIVE_INST_VALU")}
+    cj = {"kernel_hash": kernel_hash(PREFILL_SRC), "workload": "prefill",
+          "fetch_factor": f_factor, "write_factor": w_factor,
+          "fetch_kib": f, "write_kib": w,
+          "hbm_bytes_per_launch": int(round(f * 1024.0 * f_factor + w * 1024.0 * w_factor)),
+          "per_dispatch": {k: int(round(v)) for k, v in per.items()}}
+    with open(PREFILL_COUNTERS, "w") as fh:
+        json.dump(cj, fh, indent=1)
+    print(json.dumps(cj, indent=1))
 
 
 def summarize_counters(args):
@@ -478,6 +523,9 @@ def main():
     args = parse()
     if args.summarize_counters:
         summarize_counters(args)
+        return
+    if args.summarize_prefill_counters:
+        summarize_prefill_counters(args)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -880,16 +928,44 @@ def prefill_bench(torch, eb, synth, steps, warmup, seed):
     del graph
     pairs = w.B * w.Hq * w.T * (w.T + 1) // 2
     flops = 4 * w.D * pairs
-    tfs = flops / (ev.mean_ms() * 1e-3) / 1e12
+    kms = ev.mean_ms()
+    tfs = flops / (kms * 1e-3) / 1e12
+    # Counter summary of the same kernel sources (instruction counts and HBM
+    # bytes per launch), if present.
+    cj = None
+    if os.path.exists(PREFILL_COUNTERS):
+        cj = json.load(open(PREFILL_COUNTERS))
+        if cj.get("kernel_hash") != kernel_hash(PREFILL_SRC):
+            cj = None
+    alu = None
+    if cj is not None:
+        pd = cj["per_dispatch"]
+        slots = pd["SQ_INSTS_VALU"] + pd["SQ_INSTS_VALU_TRANS_F32"]
+        rate = slots / (kms * 1e-3)
+        alu = {"bound": "alu", "achieved": float(f"{rate:.4g}"),
+               "peak": float(f"{VALU_WAVE_INSTR_PER_S:.4g}"),
+               "unit": "wave64 VALU issue slots/s (transcendentals count two)",
+               "frac": round(rate / VALU_WAVE_INSTR_PER_S, 4),
+               "valu_instructions_per_launch": pd["SQ_INSTS_VALU"],
+               "transcendental_per_launch": pd["SQ_INSTS_VALU_TRANS_F32"],
+               "mfma_instructions_per_launch": pd["SQ_INSTS_MFMA"],
+               "mfma_busy_frac": round(pd["SQ_VALU_MFMA_BUSY_CYCLES"] / 1024 /
+                                       (kms * 1e-3 * 2.4e9), 4)}
     res = {"workload": f"prefill: batch {w.B}, {w.Hq} query heads on {w.H} KV heads, head dim "
                        f"{w.D}, context {w.T}, bf16 q/k/v, beta 5",
-           "ms": round(ms, 5), "kernel_ms": round(ev.mean_ms(), 5),
+           "ms": round(ms, 5), "kernel_ms": round(kms, 5),
            "tokens_per_s": round(w.B * w.T / (ms * 1e-3), 1),
            "mean_density": round(float(dens.mean()), 4),
            "roofline": {"bound": "mfma", "achieved": round(tfs, 1),
                         "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
-                        "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4), "traffic": None,
-                        "algorithmic_flops_per_launch": int(flops)}}
+                        "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4),
+                        "traffic": None if cj is None else cj["hbm_bytes_per_launch"],
+                        "algorithmic_flops_per_launch": int(flops),
+                        "algorithmic_bytes_per_launch": int(
+                            w.q.numel() * 2 + (w.k.numel() + w.v.numel()) * 2 +
+                            w.tau.numel() * 4 + out.numel() * 4 + dens.numel() * 4),
+                        "avg_launch_ms": round(kms, 5)},
+           "alu_roofline": alu}
     print(f"[bench] prefill: {json.dumps(res)}", file=sys.stderr, flush=True)
     return res
 

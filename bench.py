@@ -47,8 +47,12 @@ PREFILL_SRC = [os.path.join(CSRC, f) for f in ("kernels_prefill.hip", "eta_api.h
 # Vector-ALU issue ceiling of the chip: the fp32 vector peak (157.3 TFLOP/s,
 # 256 CUs x 4 SIMDs at 2.4 GHz) is 78.6e12 FMA lane-ops/s, i.e. 1.229e12
 # wave64 instructions per second (one every 2 cycles per SIMD).  A
-# transcendental (v_exp_f32, v_rcp_f32) is charged two issue slots.
+# transcendental (v_exp_f32, v_rcp_f32) is charged TRANS_SLOTS issue slots:
+# in long independent chains on every SIMD, counted against GRBM_GUI_ACTIVE,
+# an exp or a reciprocal took about 9.5 cycles per wave64 instruction where
+# a multiply or FMA took about 2.6.
 VALU_WAVE_INSTR_PER_S = 157.3e12 / 2 / 64
+TRANS_SLOTS = 4
 
 
 def parse():
@@ -940,11 +944,11 @@ def prefill_bench(torch, eb, synth, steps, warmup, seed):
     alu = None
     if cj is not None:
         pd = cj["per_dispatch"]
-        slots = pd["SQ_INSTS_VALU"] + pd["SQ_INSTS_VALU_TRANS_F32"]
+        slots = pd["SQ_INSTS_VALU"] + (TRANS_SLOTS - 1) * pd["SQ_INSTS_VALU_TRANS_F32"]
         rate = slots / (kms * 1e-3)
         alu = {"bound": "alu", "achieved": float(f"{rate:.4g}"),
                "peak": float(f"{VALU_WAVE_INSTR_PER_S:.4g}"),
-               "unit": "wave64 VALU issue slots/s (transcendentals count two)",
+               "unit": f"wave64 VALU issue slots/s (a transcendental counts {TRANS_SLOTS})",
                "frac": round(rate / VALU_WAVE_INSTR_PER_S, 4),
                "valu_instructions_per_launch": pd["SQ_INSTS_VALU"],
                "transcendental_per_launch": pd["SQ_INSTS_VALU_TRANS_F32"],

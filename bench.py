@@ -289,7 +289,8 @@ class DecodeBench:
     step (threshold, screen, decode) timed eagerly per kernel and as a HIP
     graph, beside the in-house dense decode at the same shape."""
 
-    def __init__(self, torch, np, eb, synth, name, seed, split=0, cap_extra_blocks=0):
+    def __init__(self, torch, np, eb, synth, name, seed, split=0, cap_extra_blocks=0,
+                 path="split"):
         self.torch, self.np, self.eb, self.name = torch, np, eb, name
         dev = "cuda"
         t0 = time.time()
@@ -304,8 +305,10 @@ class DecodeBench:
         eb.build_block_meta(self.cache)
         self.sl = w.seq_len.cpu().numpy().astype(np.int64)
         self.sumT = int(self.sl.sum())
-        self.dec = eb.Decoder(self.cache, z=w.z, scale=w.scale, blocks_per_split=split or None)
+        self.dec = eb.Decoder(self.cache, z=w.z, scale=w.scale, blocks_per_split=split or None,
+                              path=path)
         self.split = self.dec.split
+        self.fused = self.dec.path == "fused"
         self.frozen = w.W is None
         self.elt = 2 if w.kv_dtype == torch.bfloat16 else 4
         self.consts = {}
@@ -318,7 +321,8 @@ class DecodeBench:
         self.meta_bytes = int(H * (nbc * (2 * D + 1) * 4).sum())
         self.dense_bytes = self.sumT * H * D * 2 * self.elt
         print(f"[bench] workload {name}: B={B} H={H} D={D} b={bs} sumT={self.sumT} "
-              f"split={self.split} dense split={self.dec.dense_split} "
+              f"path={self.dec.path} split={self.split} chunk={self.dec.fused_chunk} "
+              f"dense split={self.dec.dense_split} "
               f"({time.time() - t0:.1f}s setup)", file=sys.stderr, flush=True)
 
     def calibrate(self, rhos):
@@ -353,11 +357,17 @@ class DecodeBench:
         if self.frozen:  # no predictor in the timed step: tau is the constants
             dec.predict(w.q, None, c)
 
+        # The timed call: eta_decode (balanced decode + combine) on the split
+        # path, eta_screen_decode (fused screen + decode + combine) on the
+        # fused one.
+        call = (lambda: dec.screen_attend(w.q)) if self.fused else (lambda: dec.attend(w.q))
+
         def step():
             if not self.frozen:
                 dec.predict(w.q, W, c)
-            dec.screen(w.q)
-            dec.attend(w.q)
+            if not self.fused:
+                dec.screen(w.q)
+            call()
 
         for _ in range(warmup):
             step()
@@ -369,8 +379,9 @@ class DecodeBench:
         for _ in range(steps):
             if not self.frozen:
                 dec.predict(w.q, W, c)
-            tscr.around(lambda: dec.screen(w.q))
-            tdec.around(lambda: dec.attend(w.q))
+            if not self.fused:
+                tscr.around(lambda: dec.screen(w.q))
+            tdec.around(call)
         torch.cuda.synchronize()
         eager = time.perf_counter() - a
         toks = (int(dec.density_ctr.item()) - ctr0) // steps
@@ -386,7 +397,16 @@ class DecodeBench:
             per_step.append((e0, e1))
         torch.cuda.synchronize()
         lat = sorted(s0.elapsed_time(s1) for s0, s1 in per_step)
-        cnt = dec.active_cnt.cpu().numpy().astype(np.int64)
+        if self.fused:  # admitted blocks per stream from the chunk bits
+            bits = dec.chunk_bits.cpu().numpy().astype(np.int64) & 0xFFFFFFFF
+            nbs = -(-self.sl // w.block)
+            live = (np.arange(bits.shape[2])[None, :] * dec.fused_chunk) < nbs[:, None]
+            bits = np.where(live[:, None, :], bits, 0)
+            cnt = np.zeros(bits.shape[:2], np.int64)
+            for i in range(dec.fused_chunk):
+                cnt += ((bits >> i) & 1).sum(axis=2)
+        else:
+            cnt = dec.active_cnt.cpu().numpy().astype(np.int64)
         ref = dec.out.clone()
 
         graph = torch.cuda.CUDAGraph()
@@ -408,18 +428,21 @@ class DecodeBench:
         del graph
         # The decode call (balanced decode + combine kernels) and the screen
         # call (screen + compaction), each replayed alone as a graph.
-        decode_ms = graph_call_ms(torch, lambda: dec.attend(w.q), steps, warmup, self.flush)
-        screen_ms = graph_call_ms(torch, lambda: dec.screen(w.q), steps, warmup, self.flush)
+        decode_ms = graph_call_ms(torch, call, steps, warmup, self.flush)
+        screen_ms = (None if self.fused else
+                     graph_call_ms(torch, lambda: dec.screen(w.q), steps, warmup, self.flush))
         pct = lambda f: lat[min(len(lat) - 1, int(f * (len(lat) - 1) + 0.5))]
         r = dict(ms=wall * 1e3 / steps, eager_ms=eager * 1e3 / steps,
                  step_ms_median=pct(0.5), step_ms_p10=pct(0.1), step_ms_p90=pct(0.9),
                  decode_ms=decode_ms, screen_ms=screen_ms,
-                 eager_decode_ms=tdec.mean_ms(), eager_screen_ms=tscr.mean_ms(),
+                 eager_decode_ms=tdec.mean_ms(),
+                 eager_screen_ms=None if self.fused else tscr.mean_ms(),
                  density=toks / (w.H * self.sumT), tokens=toks, cnt=cnt)
         r["decode_bytes"] = self.decode_bytes(r)
         r["step_bytes"] = self.step_bytes(r)
-        print(f"[bench] {self.name} rho={rho:.2f}: density {r['density']:.4f} step "
-              f"{r['ms']:.4f} ms (eager {r['eager_ms']:.4f}; screen {r['screen_ms']:.4f}, "
+        scr = "fused" if screen_ms is None else f"{screen_ms:.4f}"
+        print(f"[bench] {self.name} rho={rho:.2f} ({dec.path}): density {r['density']:.4f} step "
+              f"{r['ms']:.4f} ms (eager {r['eager_ms']:.4f}; screen {scr}, "
               f"decode {r['decode_ms']:.4f}) {r['step_bytes'] / r['ms'] / 1e6:.0f} GB/s",
               file=sys.stderr, flush=True)
         return r
@@ -446,11 +469,20 @@ class DecodeBench:
         return ms
 
     def decode_bytes(self, r):
-        """Algorithmic bytes of one eta_decode call: admitted K+V, q, the
-        active lists, partials (m, l, acc) written and read for streams split
-        over several ranges, output."""
+        """Algorithmic bytes of the timed call.  eta_decode: admitted K+V, q,
+        the active lists, partials (m, l, acc) written and read for streams
+        split over several ranges, output.  eta_screen_decode: the block
+        statistics, admitted K+V, q and thresholds, one partial per chunk of a
+        stream with several chunks (written and read), the chunk bits,
+        output."""
         np, w = self.np, self.w
         B, H, D = w.B, w.H, w.D
+        if self.fused:
+            nb = -(-self.sl // w.block)
+            nch = -(-nb // self.dec.fused_chunk)  # chunks per stream of each sequence
+            part = int(H * (np.where(nch > 1, nch, 0) * (D + 2) * 4 * 2).sum())
+            return (self.meta_bytes + r["tokens"] * D * 2 * self.elt + B * H * D * 4 * 2 +
+                    2 * B * H * 4 + int(H * nch.sum()) * 4 + part)
         chunks = -(-r["cnt"] // self.split)
         part = int((np.where(chunks > 1, chunks, 0) * (D + 2) * 4 * 2).sum())
         return (r["tokens"] * D * 2 * self.elt + B * H * D * 4 * 2 + int(r["cnt"].sum()) * 4 +
@@ -460,16 +492,21 @@ class DecodeBench:
         w = self.w
         B, H, D = w.B, w.H, w.D
         pred = 0 if self.frozen else B * H * D * 4 + H * D * H * 4 + 2 * B * H * 4
+        if self.fused:
+            return pred + r["decode_bytes"]
         screen = self.meta_bytes + B * H * D * 4 + int(r["cnt"].sum()) * 4 + B * H * 4
         return pred + screen + r["decode_bytes"]
 
     def roofline(self, r, dense_ms):
         achieved = r["decode_bytes"] / (r["decode_ms"] * 1e-3) / 1e9
         stream_gbs = self.dense_bytes / dense_ms / 1e6
-        return {"bound": "hbm", "kernel": "eta_decode (balanced decode + combine kernels)",
+        kernel = ("eta_screen_decode (fused screen + decode, combine kernels)" if self.fused
+                  else "eta_decode (balanced decode + combine kernels)")
+        return {"bound": "hbm", "kernel": kernel,
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": counters_traffic(COUNTERS, DECODE_SRC, self.name),
+                "traffic": (None if self.fused else
+                            counters_traffic(COUNTERS, DECODE_SRC, self.name)),
                 "algorithmic_bytes_per_launch": int(r["decode_bytes"]),
                 "avg_launch_ms": round(r["decode_ms"], 5),
                 "measured_stream_gbs": round(stream_gbs, 1),
@@ -481,7 +518,8 @@ class DecodeBench:
                 "tokens_per_s": round(self.sumT / (r["ms"] * 1e-3), 1),
                 "step_gbs": round(r["step_bytes"] / r["ms"] / 1e6, 1),
                 "decode_gbs": round(r["decode_bytes"] / r["decode_ms"] / 1e6, 1),
-                "screen_ms": round(r["screen_ms"], 5),
+                "screen_ms": None if r["screen_ms"] is None else round(r["screen_ms"], 5),
+                "path": self.dec.path,
                 "decode_ms": round(r["decode_ms"], 5),
                 "speedup_vs_dense": round(dense_ms / r["ms"], 3),
                 "ideal_speedup": round(self.dense_bytes / r["step_bytes"], 3)}
@@ -508,17 +546,28 @@ def config_bench(torch, np, eb, synth, name, steps, warmup, seed):
     decode call's roofline."""
     target = synth.CONFIGS[name].get("rho", 0.38)
     rho = target if isinstance(target, float) else 0.38
-    b = DecodeBench(torch, np, eb, synth, name, seed)
+    b = DecodeBench(torch, np, eb, synth, name, seed, path="auto")
     b.calibrate([rho])
     r = b.run(rho, steps, warmup)
     dense_ms = b.run_dense(steps, warmup)
     out = {"workload": b.describe(rho), **b.summary(r, dense_ms),
            "dense_ms": round(dense_ms, 5), "blocks_per_split": b.split,
+           "blocks_per_chunk": b.dec.fused_chunk if b.fused else None,
            "dense_blocks_per_split": b.dec.dense_split,
            "step_ms_median": round(r["step_ms_median"], 5),
            "step_ms_p10": round(r["step_ms_p10"], 5), "step_ms_p90": round(r["step_ms_p90"], 5),
            "llc_flushed": b.flush is not None,
            "roofline": b.roofline(r, dense_ms)}
+    if b.fused:  # the split path on the same cache and constants, for reference
+        fused_dec = b.dec
+        b.dec = eb.Decoder(b.cache, z=b.w.z, scale=b.w.scale, path="split")
+        b.split, b.fused = b.dec.split, False
+        rs = b.run(rho, steps, warmup)
+        out["split_path"] = {"ms": round(rs["ms"], 5), "decode_ms": round(rs["decode_ms"], 5),
+                             "screen_ms": round(rs["screen_ms"], 5),
+                             "speedup_vs_dense": round(dense_ms / rs["ms"], 3),
+                             "blocks_per_split": b.split}
+        b.dec = fused_dec
     b.release()
     return out
 

@@ -221,6 +221,36 @@ eta_status eta_dense_decode(const eta_cache* c, const float* q, float scale,
                             float* out, void* stream);
 
 /*
+ * Screen and block-sparse decode fused into one pass, for small steps where
+ * separate launches cost more than the work (Methodology 4, Eq. 5 for the
+ * admission; Methodology 2, Eq. 3 for the logits; Fig. 6: only admitted
+ * blocks are loaded, online softmax).  Every stream is cut into chunks of
+ * blocks_per_chunk consecutive blocks (1 <= blocks_per_chunk <= 32), one
+ * work-group each, which screens its chunk's blocks exactly as eta_screen
+ * does (the same float32 operations, so for the same tau_screen the admitted
+ * set is the same, the last block always in it) and attends over the blocks it
+ * admitted; a combine pass merges the chunks of each stream by log-sum-exp.
+ * out and the logits as in eta_decode (tau_gate may be NULL in RAW mode).
+ * q: device [batch][heads][head_dim]; tau_gate, tau_screen: device
+ * [batch][heads] (eta_predict_tau's outputs); z, scale as in eta_screen.
+ * Optional outputs (NULL: not written):
+ *   chunk_bits  device [batch][heads][ceil(cap_blocks / blocks_per_chunk)]
+ *               uint32: bit i of entry k set iff block k * blocks_per_chunk + i
+ *               is admitted (entries of chunks past a stream's end are left
+ *               unwritten);
+ *   density_ctr one uint64, += admitted tokens as in eta_screen.
+ * Workspace: eta_screen_decode_workspace_bytes(); contents need no
+ * initialisation.  A stream with T_b == 0 yields zeros.
+ */
+size_t eta_screen_decode_workspace_bytes(int32_t batch, int32_t heads, int32_t head_dim,
+                                         int32_t cap_blocks, int32_t blocks_per_chunk);
+eta_status eta_screen_decode(const eta_cache* c, const float* q, const float* tau_gate,
+                             const float* tau_screen, float z, int32_t logit_mode, float beta,
+                             float scale, int32_t blocks_per_chunk, uint32_t* chunk_bits,
+                             uint64_t* density_ctr, void* workspace, size_t workspace_bytes,
+                             float* out, void* stream);
+
+/*
  * Offline calibration of frozen per-head constants (the pages' calibration
  * algorithm freezes per-(layer, head) thresholds; its steps are not given, so
  * this is the plain quantile reading).  For head h, pool over the n_sets

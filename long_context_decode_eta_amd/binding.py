@@ -57,6 +57,11 @@ _SIGS = {
                             c_float, c_int32, c_void_p, c_void_p], c_int32),
     "eta_dense_decode": ([_P, c_void_p, c_float, c_int32, c_void_p, c_size_t, c_void_p,
                           c_void_p], c_int32),
+    "eta_screen_decode_workspace_bytes": ([c_int32, c_int32, c_int32, c_int32, c_int32],
+                                          c_size_t),
+    "eta_screen_decode": ([_P, c_void_p, c_void_p, c_void_p, c_float, c_int32, c_float, c_float,
+                           c_int32, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p, c_void_p],
+                          c_int32),
     "eta_calibrate_workspace_bytes": ([c_int32, c_int32, c_int32, c_int32], c_size_t),
     "eta_calibrate_threshold": ([_P, c_int32, c_void_p, c_void_p, c_float, c_float, c_float,
                                  c_void_p, c_size_t, c_void_p, c_void_p], c_int32),
@@ -316,6 +321,26 @@ def gated_prefill(q, k, v, tau, group, beta, scale, out, dens=None, stream=None)
            "eta_gated_prefill")
 
 
+def screen_decode_workspace_bytes(batch, heads, head_dim, cap_blocks, blocks_per_chunk) -> int:
+    return int(lib().eta_screen_decode_workspace_bytes(batch, heads, head_dim, cap_blocks,
+                                                       blocks_per_chunk))
+
+
+def screen_decode(cache: KVCache, q, tau_gate, tau_screen, z, logit_mode, beta, scale,
+                  blocks_per_chunk, chunk_bits, density_ctr, workspace, out, stream=None):
+    _check(lib().eta_screen_decode(_ref(cache), _dev(q, torch.float32, "q"),
+                                   _dev(tau_gate, torch.float32, "tau_gate"),
+                                   _dev(tau_screen, torch.float32, "tau_screen"), float(z),
+                                   int(logit_mode), float(beta), float(scale),
+                                   int(blocks_per_chunk), _dev(chunk_bits, torch.int32,
+                                                               "chunk_bits"),
+                                   _dev(density_ctr, None, "density_ctr"),
+                                   _dev(workspace, None, "workspace"),
+                                   workspace.numel() * workspace.element_size(),
+                                   _dev(out, torch.float32, "out"), _stream(stream)),
+           "eta_screen_decode")
+
+
 def workspace(nbytes: int, device="cuda") -> torch.Tensor:
     """A caller-owned byte workspace (torch allocation; 256-byte aligned)."""
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
@@ -335,13 +360,37 @@ def auto_split(units: int, cap_blocks: int, block: int, dense: bool = False) -> 
     return max(1, min(512 // block, (units * cap_blocks) // 4096))
 
 
+def auto_fused_chunk(units: int, cap_blocks: int) -> int:
+    """Blocks per chunk of the fused screen + decode: the largest of 32, 16,
+    ..., 1 that still gives at least 512 work-groups (two per compute unit).
+    Swept on MI355X at 32K x 16 heads, b=64 (8192 blocks): 16 blocks per
+    chunk (512 work-groups) at 38% and 70% density, 16 or 32 at 10%; 4 and 8
+    were slower at every density."""
+    for cb in (32, 16, 8, 4, 2):
+        if units * (-(-cap_blocks // cb)) >= 512:
+            return cb
+    return 1
+
+
+# Caches up to this many bytes of K+V take the fused screen + decode under
+# path="auto": a step that small is dominated by its launches.  Measured on
+# MI355X: at 32K x 16 heads (268 MB) the fused step takes 0.026 / 0.040 /
+# 0.051 ms against 0.036 / 0.043 / 0.059 ms for screen -> decode at 10 / 38 /
+# 70% density, while at 512K x 16 heads (4.3 GB) it loses (0.122 vs 0.118 ms
+# at 10%, 0.323 vs 0.313 ms at 38%), as at 8 x 128K and on the ragged batch.
+FUSED_MAX_KV_BYTES = 1 << 30
+
+
 class Decoder:
     """One decode step over a cache with every buffer preallocated:
     predict_tau (skipped in frozen mode when tau is precomputed) -> screen ->
-    decode.  Pure orchestration of the C entry points."""
+    decode (path "split"), or predict_tau -> the fused screen + decode (path
+    "fused"); path "auto" takes the fused one for caches of at most
+    FUSED_MAX_KV_BYTES of K+V.  Pure orchestration of the C entry points."""
 
     def __init__(self, cache: KVCache, *, z, scale=None, beta=5.0, a=0.0,
-                 logit_mode=GATED, blocks_per_split=None, dense_blocks_per_split=None):
+                 logit_mode=GATED, blocks_per_split=None, dense_blocks_per_split=None,
+                 fused_blocks_per_chunk=None, path="split"):
         self.cache, self.z, self.beta, self.a = cache, float(z), float(beta), float(a)
         self.scale = float(scale) if scale is not None else float(
             torch.tensor(1.0 / cache.head_dim ** 0.5, dtype=torch.float32).item())
@@ -360,6 +409,17 @@ class Decoder:
         self.decode_ws = workspace(decode_workspace_bytes(
             B, H, D, nbc, min(self.split, self.dense_split)), dev)
         self.out = torch.zeros((B, H, D), dtype=torch.float32, device=dev)
+        if path not in ("split", "fused", "auto"):
+            raise ValueError(f"path must be 'split', 'fused' or 'auto', got {path!r}")
+        if path == "auto":
+            kv_bytes = 2 * B * H * cache.cap_tokens * D * cache.k.element_size()
+            path = "fused" if kv_bytes <= FUSED_MAX_KV_BYTES else "split"
+        self.path = path
+        self.fused_chunk = int(fused_blocks_per_chunk or auto_fused_chunk(B * H, nbc))
+        self.chunk_bits = torch.zeros((B, H, -(-nbc // self.fused_chunk)), dtype=torch.int32,
+                                      device=dev)
+        self.fused_ws = workspace(screen_decode_workspace_bytes(B, H, D, nbc,
+                                                                self.fused_chunk), dev)
 
     def predict(self, q, W, bias_or_c, stream=None):
         predict_tau(q, W, bias_or_c, self.a, self.tau_gate, self.tau_screen, stream)
@@ -373,10 +433,26 @@ class Decoder:
                self.beta, self.scale, self.split, self.decode_ws, self.out, stream)
 
     def step(self, q, W=None, bias_or_c=None, stream=None):
+        """One step on this Decoder's path.  Path "split" leaves the admitted
+        lists in active_idx / active_cnt, path "fused" the admission bits of
+        each chunk in chunk_bits."""
+        if self.path == "fused":
+            return self.step_fused(q, W, bias_or_c, stream)
         if bias_or_c is not None:
             self.predict(q, W, bias_or_c, stream)
         self.screen(q, stream)
         self.attend(q, stream)
+        return self.out
+
+    def screen_attend(self, q, stream=None):
+        screen_decode(self.cache, q, self.tau_gate, self.tau_screen, self.z, self.mode,
+                      self.beta, self.scale, self.fused_chunk, self.chunk_bits,
+                      self.density_ctr, self.fused_ws, self.out, stream)
+
+    def step_fused(self, q, W=None, bias_or_c=None, stream=None):
+        if bias_or_c is not None:
+            self.predict(q, W, bias_or_c, stream)
+        self.screen_attend(q, stream)
         return self.out
 
     def dense(self, q, stream=None):

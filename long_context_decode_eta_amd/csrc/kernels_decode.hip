@@ -120,26 +120,31 @@ __device__ __forceinline__ void merge_groups(RowState<EPL>& st) {
   }
 }
 
-// Attention of one chunk (chunk k of stream u) by the whole work-group.  The
-// chunk's block indices are first staged in LDS (s_list), so no key or value
-// load ever waits on an index load.  Writes the final output when the chunk is
-// the stream's only one, else the partial (max, sum, weighted V).
-template <int D, int DT, int MODE, bool DENSE>
+// Where a chunk's block indices come from: consecutive blocks first,
+// first + 1, ... (dense), entries first .. first + nblk - 1 of the stream's
+// admitted list (copied to LDS here), or a list the caller already staged in
+// LDS (the fused screen + decode).
+enum ChunkSrc { kChunkDense = 0, kChunkList = 1, kChunkStaged = 2 };
+
+// Attention of one chunk (chunk k of stream u, nblk blocks) by the whole
+// work-group.  The chunk's block indices sit in LDS (s_list), so no key or
+// value load ever waits on an index load.  Writes the final output when the
+// chunk is the stream's only one (single), else the partial (max, sum,
+// weighted V) into slot k of the stream.
+template <int D, int DT, int MODE, int SRC, int NBUF = 2>
 __device__ __forceinline__ void chunk_attend(const CacheView& c, const DecodeArgs& a, int u, int k,
-                                             int T, int cnt, int* s_list, float (*s_acc)[D],
-                                             float (*s_ml)[2]) {
+                                             int T, int first, int nblk, bool single,
+                                             int* s_list, float (*s_acc)[D], float (*s_ml)[2]) {
   constexpr int EPL = Elt<DT>::kPer16B;
   constexpr int LPR = D / EPL;
   constexpr int RPI = kWave / LPR;
   constexpr int NI = (kRows / RPI) > 0 ? (kRows / RPI) : 1;
   constexpr int RB = D * Elt<DT>::kBytes;
   const int nb = (T + c.bs - 1) >> c.log2bs;
-  const int first = k * a.split;
-  const int nblk = min(a.split, cnt - first);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane / LPR, li = lane % LPR;
 
-  if constexpr (!DENSE) {
+  if constexpr (SRC == kChunkList) {
     const int32_t* list = a.active_idx + (size_t)u * c.cap_blocks + first;
     for (int i = threadIdx.x; i < nblk; i += blockDim.x) s_list[i] = list[i];
   }
@@ -169,7 +174,7 @@ __device__ __forceinline__ void chunk_attend(const CacheView& c, const DecodeArg
       int s = -1;
       if (rr < rows) {
         const int p = rr >> c.log2bs;
-        const int j = DENSE ? first + p : s_list[p];
+        const int j = SRC == kChunkDense ? first + p : s_list[p];
         s = (j << c.log2bs) + (rr & (c.bs - 1));
         // The list is trusted only as far as it stays inside the stream.
         if ((unsigned)j >= (unsigned)nb || s >= T) s = -1;
@@ -188,17 +193,22 @@ __device__ __forceinline__ void chunk_attend(const CacheView& c, const DecodeArg
     fold_tile<D, DT, MODE, NI>(st, kr, vr, sp, qs, tau, beta, T);
   };
 
-  // Two register buffers: the loads of a wave's next tile are in flight while
-  // its current tile is folded in.
-  uint4 ka[NI], va[NI], kq[NI], vq[NI];
-  int sa[NI], sq[NI];
-  if (wave < ntiles) fetch(wave, ka, va, sa);
-  for (int t = wave; t < ntiles; t += 8) {
-    const bool has_b = t + 4 < ntiles;
-    if (has_b) fetch(t + 4, kq, vq, sq);
-    consume(ka, va, sa);
-    if (t + 8 < ntiles) fetch(t + 8, ka, va, sa);
-    if (has_b) consume(kq, vq, sq);
+  // NBUF register buffers: the loads of a wave's next NBUF - 1 tiles are in
+  // flight while its current tile is folded in.  Tiles are folded in the
+  // same order (wave, wave + 4, ...) whatever NBUF, so the result is too.
+  uint4 kr[NBUF][NI], vr[NBUF][NI];
+  int sp[NBUF][NI];
+#pragma unroll
+  for (int b = 0; b + 1 < NBUF; ++b)
+    if (wave + 4 * b < ntiles) fetch(wave + 4 * b, kr[b], vr[b], sp[b]);
+  for (int t0 = wave; t0 < ntiles; t0 += 4 * NBUF) {
+#pragma unroll
+    for (int b = 0; b < NBUF; ++b) {
+      const int t = t0 + 4 * b, tp = t + 4 * (NBUF - 1);
+      if (tp < ntiles) fetch(tp, kr[(b + NBUF - 1) % NBUF], vr[(b + NBUF - 1) % NBUF],
+                             sp[(b + NBUF - 1) % NBUF]);
+      if (t < ntiles) consume(kr[b], vr[b], sp[b]);
+    }
   }
 
   merge_groups<EPL, LPR>(st);
@@ -220,8 +230,8 @@ __device__ __forceinline__ void chunk_attend(const CacheView& c, const DecodeArg
       const float a2[1] = {s_acc[w][i]};
       merge_state<1>(mm, ll, aa, s_ml[w][0], s_ml[w][1], a2);
     }
-    if (first == 0 && nblk == cnt) {
-      a.out[(size_t)u * D + i] = aa[0] / ll;  // single chunk: final output
+    if (single) {
+      a.out[(size_t)u * D + i] = aa[0] / ll;  // the stream's only chunk: final output
     } else {
       const size_t slot = (size_t)u * a.max_chunks + k;
       a.part_acc[slot * D + i] = aa[0];
@@ -374,7 +384,9 @@ __global__ __launch_bounds__(256) void decode_queue_kernel(CacheView c, DecodeAr
     const int u = lo, k = item - s_start[u];
     int T, cnt;
     stream_chunks(c, a, u, &T, &cnt);
-    chunk_attend<D, DT, MODE, DENSE>(c, a, u, k, T, cnt, s_list, s_acc, s_ml);
+    const int first = k * a.split, nblk = min(a.split, cnt - first);
+    chunk_attend<D, DT, MODE, DENSE ? kChunkDense : kChunkList>(
+        c, a, u, k, T, first, nblk, first == 0 && nblk == cnt, s_list, s_acc, s_ml);
     __syncthreads();  // LDS reuse; s_next is visible
     item = s_next;
   }
@@ -395,7 +407,9 @@ __global__ __launch_bounds__(256) void decode_grid_kernel(CacheView c, DecodeArg
   int T, cnt;
   const int nch = stream_chunks(c, a, u, &T, &cnt);
   if (k >= nch) return;
-  chunk_attend<D, DT, MODE, DENSE>(c, a, u, k, T, cnt, s_list, s_acc, s_ml);
+  const int first = k * a.split, nblk = min(a.split, cnt - first);
+  chunk_attend<D, DT, MODE, DENSE ? kChunkDense : kChunkList>(
+      c, a, u, k, T, first, nblk, first == 0 && nblk == cnt, s_list, s_acc, s_ml);
 }
 
 // Combine: one work-group per stream with two or more chunks.
@@ -412,6 +426,86 @@ __global__ __launch_bounds__(kCombWaves * kWave) void combine_kernel(CacheView c
   }
   if (nch == 1) return;  // written by the decode kernel
   combine_slots<D>(a, u, (size_t)u * a.max_chunks, nch, s_acc, s_ml);
+}
+
+// ---------------------------------------------------------------------------
+// Fused screen + decode, for steps too small to hide the separate screen,
+// compaction and decode launches.  One work-group per chunk of a.split <= 32
+// consecutive blocks, flattened as blockIdx.x = k * units + u (the first
+// chunks of every stream are dispatched first; chunks past a stream's end
+// exit).  Wave w scores blocks 8 w .. 8 w + 7 of the chunk with the screen's
+// Eq. 5 arithmetic (block_score, the same float32 operations in the same
+// order, so the admission bits equal eta_screen's for the same threshold),
+// the admitted indices go to LDS in ascending order, and the whole work-group
+// attends over them (chunk_attend).  Chunk k's partial lands in slot k of the
+// stream and the chunked combine merges a stream's ceil(nb / split) slots; a
+// chunk that admits nothing leaves the empty partial (max -inf, sum 0), and
+// the chunk holding the last block always admits it.
+// Register buffers per wave of the fused kernel's attention: four for a
+// bfloat16 cache (three tiles in flight while one is folded in; two waves per
+// SIMD suffice for the small steps it serves), two for float32 (whose tiles
+// take twice the registers).
+#ifndef ETA_FUSED_NBUF
+#define ETA_FUSED_NBUF 4
+#endif
+template <int DT>
+constexpr int fused_bufs() { return DT == ETA_DT_BF16 ? ETA_FUSED_NBUF : 2; }
+template <int D, int DT, int MODE>
+__global__ __launch_bounds__(256, 2) void screen_decode_kernel(CacheView c, DecodeArgs a,
+                                                               ScreenDecodeArgs sa) {
+  __shared__ int s_list[kMaxFusedChunk];
+  __shared__ float s_acc[4][D];
+  __shared__ float s_ml[4][2];
+  __shared__ uint32_t s_bits[4];
+  static_assert(4 * kBlocksPerIter == kMaxFusedChunk, "four waves score a whole chunk");
+  const int units = c.B * c.H;
+  const int u = blockIdx.x % units, k = blockIdx.x / units;
+  const int T = c.seq_len[u / c.H];
+  const int nb = T > 0 ? (T + c.bs - 1) >> c.log2bs : 0;
+  const int first = k * a.split;
+  if (first >= nb) return;  // uniform over the work-group
+  const int nbc = T >> c.log2bs;
+  const int nblk = min(a.split, nb - first);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (kBlocksPerIter * wave < nblk) {  // wave-uniform
+    const float ts = sa.tau_screen[u];
+    const int gi = lane / kLanesPerBlock, li = lane % kLanesPerBlock;
+    QShare<D> qs;
+    load_qshare<D>(a.q + (size_t)u * D, li, qs);
+    const int i = kBlocksPerIter * wave + gi;  // block first + i of the stream
+    const int j = first + i;
+    const bool scored = i < nblk && j < nbc;  // complete blocks of this chunk
+    const float sc = block_score<D>(c, u, j, scored, qs, li, sa.z, __builtin_isinf(sa.z), a.scale);
+    const bool on = i < nblk && (j == nb - 1 || (scored && sc >= ts));
+    const uint64_t bal = __ballot(on);
+    uint32_t bits = 0;
+#pragma unroll
+    for (int g = 0; g < kBlocksPerIter; ++g)
+      bits |= (uint32_t)((bal >> (g * kLanesPerBlock)) & 1ull) << g;
+    if (lane == 0) s_bits[wave] = bits;
+  } else if (lane == 0) {
+    s_bits[wave] = 0u;
+  }
+  __syncthreads();
+  const uint32_t word = s_bits[0] | (s_bits[1] << kBlocksPerIter) |
+                        (s_bits[2] << (2 * kBlocksPerIter)) | (s_bits[3] << (3 * kBlocksPerIter));
+  const int t = threadIdx.x;
+  if (t < kMaxFusedChunk && ((word >> t) & 1u)) s_list[__popc(word & ((1u << t) - 1u))] = first + t;
+  const int nadm = __popc(word);
+  if (t == 0) {
+    if (sa.chunk_bits) sa.chunk_bits[(size_t)u * a.max_chunks + k] = word;
+    if (sa.ctr && nadm > 0) {
+      // Admitted tokens; the stream's last block (always admitted) may be partial.
+      const bool last = first + nblk == nb;
+      const unsigned long long tokens =
+          (unsigned long long)nadm * c.bs - (last ? (unsigned long long)nb * c.bs - T : 0ull);
+      atomicAdd(reinterpret_cast<unsigned long long*>(sa.ctr), tokens);
+    }
+  }
+  const int nch = (nb + a.split - 1) / a.split;
+  // chunk_attend synchronises the work-group before reading s_list.
+  chunk_attend<D, DT, MODE, kChunkStaged, fused_bufs<DT>()>(c, a, u, k, T, first, nadm,
+                                                            nch == 1, s_list, s_acc, s_ml);
 }
 
 // ---------------------------------------------------------------------------
@@ -639,6 +733,37 @@ static hipError_t decode_dt(const CacheView& c, const DecodeArgs& a, hipStream_t
   if (a.dense) return decode_t<D, DT, ETA_LOGIT_RAW, true>(c, a, s);
   if (a.mode == ETA_LOGIT_RAW) return decode_t<D, DT, ETA_LOGIT_RAW, false>(c, a, s);
   return decode_t<D, DT, ETA_LOGIT_GATED, false>(c, a, s);
+}
+
+// Fused screen + decode, then the chunked combine (a.dense is set, so the
+// combine counts ceil(nb / split) chunks per stream).
+template <int D, int DT, int MODE>
+static hipError_t screen_decode_t(const CacheView& c, const DecodeArgs& a,
+                                  const ScreenDecodeArgs& sa, hipStream_t s) {
+  const int units = c.B * c.H;
+  const long long grid = (long long)a.max_chunks * units;
+  hipLaunchKernelGGL((screen_decode_kernel<D, DT, MODE>), dim3((unsigned)grid), dim3(256), 0, s,
+                     c, a, sa);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((combine_kernel<D>), dim3(units), dim3(kCombWaves * kWave), 0, s, c, a);
+  return hipGetLastError();
+}
+
+template <int D, int DT>
+static hipError_t screen_decode_dt(const CacheView& c, const DecodeArgs& a,
+                                   const ScreenDecodeArgs& sa, hipStream_t s) {
+  if (a.mode == ETA_LOGIT_RAW) return screen_decode_t<D, DT, ETA_LOGIT_RAW>(c, a, sa, s);
+  return screen_decode_t<D, DT, ETA_LOGIT_GATED>(c, a, sa, s);
+}
+
+hipError_t launch_screen_decode(const CacheView& c, const DecodeArgs& a,
+                                const ScreenDecodeArgs& sa, hipStream_t s) {
+  if (c.D == 128)
+    return c.dtype == ETA_DT_BF16 ? screen_decode_dt<128, ETA_DT_BF16>(c, a, sa, s)
+                                  : screen_decode_dt<128, ETA_DT_F32>(c, a, sa, s);
+  return c.dtype == ETA_DT_BF16 ? screen_decode_dt<64, ETA_DT_BF16>(c, a, sa, s)
+                                : screen_decode_dt<64, ETA_DT_F32>(c, a, sa, s);
 }
 
 hipError_t launch_decode(const CacheView& c, const DecodeArgs& a, hipStream_t s) {

@@ -9,73 +9,9 @@
 
 namespace eta {
 
-constexpr int kLanesPerBlock = 8;      // lanes that read one block's statistics
-constexpr int kBlocksPerIter = kWave / kLanesPerBlock;  // 8 blocks per wave step
 // Calibration values: each wave of a work-group scores 64 consecutive blocks.
 constexpr int kBlocksPerWave = 64;
 constexpr int kBlocksPerTile = 4 * kBlocksPerWave;
-
-// Per-lane share of the query: with 8 lanes per block, load t (t < D/32) of
-// lane li reads floats [32 t + 4 li, 32 t + 4 li + 4) of a statistics row, so
-// each load instruction covers one full 128-byte line of each of 8 blocks.
-template <int D>
-struct QShare {
-  static constexpr int kLoads = D / 32;
-  float q[4 * kLoads];
-  float q2[4 * kLoads];
-  float qn;  // ||q||_2
-};
-
-template <int D>
-__device__ __forceinline__ void load_qshare(const float* qu, int li, QShare<D>& s) {
-  float qq = 0.f;
-#pragma unroll
-  for (int t = 0; t < QShare<D>::kLoads; ++t) {
-    const float4 v = *reinterpret_cast<const float4*>(qu + 32 * t + 4 * li);
-    const float x[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      s.q[4 * t + e] = x[e];
-      s.q2[4 * t + e] = x[e] * x[e];
-      qq = fmaf(x[e], x[e], qq);
-    }
-  }
-  s.qn = sqrtf(group_sum<kLanesPerBlock>(qq));
-}
-
-// Eq. 5 score of block j of stream u.  All 8 lanes of the block's group must
-// call it together (DPP reductions); `valid` false yields garbage that the
-// caller ignores.  Every lane of the group returns the identical value.
-template <int D>
-__device__ __forceinline__ float block_score(const CacheView& c, int u, int j, bool valid,
-                                             const QShare<D>& s, int li, float z, bool z_inf,
-                                             float scale) {
-  float dot = 0.f, mom = 0.f, M = 0.f;
-  if (valid) {
-    const size_t row = ((size_t)u * c.cap_blocks + j) * D;
-    const float* mu = c.mu + row;
-    const float* var = c.var + row;
-#pragma unroll
-    for (int t = 0; t < QShare<D>::kLoads; ++t) {
-      const float4 m = ld16f_nt(mu + 32 * t + 4 * li);
-      const float4 v = ld16f_nt(var + 32 * t + 4 * li);
-      dot = fmaf(s.q[4 * t + 0], m.x, dot);
-      dot = fmaf(s.q[4 * t + 1], m.y, dot);
-      dot = fmaf(s.q[4 * t + 2], m.z, dot);
-      dot = fmaf(s.q[4 * t + 3], m.w, dot);
-      mom = fmaf(s.q2[4 * t + 0], v.x, mom);
-      mom = fmaf(s.q2[4 * t + 1], v.y, mom);
-      mom = fmaf(s.q2[4 * t + 2], v.z, mom);
-      mom = fmaf(s.q2[4 * t + 3], v.w, mom);
-    }
-    M = c.maxnorm[(size_t)u * c.cap_blocks + j];
-  }
-  dot = group_sum<kLanesPerBlock>(dot);
-  mom = group_sum<kLanesPerBlock>(mom);
-  const float geometric = s.qn * M;
-  if (z_inf) return scale * geometric;
-  return scale * fminf(fmaf(z, sqrtf(mom), dot), geometric);
-}
 
 // ---------------------------------------------------------------------------
 // Screen: one work-group per 64-block admission word.  Wave w scores blocks

@@ -91,6 +91,46 @@ def run_gpu(cache: eb.KVCache, q, *, W=None, bias_or_c=None, z, scale, mode=eb.G
                      gpu_mask(idx, cnt, cache.cap_blocks))
 
 
+def chunk_mask(bits: np.ndarray, chunk: int, seq_len: np.ndarray, b: int,
+               nbcap: int) -> np.ndarray:
+    """Admission mask [B][H][nbcap] from the fused path's per-chunk bits (bit i
+    of entry k: block k*chunk + i).  Entries of chunks that start past a
+    stream's end are unwritten by contract and read as zero here; bits past
+    the end inside the last chunk are kept (the kernel must leave them 0)."""
+    B, H, nch = bits.shape
+    u = bits.astype(np.int64) & 0xFFFFFFFF
+    nb = -(-seq_len.astype(np.int64) // b)
+    written = (np.arange(nch)[None, :] * chunk) < nb[:, None]          # [B][nch]
+    u = np.where(written[:, None, :], u, 0)
+    m = ((u[..., None] >> np.arange(chunk)) & 1).astype(np.uint8)
+    m = m.reshape(B, H, nch * chunk)
+    assert not m[..., nbcap:].any(), "admission bit beyond the cache capacity"
+    return np.ascontiguousarray(m[..., :nbcap])
+
+
+def run_gpu_fused(cache: eb.KVCache, q, *, W=None, bias_or_c=None, z, scale, mode=eb.GATED,
+                  beta=5.0, a=0.0, chunk=None, build_meta=True) -> GpuResult:
+    """predict_tau -> the fused screen + decode (eta_screen_decode)."""
+    if build_meta:
+        eb.build_block_meta(cache)
+    dec = eb.Decoder(cache, z=z, scale=scale, beta=beta, a=a, logit_mode=mode,
+                     fused_blocks_per_chunk=chunk)
+    dec.chunk_bits.zero_()
+    dec.step_fused(q, W, bias_or_c)
+    torch.cuda.synchronize()
+    sl = cache.seq_len.cpu().numpy()
+    mask = chunk_mask(dec.chunk_bits.cpu().numpy(), dec.fused_chunk, sl, cache.block,
+                      cache.cap_blocks)
+    cnt = mask.sum(axis=2).astype(np.int32)
+    idx = np.zeros(mask.shape, np.int32)
+    for bb in range(mask.shape[0]):
+        for h in range(mask.shape[1]):
+            j = np.nonzero(mask[bb, h])[0]
+            idx[bb, h, :len(j)] = j
+    return GpuResult(dec.tau_gate.cpu().numpy(), dec.tau_screen.cpu().numpy(), idx, cnt,
+                     int(dec.density_ctr.cpu().item()), dec.out.cpu().numpy(), mask)
+
+
 def gpu_tokens(cnt: np.ndarray, seq_len: np.ndarray, b: int) -> np.ndarray:
     """Admitted tokens per stream implied by the GPU counts (the last block,
     possibly partial, is always in the list)."""

@@ -1,0 +1,164 @@
+"""GPU parity of the fused screen + decode (eta_screen_decode) against the fp64
+oracle, and against the separate screen -> decode path on the same inputs.
+
+The fused path scores blocks with the screen's own float32 arithmetic, so for
+the same thresholds its admission mask must equal eta_screen's bit for bit;
+its output is held to the same bars as the separate decode (near-tie flips
+against the oracle only, outputs within the cache dtype's bar and the 1e-5
+internal bar).  Cases: the hand example, the tiny fp32 workload, ragged
+lengths around block and chunk boundaries with an empty stream and NaN-filled
+unused slots, every chunk size shape (1, 3, 8, 32 blocks), both logit modes,
+threshold extremes, determinism, and the single 32K sequence at its full size
+(all 16 heads against the oracle) at 10%, 38% and 70% density.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from long_context_decode_eta_amd import binding as eb
+from long_context_decode_eta_amd import synth
+from parity import (check_against_oracle, check_units, make_cache, note, oracle_constants,
+                    run_gpu, run_gpu_fused, to_gpu)
+from test_gpu_parity_small import LENS, hand_cache
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _name(request):
+    note(f"[gpu] {request.node.name}")
+
+
+def _same_as_separate(g_fused, g_sep):
+    """Same thresholds, same admission bits and token count as eta_screen."""
+    np.testing.assert_array_equal(g_fused.tau_gate, g_sep.tau_gate)
+    np.testing.assert_array_equal(g_fused.mask, g_sep.mask)
+    assert g_fused.density == g_sep.density
+
+
+@pytest.mark.parametrize("mode", [eb.GATED, eb.RAW])
+@pytest.mark.parametrize("z,tau", [(1.0, -math.inf), (1.0, 0.6), (2.0, 1.2), (math.inf, 1.2),
+                                   (1.0, math.inf)])
+def test_hand_example(z, tau, mode):
+    w = to_gpu(hand_cache())
+    cache = make_cache(w)
+    c = torch.full((1,), tau, dtype=torch.float32, device="cuda")
+    for chunk in (1, 3):
+        g = run_gpu_fused(cache, w.q, bias_or_c=c, z=z, scale=0.5, mode=mode, chunk=chunk)
+        st = check_against_oracle(w, g, cache, W=None, bias_or_c=c, z=z, scale=0.5, mode=mode)
+        assert st["flips"] == 0
+        assert g.out[0, 0, 1] == pytest.approx(1.0, abs=1e-6)
+
+
+@pytest.mark.parametrize("mode", [eb.GATED, eb.RAW])
+@pytest.mark.parametrize("chunk", [1, 3, 8, 32])
+def test_tiny_workload(mode, chunk):
+    w = to_gpu(synth.make("tiny", seed=1234))
+    cache = make_cache(w)
+    g = run_gpu_fused(cache, w.q, bias_or_c=w.tau_const, z=w.z, scale=w.scale, mode=mode,
+                      chunk=chunk)
+    st = check_against_oracle(w, g, cache, W=None, bias_or_c=w.tau_const, z=w.z, scale=w.scale,
+                              mode=mode)
+    s = run_gpu(cache, w.q, bias_or_c=w.tau_const, z=w.z, scale=w.scale, mode=mode,
+                build_meta=False)
+    _same_as_separate(g, s)
+    note(f"  density {st['density']:.3f} out_rel {st['out_rel']:.2e} flips {st['flips']}")
+    assert 0.0 < st["density"] < 1.0
+
+
+@pytest.mark.parametrize("kv", ["bf16", "f32"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("block", [4, 16, 64])
+def test_ragged_edges(kv, D, block):
+    # Lengths around block and chunk boundaries, an empty stream, unused slots
+    # NaN-filled, a dynamic threshold from the predictor.
+    name = "tiny" if D == 64 else "ctx32k"
+    w = synth.make(name, seed=7 + block, T=LENS, B=len(LENS), H=3, cap=1024, pad="nan",
+                   block=block, kv=kv)
+    to_gpu(w)
+    cache = make_cache(w)
+    rng = np.random.default_rng(block)
+    W = torch.from_numpy((rng.standard_normal((3 * D, 3)) / math.sqrt(D)).astype(np.float32))
+    W = W.cuda()
+    c = torch.tensor([0.2, 0.6, 1.0], dtype=torch.float32, device="cuda")
+    for mode in (eb.GATED, eb.RAW):
+        s = run_gpu(cache, w.q, W=W, bias_or_c=c, z=1.0, scale=w.scale, mode=mode)
+        for chunk in (1, 3, 8, 32):
+            g = run_gpu_fused(cache, w.q, W=W, bias_or_c=c, z=1.0, scale=w.scale, mode=mode,
+                              chunk=chunk, build_meta=False)
+            _same_as_separate(g, s)
+            st = check_against_oracle(w, g, cache, W=W, bias_or_c=c, z=1.0, scale=w.scale,
+                                      mode=mode, check_meta=False)
+            assert not np.isnan(g.out).any()
+            assert np.all(g.out[0] == 0)  # the empty stream
+    note(f"  density {st['density']:.3f} out_rel {st['out_rel']:.2e}")
+
+
+@pytest.mark.parametrize("tau", [math.inf, -math.inf])
+def test_threshold_extremes(tau):
+    w = to_gpu(synth.make("ctx128k", seed=3, T=(100, 3000), B=4, H=2, cap=3000, block=32))
+    cache = make_cache(w)
+    c = torch.full((2,), tau, dtype=torch.float32, device="cuda")
+    g = run_gpu_fused(cache, w.q, bias_or_c=c, z=1.0, scale=w.scale, chunk=8)
+    nb = -(-w.seq_len.cpu().numpy() // 32)
+    assert np.all(g.cnt == (1 if tau == math.inf else nb[:, None]))
+    check_against_oracle(w, g, cache, W=None, bias_or_c=c, z=1.0, scale=w.scale, mode=eb.GATED)
+
+
+def test_chunk_invariance_and_determinism():
+    w = to_gpu(synth.make("ctx128k", seed=11, T=(2000, 9000), B=3, H=4, cap=9000))
+    cache = make_cache(w)
+    eb.build_block_meta(cache)
+    c = torch.full((4,), 1.2, dtype=torch.float32, device="cuda")
+    ref = run_gpu(cache, w.q, bias_or_c=c, z=1.0, scale=w.scale, split=1, build_meta=False)
+    for chunk in (1, 2, 5, 16, 32):
+        first = None
+        for _ in range(2):
+            g = run_gpu_fused(cache, w.q, bias_or_c=c, z=1.0, scale=w.scale, chunk=chunk,
+                              build_meta=False)
+            if first is not None:
+                assert np.array_equal(g.out, first), "run-to-run difference"
+            first = g.out
+        np.testing.assert_array_equal(g.mask, ref.mask)
+        np.testing.assert_allclose(g.out, ref.out, rtol=2e-6, atol=2e-6)
+
+
+_held = {}
+
+
+def _ctx32k():
+    if "w" not in _held:
+        torch.cuda.empty_cache()
+        w = synth.make("ctx32k", seed=1234, device="cuda")
+        cache = make_cache(w)
+        eb.build_block_meta(cache)
+        torch.cuda.synchronize()
+        rhos = [0.10, 0.38, 0.70]
+        consts = dict(zip(rhos, [c for c, _ in oracle_constants(w, rhos, seqs=[0])]))
+        _held.update(w=w, cache=cache, consts=consts)
+    return _held["w"], _held["cache"], _held["consts"]
+
+
+@pytest.mark.parametrize("rho", [0.10, 0.38, 0.70])
+def test_ctx32k_full_size_every_head(rho):
+    """The single 32K sequence, 16 heads, d 128, block 64, bf16, dynamic tau,
+    in the chunking the Decoder picks by itself; every head against the
+    oracle, and the admission bits against the separate screen."""
+    w, cache, consts = _ctx32k()
+    c = consts[rho].cuda()
+    g = run_gpu_fused(cache, w.q, W=w.W, bias_or_c=c, z=w.z, scale=w.scale, build_meta=False)
+    s = run_gpu(cache, w.q, W=w.W, bias_or_c=c, z=w.z, scale=w.scale, build_meta=False)
+    _same_as_separate(g, s)
+    worst, flips, screened = check_units(w, g, [(0, h) for h in range(w.H)], W=w.W,
+                                         bias_or_c=c, z=w.z, scale=w.scale)
+    dens = g.density / (int(w.seq_len.sum()) * w.H)
+    note(f"  target {rho:.2f}: density {dens:.4f}, worst out rel err {worst:.2e}, "
+         f"flips {flips}/{screened}")
+    assert abs(dens - rho) < 0.1
+
+
+def test_release_ctx32k():
+    _held.clear()
+    torch.cuda.empty_cache()

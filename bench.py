@@ -358,14 +358,17 @@ class DecodeBench:
             dec.predict(w.q, None, c)
 
         # The timed call: eta_decode (balanced decode + combine) on the split
-        # path, eta_screen_decode (fused screen + decode + combine) on the
-        # fused one.
-        call = (lambda: dec.screen_attend(w.q)) if self.fused else (lambda: dec.attend(w.q))
+        # path, eta_fused_step (threshold, screen and decode, then the
+        # combine) on the fused one, which is then the whole step.
+        if self.fused:
+            call = lambda: dec.step_fused(w.q, None if self.frozen else W, c)
+        else:
+            call = lambda: dec.attend(w.q)
 
         def step():
-            if not self.frozen:
-                dec.predict(w.q, W, c)
             if not self.fused:
+                if not self.frozen:
+                    dec.predict(w.q, W, c)
                 dec.screen(w.q)
             call()
 
@@ -377,9 +380,9 @@ class DecodeBench:
         torch.cuda.synchronize()
         a = time.perf_counter()
         for _ in range(steps):
-            if not self.frozen:
-                dec.predict(w.q, W, c)
             if not self.fused:
+                if not self.frozen:
+                    dec.predict(w.q, W, c)
                 tscr.around(lambda: dec.screen(w.q))
             tdec.around(call)
         torch.cuda.synchronize()
@@ -471,18 +474,19 @@ class DecodeBench:
     def decode_bytes(self, r):
         """Algorithmic bytes of the timed call.  eta_decode: admitted K+V, q,
         the active lists, partials (m, l, acc) written and read for streams
-        split over several ranges, output.  eta_screen_decode: the block
-        statistics, admitted K+V, q and thresholds, one partial per chunk of a
-        stream with several chunks (written and read), the chunk bits,
-        output."""
+        split over several ranges, output.  eta_fused_step: the predictor
+        weights (dynamic thresholds), the block statistics, admitted K+V, q,
+        the thresholds written, one partial per chunk of a stream with several
+        chunks (written and read), the chunk bits, output."""
         np, w = self.np, self.w
         B, H, D = w.B, w.H, w.D
         if self.fused:
             nb = -(-self.sl // w.block)
             nch = -(-nb // self.dec.fused_chunk)  # chunks per stream of each sequence
             part = int(H * (np.where(nch > 1, nch, 0) * (D + 2) * 4 * 2).sum())
-            return (self.meta_bytes + r["tokens"] * D * 2 * self.elt + B * H * D * 4 * 2 +
-                    2 * B * H * 4 + int(H * nch.sum()) * 4 + part)
+            weights = 0 if self.frozen else H * D * H * 4 + H * 4
+            return (weights + self.meta_bytes + r["tokens"] * D * 2 * self.elt +
+                    B * H * D * 4 * 2 + 2 * B * H * 4 + int(H * nch.sum()) * 4 + part)
         chunks = -(-r["cnt"] // self.split)
         part = int((np.where(chunks > 1, chunks, 0) * (D + 2) * 4 * 2).sum())
         return (r["tokens"] * D * 2 * self.elt + B * H * D * 4 * 2 + int(r["cnt"].sum()) * 4 +
@@ -491,16 +495,16 @@ class DecodeBench:
     def step_bytes(self, r):
         w = self.w
         B, H, D = w.B, w.H, w.D
+        if self.fused:  # the fused call is the whole step
+            return r["decode_bytes"]
         pred = 0 if self.frozen else B * H * D * 4 + H * D * H * 4 + 2 * B * H * 4
-        if self.fused:
-            return pred + r["decode_bytes"]
         screen = self.meta_bytes + B * H * D * 4 + int(r["cnt"].sum()) * 4 + B * H * 4
         return pred + screen + r["decode_bytes"]
 
     def roofline(self, r, dense_ms):
         achieved = r["decode_bytes"] / (r["decode_ms"] * 1e-3) / 1e9
         stream_gbs = self.dense_bytes / dense_ms / 1e6
-        kernel = ("eta_screen_decode (fused screen + decode, combine kernels)" if self.fused
+        kernel = ("eta_fused_step (fused threshold + screen + decode, combine kernels)" if self.fused
                   else "eta_decode (balanced decode + combine kernels)")
         return {"bound": "hbm", "kernel": kernel,
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

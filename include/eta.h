@@ -137,7 +137,9 @@ eta_status eta_build_block_meta(const eta_cache* c, int32_t first_block, int32_t
  * Frozen mode (W == NULL): tau_gate[b][h] = bias_or_c[h] (offline-calibrated
  * per-head constants).  Both modes: tau_screen = tau_gate - a (a is the
  * threshold adjustment; 0 leaves them equal).  Outputs device [batch][heads].
- * heads <= 256.  The sum over j runs in a fixed order (deterministic).
+ * heads <= 256.  The sum over j runs in a fixed order (deterministic, and
+ * shared with eta_fused_step): 256 partial sums, partial t over j = t,
+ * t + 256, ... in turn, added by a fixed tree, then the bias.
  */
 eta_status eta_predict_tau(int32_t batch, int32_t heads, int32_t head_dim, const float* q,
                            const float* W, const float* bias_or_c, float a, float* tau_gate,
@@ -221,34 +223,38 @@ eta_status eta_dense_decode(const eta_cache* c, const float* q, float scale,
                             float* out, void* stream);
 
 /*
- * Screen and block-sparse decode fused into one pass, for small steps where
- * separate launches cost more than the work (Methodology 4, Eq. 5 for the
- * admission; Methodology 2, Eq. 3 for the logits; Fig. 6: only admitted
- * blocks are loaded, online softmax).  Every stream is cut into chunks of
- * blocks_per_chunk consecutive blocks (1 <= blocks_per_chunk <= 32), one
- * work-group each, which screens its chunk's blocks exactly as eta_screen
- * does (the same float32 operations, so for the same tau_screen the admitted
- * set is the same, the last block always in it) and attends over the blocks it
- * admitted; a combine pass merges the chunks of each stream by log-sum-exp.
- * out and the logits as in eta_decode (tau_gate may be NULL in RAW mode).
- * q: device [batch][heads][head_dim]; tau_gate, tau_screen: device
- * [batch][heads] (eta_predict_tau's outputs); z, scale as in eta_screen.
- * Optional outputs (NULL: not written):
+ * One decode step -- threshold (Methodology 1, Eq. 1), screen (Methodology
+ * 4, Eq. 5) and block-sparse decode (Methodology 2, Eq. 3 logits; Fig. 6:
+ * only admitted blocks are loaded, online softmax) -- in two launches, for
+ * small steps where the separate calls' launches cost more than their work.
+ * Every stream is cut into chunks of blocks_per_chunk consecutive blocks
+ * (1 <= blocks_per_chunk <= 32), one work-group each, which computes its
+ * stream's thresholds exactly as eta_predict_tau does (the same float32
+ * operations in the same order, so the same bits), screens its chunk's blocks
+ * exactly as eta_screen does (so the same admitted set, the last block always
+ * in it) and attends over the blocks it admitted; a combine pass merges the
+ * chunks of each stream by log-sum-exp in chunk order.
+ * Inputs: q device [batch][heads][head_dim]; W, bias_or_c and a as for
+ * eta_predict_tau (W NULL: frozen constants); z, scale as for eta_screen;
+ * logit_mode, beta as for eta_decode.  heads <= 256.
+ * Outputs: out [batch][heads][head_dim] float32 as eta_decode's (a stream with
+ * T_b == 0 yields zeros); optional (NULL: not written):
+ *   tau_gate, tau_screen  device [batch][heads], eta_predict_tau's outputs;
  *   chunk_bits  device [batch][heads][ceil(cap_blocks / blocks_per_chunk)]
  *               uint32: bit i of entry k set iff block k * blocks_per_chunk + i
  *               is admitted (entries of chunks past a stream's end are left
  *               unwritten);
  *   density_ctr one uint64, += admitted tokens as in eta_screen.
- * Workspace: eta_screen_decode_workspace_bytes(); contents need no
- * initialisation.  A stream with T_b == 0 yields zeros.
+ * Workspace: eta_fused_step_workspace_bytes(); contents need no
+ * initialisation.
  */
-size_t eta_screen_decode_workspace_bytes(int32_t batch, int32_t heads, int32_t head_dim,
-                                         int32_t cap_blocks, int32_t blocks_per_chunk);
-eta_status eta_screen_decode(const eta_cache* c, const float* q, const float* tau_gate,
-                             const float* tau_screen, float z, int32_t logit_mode, float beta,
-                             float scale, int32_t blocks_per_chunk, uint32_t* chunk_bits,
-                             uint64_t* density_ctr, void* workspace, size_t workspace_bytes,
-                             float* out, void* stream);
+size_t eta_fused_step_workspace_bytes(int32_t batch, int32_t heads, int32_t head_dim,
+                                      int32_t cap_blocks, int32_t blocks_per_chunk);
+eta_status eta_fused_step(const eta_cache* c, const float* q, const float* W,
+                          const float* bias_or_c, float a, float z, int32_t logit_mode,
+                          float beta, float scale, int32_t blocks_per_chunk, float* tau_gate,
+                          float* tau_screen, uint32_t* chunk_bits, uint64_t* density_ctr,
+                          void* workspace, size_t workspace_bytes, float* out, void* stream);
 
 /*
  * Offline calibration of frozen per-head constants (the pages' calibration

@@ -57,11 +57,11 @@ _SIGS = {
                             c_float, c_int32, c_void_p, c_void_p], c_int32),
     "eta_dense_decode": ([_P, c_void_p, c_float, c_int32, c_void_p, c_size_t, c_void_p,
                           c_void_p], c_int32),
-    "eta_screen_decode_workspace_bytes": ([c_int32, c_int32, c_int32, c_int32, c_int32],
-                                          c_size_t),
-    "eta_screen_decode": ([_P, c_void_p, c_void_p, c_void_p, c_float, c_int32, c_float, c_float,
-                           c_int32, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p, c_void_p],
-                          c_int32),
+    "eta_fused_step_workspace_bytes": ([c_int32, c_int32, c_int32, c_int32, c_int32],
+                                       c_size_t),
+    "eta_fused_step": ([_P, c_void_p, c_void_p, c_void_p, c_float, c_float, c_int32, c_float,
+                        c_float, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                        c_size_t, c_void_p, c_void_p], c_int32),
     "eta_calibrate_workspace_bytes": ([c_int32, c_int32, c_int32, c_int32], c_size_t),
     "eta_calibrate_threshold": ([_P, c_int32, c_void_p, c_void_p, c_float, c_float, c_float,
                                  c_void_p, c_size_t, c_void_p, c_void_p], c_int32),
@@ -321,24 +321,25 @@ def gated_prefill(q, k, v, tau, group, beta, scale, out, dens=None, stream=None)
            "eta_gated_prefill")
 
 
-def screen_decode_workspace_bytes(batch, heads, head_dim, cap_blocks, blocks_per_chunk) -> int:
-    return int(lib().eta_screen_decode_workspace_bytes(batch, heads, head_dim, cap_blocks,
-                                                       blocks_per_chunk))
+def fused_step_workspace_bytes(batch, heads, head_dim, cap_blocks, blocks_per_chunk) -> int:
+    return int(lib().eta_fused_step_workspace_bytes(batch, heads, head_dim, cap_blocks,
+                                                    blocks_per_chunk))
 
 
-def screen_decode(cache: KVCache, q, tau_gate, tau_screen, z, logit_mode, beta, scale,
-                  blocks_per_chunk, chunk_bits, density_ctr, workspace, out, stream=None):
-    _check(lib().eta_screen_decode(_ref(cache), _dev(q, torch.float32, "q"),
-                                   _dev(tau_gate, torch.float32, "tau_gate"),
-                                   _dev(tau_screen, torch.float32, "tau_screen"), float(z),
-                                   int(logit_mode), float(beta), float(scale),
-                                   int(blocks_per_chunk), _dev(chunk_bits, torch.int32,
-                                                               "chunk_bits"),
-                                   _dev(density_ctr, None, "density_ctr"),
-                                   _dev(workspace, None, "workspace"),
-                                   workspace.numel() * workspace.element_size(),
-                                   _dev(out, torch.float32, "out"), _stream(stream)),
-           "eta_screen_decode")
+def fused_step(cache: KVCache, q, W, bias_or_c, a, z, logit_mode, beta, scale, blocks_per_chunk,
+               tau_gate, tau_screen, chunk_bits, density_ctr, workspace, out, stream=None):
+    _check(lib().eta_fused_step(_ref(cache), _dev(q, torch.float32, "q"),
+                                _dev(W, torch.float32, "W"),
+                                _dev(bias_or_c, torch.float32, "bias_or_c"), float(a), float(z),
+                                int(logit_mode), float(beta), float(scale),
+                                int(blocks_per_chunk), _dev(tau_gate, torch.float32, "tau_gate"),
+                                _dev(tau_screen, torch.float32, "tau_screen"),
+                                _dev(chunk_bits, torch.int32, "chunk_bits"),
+                                _dev(density_ctr, None, "density_ctr"),
+                                _dev(workspace, None, "workspace"),
+                                workspace.numel() * workspace.element_size(),
+                                _dev(out, torch.float32, "out"), _stream(stream)),
+           "eta_fused_step")
 
 
 def workspace(nbytes: int, device="cuda") -> torch.Tensor:
@@ -361,13 +362,13 @@ def auto_split(units: int, cap_blocks: int, block: int, dense: bool = False) -> 
 
 
 def auto_fused_chunk(units: int, cap_blocks: int) -> int:
-    """Blocks per chunk of the fused screen + decode: the largest of 32, 16,
-    ..., 1 that still gives at least 512 work-groups (two per compute unit).
-    Swept on MI355X at 32K x 16 heads, b=64 (8192 blocks): 16 blocks per
-    chunk (512 work-groups) at 38% and 70% density, 16 or 32 at 10%; 4 and 8
-    were slower at every density."""
+    """Blocks per chunk of the fused step: the largest of 32, 16, ..., 1 that
+    still gives at least 256 work-groups (one per compute unit).  Swept on
+    MI355X at 32K x 16 heads, b=64 (8192 blocks): 32 blocks per chunk (256
+    work-groups) took 0.023 / 0.037 / 0.049 ms at 10 / 38 / 70% density, 16
+    blocks 0.026 / 0.038 / 0.050 ms; 4 and 8 were slower at every density."""
     for cb in (32, 16, 8, 4, 2):
-        if units * (-(-cap_blocks // cb)) >= 512:
+        if units * (-(-cap_blocks // cb)) >= 256:
             return cb
     return 1
 
@@ -418,8 +419,8 @@ class Decoder:
         self.fused_chunk = int(fused_blocks_per_chunk or auto_fused_chunk(B * H, nbc))
         self.chunk_bits = torch.zeros((B, H, -(-nbc // self.fused_chunk)), dtype=torch.int32,
                                       device=dev)
-        self.fused_ws = workspace(screen_decode_workspace_bytes(B, H, D, nbc,
-                                                                self.fused_chunk), dev)
+        self.fused_ws = workspace(fused_step_workspace_bytes(B, H, D, nbc, self.fused_chunk),
+                                  dev)
 
     def predict(self, q, W, bias_or_c, stream=None):
         predict_tau(q, W, bias_or_c, self.a, self.tau_gate, self.tau_screen, stream)
@@ -444,15 +445,15 @@ class Decoder:
         self.attend(q, stream)
         return self.out
 
-    def screen_attend(self, q, stream=None):
-        screen_decode(self.cache, q, self.tau_gate, self.tau_screen, self.z, self.mode,
-                      self.beta, self.scale, self.fused_chunk, self.chunk_bits,
-                      self.density_ctr, self.fused_ws, self.out, stream)
-
     def step_fused(self, q, W=None, bias_or_c=None, stream=None):
-        if bias_or_c is not None:
-            self.predict(q, W, bias_or_c, stream)
-        self.screen_attend(q, stream)
+        """eta_fused_step: thresholds (into tau_gate / tau_screen), screen
+        and decode in two launches.  bias_or_c is required (the fused step
+        always computes its thresholds)."""
+        if bias_or_c is None:
+            raise ValueError("the fused step needs bias_or_c (and W in dynamic mode)")
+        fused_step(self.cache, q, W, bias_or_c, self.a, self.z, self.mode, self.beta, self.scale,
+                   self.fused_chunk, self.tau_gate, self.tau_screen, self.chunk_bits,
+                   self.density_ctr, self.fused_ws, self.out, stream)
         return self.out
 
     def dense(self, q, stream=None):

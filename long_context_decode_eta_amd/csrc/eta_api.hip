@@ -396,21 +396,22 @@ eta_status eta_dense_decode(const eta_cache* c, const float* q, float scale,
                        blocks_per_split, workspace, workspace_bytes, out, stream);
 }
 
-size_t eta_screen_decode_workspace_bytes(int32_t batch, int32_t heads, int32_t head_dim,
-                                         int32_t cap_blocks, int32_t blocks_per_chunk) {
+size_t eta_fused_step_workspace_bytes(int32_t batch, int32_t heads, int32_t head_dim,
+                                      int32_t cap_blocks, int32_t blocks_per_chunk) {
   if (batch <= 0 || heads <= 0 || head_dim <= 0 || cap_blocks <= 0 || blocks_per_chunk <= 0)
     return 256;
   const long long units = (long long)batch * heads;
   return decode_ws_slots(units, head_dim, grid_slots(units, cap_blocks, blocks_per_chunk));
 }
 
-eta_status eta_screen_decode(const eta_cache* c, const float* q, const float* tau_gate,
-                             const float* tau_screen, float z, int32_t logit_mode, float beta,
-                             float scale, int32_t blocks_per_chunk, uint32_t* chunk_bits,
-                             uint64_t* density_ctr, void* workspace, size_t workspace_bytes,
-                             float* out, void* stream) {
+eta_status eta_fused_step(const eta_cache* c, const float* q, const float* W,
+                          const float* bias_or_c, float a, float z, int32_t logit_mode,
+                          float beta, float scale, int32_t blocks_per_chunk, float* tau_gate,
+                          float* tau_screen, uint32_t* chunk_bits, uint64_t* density_ctr,
+                          void* workspace, size_t workspace_bytes, float* out, void* stream) {
   eta::CacheView v;
   if (eta_status s = check_cache(c, &v)) return s;
+  if (v.H > 256) return fail(ETA_ERR_BAD_SHAPE, "heads %d > 256", v.H);
   if (logit_mode != ETA_LOGIT_GATED && logit_mode != ETA_LOGIT_RAW)
     return fail(ETA_ERR_BAD_ARG, "logit_mode %d unknown", logit_mode);
   if (logit_mode == ETA_LOGIT_GATED && (bad_float(beta) || !(beta > 0.f) || isinf(beta)))
@@ -418,43 +419,45 @@ eta_status eta_screen_decode(const eta_cache* c, const float* q, const float* ta
   if (bad_float(scale) || !(scale > 0.f) || isinf(scale))
     return fail(ETA_ERR_BAD_ARG, "scale must be finite and > 0");
   if (bad_float(z) || z < 0.f) return fail(ETA_ERR_BAD_ARG, "z must be >= 0 (or +inf)");
+  if (bad_float(a)) return fail(ETA_ERR_BAD_ARG, "a is NaN");
   if (blocks_per_chunk < 1 || blocks_per_chunk > eta::kMaxFusedChunk)
     return fail(ETA_ERR_BAD_ARG, "blocks_per_chunk %d outside [1, %d]", blocks_per_chunk,
                 eta::kMaxFusedChunk);
   if (empty(v)) return ok();
-  if (!q || !out || !tau_screen) return fail(ETA_ERR_NULL_PTR, "q/tau_screen/out is NULL");
-  if (logit_mode == ETA_LOGIT_GATED && !tau_gate)
-    return fail(ETA_ERR_NULL_PTR, "tau_gate is NULL in GATED mode");
+  if (!q || !out || !bias_or_c) return fail(ETA_ERR_NULL_PTR, "q/bias_or_c/out is NULL");
   const long long units = (long long)v.B * v.H;
+  if ((long long)v.H * v.D > 0x7fffffffLL / 4) return fail(ETA_ERR_BAD_SHAPE, "heads * head_dim too large");
   const int maxc = eta::ceil_div(v.cap_blocks, blocks_per_chunk);
   if ((long long)maxc * units > kMaxGrid) return fail(ETA_ERR_BAD_SHAPE, "grid too large");
   const size_t slots = grid_slots(units, v.cap_blocks, blocks_per_chunk);
   const size_t need = decode_ws_slots(units, v.D, slots);
   if (!workspace || workspace_bytes < need)
-    return fail(ETA_ERR_WORKSPACE, "screen-decode workspace %zu bytes < %zu", workspace_bytes,
-                need);
+    return fail(ETA_ERR_WORKSPACE, "fused-step workspace %zu bytes < %zu", workspace_bytes, need);
   char* w = static_cast<char*>(workspace);
   const size_t off_parts = 256 + align256((size_t)(units + 1) * 4);
-  eta::DecodeArgs a = {};
-  a.q = q;
-  a.tau = tau_gate;
-  a.mode = logit_mode;
-  a.dense = true;  // the combine merges every chunk of a stream
-  a.beta = beta;
-  a.scale = scale;
-  a.split = blocks_per_chunk;
-  a.max_chunks = maxc;
-  a.part_m = reinterpret_cast<float*>(w + off_parts);
-  a.part_l = reinterpret_cast<float*>(w + off_parts + align256(slots * 4));
-  a.part_acc = reinterpret_cast<float*>(w + off_parts + 2 * align256(slots * 4));
-  a.out = out;
+  eta::DecodeArgs d = {};
+  d.q = q;
+  d.mode = logit_mode;
+  d.dense = true;  // the combine merges every chunk of a stream
+  d.beta = beta;
+  d.scale = scale;
+  d.split = blocks_per_chunk;
+  d.max_chunks = maxc;
+  d.part_m = reinterpret_cast<float*>(w + off_parts);
+  d.part_l = reinterpret_cast<float*>(w + off_parts + align256(slots * 4));
+  d.part_acc = reinterpret_cast<float*>(w + off_parts + 2 * align256(slots * 4));
+  d.out = out;
   eta::ScreenDecodeArgs sa;
-  sa.tau_screen = tau_screen;
+  sa.W = W;
+  sa.bias = bias_or_c;
+  sa.a = a;
   sa.z = z;
+  sa.tau_gate = tau_gate;
+  sa.tau_screen = tau_screen;
   sa.chunk_bits = chunk_bits;
   sa.ctr = density_ctr;
-  return hip_status(eta::launch_screen_decode(v, a, sa, (hipStream_t)stream),
-                    "eta_screen_decode launch");
+  return hip_status(eta::launch_screen_decode(v, d, sa, (hipStream_t)stream),
+                    "eta_fused_step launch");
 }
 
 size_t eta_calibrate_workspace_bytes(int32_t n_sets, int32_t batch, int32_t heads,

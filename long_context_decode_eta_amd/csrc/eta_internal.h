@@ -346,6 +346,41 @@ __device__ __forceinline__ float block_score(const CacheView& c, int u, int j, b
 }
 
 // ---------------------------------------------------------------------------
+// Eq. 1 threshold of one (sequence, head), tau = sum_j q_j W[j][h] + bias[h]
+// over the n = H*D entries of the sequence's query, by the 256 threads of a
+// work-group in one fixed order shared by the threshold kernel and the fused
+// screen + decode (so both produce the same bits): thread t adds q_j W[j][h]
+// for j = t, t + 256, ... in that order (fmaf, four loads in flight), the 64
+// lanes of a wave are summed by an xor butterfly (every lane ends with the
+// same bits), the four wave sums as (w0 + w1) + (w2 + w3), the bias last.
+// W == NULL (frozen thresholds) gives bias[h] alone.  Every thread returns
+// the value; with W it contains one barrier (s_red: 4 floats of LDS).
+constexpr int kTauThreads = 256;
+__device__ __forceinline__ float tau_of_head(const float* qb, const float* W, const float* bias,
+                                             int H, int n, int h, float* s_red) {
+  if (!W) return bias[h];
+  const int t = threadIdx.x;
+  float acc = 0.f;
+  int j = t;
+  for (; j + 3 * kTauThreads < n; j += 4 * kTauThreads) {
+    float qv[4], wv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      qv[r] = qb[j + r * kTauThreads];
+      wv[r] = W[(size_t)(j + r * kTauThreads) * H + h];
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc = fmaf(qv[r], wv[r], acc);
+  }
+  for (; j < n; j += kTauThreads) acc = fmaf(qb[j], W[(size_t)j * H + h], acc);
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, kWave);
+  if ((t & (kWave - 1)) == 0) s_red[t / kWave] = acc;
+  __syncthreads();
+  return ((s_red[0] + s_red[1]) + (s_red[2] + s_red[3])) + bias[h];
+}
+
+// ---------------------------------------------------------------------------
 // Launchers (defined in the kernel translation units).  Each returns the
 // hipError_t of its launch; shapes were validated by the caller.
 hipError_t launch_append(const CacheView& c, const void* k_new, const void* v_new,
@@ -390,13 +425,18 @@ constexpr int kMaxFlowUnits = 8191;
 constexpr int kMaxQueueUnits = 8192;
 constexpr long long kQueueAboveGrid = 49152;
 hipError_t launch_decode(const CacheView& c, const DecodeArgs& a, hipStream_t s);
-// Fused screen + decode: the screen's inputs and optional outputs beside the
-// decode arguments (split = blocks per chunk <= kMaxFusedChunk, dense set so
-// that the combine counts every chunk of a stream).
+// Fused threshold + screen + decode: the threshold's and the screen's inputs
+// and optional outputs beside the decode arguments (split = blocks per chunk
+// <= kMaxFusedChunk, dense set so that the combine counts every chunk of a
+// stream).
 constexpr int kMaxFusedChunk = 32;
 struct ScreenDecodeArgs {
-  const float* tau_screen;  // [B*H]
+  const float* W;           // [H*D][H] predictor weights, or NULL (frozen constants)
+  const float* bias;        // [H]: bias (with W) or the frozen per-head constants
+  float a;                  // threshold adjustment: tau_screen = tau - a
   float z;
+  float* tau_gate;          // [B*H] written by each stream's first chunk, or NULL
+  float* tau_screen;        // [B*H] likewise, or NULL
   uint32_t* chunk_bits;     // [B*H][max_chunks] admission bits of each chunk, or NULL
   uint64_t* ctr;            // += admitted tokens, or NULL
 };

@@ -133,7 +133,7 @@ enum ChunkSrc { kChunkDense = 0, kChunkList = 1, kChunkStaged = 2 };
 // weighted V) into slot k of the stream.
 template <int D, int DT, int MODE, int SRC, int NBUF = 2>
 __device__ __forceinline__ void chunk_attend(const CacheView& c, const DecodeArgs& a, int u, int k,
-                                             int T, int first, int nblk, bool single,
+                                             int T, int first, int nblk, bool single, float tau,
                                              int* s_list, float (*s_acc)[D], float (*s_ml)[2]) {
   constexpr int EPL = Elt<DT>::kPer16B;
   constexpr int LPR = D / EPL;
@@ -154,7 +154,6 @@ __device__ __forceinline__ void chunk_attend(const CacheView& c, const DecodeArg
 #pragma unroll
     for (int e = 0; e < EPL; ++e) qs[e] = qu[e] * a.scale;
   }
-  const float tau = (MODE == ETA_LOGIT_GATED) ? a.tau[u] : 0.f;
   const float beta = a.beta;
   const char* kb = static_cast<const char*>(c.k) + (size_t)u * c.cap * RB + li * 16;
   const char* vb = static_cast<const char*>(c.v) + (size_t)u * c.cap * RB + li * 16;
@@ -254,14 +253,13 @@ __device__ __forceinline__ int stream_chunks(const CacheView& c, const DecodeArg
 }
 
 // Log-sum-exp merge of the nch partials in slots slot0 .. slot0 + nch - 1 into
-// out[u], by the
-// whole work-group of kCombWaves waves: wave w folds chunks w, w+kCombWaves,
+// out[u], by the whole work-group of NWV waves: wave w folds chunks w, w+NWV,
 // ... into a running (max, sum, weighted V) in one pass with kInflight chunks
 // loaded before any is used; lane i owns columns [i*CPL, i*CPL+CPL).  The wave
 // states are then merged in a fixed order (deterministic).
 constexpr int kInflight = 8;
 constexpr int kCombWaves = 16;
-template <int D>
+template <int D, int NWV = kCombWaves>
 __device__ void combine_slots(const DecodeArgs& a, int u, size_t slot0, int nch,
                               float (*s_acc)[D], float (*s_ml)[2]) {
   constexpr int CPL = D / kWave;
@@ -272,11 +270,11 @@ __device__ void combine_slots(const DecodeArgs& a, int u, size_t slot0, int nch,
   float m = -__builtin_inff(), l = 0.f, acc[CPL];
 #pragma unroll
   for (int e = 0; e < CPL; ++e) acc[e] = 0.f;
-  for (int base = wave; base < nch; base += kCombWaves * kInflight) {
+  for (int base = wave; base < nch; base += NWV * kInflight) {
     float mc[kInflight], lc[kInflight], ac[kInflight][CPL];
 #pragma unroll
     for (int i = 0; i < kInflight; ++i) {
-      const int ch = base + kCombWaves * i;
+      const int ch = base + NWV * i;
       const bool ok = ch < nch;
       mc[i] = ok ? pm[ch] : -__builtin_inff();
       lc[i] = ok ? pl[ch] : 0.f;
@@ -310,7 +308,7 @@ __device__ void combine_slots(const DecodeArgs& a, int u, size_t slot0, int nch,
   if (t < D) {
     float mm = s_ml[0][0], ll = s_ml[0][1], aa[1] = {s_acc[0][t]};
 #pragma unroll
-    for (int w = 1; w < kCombWaves; ++w) {
+    for (int w = 1; w < NWV; ++w) {
       const float a2[1] = {s_acc[w][t]};
       merge_state<1>(mm, ll, aa, s_ml[w][0], s_ml[w][1], a2);
     }
@@ -386,7 +384,8 @@ __global__ __launch_bounds__(256) void decode_queue_kernel(CacheView c, DecodeAr
     stream_chunks(c, a, u, &T, &cnt);
     const int first = k * a.split, nblk = min(a.split, cnt - first);
     chunk_attend<D, DT, MODE, DENSE ? kChunkDense : kChunkList>(
-        c, a, u, k, T, first, nblk, first == 0 && nblk == cnt, s_list, s_acc, s_ml);
+        c, a, u, k, T, first, nblk, first == 0 && nblk == cnt,
+        MODE == ETA_LOGIT_GATED ? a.tau[u] : 0.f, s_list, s_acc, s_ml);
     __syncthreads();  // LDS reuse; s_next is visible
     item = s_next;
   }
@@ -409,7 +408,8 @@ __global__ __launch_bounds__(256) void decode_grid_kernel(CacheView c, DecodeArg
   if (k >= nch) return;
   const int first = k * a.split, nblk = min(a.split, cnt - first);
   chunk_attend<D, DT, MODE, DENSE ? kChunkDense : kChunkList>(
-      c, a, u, k, T, first, nblk, first == 0 && nblk == cnt, s_list, s_acc, s_ml);
+      c, a, u, k, T, first, nblk, first == 0 && nblk == cnt,
+      MODE == ETA_LOGIT_GATED ? a.tau[u] : 0.f, s_list, s_acc, s_ml);
 }
 
 // Combine: one work-group per stream with two or more chunks.
@@ -429,15 +429,17 @@ __global__ __launch_bounds__(kCombWaves * kWave) void combine_kernel(CacheView c
 }
 
 // ---------------------------------------------------------------------------
-// Fused screen + decode, for steps too small to hide the separate screen,
-// compaction and decode launches.  One work-group per chunk of a.split <= 32
-// consecutive blocks, flattened as blockIdx.x = k * units + u (the first
-// chunks of every stream are dispatched first; chunks past a stream's end
-// exit).  Wave w scores blocks 8 w .. 8 w + 7 of the chunk with the screen's
-// Eq. 5 arithmetic (block_score, the same float32 operations in the same
-// order, so the admission bits equal eta_screen's for the same threshold),
-// the admitted indices go to LDS in ascending order, and the whole work-group
-// attends over them (chunk_attend).  Chunk k's partial lands in slot k of the
+// Fused threshold + screen + decode, for steps too small to hide the
+// separate threshold, screen, compaction and decode launches.  One
+// work-group per chunk of a.split <= 32 consecutive blocks, flattened as
+// blockIdx.x = k * units + u (the first chunks of every stream are dispatched
+// first; chunks past a stream's end exit).  The work-group computes its
+// stream's Eq. 1 threshold (tau_of_head: the threshold kernel's order, so the
+// same bits), then wave w scores blocks 8 w .. 8 w + 7 of the chunk with the
+// screen's Eq. 5 arithmetic (block_score, the same float32 operations in the
+// same order, so the admission bits equal eta_screen's), the admitted
+// indices go to LDS in ascending order, and the whole work-group attends over
+// them (chunk_attend).  Chunk k's partial lands in slot k of the
 // stream and the chunked combine merges a stream's ceil(nb / split) slots; a
 // chunk that admits nothing leaves the empty partial (max -inf, sum 0), and
 // the chunk holding the last block always admits it.
@@ -457,18 +459,29 @@ __global__ __launch_bounds__(256, 2) void screen_decode_kernel(CacheView c, Deco
   __shared__ float s_acc[4][D];
   __shared__ float s_ml[4][2];
   __shared__ uint32_t s_bits[4];
+  __shared__ float s_red[kTauThreads / kWave];
   static_assert(4 * kBlocksPerIter == kMaxFusedChunk, "four waves score a whole chunk");
+  static_assert(kTauThreads == 256, "the threshold takes the whole work-group");
   const int units = c.B * c.H;
   const int u = blockIdx.x % units, k = blockIdx.x / units;
   const int T = c.seq_len[u / c.H];
   const int nb = T > 0 ? (T + c.bs - 1) >> c.log2bs : 0;
   const int first = k * a.split;
-  if (first >= nb) return;  // uniform over the work-group
+  // Uniform over the work-group.  The first chunk of a stream always runs far
+  // enough to report the stream's thresholds, as the threshold kernel does.
+  if (first >= nb && k > 0) return;
+  const float tg = tau_of_head(a.q + (size_t)(u / c.H) * c.H * D, sa.W, sa.bias, c.H, c.H * D,
+                               u % c.H, s_red);
+  const float ts = tg - sa.a;
+  if (k == 0 && threadIdx.x == 0) {
+    if (sa.tau_gate) sa.tau_gate[u] = tg;
+    if (sa.tau_screen) sa.tau_screen[u] = ts;
+  }
+  if (first >= nb) return;  // an empty stream (T == 0): the combine writes zeros
   const int nbc = T >> c.log2bs;
   const int nblk = min(a.split, nb - first);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   if (kBlocksPerIter * wave < nblk) {  // wave-uniform
-    const float ts = sa.tau_screen[u];
     const int gi = lane / kLanesPerBlock, li = lane % kLanesPerBlock;
     QShare<D> qs;
     load_qshare<D>(a.q + (size_t)u * D, li, qs);
@@ -505,7 +518,7 @@ __global__ __launch_bounds__(256, 2) void screen_decode_kernel(CacheView c, Deco
   const int nch = (nb + a.split - 1) / a.split;
   // chunk_attend synchronises the work-group before reading s_list.
   chunk_attend<D, DT, MODE, kChunkStaged, fused_bufs<DT>()>(c, a, u, k, T, first, nadm,
-                                                            nch == 1, s_list, s_acc, s_ml);
+                                                            nch == 1, tg, s_list, s_acc, s_ml);
 }
 
 // ---------------------------------------------------------------------------
@@ -735,8 +748,12 @@ static hipError_t decode_dt(const CacheView& c, const DecodeArgs& a, hipStream_t
   return decode_t<D, DT, ETA_LOGIT_GATED, false>(c, a, s);
 }
 
-// Fused screen + decode, then the chunked combine (a.dense is set, so the
-// combine counts ceil(nb / split) chunks per stream).
+// Fused threshold + screen + decode, then the chunked combine (a.dense is
+// set, so the combine counts ceil(nb / split) chunks per stream).  Merging
+// inside the fused kernel (the last chunk of a stream to finish merging the
+// others' partials) needs device-scope release and acquire fences around
+// every partial, which cost more here than the combine's launch: 0.072 vs
+// 0.038 ms per step at 32K x 16 heads, 38%, on MI355X.
 template <int D, int DT, int MODE>
 static hipError_t screen_decode_t(const CacheView& c, const DecodeArgs& a,
                                   const ScreenDecodeArgs& sa, hipStream_t s) {

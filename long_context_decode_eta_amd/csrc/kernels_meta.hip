@@ -180,105 +180,19 @@ __global__ __launch_bounds__(256) void block_meta_kernel(CacheView c, int first,
 }
 
 // ---------------------------------------------------------------------------
-// Threshold (Eq. 1).  Grid (B, ceil(H / 16)), 1024 threads: work-group (b, y)
-// computes heads h0 .. h0+15 (h0 = 16 y) of sequence b.  Thread t owns rows
-// j = t, t+1024, ... of the H*D-long sum and keeps 16 partial sums, one per
-// head; a row's 16 weights are one 64-byte run of W (four 128-bit loads when
-// H is a multiple of 16), and a thread's loads of a round are issued before
-// its arithmetic.  The partials are then added in a fixed order
-// (deterministic): within each wave by an exchange butterfly over lane bits
-// 5..2 (at each step a lane keeps half of its heads and adds its partner's
-// copy of them, so 15 shuffles leave lane l with one head's sum over 16
-// lanes), then over lane bits 1..0, then across the 16 waves by a 4-level
-// tree in LDS.
-constexpr int kPredHeads = 16;
-constexpr int kPredThreads = 1024;
-constexpr int kPredRows = 4;  // rows per thread per round (loads in flight)
-
-// Keep half of the N values of x (the upper half when `upper`), adding the
-// partner lane's (lane ^ M) copy of the kept half.
-template <int N, int M>
-__device__ __forceinline__ void fold_half(float* x, bool upper) {
-#pragma unroll
-  for (int i = 0; i < N / 2; ++i) {
-    const float send = upper ? x[i] : x[N / 2 + i];
-    const float keep = upper ? x[N / 2 + i] : x[i];
-    x[i] = keep + __shfl_xor(send, M, kWave);
-  }
-}
-
-template <bool VEC>
-__global__ __launch_bounds__(kPredThreads) void predict_kernel(int H, int D, const float* q,
-                                                               const float* W, const float* bias,
-                                                               float a, float* tau,
-                                                               float* tau_screen) {
-  constexpr int NW = kPredThreads / kWave;
-  __shared__ float red[NW][kPredHeads];
-  const int b = blockIdx.x, h0 = blockIdx.y * kPredHeads, t = threadIdx.x;
-  const int lane = t & 63, wave = t >> 6;
-  const int hw = min(kPredHeads, H - h0);
-  const int n = H * D;
-  if (W) {
-    float acc[kPredHeads];
-#pragma unroll
-    for (int e = 0; e < kPredHeads; ++e) acc[e] = 0.f;
-    const float* qb = q + (size_t)b * n;
-    for (int j0 = t; j0 < n; j0 += kPredThreads * kPredRows) {
-      float qj[kPredRows], wv[kPredRows][kPredHeads];
-#pragma unroll
-      for (int r = 0; r < kPredRows; ++r) {
-        const int j = j0 + kPredThreads * r;
-        const bool ok = j < n;
-        qj[r] = ok ? qb[j] : 0.f;
-        const float* wr = W + (size_t)(ok ? j : 0) * H + h0;
-        if constexpr (VEC) {
-#pragma unroll
-          for (int v = 0; v < kPredHeads / 4; ++v) {
-            const float4 x = ok ? *reinterpret_cast<const float4*>(wr + 4 * v)
-                                : make_float4(0.f, 0.f, 0.f, 0.f);
-            wv[r][4 * v] = x.x; wv[r][4 * v + 1] = x.y;
-            wv[r][4 * v + 2] = x.z; wv[r][4 * v + 3] = x.w;
-          }
-        } else {
-#pragma unroll
-          for (int e = 0; e < kPredHeads; ++e) wv[r][e] = (ok && e < hw) ? wr[e] : 0.f;
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < kPredRows; ++r)
-#pragma unroll
-        for (int e = 0; e < kPredHeads; ++e) acc[e] = fmaf(qj[r], wv[r][e], acc[e]);
-    }
-    // Lane l ends with head 8 b5 + 4 b4 + 2 b3 + b2 (b_i: bit i of l).
-    fold_half<16, 32>(acc, lane & 32);
-    fold_half<8, 16>(acc, lane & 16);
-    fold_half<4, 8>(acc, lane & 8);
-    fold_half<2, 4>(acc, lane & 4);
-    float x = acc[0];
-    x += __shfl_xor(x, 2, kWave);
-    x += __shfl_xor(x, 1, kWave);
-    if ((lane & 3) == 0) {
-      const int e = ((lane >> 5) & 1) * 8 + ((lane >> 4) & 1) * 4 + ((lane >> 3) & 1) * 2 +
-                    ((lane >> 2) & 1);
-      red[wave][e] = x;
-    }
-    __syncthreads();
-  }
-  if (t < hw) {
-    const int h = h0 + t;
-    float v = bias[h];
-    if (W) {
-      float w8[NW / 2];
-#pragma unroll
-      for (int i = 0; i < NW / 2; ++i) w8[i] = red[2 * i][t] + red[2 * i + 1][t];
-#pragma unroll
-      for (int i = 0; i < NW / 4; ++i) w8[i] = w8[2 * i] + w8[2 * i + 1];
-#pragma unroll
-      for (int i = 0; i < NW / 8; ++i) w8[i] = w8[2 * i] + w8[2 * i + 1];
-      v = (w8[0] + w8[1]) + v;
-    }
-    tau[(size_t)b * H + h] = v;
-    tau_screen[(size_t)b * H + h] = v - a;
+// Threshold (Eq. 1): one work-group of 256 threads per (sequence, head), in
+// the fixed order of tau_of_head (the fused screen + decode computes the
+// same bits).
+__global__ __launch_bounds__(kTauThreads) void predict_kernel(int H, int D, const float* q,
+                                                              const float* W, const float* bias,
+                                                              float a, float* tau,
+                                                              float* tau_screen) {
+  __shared__ float s_red[kTauThreads / kWave];
+  const int u = blockIdx.x, b = u / H, h = u % H;
+  const float v = tau_of_head(q + (size_t)b * H * D, W, bias, H, H * D, h, s_red);
+  if (threadIdx.x == 0) {
+    tau[u] = v;
+    tau_screen[u] = v - a;
   }
 }
 
@@ -315,13 +229,8 @@ hipError_t launch_block_meta(const CacheView& c, int first, int n, hipStream_t s
 
 hipError_t launch_predict(int B, int H, int D, const float* q, const float* W, const float* bias,
                           float a, float* tau, float* tau_screen, hipStream_t s) {
-  const dim3 grid(B, ceil_div(H, kPredHeads));
-  if (H % kPredHeads == 0)
-    hipLaunchKernelGGL(predict_kernel<true>, grid, dim3(kPredThreads), 0, s, H, D, q, W, bias, a,
-                       tau, tau_screen);
-  else
-    hipLaunchKernelGGL(predict_kernel<false>, grid, dim3(kPredThreads), 0, s, H, D, q, W, bias, a,
-                       tau, tau_screen);
+  hipLaunchKernelGGL(predict_kernel, dim3(B * H), dim3(kTauThreads), 0, s, H, D, q, W, bias, a,
+                     tau, tau_screen);
   return hipGetLastError();
 }
 

@@ -110,7 +110,7 @@ def chunk_mask(bits: np.ndarray, chunk: int, seq_len: np.ndarray, b: int,
 
 def run_gpu_fused(cache: eb.KVCache, q, *, W=None, bias_or_c=None, z, scale, mode=eb.GATED,
                   beta=5.0, a=0.0, chunk=None, build_meta=True) -> GpuResult:
-    """predict_tau -> the fused screen + decode (eta_screen_decode)."""
+    """The fused step (eta_fused_step): thresholds, screen and decode."""
     if build_meta:
         eb.build_block_meta(cache)
     dec = eb.Decoder(cache, z=z, scale=scale, beta=beta, a=a, logit_mode=mode,

@@ -142,31 +142,33 @@ def test_decode_noalloc_validation(lib):
     assert "scratch" in err(L)
 
 
-def test_screen_decode_validation(lib):
+def test_fused_step_validation(lib):
     L = lib
-    ws = L.eta_screen_decode_workspace_bytes(2, 4, 128, 32, 8)
+    ws = L.eta_fused_step_workspace_bytes(2, 4, 128, 32, 8)
     # the size covers one partial (max, sum, 128 floats) per possible chunk
     assert ws >= 2 * 4 * 4 * (128 + 2) * 4
 
     def call(**o):
-        return L.eta_screen_decode(o.get("c", cache()), FAKE, o.get("tg", FAKE),
-                                   o.get("ts", FAKE), o.get("z", 1.0), o.get("mode", 0),
-                                   o.get("beta", 5.0), o.get("scale", 0.088), o.get("cb", 8),
-                                   None, None, o.get("ws", FAKE), o.get("wsb", ws),
-                                   o.get("out", FAKE), None)
+        return L.eta_fused_step(o.get("c", cache()), o.get("q", FAKE), o.get("W", FAKE),
+                                o.get("bias", FAKE), o.get("a", 0.0), o.get("z", 1.0),
+                                o.get("mode", 0), o.get("beta", 5.0), o.get("scale", 0.088),
+                                o.get("cb", 8), None, None, None, None, o.get("ws", FAKE),
+                                o.get("wsb", ws), o.get("out", FAKE), None)
 
     assert call(cb=0) == eb.ETA_ERR_BAD_ARG
     assert call(cb=33) == eb.ETA_ERR_BAD_ARG
     assert call(z=-1.0) == eb.ETA_ERR_BAD_ARG
     assert call(z=float("nan")) == eb.ETA_ERR_BAD_ARG
+    assert call(a=float("nan")) == eb.ETA_ERR_BAD_ARG
     assert call(beta=0.0) == eb.ETA_ERR_BAD_ARG
     assert call(scale=float("inf")) == eb.ETA_ERR_BAD_ARG
     assert call(mode=7) == eb.ETA_ERR_BAD_ARG
-    assert call(ts=None) == eb.ETA_ERR_NULL_PTR
+    assert call(q=None) == eb.ETA_ERR_NULL_PTR
+    assert call(bias=None) == eb.ETA_ERR_NULL_PTR
     assert call(out=None) == eb.ETA_ERR_NULL_PTR
-    assert call(tg=None) == eb.ETA_ERR_NULL_PTR          # GATED needs tau_gate
     assert call(wsb=ws - 1) == eb.ETA_ERR_WORKSPACE
     assert call(ws=None) == eb.ETA_ERR_WORKSPACE
+    assert call(c=cache(heads=300)) == eb.ETA_ERR_BAD_SHAPE
     assert call(c=cache(batch=0, k=None, v=None, mu=None, var=None, maxnorm=None,
                         seq_len=None)) == eb.ETA_OK
 

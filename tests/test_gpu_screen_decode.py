@@ -1,14 +1,16 @@
-"""GPU parity of the fused screen + decode (eta_screen_decode) against the fp64
-oracle, and against the separate screen -> decode path on the same inputs.
+"""GPU parity of the fused step (eta_fused_step: thresholds, screen and decode
+in two launches) against the fp64 oracle, and against the separate
+predict_tau -> screen -> decode path on the same inputs.
 
-The fused path scores blocks with the screen's own float32 arithmetic, so for
-the same thresholds its admission mask must equal eta_screen's bit for bit;
+The fused step computes its thresholds in the threshold kernel's order and
+scores blocks with the screen's own float32 arithmetic, so its thresholds and
+admission mask must equal the separate path's bit for bit;
 its output is held to the same bars as the separate decode (near-tie flips
 against the oracle only, outputs within the cache dtype's bar and the 1e-5
 internal bar).  Cases: the hand example, the tiny fp32 workload, ragged
 lengths around block and chunk boundaries with an empty stream and NaN-filled
 unused slots, every chunk size shape (1, 3, 8, 32 blocks), both logit modes,
-threshold extremes, determinism, and the single 32K sequence at its full size
+threshold extremes and offsets, 40 heads, determinism, and the single 32K sequence at its full size
 (all 16 heads against the oracle) at 10%, 38% and 70% density.
 """
 import math
@@ -32,8 +34,10 @@ def _name(request):
 
 
 def _same_as_separate(g_fused, g_sep):
-    """Same thresholds, same admission bits and token count as eta_screen."""
+    """Same thresholds, admission bits and token count as predict_tau and
+    eta_screen."""
     np.testing.assert_array_equal(g_fused.tau_gate, g_sep.tau_gate)
+    np.testing.assert_array_equal(g_fused.tau_screen, g_sep.tau_screen)
     np.testing.assert_array_equal(g_fused.mask, g_sep.mask)
     assert g_fused.density == g_sep.density
 
@@ -96,6 +100,25 @@ def test_ragged_edges(kv, D, block):
     note(f"  density {st['density']:.3f} out_rel {st['out_rel']:.2e}")
 
 
+@pytest.mark.parametrize("a", [-0.5, 0.7])
+def test_threshold_offset_and_many_heads(a):
+    # tau_screen = tau_gate - a, and a dynamic predictor over 40 heads
+    # (H*D = 2560 terms per threshold, not a multiple of the 1024-term rounds).
+    w = to_gpu(synth.make("tiny", seed=21, T=[300, 1000], B=2, H=40, cap=1024, block=16))
+    cache = make_cache(w)
+    rng = np.random.default_rng(3)
+    W = torch.from_numpy((rng.standard_normal((40 * 64, 40)) / 8.0).astype(np.float32)).cuda()
+    c = torch.from_numpy(rng.uniform(0.3, 1.2, 40).astype(np.float32)).cuda()
+    s = run_gpu(cache, w.q, W=W, bias_or_c=c, z=1.5, scale=w.scale, a=a)
+    g = run_gpu_fused(cache, w.q, W=W, bias_or_c=c, z=1.5, scale=w.scale, a=a, chunk=8,
+                      build_meta=False)
+    _same_as_separate(g, s)
+    np.testing.assert_array_equal(g.tau_screen, g.tau_gate - np.float32(a))
+    st = check_against_oracle(w, g, cache, W=W, bias_or_c=c, z=1.5, scale=w.scale, a=a,
+                              mode=eb.GATED, check_meta=False)
+    note(f"  a {a}: density {st['density']:.3f} out_rel {st['out_rel']:.2e}")
+
+
 @pytest.mark.parametrize("tau", [math.inf, -math.inf])
 def test_threshold_extremes(tau):
     w = to_gpu(synth.make("ctx128k", seed=3, T=(100, 3000), B=4, H=2, cap=3000, block=32))
@@ -123,6 +146,29 @@ def test_chunk_invariance_and_determinism():
             first = g.out
         np.testing.assert_array_equal(g.mask, ref.mask)
         np.testing.assert_allclose(g.out, ref.out, rtol=2e-6, atol=2e-6)
+
+
+def test_reused_workspace_and_changing_lengths():
+    # One Decoder (one workspace) over many calls: repeated calls agree bit
+    # for bit, and shorter and longer sequences on the same workspace match a
+    # fresh one (no state carries over between calls).
+    w = to_gpu(synth.make("ctx128k", seed=12, T=(3000, 9000), B=3, H=4, cap=9000, block=32))
+    cache = make_cache(w)
+    eb.build_block_meta(cache)
+    c = torch.full((4,), 1.0, dtype=torch.float32, device="cuda")
+    dec = eb.Decoder(cache, z=1.0, scale=w.scale, fused_blocks_per_chunk=8)
+    first = dec.step_fused(w.q, None, c).clone()
+    for _ in range(30):
+        assert torch.equal(dec.step_fused(w.q, None, c), first)
+    full = cache.seq_len.clone()
+    for lens in ([1000, 9000, 4097], [0, 33, 8999], full.tolist()):
+        cache.seq_len.copy_(torch.tensor(lens, dtype=torch.int32))
+        got = dec.step_fused(w.q, None, c).clone()
+        fresh = eb.Decoder(cache, z=1.0, scale=w.scale, fused_blocks_per_chunk=8)
+        assert torch.equal(got, fresh.step_fused(w.q, None, c))
+        if lens[0] == 0:
+            assert torch.count_nonzero(got[0]).item() == 0  # the empty stream
+    assert torch.equal(got, first)
 
 
 _held = {}

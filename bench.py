@@ -645,9 +645,12 @@ def main():
         for name in [x for x in args.configs.split(",") if x and x != args.workload]:
             configs[name] = config_bench(torch, np, eb, synth, name, args.steps, args.warmup,
                                          args.seed)
-    gqa = None
+    gqa = gqa_d128 = None
     if not args.no_gqa:
         gqa = gqa_bench(torch, np, eb, synth, args.steps, args.warmup, args.seed, gqa_rhos)
+        # the same grouped batch at head dim 128, at the 38% head density
+        gqa_d128 = gqa_bench(torch, np, eb, synth, args.steps, args.warmup, args.seed, (0.38,),
+                             D=128)
     prefill = None
     if not args.no_prefill:
         prefill = prefill_bench(torch, eb, synth, args.steps, args.warmup, args.seed)
@@ -688,6 +691,7 @@ def main():
         "upkeep": upkeep,
         "cpu_baseline": cpu,
         "gqa": gqa,
+        "gqa_d128": gqa_d128,
         "prefill": prefill,
     }
     print(json.dumps(out), flush=True)
@@ -811,17 +815,17 @@ def measure_upkeep(torch, eb, w, cache, dec, c, frozen, sumT):
             "tokens_timed": n}
 
 
-def gqa_bench(torch, np, eb, synth, steps, warmup, seed, rhos=(0.38, 0.25, 0.10)):
+def gqa_bench(torch, np, eb, synth, steps, warmup, seed, rhos=(0.38, 0.25, 0.10), D=None):
     """Grouped-query decode at the pages' benchmark shape (32 sequences x
-    128K, 32 query heads on 4 KV heads, d 64, b 64, bf16): dynamic Eq. 1
-    thresholds over the query heads with constants calibrated per query head
-    (the library's calibration, one call per head position in the group) to
-    38%, 25% and 10% head density; step = predict + screen_gqa + decode_gqa,
-    graph-captured; the grouped dense decode at the same shape alongside.
-    Decode bytes: union K+V rows, q, head masks and union lists, chunk
-    partials, outputs."""
+    128K, 32 query heads on 4 KV heads, d 64, b 64, bf16; D overrides the
+    head dim): dynamic Eq. 1 thresholds over the query heads with constants
+    calibrated per query head (the library's calibration, one call per head
+    position in the group) to 38%, 25% and 10% head density; step = predict +
+    screen_gqa + decode_gqa, graph-captured; the grouped dense decode at the
+    same shape alongside.  Decode bytes: union K+V rows, q, head masks and
+    union lists, chunk partials, outputs."""
     dev = "cuda"
-    w = synth.make("gqa128k", seed=seed, device=dev)
+    w = synth.make("gqa128k", seed=seed, device=dev, D=D)
     B, Hkv, G, D, bs = w.B, w.H, w.G, w.D, w.block
     Hq = Hkv * G
     cache = eb.KVCache(B, Hkv, D, bs, w.cap, w.kv_dtype, device=dev, k=w.k, v=w.v)
@@ -921,12 +925,14 @@ def gqa_bench(torch, np, eb, synth, steps, warmup, seed, rhos=(0.38, 0.25, 0.10)
         roofline = {"bound": "hbm", "kernel": "eta_decode_gqa (balanced decode + combine kernels), 38% head",
                     "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(ach / HBM_PEAK_GBS, 4),
-                    "traffic": counters_traffic(GQA_COUNTERS, GQA_SRC, "gqa128k"),
+                    "traffic": counters_traffic(GQA_COUNTERS, GQA_SRC,
+                                                "gqa128k" if D in (None, 64) else f"gqa128k_d{D}"),
                     "algorithmic_bytes_per_launch": r["decode_bytes"],
                     "avg_launch_ms": r["decode_ms"],
                     "measured_stream_gbs": round(dense_bytes / dense_ms / 1e6, 1),
                     "frac_of_measured_stream": round(ach / (dense_bytes / dense_ms / 1e6), 4)}
-    out = {"workload": f"gqa128k: batch {B}, {Hq} query heads on {Hkv} KV heads, head dim {D}, "
+    name = "gqa128k" if D == 64 else f"gqa128k_d{D}"
+    out = {"workload": f"{name}: batch {B}, {Hq} query heads on {Hkv} KV heads, head dim {D}, "
                        f"context {int(w.seq_len.max())}, block {bs}, z {w.z}, bf16 KV, "
                        "dynamic linear tau",
            "roofline": roofline,

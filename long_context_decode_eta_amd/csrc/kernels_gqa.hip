@@ -690,6 +690,11 @@ __global__ __launch_bounds__(1024) void combine_gqa_kernel(CacheView c, GqaArgs 
 // all G heads run on the matrix cores as in the chunked kernel; the partial
 // of (stream segment, head g) goes to slot (w + u) * G + g.  Measured on
 // 32 x 128K, 38% head density: about 6% faster than the chunked kernel.
+// Two waves per SIMD at either head dim: d = 64 needs about 175 registers; at
+// d = 128 (about 300 registers unconstrained, one wave per SIMD) the bound
+// costs a few spilled registers and gains 12% (32 x 128K, 38% head density:
+// 0.80 ms against 0.91 ms at one wave per SIMD and 0.86 ms for the chunked
+// kernel).
 template <int D>
 struct GqaFlowShape {
   static constexpr int NK = D / 32;             // 32-dim slabs (score product)
@@ -703,7 +708,7 @@ struct GqaFlowShape {
 };
 
 template <int D, int MODE>
-__global__ __launch_bounds__(64) void decode_gqa_flow_kernel(CacheView c, GqaArgs a) {
+__global__ __launch_bounds__(64, 2) void decode_gqa_flow_kernel(CacheView c, GqaArgs a) {
   using Sh = GqaFlowShape<D>;
   constexpr int NK = Sh::NK, NV = Sh::NV, RB = Sh::RB, LPR = Sh::LPR, RPI = Sh::RPI;
   constexpr int NI = Sh::NI, TB = Sh::TB;
@@ -1118,7 +1123,7 @@ template <int D, int MODE, bool DENSE>
 static hipError_t decode_gqa_t(const CacheView& c, const GqaDecode& g, hipStream_t s) {
   const GqaArgs& a = g;
   const int units = c.B * c.H;
-  if constexpr (!DENSE && D == 64) {
+  if constexpr (!DENSE) {
     if (g.use_flow) {
       GqaArgs f = g;
       f.flow_grid = gqa_flow_grid<D, MODE>(units);

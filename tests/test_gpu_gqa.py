@@ -223,31 +223,34 @@ def oracle_gqa_constants(w: synth.Workload, rho, seqs=None):
     return res if isinstance(rho, (list, tuple)) else res[0]
 
 
-# The head densities the benchmark reports at the full grouped shape.
-FULL_RHOS = [0.38, 0.25, 0.10]
+# The head densities the benchmark reports at the full grouped shape, per
+# head dim (d 64: the pages' shape; d 128: the same batch at the wider head).
+FULL_RHOS = {64: [0.38, 0.25, 0.10], 128: [0.38]}
 _full = {}
 
 
-def _full_workload():
-    if not _full:
+def _full_workload(D):
+    if _full.get("D") != D:
+        _full.clear()
         torch.cuda.empty_cache()
-        w = synth.make("gqa128k", seed=1234, device="cuda")
+        w = synth.make("gqa128k", seed=1234, device="cuda", D=D)
         cache = make_cache(w)
         eb.build_block_meta(cache)
         torch.cuda.synchronize()
-        _full["w"], _full["cache"] = w, cache
-        _full["c"] = dict(zip(FULL_RHOS, oracle_gqa_constants(w, FULL_RHOS)))
+        _full.update(D=D, w=w, cache=cache)
+        _full["c"] = dict(zip(FULL_RHOS[D], oracle_gqa_constants(w, FULL_RHOS[D])))
     return _full["w"], _full["cache"], _full["c"]
 
 
-@pytest.mark.parametrize("rho", FULL_RHOS)
-def test_gqa_full_size_sampled_streams(rho):
-    # 32 sequences x 128K, 4 KV heads, 8 query heads each, d 64, b 64, in the
-    # launch configuration of the benchmark (automatic blocks_per_split), at
-    # each head density the benchmark reports.  Constants are calibrated by
-    # the oracle over the whole batch (as the benchmark's are); the oracle
-    # then recomputes whole KV groups (all 8 heads) of sampled streams.
-    w, cache, consts = _full_workload()
+@pytest.mark.parametrize("D,rho", [(d, r) for d, rs in FULL_RHOS.items() for r in rs])
+def test_gqa_full_size_sampled_streams(D, rho):
+    # 32 sequences x 128K, 4 KV heads, 8 query heads each, b 64, d 64 (and
+    # 128), in the launch configuration of the benchmark (automatic
+    # blocks_per_split), at each head density the benchmark reports.
+    # Constants are calibrated by the oracle over the whole batch (as the
+    # benchmark's are); the oracle then recomputes whole KV groups (all 8
+    # heads) of sampled streams.
+    w, cache, consts = _full_workload(D)
     c = consts[rho]
     g = run_gpu_gqa(cache, w.G, w.q, W=w.W, bias_or_c=c.cuda(), z=w.z, scale=w.scale,
                     build_meta=False)

@@ -318,7 +318,8 @@ class DecodeBench:
         self.flush = (torch.empty((512 << 20) // 4, dtype=torch.float32, device=dev)
                       if kv_bytes < (2 << 30) else None)
         nbc = self.sl // bs
-        self.meta_bytes = int(H * (nbc * (2 * D + 1) * 4).sum())
+        # block index bytes the screen reads: mu, var (bf16) and maxnorm (fp32)
+        self.meta_bytes = int(H * (nbc * (2 * D * 2 + 4)).sum())
         self.dense_bytes = self.sumT * H * D * 2 * self.elt
         print(f"[bench] workload {name}: B={B} H={H} D={D} b={bs} sumT={self.sumT} "
               f"path={self.dec.path} split={self.split} chunk={self.dec.fused_chunk} "
@@ -771,7 +772,7 @@ def measure_upkeep(torch, eb, w, cache, dec, c, frozen, sumT):
     torch.cuda.synchronize()
     meta_ms = s0.elapsed_time(e0) / 3
     elt = cache.k.element_size()
-    meta_bytes = sumT * H * D * elt + (sumT // bs) * H * (2 * D + 1) * 4
+    meta_bytes = sumT * H * D * elt + (sumT // bs) * H * (2 * D * 2 + 4)
 
     g = torch.Generator(device="cuda").manual_seed(99)
     kn = torch.randn((B, H, D), generator=g, device="cuda").to(cache.kv_dtype)
@@ -1049,7 +1050,7 @@ def cpu_baseline(w, c_gpu, rho):
     V = synth.kv_numpy(w.v[b0:b0 + 1])
     q = w.q[b0:b0 + 1].cpu().numpy()
     sl = w.seq_len[b0:b0 + 1].cpu().numpy().astype(np.int32)
-    meta = oracle.meta_batch(K, sl, w.block)
+    meta = oracle.index_batch(K, sl, w.block)
     H = w.H
     if w.W is not None:
         Wn = w.W.cpu().numpy()

@@ -35,9 +35,11 @@
  *     stream).  Every call only enqueues kernels on that stream; results are
  *     ready when the stream reaches them.  Two calls that write the same
  *     buffers must not run concurrently on different streams.
- *   - Types: q, tau, statistics and outputs are float32.  The K/V cache is
+ *   - Types: q, tau, maxnorm and outputs are float32; the block statistics
+ *     mu and var are stored as bfloat16 (see eta_cache).  The K/V cache is
  *     float32 (ETA_DT_F32) or bfloat16 (ETA_DT_BF16); bf16 is widened exactly
- *     to float32 and every accumulation is float32.
+ *     to float32 and every accumulation is float32 (float64 for mu and var
+ *     before their rounding).
  *   - Supported shapes: head_dim in {64, 128}; block in {4, 8, 16, 32, 64,
  *     128}.  Smaller head dimensions run zero-padded to 64 with `scale` given
  *     explicitly (zero coordinates change no dot product, norm or variance).
@@ -53,7 +55,7 @@
 extern "C" {
 #endif
 
-#define ETA_ABI_VERSION 3
+#define ETA_ABI_VERSION 4
 
 typedef int32_t eta_status;
 enum {
@@ -75,7 +77,10 @@ enum { ETA_LOGIT_GATED = 0, ETA_LOGIT_RAW = 1 };
  * mu, per-coordinate population variance var and largest key norm maxnorm).
  *
  *   k, v      device, [batch][heads][cap_tokens][head_dim], kv_dtype elements
- *   mu, var   device, [batch][heads][cap_blocks][head_dim] float32
+ *   mu, var   device, [batch][heads][cap_blocks][head_dim] bfloat16 (bit
+ *             patterns): the block mean and population variance, computed in
+ *             float64 and rounded to the nearest bfloat16 (ties to even), so
+ *             the screen reads 4 bytes per coordinate instead of 8
  *   maxnorm   device, [batch][heads][cap_blocks] float32
  *   seq_len   device, [batch] int32: current length T_b of sequence b
  *             (ragged batches allowed, 0 <= T_b <= cap_tokens)
@@ -89,8 +94,8 @@ typedef struct eta_cache {
   int32_t batch, heads, head_dim, block, cap_tokens, kv_dtype;
   void* k;
   void* v;
-  float* mu;
-  float* var;
+  uint16_t* mu;
+  uint16_t* var;
   float* maxnorm;
   int32_t* seq_len;
 } eta_cache;

@@ -137,7 +137,8 @@ class KVCache:
         self.v = v if v is not None else torch.zeros(shape, dtype=kv_dtype, device=device)
         assert tuple(self.k.shape) == shape and tuple(self.v.shape) == shape
         assert self.k.dtype == kv_dtype and self.v.dtype == kv_dtype
-        self.mu = torch.zeros((batch, heads, self.cap_blocks, head_dim), dtype=torch.float32,
+        # block statistics: mu and var as bfloat16, maxnorm as float32
+        self.mu = torch.zeros((batch, heads, self.cap_blocks, head_dim), dtype=torch.bfloat16,
                               device=device)
         self.var = torch.zeros_like(self.mu)
         self.maxnorm = torch.zeros((batch, heads, self.cap_blocks), dtype=torch.float32,
@@ -151,7 +152,7 @@ class KVCache:
         return EtaCacheStruct(
             self.batch, self.heads, self.head_dim, self.block, self.cap_tokens, dt,
             _dev(self.k, self.kv_dtype, "k"), _dev(self.v, self.kv_dtype, "v"),
-            _dev(self.mu, torch.float32, "mu"), _dev(self.var, torch.float32, "var"),
+            _dev(self.mu, torch.bfloat16, "mu"), _dev(self.var, torch.bfloat16, "var"),
             _dev(self.maxnorm, torch.float32, "maxnorm"),
             _dev(self.seq_len, torch.int32, "seq_len"))
 

@@ -253,8 +253,8 @@ struct CacheView {
   int B, H, D, bs, log2bs, cap, cap_blocks, dtype;
   const void* k;
   const void* v;
-  float* mu;
-  float* var;
+  uint16_t* mu;   // bfloat16 bits
+  uint16_t* var;  // bfloat16 bits
   float* maxnorm;
   const int32_t* seq_len;
 };
@@ -283,14 +283,17 @@ struct FlowPlan {
 constexpr int kLanesPerBlock = 8;  // lanes that read one block's statistics
 constexpr int kBlocksPerIter = kWave / kLanesPerBlock;  // 8 blocks per wave step
 
-// Per-lane share of the query: with 8 lanes per block, load t (t < D/32) of
-// lane li reads floats [32 t + 4 li, 32 t + 4 li + 4) of a statistics row, so
-// each load instruction covers one full 128-byte line of each of 8 blocks.
+// The block statistics mu and var are stored as bfloat16 (8 per 128-bit
+// load).  Per-lane share of the query: with 8 lanes per block, load t
+// (t < D/64) of lane li reads elements [64 t + 8 li, 64 t + 8 li + 8) of a
+// statistics row, so each load instruction covers one full 128-byte line of
+// each of 8 blocks; the lane keeps the matching query elements.
 template <int D>
 struct QShare {
-  static constexpr int kLoads = D / 32;
-  float q[4 * kLoads];
-  float q2[4 * kLoads];
+  static constexpr int kLoads = D / 64;
+  static constexpr int kElems = 8 * kLoads;
+  float q[kElems];
+  float q2[kElems];
   float qn;  // ||q||_2
 };
 
@@ -299,16 +302,34 @@ __device__ __forceinline__ void load_qshare(const float* qu, int li, QShare<D>& 
   float qq = 0.f;
 #pragma unroll
   for (int t = 0; t < QShare<D>::kLoads; ++t) {
-    const float4 v = *reinterpret_cast<const float4*>(qu + 32 * t + 4 * li);
-    const float x[4] = {v.x, v.y, v.z, v.w};
+    const float4 v0 = *reinterpret_cast<const float4*>(qu + 64 * t + 8 * li);
+    const float4 v1 = *reinterpret_cast<const float4*>(qu + 64 * t + 8 * li + 4);
+    const float x[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      s.q[4 * t + e] = x[e];
-      s.q2[4 * t + e] = x[e] * x[e];
+    for (int e = 0; e < 8; ++e) {
+      s.q[8 * t + e] = x[e];
+      s.q2[8 * t + e] = x[e] * x[e];
       qq = fmaf(x[e], x[e], qq);
     }
   }
   s.qn = sqrtf(group_sum<kLanesPerBlock>(qq));
+}
+
+// This lane's partial sums q . mu and (q * q) . var over its elements of one
+// block (raw bf16 statistics loads m[t], v[t]), in element order.
+template <int D>
+__device__ __forceinline__ void score_partials(const QShare<D>& s, const uint4* m,
+                                               const uint4* v, float& dot, float& mom) {
+#pragma unroll
+  for (int t = 0; t < QShare<D>::kLoads; ++t) {
+    float mf[8], vf[8];
+    widen<ETA_DT_BF16>(m[t], mf);
+    widen<ETA_DT_BF16>(v[t], vf);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dot = fmaf(s.q[8 * t + e], mf[e], dot);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) mom = fmaf(s.q2[8 * t + e], vf[e], mom);
+  }
 }
 
 // Eq. 5 score of block j of stream u.  All 8 lanes of the block's group must
@@ -321,21 +342,13 @@ __device__ __forceinline__ float block_score(const CacheView& c, int u, int j, b
   float dot = 0.f, mom = 0.f, M = 0.f;
   if (valid) {
     const size_t row = ((size_t)u * c.cap_blocks + j) * D;
-    const float* mu = c.mu + row;
-    const float* var = c.var + row;
+    uint4 m[QShare<D>::kLoads], v[QShare<D>::kLoads];
 #pragma unroll
     for (int t = 0; t < QShare<D>::kLoads; ++t) {
-      const float4 m = ld16f_nt(mu + 32 * t + 4 * li);
-      const float4 v = ld16f_nt(var + 32 * t + 4 * li);
-      dot = fmaf(s.q[4 * t + 0], m.x, dot);
-      dot = fmaf(s.q[4 * t + 1], m.y, dot);
-      dot = fmaf(s.q[4 * t + 2], m.z, dot);
-      dot = fmaf(s.q[4 * t + 3], m.w, dot);
-      mom = fmaf(s.q2[4 * t + 0], v.x, mom);
-      mom = fmaf(s.q2[4 * t + 1], v.y, mom);
-      mom = fmaf(s.q2[4 * t + 2], v.z, mom);
-      mom = fmaf(s.q2[4 * t + 3], v.w, mom);
+      m[t] = ld16_nt(c.mu + row + 64 * t + 8 * li);
+      v[t] = ld16_nt(c.var + row + 64 * t + 8 * li);
     }
+    score_partials<D>(s, m, v, dot, mom);
     M = c.maxnorm[(size_t)u * c.cap_blocks + j];
   }
   dot = group_sum<kLanesPerBlock>(dot);

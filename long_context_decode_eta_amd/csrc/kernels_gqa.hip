@@ -68,7 +68,7 @@ __global__ __launch_bounds__(256) void screen_gqa_kernel(CacheView c, int G, con
                                                          uint64_t* words, uint32_t* word_tokens,
                                                          int words_per_unit) {
   constexpr int LPB = 8;            // lanes per block
-  constexpr int NL = D / 32;        // float4 loads per lane per statistics row
+  constexpr int NL = D / 64;        // 128-bit loads (8 bf16) per lane per statistics row
   constexpr int PER = NH / 8;       // heads per lane after the butterfly
   __shared__ __align__(16) float s_q[NH][D];
   __shared__ __align__(16) float s_q2[NH][D];
@@ -86,8 +86,9 @@ __global__ __launch_bounds__(256) void screen_gqa_kernel(CacheView c, int G, con
   const int gi = lane / LPB, li = lane % LPB;
   // The word's statistics are requested first, so their latency overlaps the
   // staging of the queries below.
-  float4 m4[2][NL], v4[2][NL];
+  uint4 m4[2][NL], v4[2][NL];
   float Ms[2];
+  const uint4 zero4 = make_uint4(0, 0, 0, 0);
 #pragma unroll
   for (int it = 0; it < 2; ++it) {
     const int j = (wd << 6) + wave * 16 + it * 8 + gi;
@@ -95,8 +96,8 @@ __global__ __launch_bounds__(256) void screen_gqa_kernel(CacheView c, int G, con
     const size_t row = ((size_t)u * c.cap_blocks + j) * D;
 #pragma unroll
     for (int t = 0; t < NL; ++t) {
-      m4[it][t] = scored ? ld16f_nt(c.mu + row + 32 * t + 4 * li) : make_float4(0, 0, 0, 0);
-      v4[it][t] = scored ? ld16f_nt(c.var + row + 32 * t + 4 * li) : make_float4(0, 0, 0, 0);
+      m4[it][t] = scored ? ld16_nt(c.mu + row + 64 * t + 8 * li) : zero4;
+      v4[it][t] = scored ? ld16_nt(c.var + row + 64 * t + 8 * li) : zero4;
     }
     Ms[it] = scored ? c.maxnorm[(size_t)u * c.cap_blocks + j] : 0.f;
   }
@@ -117,11 +118,11 @@ __global__ __launch_bounds__(256) void screen_gqa_kernel(CacheView c, int G, con
     if (hg < NH) {
 #pragma unroll
       for (int t = 0; t < NL; ++t) {
-        const float4 v = *reinterpret_cast<const float4*>(&s_q[hg][32 * t + 4 * li]);
-        qq = fmaf(v.x, v.x, qq);
-        qq = fmaf(v.y, v.y, qq);
-        qq = fmaf(v.z, v.z, qq);
-        qq = fmaf(v.w, v.w, qq);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = s_q[hg][64 * t + 8 * li + e];
+          qq = fmaf(x, x, qq);
+        }
       }
     }
     qq = group_sum<LPB>(qq);
@@ -136,22 +137,28 @@ __global__ __launch_bounds__(256) void screen_gqa_kernel(CacheView c, int G, con
     const int j = (wd << 6) + wave * 16 + it * 8 + gi;
     const bool scored = j < nbc;
     // v[2 g] = q_g . mu, v[2 g + 1] = (q_g * q_g) . var over this lane's dims
+    float mf[NL][8], vf[NL][8];
+#pragma unroll
+    for (int t = 0; t < NL; ++t) {
+      widen<ETA_DT_BF16>(m4[it][t], mf[t]);
+      widen<ETA_DT_BF16>(v4[it][t], vf[t]);
+    }
     float v[2 * NH];
 #pragma unroll
     for (int g = 0; g < NH; ++g) {
       float dot = 0.f, mom = 0.f;
 #pragma unroll
       for (int t = 0; t < NL; ++t) {
-        const float4 qv = *reinterpret_cast<const float4*>(&s_q[g][32 * t + 4 * li]);
-        const float4 q2 = *reinterpret_cast<const float4*>(&s_q2[g][32 * t + 4 * li]);
-        dot = fmaf(qv.x, m4[it][t].x, dot);
-        dot = fmaf(qv.y, m4[it][t].y, dot);
-        dot = fmaf(qv.z, m4[it][t].z, dot);
-        dot = fmaf(qv.w, m4[it][t].w, dot);
-        mom = fmaf(q2.x, v4[it][t].x, mom);
-        mom = fmaf(q2.y, v4[it][t].y, mom);
-        mom = fmaf(q2.z, v4[it][t].z, mom);
-        mom = fmaf(q2.w, v4[it][t].w, mom);
+        const float4 qa = *reinterpret_cast<const float4*>(&s_q[g][64 * t + 8 * li]);
+        const float4 qb = *reinterpret_cast<const float4*>(&s_q[g][64 * t + 8 * li + 4]);
+        const float4 ra = *reinterpret_cast<const float4*>(&s_q2[g][64 * t + 8 * li]);
+        const float4 rb = *reinterpret_cast<const float4*>(&s_q2[g][64 * t + 8 * li + 4]);
+        const float qv[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
+        const float q2[8] = {ra.x, ra.y, ra.z, ra.w, rb.x, rb.y, rb.z, rb.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dot = fmaf(qv[e], mf[t][e], dot);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mom = fmaf(q2[e], vf[t][e], mom);
       }
       v[2 * g] = dot;
       v[2 * g + 1] = mom;

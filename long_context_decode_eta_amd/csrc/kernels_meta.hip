@@ -3,6 +3,9 @@
 // Block statistics (paper: "Elastic Threshold Attention ...", Methodology 4):
 // per complete block of b keys, the centroid mu, the per-coordinate
 // population variance var (two passes) and the largest key norm maxnorm.
+// mu and var are accumulated in float64 and stored as bfloat16 rounded to
+// nearest even from the float64 values (half the bytes for the screen to
+// read); maxnorm is float32.
 // Threshold (Methodology 1, Eq. 1): tau = qbar W_tau + b_tau, or frozen
 // per-head constants.
 #include "eta_internal.h"
@@ -22,6 +25,21 @@ namespace eta {
 // complete without re-reading).  Both the append and the bulk path call this
 // function with the same summation order, so they produce bit-identical
 // statistics.
+// x rounded to the nearest bfloat16 (ties to even), as its bit pattern.
+// First to float32 rounded to odd (toward zero, the last bit set when
+// inexact), then float32 to bfloat16 to nearest even: float32 keeps 16 more
+// bits than bfloat16, so the first rounding can neither create nor cross a
+// tie of the second (round-to-odd), and the result is the direct rounding of
+// x.  For finite x within the float32 range.
+__device__ __forceinline__ uint16_t bf16_rne(double x) {
+  const float f = (float)x;
+  uint32_t u = __float_as_uint(f);
+  if (fabs((double)f) > fabs(x)) u -= 1u;  // one step back toward zero
+  if ((double)__uint_as_float(u) != x) u |= 1u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
 template <int D, int DT, int NR>
 __device__ __forceinline__ void block_stats_wave(const CacheView& c, int u, int j,
                                                  const void* last_row, int lane) {
@@ -46,9 +64,9 @@ __device__ __forceinline__ void block_stats_wave(const CacheView& c, int u, int 
       rows[i] = (i < nr && r < c.bs) ? ld16_nt(row_ptr(r)) : make_uint4(0, 0, 0, 0);
     }
   }
-  float sum[EPL];
+  double sum[EPL];
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) sum[e] = 0.f;
+  for (int e = 0; e < EPL; ++e) sum[e] = 0.0;
   float best = 0.f;  // largest squared row norm
   auto first_pass = [&](int r, const uint4& raw) {
     float n2 = 0.f;
@@ -57,7 +75,7 @@ __device__ __forceinline__ void block_stats_wave(const CacheView& c, int u, int 
       widen<DT>(raw, x);
 #pragma unroll
       for (int e = 0; e < EPL; ++e) {
-        sum[e] += x[e];
+        sum[e] += (double)x[e];
         n2 = fmaf(x[e], x[e], n2);
       }
     }
@@ -80,12 +98,12 @@ __device__ __forceinline__ void block_stats_wave(const CacheView& c, int u, int 
     for (int e = 0; e < EPL; ++e) sum[e] += __shfl_xor(sum[e], off, kWave);
     best = fmaxf(best, __shfl_xor(best, off, kWave));
   }
-  const float inv_b = 1.0f / (float)c.bs;  // exact: b is a power of two
-  float mean[EPL], ss[EPL];
+  const double inv_b = 1.0 / (double)c.bs;  // exact: b is a power of two
+  double mean[EPL], ss[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) {
     mean[e] = sum[e] * inv_b;
-    ss[e] = 0.f;
+    ss[e] = 0.0;
   }
   auto second_pass = [&](int r, const uint4& raw) {
     if (r < c.bs) {
@@ -93,8 +111,8 @@ __device__ __forceinline__ void block_stats_wave(const CacheView& c, int u, int 
       widen<DT>(raw, x);
 #pragma unroll
       for (int e = 0; e < EPL; ++e) {
-        const float dlt = x[e] - mean[e];
-        ss[e] = fmaf(dlt, dlt, ss[e]);
+        const double dlt = (double)x[e] - mean[e];
+        ss[e] = fma(dlt, dlt, ss[e]);
       }
     }
   };
@@ -115,10 +133,19 @@ __device__ __forceinline__ void block_stats_wave(const CacheView& c, int u, int 
   }
   if (g == 0) {
     const size_t row = ((size_t)u * c.cap_blocks + j) * D + li * EPL;
+    uint32_t pm[EPL / 2], pv[EPL / 2];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      c.mu[row + e] = mean[e];
-      c.var[row + e] = ss[e] * inv_b;
+    for (int e = 0; e < EPL; e += 2) {  // two bf16 per 32-bit word
+      pm[e / 2] = (uint32_t)bf16_rne(mean[e]) | ((uint32_t)bf16_rne(mean[e + 1]) << 16);
+      pv[e / 2] = (uint32_t)bf16_rne(ss[e] * inv_b) |
+                  ((uint32_t)bf16_rne(ss[e + 1] * inv_b) << 16);
+    }
+    if constexpr (EPL == 8) {
+      *reinterpret_cast<uint4*>(c.mu + row) = make_uint4(pm[0], pm[1], pm[2], pm[3]);
+      *reinterpret_cast<uint4*>(c.var + row) = make_uint4(pv[0], pv[1], pv[2], pv[3]);
+    } else {
+      *reinterpret_cast<uint2*>(c.mu + row) = make_uint2(pm[0], pm[1]);
+      *reinterpret_cast<uint2*>(c.var + row) = make_uint2(pv[0], pv[1]);
     }
     if (lane == 0) c.maxnorm[(size_t)u * c.cap_blocks + j] = sqrtf(best);
   }

@@ -2,8 +2,9 @@
 //
 // Screen (paper: "Elastic Threshold Attention ...", Methodology 4, Eq. 5):
 //   s_j = scale * min(<q, mu_j> + z sqrt(sum_i q_i^2 var_j,i), ||q|| maxnorm_j)
-// A block is skipped iff s_j < threshold; only the statistics (2D+1 floats per
-// block) are read, never the keys.  The block holding the newest key is always
+// A block is skipped iff s_j < threshold; only the statistics (mu and var in
+// bfloat16, maxnorm in float32: 4D+4 bytes per block) are read, never the
+// keys.  The block holding the newest key is always
 // admitted (it holds the query's own, never-gated key of Eq. 3).
 #include "eta_internal.h"
 
@@ -42,8 +43,9 @@ __global__ __launch_bounds__(256) void screen_kernel(CacheView c, const float* q
   const float ts = tau_screen[u];
   const bool z_inf = __builtin_isinf(z);
   const int jw = (wd << 6) + wave * (kScreenSteps * kBlocksPerIter) + gi;
-  float4 m4[kScreenSteps][NL], v4[kScreenSteps][NL];
+  uint4 m4[kScreenSteps][NL], v4[kScreenSteps][NL];
   float M[kScreenSteps];
+  const uint4 zero4 = make_uint4(0, 0, 0, 0);
 #pragma unroll
   for (int it = 0; it < kScreenSteps; ++it) {
     const int j = jw + it * kBlocksPerIter;
@@ -51,8 +53,8 @@ __global__ __launch_bounds__(256) void screen_kernel(CacheView c, const float* q
     const bool scored = j < nbc;
 #pragma unroll
     for (int t = 0; t < NL; ++t) {
-      m4[it][t] = scored ? ld16f_nt(c.mu + row + 32 * t + 4 * li) : make_float4(0, 0, 0, 0);
-      v4[it][t] = scored ? ld16f_nt(c.var + row + 32 * t + 4 * li) : make_float4(0, 0, 0, 0);
+      m4[it][t] = scored ? ld16_nt(c.mu + row + 64 * t + 8 * li) : zero4;
+      v4[it][t] = scored ? ld16_nt(c.var + row + 64 * t + 8 * li) : zero4;
     }
     M[it] = scored ? c.maxnorm[(size_t)u * c.cap_blocks + j] : 0.f;
   }
@@ -61,17 +63,7 @@ __global__ __launch_bounds__(256) void screen_kernel(CacheView c, const float* q
   for (int it = 0; it < kScreenSteps; ++it) {
     const int j = jw + it * kBlocksPerIter;
     float dot = 0.f, mom = 0.f;
-#pragma unroll
-    for (int t = 0; t < NL; ++t) {
-      dot = fmaf(qs.q[4 * t + 0], m4[it][t].x, dot);
-      dot = fmaf(qs.q[4 * t + 1], m4[it][t].y, dot);
-      dot = fmaf(qs.q[4 * t + 2], m4[it][t].z, dot);
-      dot = fmaf(qs.q[4 * t + 3], m4[it][t].w, dot);
-      mom = fmaf(qs.q2[4 * t + 0], v4[it][t].x, mom);
-      mom = fmaf(qs.q2[4 * t + 1], v4[it][t].y, mom);
-      mom = fmaf(qs.q2[4 * t + 2], v4[it][t].z, mom);
-      mom = fmaf(qs.q2[4 * t + 3], v4[it][t].w, mom);
-    }
+    score_partials<D>(qs, m4[it], v4[it], dot, mom);
     dot = group_sum<kLanesPerBlock>(dot);
     mom = group_sum<kLanesPerBlock>(mom);
     const float geometric = qs.qn * M[it];

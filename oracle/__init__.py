@@ -90,6 +90,10 @@ def load(path: str | None = None):
     lib.eta_oracle_gqa_dense_batch.restype = None
     lib.eta_oracle_prefill.argtypes = [_i] * 6 + [_p] * 4 + [_d, _d, _p, _p]
     lib.eta_oracle_prefill.restype = None
+    lib.eta_oracle_round_bf16.argtypes = [_d]
+    lib.eta_oracle_round_bf16.restype = _d
+    lib.eta_oracle_round_bf16_array.argtypes = [_p, ctypes.c_size_t]
+    lib.eta_oracle_round_bf16_array.restype = None
     lib.eta_oracle_threads.argtypes = []
     lib.eta_oracle_threads.restype = _i
     lib.eta_oracle_set_threads.argtypes = [_i]
@@ -193,6 +197,26 @@ def meta_batch(K, seq_len, b, lib=None):
     mu = np.zeros((B, H, nbcap, d)); var = np.zeros((B, H, nbcap, d)); M = np.zeros((B, H, nbcap))
     lib.eta_oracle_meta_batch(B, H, d, b, cap, dt, _ptr(sl), _ptr(K), _ptr(mu), _ptr(var), _ptr(M))
     return mu, var, M
+
+
+def round_bf16(x, lib=None):
+    """x (float64 array) rounded to the nearest bfloat16, ties to even."""
+    lib = lib or load()
+    out = np.array(x, dtype=np.float64, copy=True, order="C")
+    lib.eta_oracle_round_bf16_array(_ptr(out), out.size)
+    return out
+
+
+def stored_meta(meta, lib=None):
+    """The block index as the cache stores it: exact mu and var rounded to
+    bfloat16, maxnorm exact."""
+    mu, var, M = meta
+    return round_bf16(mu, lib), round_bf16(var, lib), M
+
+
+def index_batch(K, seq_len, b, lib=None):
+    """meta_batch in the stored form (stored_meta): what the screen uses."""
+    return stored_meta(meta_batch(K, seq_len, b, lib), lib)
 
 
 def step_batch(q, K, V, seq_len, b, meta, W, bias_or_c, *, a=0.0, z=1.0, scale=None,

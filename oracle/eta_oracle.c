@@ -103,6 +103,25 @@ int eta_oracle_block_meta(const void* K, int dtype, int T, int d, int b,
 }
 
 /* ---------------------------------------------------------------------- */
+/* Stored form of the block index.  The pages fix no storage precision; this
+ * implementation stores mu and var as bfloat16, each rounded to nearest (ties
+ * to even) from its exact value: 8 significant bits.  x = m 2^e with
+ * 0.5 <= |m| < 1, so m 2^8 lies in [128, 256) and rounding it to an integer
+ * (nearbyint: the default round-to-nearest-even mode) keeps 8 bits.  Zero,
+ * infinities and NaN pass unchanged; values below the bfloat16 normal range
+ * do not occur in block statistics of finite keys of moderate size. */
+double eta_oracle_round_bf16(double x) {
+  if (x == 0.0 || !isfinite(x)) return x;
+  int e;
+  double m = frexp(x, &e);
+  return ldexp(nearbyint(ldexp(m, 8)), e - 8);
+}
+
+void eta_oracle_round_bf16_array(double* x, size_t n) {
+  for (size_t i = 0; i < n; ++i) x[i] = eta_oracle_round_bf16(x[i]);
+}
+
+/* ---------------------------------------------------------------------- */
 /* Threshold (Methodology 1, Eq. 1).  Dynamic: tau[b][h] = sum_j qbar[b][j]
  * W[j][h] + bias[h].  Frozen (W == NULL): tau[b][h] = c[h], the per-head
  * constants of offline calibration.  The screen uses tau - a. */

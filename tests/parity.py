@@ -203,6 +203,31 @@ def host_kv(w: synth.Workload):
     return synth.kv_numpy(w.k), synth.kv_numpy(w.v)
 
 
+def check_stored_meta(cache: eb.KVCache, exact, stored, seq_len, b):
+    """The cache's block index against the oracle's: mu and var (bfloat16)
+    equal to the oracle's exact values rounded to bfloat16, bit for bit, except
+    where an exact value lies within 1e-12 (relative) of a rounding midpoint
+    (float64 sums in another order may then round the other way); maxnorm
+    (float32) within 1e-5."""
+    mu = cache.mu.float().cpu().numpy().astype(np.float64)
+    var = cache.var.float().cpu().numpy().astype(np.float64)
+    M = cache.maxnorm.cpu().numpy()
+    for bb in range(cache.batch):
+        nbc = int(seq_len[bb]) // b
+        for name, g, x, r in (("mu", mu, exact[0], stored[0]), ("var", var, exact[1], stored[1])):
+            g, x, r = g[bb, :, :nbc], x[bb, :, :nbc], r[bb, :, :nbc]
+            off = g != r
+            if off.any():
+                # the two bfloat16 neighbours of x bracket a midpoint within 1e-12
+                m, e = np.frexp(x[off])
+                frac = np.abs(m) * 256.0 - np.floor(np.abs(m) * 256.0)
+                near = np.abs(frac - 0.5) <= 1e-12 * 256.0
+                assert near.all(), (f"{name}: {int((~near).sum())} stored values differ from the "
+                                    f"rounded oracle, first gpu {g[off][~near][0]!r} vs "
+                                    f"{r[off][~near][0]!r} (exact {x[off][~near][0]!r})")
+        close(M[bb, :, :nbc], exact[2][bb, :, :nbc], 1e-5, "maxnorm")
+
+
 def check_against_oracle(w: synth.Workload, g: GpuResult, cache: eb.KVCache, *, W, bias_or_c,
                          z, scale, mode, beta=5.0, a=0.0, check_meta=True, K=None, V=None):
     """Full (every stream) comparison; returns a dict of the worst errors."""
@@ -210,19 +235,15 @@ def check_against_oracle(w: synth.Workload, g: GpuResult, cache: eb.KVCache, *, 
         K, V = host_kv(w)
     sl = w.seq_len.cpu().numpy().astype(np.int32)
     q = w.q.cpu().numpy()
-    meta = oracle.meta_batch(K, sl, w.block)
+    exact = oracle.meta_batch(K, sl, w.block)
+    meta = oracle.stored_meta(exact)
     Wn = None if W is None else W.cpu().numpy()
     cn = bias_or_c.cpu().numpy()
     r = oracle.step_batch(q, K, V, sl, w.block, meta, Wn, cn, a=a, z=z, scale=scale,
                           mode=mode, beta=beta)
     stats = {}
     if check_meta:
-        mu = cache.mu.cpu().numpy(); var = cache.var.cpu().numpy(); M = cache.maxnorm.cpu().numpy()
-        for bb in range(w.B):
-            nbc = int(sl[bb]) // w.block
-            close(mu[bb, :, :nbc], meta[0][bb, :, :nbc], 1e-5, "mu")
-            close(var[bb, :, :nbc], meta[1][bb, :, :nbc], 1e-5, "var")
-            close(M[bb, :, :nbc], meta[2][bb, :, :nbc], 1e-5, "maxnorm")
+        check_stored_meta(cache, exact, meta, sl, w.block)
     close(g.tau_gate, r["tau"], 1e-5, "tau_gate")
     close(g.tau_screen, r["tau_screen"], 1e-5, "tau_screen")
     flips, screened = compare_masks(r["active"], r["score"], r["tau_screen"], g.mask, sl, w.block)
@@ -258,7 +279,7 @@ def check_units(w: synth.Workload, g: GpuResult, units, *, W, bias_or_c, z, scal
         K = synth.kv_numpy(w.k[b:b + 1, h:h + 1, :T])
         V = synth.kv_numpy(w.v[b:b + 1, h:h + 1, :T])
         sl = np.array([T], np.int32)
-        meta = oracle.meta_batch(K, sl, w.block)
+        meta = oracle.index_batch(K, sl, w.block)
         r = oracle.screen_attend_batch(q[b:b + 1, h:h + 1], K, V, sl, w.block, meta,
                                        tau[b, h], ts[b, h], z=z, scale=scale, mode=mode,
                                        beta=beta)
@@ -284,13 +305,14 @@ def check_units(w: synth.Workload, g: GpuResult, units, *, W, bias_or_c, z, scal
 
 
 def meta_of_sequences(w: synth.Workload, seqs):
-    """The oracle's block statistics of the sequences `seqs`, computed one
-    sequence at a time (bounded host memory at full size) and stacked."""
+    """The oracle's block index (stored form) of the sequences `seqs`,
+    computed one sequence at a time (bounded host memory at full size) and
+    stacked."""
     parts = []
     for b in seqs:
         K = synth.kv_numpy(w.k[b:b + 1])
-        parts.append(oracle.meta_batch(K, w.seq_len.cpu().numpy()[b:b + 1].astype(np.int32),
-                                       w.block))
+        parts.append(oracle.index_batch(K, w.seq_len.cpu().numpy()[b:b + 1].astype(np.int32),
+                                        w.block))
         del K
     return tuple(np.concatenate([p[i] for p in parts], axis=0) for i in range(3))
 
@@ -392,7 +414,7 @@ def check_gqa(w: synth.Workload, g: GqaGpuResult, *, W, bias_or_c, z, scale, mod
     G = w.G
     sl = w.seq_len.cpu().numpy().astype(np.int32)
     q = w.q.cpu().numpy()
-    meta = oracle.meta_batch(K, sl, w.block)
+    meta = oracle.index_batch(K, sl, w.block)
     Wn = None if W is None else W.cpu().numpy()
     tau, ts = oracle.predict_tau(q, Wn, bias_or_c.cpu().numpy(), a=a)
     close(g.tau_gate, tau, 1e-5, "tau_gate")

@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.eta_abi_version() == 3
+    assert lib.eta_abi_version() == 4
     for s, name in [(0, b"ETA_OK"), (1, b"ETA_ERR_NULL_PTR"), (5, b"ETA_ERR_WORKSPACE"),
                     (6, b"ETA_ERR_HIP")]:
         assert lib.eta_status_string(s) == name

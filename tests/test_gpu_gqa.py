@@ -264,7 +264,7 @@ def test_gqa_full_size_sampled_streams(D, rho):
         K = synth.kv_numpy(w.k[b:b + 1, kv:kv + 1, :T])
         V = synth.kv_numpy(w.v[b:b + 1, kv:kv + 1, :T])
         sl = np.array([T], np.int32)
-        meta = oracle.meta_batch(K, sl, w.block)
+        meta = oracle.index_batch(K, sl, w.block)
         hs = slice(kv * G, (kv + 1) * G)
         r = oracle.gqa_screen_attend_batch(q[b:b + 1, hs], K, V, sl, w.block, meta,
                                            tau[b:b + 1, hs], ts[b:b + 1, hs], G, z=w.z,

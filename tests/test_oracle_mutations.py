@@ -56,6 +56,10 @@ MUTANTS = {
     "calibration_off_by_one": ("c = 0.5 * (x[k - 1] + x[k]);", "c = 0.5 * (x[k] + x[k + 1 < (long long)n ? k + 1 : k]);"),
     "calibration_forced_ignored": ("double want = (rho * total - forced) / b;",
                                    "double want = (rho * total) / b;"),
+    "index_round_half_up": ("return ldexp(nearbyint(ldexp(m, 8)), e - 8);",
+                            "return ldexp(floor(ldexp(m, 8) + 0.5), e - 8);"),
+    "index_seven_bits": ("return ldexp(nearbyint(ldexp(m, 8)), e - 8);",
+                         "return ldexp(nearbyint(ldexp(m, 7)), e - 7);"),
     "gqa_wrong_kv_head": ("int bb = uq / Hq, kv = (uq % Hq) / G;",
                           "int bb = uq / Hq, kv = (uq % Hq) % Hkv;", 2),
     "gqa_union_counts_first_head": ("for (int g = 0; g < G; ++g) on |= active",

@@ -369,3 +369,63 @@ def test_calibration_hits_target_density(rho):
         assert np.all(np.isneginf(c))
     if rho == 0.0:
         assert np.all(np.isposinf(c))
+
+
+# ---------------------------------------------------------------------------
+# The stored form of the block index: mu and var rounded to bfloat16.
+def _nearest_bf16_by_search(x: float) -> float:
+    """The bfloat16 nearest to x (ties to the even significand), found by
+    comparing x exactly (Fractions) with every bfloat16 of its binade and the
+    next power of two: the 129 values 2^k (1 + i/128), i = 0..128."""
+    from fractions import Fraction
+    if x == 0.0:
+        return 0.0
+    s = -1.0 if x < 0 else 1.0
+    ax = Fraction(abs(x))
+    k = math.floor(math.log2(abs(x)))
+    while Fraction(2) ** k > ax:
+        k -= 1
+    while Fraction(2) ** (k + 1) <= ax:
+        k += 1
+    best, best_i, best_d = None, None, None
+    for i in range(129):
+        v = Fraction(2) ** k * (1 + Fraction(i, 128))
+        dist = abs(ax - v)
+        # significand index i (i = 128 is the next binade's 1.0: even)
+        even = (i % 2 == 0)
+        if best is None or dist < best_d or (dist == best_d and even):
+            best, best_i, best_d = v, i, dist
+    return s * float(best)
+
+
+def test_index_rounding_is_nearest_bf16_ties_to_even():
+    rng = np.random.default_rng(11)
+    xs = list(rng.standard_normal(400) * np.exp(rng.uniform(-20, 20, 400)))
+    # exact ties between two bfloat16 values: odd and even lower neighbours
+    for base in (1.0, 1.0078125, 3.0, 0.15625, 1000.0):
+        for k in range(3):
+            lo = base * (1 + k / 128.0)
+            ulp = 2.0 ** (math.floor(math.log2(lo)) - 7)
+            xs += [lo + ulp / 2, -(lo + ulp / 2), lo + ulp / 2 * (1 + 1e-15), lo + ulp * 0.4999]
+    xs += [0.0, 1.0, -2.0, 255.5, 2.0 ** -100, 3.0 * 2.0 ** 100]
+    got = oracle.round_bf16(np.array(xs))
+    for x, g in zip(xs, got):
+        assert g == _nearest_bf16_by_search(float(x)), (x, g)
+    # every result is a bfloat16: its float32 bits have a zero low half
+    bits = got.astype(np.float32).view(np.uint32)
+    assert np.all(bits & 0xFFFF == 0)
+
+
+def test_stored_meta_rounds_mu_and_var_only():
+    rng = np.random.default_rng(12)
+    K = rng.standard_normal((2, 3, 64, 16)).astype(np.float32)
+    sl = np.array([64, 40], np.int32)
+    exact = oracle.meta_batch(K, sl, 8)
+    mu, var, M = oracle.stored_meta(exact)
+    np.testing.assert_array_equal(M, exact[2])
+    np.testing.assert_array_equal(mu, oracle.round_bf16(exact[0]))
+    np.testing.assert_array_equal(var, oracle.round_bf16(exact[1]))
+    # within half a bfloat16 step (2^-8 relative) of the exact values
+    nz = exact[1] != 0
+    assert np.all(np.abs(var[nz] - exact[1][nz]) <= 2.0 ** -8 * np.abs(exact[1][nz]))
+    assert np.any(mu != exact[0])

@@ -367,28 +367,32 @@ __device__ __forceinline__ float block_score(const CacheView& c, int u, int j, b
 // lanes of a wave are summed by an xor butterfly (every lane ends with the
 // same bits), the four wave sums as (w0 + w1) + (w2 + w3), the bias last.
 // W == NULL (frozen thresholds) gives bias[h] alone.  Every thread returns
-// the value; with W it contains one barrier (s_red: 4 floats of LDS).
+// the value; with W it contains one barrier (s_red: 4 floats of LDS).  The
+// first 256 threads of the work-group do the sum; further threads (a larger
+// work-group) take part only in the barrier.
 constexpr int kTauThreads = 256;
 __device__ __forceinline__ float tau_of_head(const float* qb, const float* W, const float* bias,
                                              int H, int n, int h, float* s_red) {
   if (!W) return bias[h];
   const int t = threadIdx.x;
-  float acc = 0.f;
-  int j = t;
-  for (; j + 3 * kTauThreads < n; j += 4 * kTauThreads) {
-    float qv[4], wv[4];
+  if (t < kTauThreads) {
+    float acc = 0.f;
+    int j = t;
+    for (; j + 3 * kTauThreads < n; j += 4 * kTauThreads) {
+      float qv[4], wv[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      qv[r] = qb[j + r * kTauThreads];
-      wv[r] = W[(size_t)(j + r * kTauThreads) * H + h];
+      for (int r = 0; r < 4; ++r) {
+        qv[r] = qb[j + r * kTauThreads];
+        wv[r] = W[(size_t)(j + r * kTauThreads) * H + h];
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc = fmaf(qv[r], wv[r], acc);
     }
+    for (; j < n; j += kTauThreads) acc = fmaf(qb[j], W[(size_t)j * H + h], acc);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) acc = fmaf(qv[r], wv[r], acc);
+    for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, kWave);
+    if ((t & (kWave - 1)) == 0) s_red[t / kWave] = acc;
   }
-  for (; j < n; j += kTauThreads) acc = fmaf(qb[j], W[(size_t)j * H + h], acc);
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, kWave);
-  if ((t & (kWave - 1)) == 0) s_red[t / kWave] = acc;
   __syncthreads();
   return ((s_red[0] + s_red[1]) + (s_red[2] + s_red[3])) + bias[h];
 }

@@ -363,7 +363,7 @@ __device__ __forceinline__ float block_score(const CacheView& c, int u, int j, b
 // over the n = H*D entries of the sequence's query, by the 256 threads of a
 // work-group in one fixed order shared by the threshold kernel and the fused
 // screen + decode (so both produce the same bits): thread t adds q_j W[j][h]
-// for j = t, t + 256, ... in that order (fmaf, four loads in flight), the 64
+// for j = t, t + 256, ... in that order (fmaf, eight loads in flight), the 64
 // lanes of a wave are summed by an xor butterfly (every lane ends with the
 // same bits), the four wave sums as (w0 + w1) + (w2 + w3), the bias last.
 // W == NULL (frozen thresholds) gives bias[h] alone.  Every thread returns
@@ -378,15 +378,15 @@ __device__ __forceinline__ float tau_of_head(const float* qb, const float* W, co
   if (t < kTauThreads) {
     float acc = 0.f;
     int j = t;
-    for (; j + 3 * kTauThreads < n; j += 4 * kTauThreads) {
-      float qv[4], wv[4];
+    for (; j + 7 * kTauThreads < n; j += 8 * kTauThreads) {
+      float qv[8], wv[8];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
+      for (int r = 0; r < 8; ++r) {
         qv[r] = qb[j + r * kTauThreads];
         wv[r] = W[(size_t)(j + r * kTauThreads) * H + h];
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc = fmaf(qv[r], wv[r], acc);
+      for (int r = 0; r < 8; ++r) acc = fmaf(qv[r], wv[r], acc);
     }
     for (; j < n; j += kTauThreads) acc = fmaf(qb[j], W[(size_t)j * H + h], acc);
 #pragma unroll

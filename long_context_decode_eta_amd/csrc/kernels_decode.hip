@@ -479,6 +479,30 @@ __global__ __launch_bounds__(kFusedWaves * kWave, 8 / kFusedWaves) void screen_d
   // Uniform over the work-group.  The first chunk of a stream always runs far
   // enough to report the stream's thresholds, as the threshold kernel does.
   if (first >= nb && k > 0) return;
+  const int nbc = T >> c.log2bs;
+  const int nblk = first < nb ? min(a.split, nb - first) : 0;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // Waves 0-3 request their blocks' statistics and their query share before
+  // the threshold's sum, so those loads overlap it; the score is block_score's
+  // arithmetic on the loaded values.
+  const bool screener = wave < 4 && kBlocksPerIter * wave < nblk;  // wave-uniform
+  const int gi = lane / kLanesPerBlock, li = lane % kLanesPerBlock;
+  const int i = kBlocksPerIter * wave + gi;  // block first + i of the stream
+  const int j = first + i;
+  const bool scored = screener && i < nblk && j < nbc;  // complete blocks of this chunk
+  QShare<D> qs;
+  uint4 m4[QShare<D>::kLoads], v4[QShare<D>::kLoads];
+  float M = 0.f;
+  if (screener) {
+    load_qshare<D>(a.q + (size_t)u * D, li, qs);
+    const size_t row = ((size_t)u * c.cap_blocks + (scored ? j : 0)) * D;
+#pragma unroll
+    for (int t = 0; t < QShare<D>::kLoads; ++t) {
+      m4[t] = scored ? ld16_nt(c.mu + row + 64 * t + 8 * li) : make_uint4(0, 0, 0, 0);
+      v4[t] = scored ? ld16_nt(c.var + row + 64 * t + 8 * li) : make_uint4(0, 0, 0, 0);
+    }
+    M = scored ? c.maxnorm[(size_t)u * c.cap_blocks + j] : 0.f;
+  }
   const float tg = tau_of_head(a.q + (size_t)(u / c.H) * c.H * D, sa.W, sa.bias, c.H, c.H * D,
                                u % c.H, s_red);
   const float ts = tg - sa.a;
@@ -487,17 +511,14 @@ __global__ __launch_bounds__(kFusedWaves * kWave, 8 / kFusedWaves) void screen_d
     if (sa.tau_screen) sa.tau_screen[u] = ts;
   }
   if (first >= nb) return;  // an empty stream (T == 0): the combine writes zeros
-  const int nbc = T >> c.log2bs;
-  const int nblk = min(a.split, nb - first);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  if (wave < 4 && kBlocksPerIter * wave < nblk) {  // wave-uniform; waves 0-3 screen
-    const int gi = lane / kLanesPerBlock, li = lane % kLanesPerBlock;
-    QShare<D> qs;
-    load_qshare<D>(a.q + (size_t)u * D, li, qs);
-    const int i = kBlocksPerIter * wave + gi;  // block first + i of the stream
-    const int j = first + i;
-    const bool scored = i < nblk && j < nbc;  // complete blocks of this chunk
-    const float sc = block_score<D>(c, u, j, scored, qs, li, sa.z, __builtin_isinf(sa.z), a.scale);
+  if (screener) {
+    float dot = 0.f, mom = 0.f;
+    score_partials<D>(qs, m4, v4, dot, mom);
+    dot = group_sum<kLanesPerBlock>(dot);
+    mom = group_sum<kLanesPerBlock>(mom);
+    const float geometric = qs.qn * M;
+    const float sc = __builtin_isinf(sa.z) ? a.scale * geometric
+                                           : a.scale * fminf(fmaf(sa.z, sqrtf(mom), dot), geometric);
     const bool on = i < nblk && (j == nb - 1 || (scored && sc >= ts));
     const uint64_t bal = __ballot(on);
     uint32_t bits = 0;

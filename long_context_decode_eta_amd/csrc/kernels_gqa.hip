@@ -697,8 +697,10 @@ __global__ __launch_bounds__(1024) void combine_gqa_kernel(CacheView c, GqaArgs 
 // all G heads run on the matrix cores as in the chunked kernel; the partial
 // of (stream segment, head g) goes to slot (w + u) * G + g.  Measured on
 // 32 x 128K, 38% head density: about 6% faster than the chunked kernel.
-// Two waves per SIMD at either head dim: d = 64 needs about 175 registers; at
-// d = 128 (about 300 registers unconstrained, one wave per SIMD) the bound
+// Two waves per SIMD at either head dim.  At d = 64 a second tile in flight
+// and the uniform tile checks of the WHOLE form together took the 38% call
+// (32 x 128K) from 0.40 to 0.38 ms (6.2 to 6.5 TB/s; either alone gave at most
+// 3%).  At d = 128 (about 300 registers unconstrained, one wave per SIMD) the bound
 // costs a few spilled registers and gains 12% (32 x 128K, 38% head density:
 // 0.80 ms against 0.91 ms at one wave per SIMD and 0.86 ms for the chunked
 // kernel).
@@ -712,9 +714,15 @@ struct GqaFlowShape {
   static constexpr int NI = kTileKeys / RPI;    // load instructions per tile and tensor
   static constexpr int TB = kTileKeys * RB;     // one tensor's tile, bytes
   static constexpr int StageBytes = 2 * TB;     // K rows | V rows
+  // Tiles in flight per wave beyond the one computed: two at d = 64 (32 more
+  // registers, about 222 in all, still two waves per SIMD), one at d = 128.
+  static constexpr int Ahead = D == 64 ? 2 : 1;
 };
 
-template <int D, int MODE>
+// WHOLE: every 32-key tile lies inside one block (b >= 32), so a tile's
+// block index, head mask and position checks are wave-uniform: one lookup per
+// tile, scalar base addresses, and per-key tests only in a stream's last tile.
+template <int D, int MODE, bool WHOLE>
 __global__ __launch_bounds__(64, 2) void decode_gqa_flow_kernel(CacheView c, GqaArgs a) {
   using Sh = GqaFlowShape<D>;
   constexpr int NK = Sh::NK, NV = Sh::NV, RB = Sh::RB, LPR = Sh::LPR, RPI = Sh::RPI;
@@ -758,15 +766,15 @@ __global__ __launch_bounds__(64, 2) void decode_gqa_flow_kernel(CacheView c, Gqa
   if (w >= plan.wn) return;
   const int n = lane & 15, grp = lane >> 4;  // operand layout: row/column n, k group grp
   const int ri = lane / LPR, cc = lane % LPR;  // load layout: row ri, 16-byte chunk cc
-  const bool whole = c.bs >= kTileKeys;      // every tile lies inside one block
   const float gk1 = -a.beta * kLog2e;
   // Value-operand rows of the transposing read (as in the prefill kernel).
   const int trow0 = tile_key(0, 4 * grp + ((lane & 15) >> 2));
   const int trow1 = tile_key(1, 4 * grp + ((lane & 15) >> 2));
   const int tr4 = lane & 3;
 
-  int p = plan.lo(w);
-  const int pend = plan.lo(w + 1);
+  // Range bounds and streams are wave-uniform (read into scalar registers).
+  int p = __builtin_amdgcn_readfirstlane(plan.lo(w));
+  const int pend = __builtin_amdgcn_readfirstlane(plan.lo(w + 1));
   int u = 0;  // the last stream with start[u] <= p (so start[u + 1] > p)
   {
     int hi = units - 1;
@@ -774,10 +782,12 @@ __global__ __launch_bounds__(64, 2) void decode_gqa_flow_kernel(CacheView c, Gqa
       const int mid = (u + hi + 1) >> 1;
       if (s_start[mid] <= p) u = mid; else hi = mid - 1;
     }
+    u = __builtin_amdgcn_readfirstlane(u);
   }
   while (p < pend) {
-    const int base = s_start[u];
-    const int i0 = p - base, i1 = min(pend, s_start[u + 1]) - base;  // local blocks
+    const int base = __builtin_amdgcn_readfirstlane(s_start[u]);
+    const int i1 = __builtin_amdgcn_readfirstlane(min(pend, s_start[u + 1]) - base);
+    const int i0 = p - base;  // local blocks i0 .. i1 - 1 of stream u
     const int nblk = i1 - i0;
     const int T = c.seq_len[u / c.H];
     const int nb = (T + c.bs - 1) >> c.log2bs;
@@ -811,8 +821,9 @@ __global__ __launch_bounds__(64, 2) void decode_gqa_flow_kernel(CacheView c, Gqa
     const float gk0 = a.beta * kLog2e * tau_n;
     // Block indices and head masks, 64 per register: lane x holds entry
     // bb + x in (lst0, hm0) and bb + 64 + x in (lst1, hm1).  The window moves
-    // on by 64 when a tile about to be loaded reaches past it; the tile still
-    // to be computed then lies inside the new window.
+    // on by 64 when a tile about to be loaded reaches past it (a tile spans at
+    // most 8 blocks, so one move suffices); the tiles still to be computed,
+    // at most two tiles behind it, then lie inside the new window.
     int bb = 0, lst0, lst1;
     uint32_t hm0, hm1;
     auto load_entry = [&](int x, int& j, uint32_t& hm) {
@@ -824,7 +835,7 @@ __global__ __launch_bounds__(64, 2) void decode_gqa_flow_kernel(CacheView c, Gqa
     // (block index, head mask) of segment row rr; every lane takes part.
     auto entry = [&](int rr, int& j, uint32_t& hm) {
       const int o = (rr >> c.log2bs) - bb;
-      if (whole) {  // the same entry for every lane
+      if constexpr (WHOLE) {  // the same entry for every lane
         const int ou = __builtin_amdgcn_readfirstlane(o);
         const int src0 = ou < 64 ? lst0 : lst1;
         const int src1 = (int)(ou < 64 ? hm0 : hm1);
@@ -854,6 +865,22 @@ __global__ __launch_bounds__(64, 2) void decode_gqa_flow_kernel(CacheView c, Gqa
         hm0 = hm1;
         bb += 64;
         load_entry(bb + 64 + lane, lst1, hm1);
+      }
+      if constexpr (WHOLE) {
+        int j;
+        uint32_t hm;
+        entry(t * kTileKeys, j, hm);
+        const int s0 = (j << c.log2bs) + ((t * kTileKeys) & (c.bs - 1));  // tile row 0
+        if ((unsigned)j < (unsigned)nb && s0 + kTileKeys <= T) {  // every row valid
+          const size_t tb = (size_t)s0 * RB;
+#pragma unroll
+          for (int it = 0; it < NI; ++it) {
+            const size_t off = tb + (size_t)((it * RPI + ri) * RB + 16 * cc);
+            kr[it] = ld16_nt(kbase + off);
+            vr[it] = ld16_nt(vbase + off);
+          }
+          return;
+        }
       }
 #pragma unroll
       for (int it = 0; it < NI; ++it) {
@@ -904,22 +931,46 @@ __global__ __launch_bounds__(64, 2) void decode_gqa_flow_kernel(CacheView c, Gqa
       // key 2 grp + st + 8 i of the tile.
       float lg[8];
       float tmax = -__builtin_inff();
+      auto gated = [&](float d) {
+        return d * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(fmaf(d, gk1, gk0)));
+      };
+      bool fast = false;
+      if constexpr (WHOLE) {
+        int j;
+        uint32_t hm;
+        entry(r0, j, hm);
+        const int s0 = (j << c.log2bs) + (r0 & (c.bs - 1));
+        // Every key valid and none of them the own key T - 1.
+        fast = (unsigned)j < (unsigned)nb && s0 + kTileKeys < T;
+        if (fast) {
+          const bool hb = (hm >> n) & 1u;
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
+          for (int st = 0; st < 2; ++st)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int rr = r0 + 2 * grp + st + 8 * i;
-          int j;
-          uint32_t hm;
-          entry(rr, j, hm);
-          const int s = key_pos(rr, j);
-          const bool on = (s >= 0) & ((hm >> n) & 1u);
-          const float d = S[st][i];
-          float lv = d;
-          if (MODE == ETA_LOGIT_GATED && s != T - 1)
-            lv = d * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(fmaf(d, gk1, gk0)));
-          lg[4 * st + i] = on ? lv : -__builtin_inff();
-          tmax = fmaxf(tmax, lg[4 * st + i]);
+            for (int i = 0; i < 4; ++i) {
+              const float d = S[st][i];
+              lg[4 * st + i] = hb ? (MODE == ETA_LOGIT_GATED ? gated(d) : d) : -__builtin_inff();
+              tmax = fmaxf(tmax, lg[4 * st + i]);
+            }
+        }
+      }
+      if (!fast) {
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int rr = r0 + 2 * grp + st + 8 * i;
+            int j;
+            uint32_t hm;
+            entry(rr, j, hm);
+            const int s = key_pos(rr, j);
+            const bool on = (s >= 0) & ((hm >> n) & 1u);
+            const float d = S[st][i];
+            float lv = d;
+            if (MODE == ETA_LOGIT_GATED && s != T - 1) lv = gated(d);
+            lg[4 * st + i] = on ? lv : -__builtin_inff();
+            tmax = fmaxf(tmax, lg[4 * st + i]);
+          }
         }
       }
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
@@ -966,16 +1017,37 @@ __global__ __launch_bounds__(64, 2) void decode_gqa_flow_kernel(CacheView c, Gqa
         O[nv] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo, vb, O[nv], 0, 0, 0);
       }
     };
-    // The next tile's loads are issued once the current one is staged, so
-    // they are in flight during its compute.
-    uint4 kr[NI], vr[NI];
-    fetch(0, kr, vr);
-    for (int t = 0; t < ntiles; ++t) {
-      stage(kr, vr);
-      if (t + 1 < ntiles) fetch(t + 1, kr, vr);
-      wave_lds_sync();
-      compute(t);
-      wave_lds_sync();
+    if constexpr (Sh::Ahead == 2) {
+      // Two register sets: tiles t + 1 and t + 2 are in flight during the
+      // compute of tile t (tile t + 2 is requested once tile t is staged).
+      uint4 ka[NI], va[NI], kb[NI], vb2[NI];
+      fetch(0, ka, va);
+      if (1 < ntiles) fetch(1, kb, vb2);
+      for (int t = 0; t < ntiles; t += 2) {
+        stage(ka, va);
+        if (t + 2 < ntiles) fetch(t + 2, ka, va);
+        wave_lds_sync();
+        compute(t);
+        wave_lds_sync();
+        if (t + 1 >= ntiles) break;
+        stage(kb, vb2);
+        if (t + 3 < ntiles) fetch(t + 3, kb, vb2);
+        wave_lds_sync();
+        compute(t + 1);
+        wave_lds_sync();
+      }
+    } else {
+      // The next tile's loads are issued once the current one is staged, so
+      // they are in flight during its compute.
+      uint4 kr[NI], vr[NI];
+      fetch(0, kr, vr);
+      for (int t = 0; t < ntiles; ++t) {
+        stage(kr, vr);
+        if (t + 1 < ntiles) fetch(t + 1, kr, vr);
+        wave_lds_sync();
+        compute(t);
+        wave_lds_sync();
+      }
     }
     // Head n's sum over the 4 lane groups (they share the reference max).
     lsum += __shfl_xor(lsum, 16, kWave);
@@ -994,8 +1066,10 @@ __global__ __launch_bounds__(64, 2) void decode_gqa_flow_kernel(CacheView c, Gqa
       a.part_l[slot + n] = lsum;
     }
     p = base + i1;
-    if (p < pend)  // next non-empty stream
+    if (p < pend) {  // next non-empty stream
       do ++u; while (s_start[u + 1] <= p);
+      u = __builtin_amdgcn_readfirstlane(u);
+    }
   }
 }
 
@@ -1115,11 +1189,11 @@ size_t gqa_decode_lds_bytes(int D, int split) {
 
 // Work-groups of the balanced grouped decode: as many as are resident at once
 // (one wave each; registers and LDS set the count).
-template <int D, int MODE>
+template <int D, int MODE, bool WHOLE>
 static int gqa_flow_grid(int units) {
   int per_cu = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &per_cu, reinterpret_cast<const void*>(decode_gqa_flow_kernel<D, MODE>), 64,
+          &per_cu, reinterpret_cast<const void*>(decode_gqa_flow_kernel<D, MODE, WHOLE>), 64,
           (size_t)(units + 1) * 4) != hipSuccess ||
       per_cu < 1)
     per_cu = 1;
@@ -1133,9 +1207,15 @@ static hipError_t decode_gqa_t(const CacheView& c, const GqaDecode& g, hipStream
   if constexpr (!DENSE) {
     if (g.use_flow) {
       GqaArgs f = g;
-      f.flow_grid = gqa_flow_grid<D, MODE>(units);
-      hipLaunchKernelGGL((decode_gqa_flow_kernel<D, MODE>), dim3(f.flow_grid), dim3(64),
-                         (size_t)(units + 1) * 4, s, c, f);
+      if (c.bs >= kTileKeys) {
+        f.flow_grid = gqa_flow_grid<D, MODE, true>(units);
+        hipLaunchKernelGGL((decode_gqa_flow_kernel<D, MODE, true>), dim3(f.flow_grid), dim3(64),
+                           (size_t)(units + 1) * 4, s, c, f);
+      } else {
+        f.flow_grid = gqa_flow_grid<D, MODE, false>(units);
+        hipLaunchKernelGGL((decode_gqa_flow_kernel<D, MODE, false>), dim3(f.flow_grid),
+                           dim3(64), (size_t)(units + 1) * 4, s, c, f);
+      }
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL((combine_gqa_flow_kernel<D>), dim3(units * g.G), dim3(256), 0, s, c,

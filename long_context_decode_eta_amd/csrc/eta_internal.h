@@ -432,10 +432,14 @@ struct DecodeArgs {
   int* flow_info;    // [1] total admitted blocks N
 };
 // Work-group size and work-groups per compute unit of the balanced decode
-// (3 waves per SIMD, its occupancy: all of them are resident at once) and the
-// stream count up to which it is used (its offsets live in LDS).
+// (2 waves per SIMD, its occupancy: all of them are resident at once) and the
+// stream count up to which it is used (its offsets live in LDS).  Two
+// work-groups per CU leave 256 registers per lane (about 171 used, no spills);
+// against three (168 registers, a few spilled) the 38% 128K call went from
+// 0.52 to 0.50-0.51 ms, 10% from 0.152 to 0.147, 512K from 0.274 to
+// 0.259-0.270; four (128 registers) doubled the time.
 constexpr int kFlowThreads = 256;
-constexpr int kFlowWGsPerCU = 3 * 256 / kFlowThreads;
+constexpr int kFlowWGsPerCU = 2;
 constexpr int kMaxFlowUnits = 8191;
 // Streams up to which the queue kernel can be used (its chunk table lives in
 // LDS), and the flat-grid size above which it is.

@@ -573,7 +573,8 @@ __device__ __forceinline__ int stream_blocks(const CacheView& c, const DecodeArg
 }
 
 template <int D, int DT, int MODE>
-__global__ __launch_bounds__(kFlowThreads, 3) void decode_flow_kernel(CacheView c, DecodeArgs a) {
+__global__ __launch_bounds__(kFlowThreads, kFlowWGsPerCU) void decode_flow_kernel(CacheView c,
+                                                                                  DecodeArgs a) {
   constexpr int EPL = Elt<DT>::kPer16B;
   constexpr int LPR = D / EPL;
   constexpr int RPI = kWave / LPR;

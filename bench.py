@@ -265,11 +265,10 @@ def summarize_counters(args):
         w, nw = mean_of(wrows, "WRITE_SIZE", lambda k: k == kname)
         rd, wr = f * 1024.0 * f_factor, w * 1024.0 * w_factor
         table.append((short, max(nf, nw), f, w, rd, wr))
-        # the sparse decode call: balanced decode + combine (the dense
-        # baseline runs other kernels: decode_grid_kernel / decode_gqa_kernel
-        # with a trailing `true` argument, and combine_kernel /
-        # combine_gqa_kernel)
-        if any(short.startswith(f"eta::{p}<") for p in parts):
+        # the sparse decode call: balanced decode + combine, not the dense
+        # baseline's decode (template arguments ending in `true`).  The grouped
+        # dense baseline shares the combine kernel, so that row averages both.
+        if any(short.startswith(f"eta::{p}<") for p in parts) and not short.endswith("true>"):
             total += rd + wr
     workload = "gqa128k" if gqa else args.workload + ("_fused" if fused else "")
     path = GQA_COUNTERS if gqa else COUNTERS

@@ -611,9 +611,9 @@ static eta_status decode_gqa_common(const eta_cache* c, int32_t group, const flo
   g.part_l = reinterpret_cast<float*>(w + off_parts + align256(slots * 4));
   g.part_acc = reinterpret_cast<float*>(w + off_parts + 2 * align256(slots * 4));
   g.out = out;
-  // Sparse grouped decode runs balanced (equal ranges of all union blocks per
-  // wave) whenever its stream offsets fit in LDS.
-  g.use_flow = !dense && units <= eta::kMaxGqaFlowUnits &&
+  // The grouped decode, sparse or dense, runs balanced (equal ranges of all
+  // union blocks per wave) whenever its stream offsets fit in LDS.
+  g.use_flow = units <= eta::kMaxGqaFlowUnits &&
                units * (long long)v.cap_blocks < 0x7fffffffLL;
   g.flow_grid = 0;
   g.flow_start = reinterpret_cast<int*>(w + 256);

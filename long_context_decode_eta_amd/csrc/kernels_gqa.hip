@@ -722,7 +722,9 @@ struct GqaFlowShape {
 // WHOLE: every 32-key tile lies inside one block (b >= 32), so a tile's
 // block index, head mask and position checks are wave-uniform: one lookup per
 // tile, scalar base addresses, and per-key tests only in a stream's last tile.
-template <int D, int MODE, bool WHOLE>
+// DENSE: every block of every stream, for every head (the dense baseline,
+// RAW logits): the list is the identity and every head mask is full.
+template <int D, int MODE, bool WHOLE, bool DENSE>
 __global__ __launch_bounds__(64, 2) void decode_gqa_flow_kernel(CacheView c, GqaArgs a) {
   using Sh = GqaFlowShape<D>;
   constexpr int NK = Sh::NK, NV = Sh::NV, RB = Sh::RB, LPR = Sh::LPR, RPI = Sh::RPI;
@@ -738,7 +740,7 @@ __global__ __launch_bounds__(64, 2) void decode_gqa_flow_kernel(CacheView c, Gqa
     int sum = 0;
     for (int u = u0; u < u1; ++u) {
       int T, cnt;
-      gqa_stream(c, a, false, u, &T, &cnt);
+      gqa_stream(c, a, DENSE, u, &T, &cnt);
       s_start[u] = cnt;
       sum += cnt;
     }
@@ -791,8 +793,8 @@ __global__ __launch_bounds__(64, 2) void decode_gqa_flow_kernel(CacheView c, Gqa
     const int nblk = i1 - i0;
     const int T = c.seq_len[u / c.H];
     const int nb = (T + c.bs - 1) >> c.log2bs;
-    const int32_t* list = a.union_idx + (size_t)u * c.cap_blocks + i0;
-    const uint32_t* hmask = a.head_mask + (size_t)u * c.cap_blocks;
+    const int32_t* list = DENSE ? nullptr : a.union_idx + (size_t)u * c.cap_blocks + i0;
+    const uint32_t* hmask = DENSE ? nullptr : a.head_mask + (size_t)u * c.cap_blocks;
     const char* kbase = static_cast<const char*>(c.k) + (size_t)u * c.cap * RB;
     const char* vbase = static_cast<const char*>(c.v) + (size_t)u * c.cap * RB;
     // Query operand (head n, dims 32 kk + 8 grp + i), scaled, split hi + lo.
@@ -827,8 +829,13 @@ __global__ __launch_bounds__(64, 2) void decode_gqa_flow_kernel(CacheView c, Gqa
     int bb = 0, lst0, lst1;
     uint32_t hm0, hm1;
     auto load_entry = [&](int x, int& j, uint32_t& hm) {
-      j = x < nblk ? list[x] : -1;
-      hm = (unsigned)j < (unsigned)nb ? hmask[j] : 0u;
+      if constexpr (DENSE) {
+        j = x < nblk ? i0 + x : -1;
+        hm = G >= 32 ? 0xffffffffu : (1u << G) - 1u;
+      } else {
+        j = x < nblk ? list[x] : -1;
+        hm = (unsigned)j < (unsigned)nb ? hmask[j] : 0u;
+      }
     };
     load_entry(lane, lst0, hm0);
     load_entry(64 + lane, lst1, hm1);
@@ -1189,11 +1196,12 @@ size_t gqa_decode_lds_bytes(int D, int split) {
 
 // Work-groups of the balanced grouped decode: as many as are resident at once
 // (one wave each; registers and LDS set the count).
-template <int D, int MODE, bool WHOLE>
+template <int D, int MODE, bool WHOLE, bool DENSE>
 static int gqa_flow_grid(int units) {
   int per_cu = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &per_cu, reinterpret_cast<const void*>(decode_gqa_flow_kernel<D, MODE, WHOLE>), 64,
+          &per_cu,
+          reinterpret_cast<const void*>(decode_gqa_flow_kernel<D, MODE, WHOLE, DENSE>), 64,
           (size_t)(units + 1) * 4) != hipSuccess ||
       per_cu < 1)
     per_cu = 1;
@@ -1204,24 +1212,21 @@ template <int D, int MODE, bool DENSE>
 static hipError_t decode_gqa_t(const CacheView& c, const GqaDecode& g, hipStream_t s) {
   const GqaArgs& a = g;
   const int units = c.B * c.H;
-  if constexpr (!DENSE) {
-    if (g.use_flow) {
-      GqaArgs f = g;
-      if (c.bs >= kTileKeys) {
-        f.flow_grid = gqa_flow_grid<D, MODE, true>(units);
-        hipLaunchKernelGGL((decode_gqa_flow_kernel<D, MODE, true>), dim3(f.flow_grid), dim3(64),
-                           (size_t)(units + 1) * 4, s, c, f);
-      } else {
-        f.flow_grid = gqa_flow_grid<D, MODE, false>(units);
-        hipLaunchKernelGGL((decode_gqa_flow_kernel<D, MODE, false>), dim3(f.flow_grid),
-                           dim3(64), (size_t)(units + 1) * 4, s, c, f);
-      }
-      hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((combine_gqa_flow_kernel<D>), dim3(units * g.G), dim3(256), 0, s, c,
-                         f);
-      return hipGetLastError();
+  if (g.use_flow) {
+    GqaArgs f = g;
+    if (c.bs >= kTileKeys) {
+      f.flow_grid = gqa_flow_grid<D, MODE, true, DENSE>(units);
+      hipLaunchKernelGGL((decode_gqa_flow_kernel<D, MODE, true, DENSE>), dim3(f.flow_grid),
+                         dim3(64), (size_t)(units + 1) * 4, s, c, f);
+    } else {
+      f.flow_grid = gqa_flow_grid<D, MODE, false, DENSE>(units);
+      hipLaunchKernelGGL((decode_gqa_flow_kernel<D, MODE, false, DENSE>), dim3(f.flow_grid),
+                         dim3(64), (size_t)(units + 1) * 4, s, c, f);
     }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((combine_gqa_flow_kernel<D>), dim3(units * g.G), dim3(256), 0, s, c, f);
+    return hipGetLastError();
   }
   const long long grid = (long long)g.max_chunks * c.B * c.H;
   hipLaunchKernelGGL((decode_gqa_kernel<D, MODE, DENSE>), dim3((unsigned)grid),

@@ -72,8 +72,10 @@ LENS = [0, 1, 15, 16, 17, 700, 1024, 2053]
 
 @pytest.mark.parametrize("G", [1, 2, 3, 8, 16])
 @pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("block", [4, 16, 64, 128])
+@pytest.mark.parametrize("block", [4, 16, 32, 64, 128])
 def test_gqa_ragged_edges(G, D, block):
+    # Blocks of 32 or more hold whole 32-key tiles (the balanced decode's
+    # uniform per-tile form); smaller ones take the per-key lookups.
     w = synth.make("gqa_tiny", seed=3 + G + block, T=LENS, B=len(LENS), H=2, cap=2053,
                    pad="nan", block=block, D=D, G=G)
     to_gpu(w)

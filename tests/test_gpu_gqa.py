@@ -89,14 +89,30 @@ def test_gqa_ragged_edges(G, D, block):
     note(f"  D_head {st['d_head']:.3f} D_union {st['d_union']:.3f} out_rel {st['out_rel']:.2e}")
 
 
-def test_gqa_balanced_decode_at_its_stream_limit():
-    # 6143 KV streams, the most the balanced grouped decode keeps offsets for.
-    w = to_gpu(synth.make("gqa_tiny", seed=31, T=(1, 64), B=6143, H=1, G=2, cap=64, block=16))
+def _check_dense(w, cache, split):
+    """eta_dense_decode_gqa on the workload's streams against the oracle."""
+    ws = eb.workspace(eb.decode_gqa_workspace_bytes(w.B, w.H, w.G, w.D, cache.cap_blocks,
+                                                    split))
+    out = torch.zeros((w.B, w.Hq, w.D), device="cuda")
+    eb.dense_decode_gqa(cache, w.G, w.q, w.scale, split, ws, out)
+    torch.cuda.synchronize()
+    ref = oracle.gqa_dense_batch(w.q.cpu().numpy(), synth.kv_numpy(w.k), synth.kv_numpy(w.v),
+                                 w.seq_len.cpu().numpy(), w.G, scale=w.scale)
+    compare_outputs(out.cpu().numpy(), ref, w.kv_dtype, "dense", internal=1e-4)
+
+
+@pytest.mark.parametrize("block", [16, 32])
+def test_gqa_balanced_decode_at_its_stream_limit(block):
+    # 6143 KV streams, the most the balanced grouped decode keeps offsets for
+    # (block 32: the whole-tile form, one or two tiles per stream).
+    w = to_gpu(synth.make("gqa_tiny", seed=31, T=(1, 64), B=6143, H=1, G=2, cap=64,
+                          block=block))
     cache = make_cache(w)
     c = torch.tensor([0.8, 1.2], device="cuda")
     g = run_gpu_gqa(cache, 2, w.q, bias_or_c=c, z=w.z, scale=w.scale, split=2)
     st = check_gqa(w, g, W=None, bias_or_c=c, z=w.z, scale=w.scale, mode=eb.GATED)
     note(f"  D_head {st['d_head']:.3f} D_union {st['d_union']:.3f} out_rel {st['out_rel']:.2e}")
+    _check_dense(w, cache, split=2)  # the balanced kernel's dense form
 
 
 def test_gqa_more_streams_than_the_balanced_decode_holds():
@@ -111,6 +127,7 @@ def test_gqa_more_streams_than_the_balanced_decode_holds():
     g = run_gpu_gqa(cache, w.G, w.q, bias_or_c=c, z=1.0, scale=w.scale, mode=eb.GATED, split=2)
     st = check_gqa(w, g, W=None, bias_or_c=c, z=1.0, scale=w.scale, mode=eb.GATED)
     note(f"  D_head {st['d_head']:.3f} D_union {st['d_union']:.3f} out_rel {st['out_rel']:.2e}")
+    _check_dense(w, cache, split=2)  # the chunked kernel's dense form
 
 
 @pytest.mark.parametrize("tau", [math.inf, -math.inf])

@@ -365,9 +365,11 @@ def auto_split(units: int, cap_blocks: int, block: int, dense: bool = False) -> 
 def auto_fused_chunk(units: int, cap_blocks: int) -> int:
     """Blocks per chunk of the fused step: the largest of 32, 16, ..., 1 that
     still gives at least 256 work-groups (one per compute unit).  Swept on
-    MI355X at 32K x 16 heads, b=64 (8192 blocks): 32 blocks per chunk (256
-    work-groups) took 0.023 / 0.037 / 0.049 ms at 10 / 38 / 70% density, 16
-    blocks 0.026 / 0.038 / 0.050 ms; 4 and 8 were slower at every density."""
+    MI355X at 32K x 16 heads, b=64 (8192 blocks), 8 waves per chunk: 32
+    blocks per chunk (256 work-groups) took 0.021 / 0.035 / 0.047 ms at 10 /
+    38 / 70% density, 16 blocks 0.027 / 0.039 / 0.052 ms, 8 blocks 0.035 /
+    0.049 / 0.060 ms (one work-group fits a compute unit at a time, so
+    smaller chunks queue behind each other)."""
     for cb in (32, 16, 8, 4, 2):
         if units * (-(-cap_blocks // cb)) >= 256:
             return cb

@@ -317,11 +317,12 @@ eta_status eta_screen_gqa(const eta_cache* c, int32_t group, const float* q,
  * once for its whole group; query head kv * group + g attends over the keys of
  * the blocks whose head_mask bit g is set, with the logits of eta_decode
  * (Eq. 3, its own tau_gate; the query's own key is never gated), normalised
- * over its own admitted set.  With at most 6143 KV streams (head_dim 64 or
- * 128) the union blocks of all streams, taken in order, are cut into
- * min(resident waves, ceil(N / blocks_per_split)) equal ranges, one per wave
- * (N = total union blocks); otherwise into chunks of blocks_per_split union
- * blocks of one stream.  Partial results per query head, log-sum-exp combine;
+ * over its own admitted set.  The union blocks of all streams, taken in
+ * order, are cut into min(resident waves, ceil(N / blocks_per_split)) equal
+ * ranges, one per wave (N = total union blocks); above 6143 KV streams a
+ * one-work-group scan kernel first writes the stream offsets to the
+ * workspace.  B * H_kv * cap_blocks must be below 2^31 (ETA_ERR_BAD_SHAPE).
+ * Partial results per query head, log-sum-exp combine;
  * out is device
  * [batch][H_kv * group][head_dim] float32, zeros for T_b == 0.
  * Requires kv_dtype == ETA_DT_BF16: the scores and value sums run on the

@@ -465,10 +465,11 @@ class Decoder:
 
 
 def auto_split_gqa(units: int, cap_blocks: int, block: int, dense: bool = False) -> int:
-    """Blocks per chunk of the grouped-query decode: about 1024 keys per chunk
-    (4096 dense), fewer for a small cache so the grid still fills the chip.
-    From sweeps on MI355X at 32 x 128K, 4 KV heads, b = 64: 16 blocks at 57%
-    and 19% union (vs 8 or 32), 64 blocks dense."""
+    """blocks_per_split of the grouped-query decode: the least union blocks
+    of a wave's range, about 1024 keys (4096 dense), fewer for a small cache
+    so the ranges still spread over the chip.  From sweeps on MI355X at 32 x
+    128K, 4 KV heads, b = 64: 16 blocks at 57% and 19% union (vs 8 or 32), 64
+    blocks dense."""
     if dense:
         return max(1, min(4096 // block, (units * cap_blocks) // 2048))
     return max(1, min(1024 // block, (units * cap_blocks) // 1024))

@@ -534,17 +534,23 @@ eta_status eta_screen_gqa(const eta_cache* c, int32_t group, const float* q,
 // slots: one per query head and chunk of the flat grid; for the balanced
 // decode one per query head and (wave, stream) slot, with at most
 // kMaxFlowWavesPerCU waves per compute unit.
-static size_t decode_gqa_slots(long long units, int group, int cap_blocks, int split) {
-  const long long maxc = (cap_blocks + split - 1) / split;
-  const long long grid = units * group * maxc;
-  const long long flow = ((long long)eta::kMaxFlowWavesPerCU * device_cus() + units) * group;
-  return (size_t)(grid > flow ? grid : flow);
+// Partial slots of the balanced grouped decode: one per (wave, KV stream)
+// segment, at most kMaxFlowWavesPerCU waves per compute unit, per query head.
+static size_t decode_gqa_slots(long long units, int group) {
+  return (size_t)(((long long)eta::kMaxFlowWavesPerCU * device_cus() + units) * group);
+}
+
+// Per-wave first streams of the balanced grouped decode's global form.
+static size_t gqa_wave_table_bytes() {
+  return align256((size_t)eta::kMaxFlowWavesPerCU * device_cus() * 4);
 }
 
 static size_t decode_gqa_ws(long long units, int group, int D, int cap_blocks, int split) {
-  const size_t slots = decode_gqa_slots(units, group, cap_blocks, split);
-  return 256 + align256((size_t)(units + 1) * 4) + align256(slots * 4) * 2 +
-         align256(slots * (size_t)D * 4);
+  (void)cap_blocks;
+  (void)split;
+  const size_t slots = decode_gqa_slots(units, group);
+  return 256 + align256((size_t)(units + 1) * 4) + gqa_wave_table_bytes() +
+         align256(slots * 4) * 2 + align256(slots * (size_t)D * 4);
 }
 
 size_t eta_decode_gqa_workspace_bytes(int32_t batch, int32_t kv_heads, int32_t group,
@@ -585,15 +591,18 @@ static eta_status decode_gqa_common(const eta_cache* c, int32_t group, const flo
   if (!dense && mode == ETA_LOGIT_GATED && !tau_gate)
     return fail(ETA_ERR_NULL_PTR, "tau_gate is NULL in GATED mode");
   const long long units = (long long)v.B * v.H;
-  const int maxc = eta::ceil_div(v.cap_blocks, split);
-  if ((long long)maxc * units > kMaxGrid || units * group > kMaxGrid)
-    return fail(ETA_ERR_BAD_SHAPE, "grid too large");
+  if (units * group > kMaxGrid) return fail(ETA_ERR_BAD_SHAPE, "grid too large");
+  // Block positions of all streams together are int32 (more than any one
+  // device holds: 2^31 blocks of at least 4 keys of d >= 64 are over 2 TB).
+  if (units * (long long)v.cap_blocks >= 0x7fffffffLL)
+    return fail(ETA_ERR_BAD_SHAPE, "B*H_kv*cap_blocks must be below 2^31");
   const size_t need = decode_gqa_ws(units, group, v.D, v.cap_blocks, split);
   if (!ws || ws_bytes < need)
     return fail(ETA_ERR_WORKSPACE, "decode workspace %zu bytes < %zu", ws_bytes, need);
-  const size_t slots = decode_gqa_slots(units, group, v.cap_blocks, split);
+  const size_t slots = decode_gqa_slots(units, group);
   char* w = static_cast<char*>(ws);
-  const size_t off_parts = 256 + align256((size_t)(units + 1) * 4);
+  const size_t off_waves = 256 + align256((size_t)(units + 1) * 4);
+  const size_t off_parts = off_waves + gqa_wave_table_bytes();
   eta::GqaDecode g;
   g.G = group;
   g.q = q;
@@ -606,18 +615,18 @@ static eta_status decode_gqa_common(const eta_cache* c, int32_t group, const flo
   g.beta = beta;
   g.scale = scale;
   g.split = split;
-  g.max_chunks = maxc;
   g.part_m = reinterpret_cast<float*>(w + off_parts);
   g.part_l = reinterpret_cast<float*>(w + off_parts + align256(slots * 4));
   g.part_acc = reinterpret_cast<float*>(w + off_parts + 2 * align256(slots * 4));
   g.out = out;
   // The grouped decode, sparse or dense, runs balanced (equal ranges of all
-  // union blocks per wave) whenever its stream offsets fit in LDS.
-  g.use_flow = units <= eta::kMaxGqaFlowUnits &&
-               units * (long long)v.cap_blocks < 0x7fffffffLL;
+  // union blocks per wave), with its stream offsets in LDS up to
+  // kMaxGqaFlowUnits streams and in global memory above.
+  g.flow_global = units > eta::kMaxGqaFlowUnits;
   g.flow_grid = 0;
   g.flow_start = reinterpret_cast<int*>(w + 256);
   g.flow_info = reinterpret_cast<int*>(w);
+  g.flow_wave_u = reinterpret_cast<int*>(w + off_waves);
   return hip_status(eta::launch_decode_gqa(v, g, (hipStream_t)stream), "eta_decode_gqa launch");
 }
 

@@ -171,35 +171,19 @@ __device__ __forceinline__ int wg_exclusive_scan(int v, int* s_w, int* total) {
 
 // ---------------------------------------------------------------------------
 // Matrix-core tiles (grouped-query decode, gated prefill).  A 32-key tile of K
-// and V passes through LDS: K rows as stored with their 16-byte chunks
-// permuted, V transposed (vt[dim][k], k = 4 (key % 8) + key / 8, rows of
-// kVtWords words), so that v_mfma_f32_16x16x32_bf16 operands are single
-// conflict-free LDS reads.
+// and V passes through LDS as rows, with their 16-byte chunks permuted, so
+// that the v_mfma_f32_16x16x32_bf16 operands (K by 128-bit reads, V by the
+// transposing read) are conflict-free LDS reads.
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr int kTileKeys = 32;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazyRaise = 8.f;  // natural-log units
-constexpr int kVtWords = 18;       // 32-bit words per vt row: 32 keys + 8 bytes of padding
 
-// x where on, zeros elsewhere (component-wise, so it stays in registers).
-__device__ __forceinline__ uint4 keep(const uint4& x, bool on) {
-  const uint32_t m = on ? 0xffffffffu : 0u;
-  return make_uint4(x.x & m, x.y & m, x.z & m, x.w & m);
-}
-
-__device__ __forceinline__ uint32_t word(const uint4& x, int i) {
-  return i == 0 ? x.x : i == 1 ? x.y : i == 2 ? x.z : x.w;
-}
-
-// LDS layout permutations of the staged tiles (chosen for conflict-free
-// 128-bit operand reads of K, 64-bit writes and reads of vt, and cheap K
-// writes): K chunk c of key r is stored at chunk c ^ k_swz(r); the 4-key
-// group g of vt row dim is stored at group g ^ v_swz(dim) (even, so the two
-// groups an operand read takes stay adjacent).
+// K chunk permutation of 256-byte rows: chunk c of key r is stored at chunk
+// c ^ k_swz(r), conflict-free for the 128-bit operand reads and cheap writes.
 __device__ __forceinline__ int k_swz(int key) { return ((key >> 3) & 3) ^ (((key >> 1) & 1) << 2); }
-__device__ __forceinline__ int v_swz(int dim) { return 2 * ((dim >> 4) & 3); }
 
 // Orders this wave's LDS writes before its later LDS reads (and vice versa).
 __device__ __forceinline__ void wave_lds_sync() {
@@ -475,27 +459,29 @@ struct GqaDecode {
   int mode;
   bool dense;
   float beta, scale;
-  int split, max_chunks;
-  float* part_m;    // [B*H*G][max_chunks]
-  float* part_l;    // [B*H*G][max_chunks]
-  float* part_acc;  // [B*H*G][max_chunks][D]
+  int split;        // blocks_per_split: the least union blocks per wave's range
+  float* part_m;    // [(waves + B*H) * G] partials, slot (w + u) * G + g
+  float* part_l;    // [(waves + B*H) * G]
+  float* part_acc;  // [(waves + B*H) * G][D]
   float* out;       // [B*H*G][D]
-  bool use_flow;    // balanced decode: an equal range of all union blocks per wave
-  int flow_grid;    // its one-wave work-groups (set at launch)
+  int flow_grid;    // one-wave work-groups of the balanced decode (set at launch)
   int* flow_start;  // [B*H + 1] union-block offsets, written by the balanced decode
   int* flow_info;   // [1] total union blocks N
+  bool flow_global; // offsets in global memory (flow_scan_gqa_kernel), not in LDS
+  int* flow_wave_u; // [waves] first stream of each wave's range (flow_global only)
 };
 constexpr int kMaxGroup = 16;
 // Resident one-wave work-groups per compute unit of the balanced grouped
 // decode are at most this many (8 waves per SIMD); it bounds its partial
-// slots.  The stream count up to which it is used (offsets in LDS).
+// slots and the per-wave start table.  Up to kMaxGqaFlowUnits KV streams every
+// work-group scans the stream offsets into LDS; above, a one-work-group scan
+// kernel writes them (and each wave's first stream) to global memory.
 constexpr int kMaxFlowWavesPerCU = 32;
 constexpr int kMaxGqaFlowUnits = 6143;
 int device_cus();
 hipError_t launch_screen_gqa(const CacheView& c, int G, const float* q, const float* tau_screen,
                              float z, float scale, int32_t* union_idx, uint32_t* head_mask,
                              int32_t* union_cnt, uint64_t* ctr, uint64_t* words, hipStream_t s);
-size_t gqa_decode_lds_bytes(int D, int split);
 hipError_t launch_decode_gqa(const CacheView& c, const GqaDecode& g, hipStream_t s);
 // Gated causal attention forward over whole sequences (bf16 q, K, V).
 struct PrefillArgs {

@@ -268,442 +268,49 @@ __global__ __launch_bounds__(256) void compact_gqa_kernel(CacheView c, const uin
   }
 }
 
-// ---------------------------------------------------------------------------
-// Decode.  One work-group of W waves (4 for d = 64, 2 for d = 128) per chunk
-// of `split` union blocks of KV stream u; wave w takes the 32-key tiles w,
-// w + W, ...  A tile passes through the wave's own LDS area:
-//   load    coalesced 128-bit reads of whole K and V rows (d/8 lanes per row)
-//           into registers.  The loads of the wave's next tile are issued as
-//           soon as these registers are in LDS, so they overlap the compute of
-//           the current tile at no register cost;
-//   stage   K rows as stored, each row's 16-byte chunks permuted by an XOR
-//           with a function of the key so that the operand reads below hit
-//           distinct LDS banks; V transposed, vt[dim][k] with k = 4 (key % 8)
-//           + key / 8, rows of 18 words, the 8-byte groups of 4 keys permuted
-//           by an XOR with a function of the dim (the same goal, for writes
-//           and reads);
-//   scores  for each 16-key half st: S[16 keys x 16 heads] = K (A operand:
-//           lane l holds key rho(st, l % 16) = 2 ((l%16) / 4) + st +
-//           8 ((l%16) % 4), dims 32 kk + 8 (l / 16) .. + 7) times Q^T (B: head
-//           l % 16, the same dims; q split hi + lo).  Lane l receives head
-//           l % 16 and keys rho(st, 4 (l / 16) + i), i < 4;
-//   softmax per head with a lazily moved reference max; weights split hi + lo;
-//   values  O[16 heads x 16 dims] += P (A: head l % 16, contraction slots
-//           k = 8 (l / 16) + i: by the choice of rho and of the vt order these
-//           are exactly the lane's 8 score keys) times V (B: dim l % 16, the
-//           same slots, one 16-byte read of vt).
-// The W waves' (max, sum, O) are merged through LDS and written as the
-// chunk's partial per query head (or the output for single-chunk streams).
-
-template <int D>
-struct GqaShape {
-  static constexpr int W = D == 64 ? 4 : 2;        // waves per work-group
-  // d = 64: at most 168 registers per lane, 3 work-groups (12 waves) per CU.
-  // The register budget holds the wave's next tile in flight during the
-  // compute of the current one; at 4 per CU (128 registers) it spills.
-  // Measured on 32 x 128K at 57% union: 431 us (3 per CU) vs 448 us (4, with
-  // spills).
-  static constexpr int MinBlocks = D == 64 ? 3 : 1;
-  static constexpr int NK = D / 32;                 // 32-dim slabs (score product)
-  static constexpr int NV = D / 16;                 // 16-dim slabs (value product)
-  static constexpr int RB = D * 2;                  // bytes per bf16 row
-  static constexpr int LPR = D / 8;                 // lanes per row in a coalesced load
-  static constexpr int RPI = 64 / LPR;              // rows per load instruction
-  static constexpr int NI = kTileKeys / RPI;        // load instructions per tile and tensor
-  static constexpr int QPL = 8 / RPI;               // vt key groups per lane
-  static constexpr int KStride = RB;                // staged K row stride, bytes
-  static constexpr int KBytes = kTileKeys * KStride;
-  static constexpr int VBytes = D * kVtWords * 4;
-  static constexpr int WaveBytes = KBytes + VBytes;  // per-wave LDS area
-  static constexpr int MergeBytes = W * 16 * D * 4;
-  static_assert(MergeBytes <= W * WaveBytes, "merge area reuses the staging areas");
-};
-
 using GqaArgs = GqaDecode;
 
-__device__ __forceinline__ int gqa_stream(const CacheView& c, const GqaArgs& a, bool dense, int u,
-                                          int* T_out, int* cnt_out) {
+// Length T_b of KV stream u's sequence and its block count to decode: every
+// block (dense) or the union count, clamped to the blocks the stream holds.
+__device__ __forceinline__ void gqa_stream(const CacheView& c, const GqaArgs& a, bool dense, int u,
+                                           int* T_out, int* cnt_out) {
   const int T = c.seq_len[u / c.H];
   const int nb = T > 0 ? (T + c.bs - 1) >> c.log2bs : 0;
-  const int cnt = dense ? nb : max(0, min(a.union_cnt[u], nb));
   *T_out = T;
-  *cnt_out = cnt;
-  return (cnt + a.split - 1) / a.split;
-}
-
-template <int D, int MODE, bool DENSE>
-__global__ __launch_bounds__(GqaShape<D>::W * 64, GqaShape<D>::MinBlocks) void decode_gqa_kernel(CacheView c, GqaArgs a) {
-  using Sh = GqaShape<D>;
-  constexpr int W = Sh::W, NK = Sh::NK, NV = Sh::NV, RB = Sh::RB;
-  constexpr int LPR = Sh::LPR, RPI = Sh::RPI, NI = Sh::NI, QPL = Sh::QPL;
-  extern __shared__ __align__(16) char s_raw[];
-  float* s_o = reinterpret_cast<float*>(s_raw);                        // merge: [W][16][D]
-  // chunk's block list: (block index, head mask) per slot
-  int2* s_blk = reinterpret_cast<int2*>(s_raw + W * Sh::WaveBytes);    // [split]
-  __shared__ float s_ml[W][16][2];
-
-  const int u = blockIdx.x / a.max_chunks;
-  const int k = rotated_chunk(blockIdx.x % a.max_chunks, u, a.max_chunks);
-  int T, cnt;
-  const int nch = gqa_stream(c, a, DENSE, u, &T, &cnt);
-  if (k >= nch) return;
-  const int nb = (T + c.bs - 1) >> c.log2bs;
-  const int first = k * a.split, nblk = min(a.split, cnt - first);
-  const int G = a.G;
-  const uint32_t all = (1u << G) - 1u;
-  for (int i = threadIdx.x; i < nblk; i += blockDim.x) {
-    if constexpr (DENSE) {
-      s_blk[i] = make_int2(first + i, (int)all);
-    } else {
-      const int j = a.union_idx[(size_t)u * c.cap_blocks + first + i];
-      const uint32_t hm =
-          ((unsigned)j < (unsigned)nb) ? a.head_mask[(size_t)u * c.cap_blocks + j] : 0u;
-      s_blk[i] = make_int2(j, (int)hm);
-    }
-  }
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int n = lane & 15, grp = lane >> 4;  // operand layout: row/column n, k group grp
-  char* s_k = s_raw + wave * Sh::WaveBytes;  // staged K tile
-  char* s_v = s_k + Sh::KBytes;              // transposed V tile
-
-  // Query operand (head n, dims 32*kk + 8*grp + i), scaled, split hi + lo.
-  // Lanes of padding heads (n >= G) load head G-1 and use zeros.
-  bf16x8 qhi[NK], qlo[NK];
-  {
-    const int hn = min(n, G - 1);
-    const float4* qn =
-        reinterpret_cast<const float4*>(a.q + ((size_t)u * G + hn) * D + 8 * grp);
-    float4 qv[NK][2];
-#pragma unroll
-    for (int kk = 0; kk < NK; ++kk) {
-      qv[kk][0] = qn[8 * kk];
-      qv[kk][1] = qn[8 * kk + 1];
-    }
-    const float sc = n < G ? a.scale : 0.f;
-#pragma unroll
-    for (int kk = 0; kk < NK; ++kk) {
-      const float x8[8] = {qv[kk][0].x, qv[kk][0].y, qv[kk][0].z, qv[kk][0].w,
-                           qv[kk][1].x, qv[kk][1].y, qv[kk][1].z, qv[kk][1].w};
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float x = x8[i] * sc;
-        const __bf16 h = (__bf16)x;
-        qhi[kk][i] = h;
-        qlo[kk][i] = (__bf16)(x - (float)h);
-      }
-    }
-  }
-  const float tau_n = MODE == ETA_LOGIT_GATED ? a.tau[(size_t)u * G + min(n, G - 1)] : 0.f;
-  // Gate of Eq. 3: sigmoid(beta (S - tau)) = 1 / (1 + 2^(S gk1 + gk0)).
-  const float gk1 = -a.beta * kLog2e, gk0 = a.beta * kLog2e * tau_n;
-  const char* kbase = static_cast<const char*>(c.k) + (size_t)u * c.cap * RB;
-  const char* vbase = static_cast<const char*>(c.v) + (size_t)u * c.cap * RB;
-  __syncthreads();  // s_blk
-
-  floatx4 O[NV];
-#pragma unroll
-  for (int nv = 0; nv < NV; ++nv) O[nv] = floatx4{0.f, 0.f, 0.f, 0.f};
-  float m = -__builtin_inff(), lsum = 0.f;
-
-  const int rows = nblk << c.log2bs;
-  const int ntiles = (rows + kTileKeys - 1) / kTileKeys;
-  // Chunk row rr -> absolute key position, or -1 past the chunk, past the
-  // stream or for an out-of-range list entry.
-  auto key_pos = [&](int rr, int j) {
-    const int s = (j << c.log2bs) + (rr & (c.bs - 1));
-    return (rr < rows && (unsigned)j < (unsigned)nb && s < T) ? s : -1;
-  };
-  auto slot_of = [&](int rr) { return min(rr >> c.log2bs, nblk - 1); };
-
-  // Coalesced loads of tile t: instruction it reads key it*RPI + lane/LPR,
-  // bytes 16 (lane % LPR) .. +15.  Invalid keys read row 0 of the stream
-  // (always in bounds) and are zeroed when staged; bit it of `ok` records
-  // validity.  Nothing here waits for the data.
-  const int ri = lane / LPR, cc = lane % LPR;
-  auto fetch = [&](int t, uint4 (&kr)[NI], uint4 (&vr)[NI], uint32_t& ok) {
-    int js[NI];
-#pragma unroll
-    for (int it = 0; it < NI; ++it) js[it] = s_blk[slot_of(t * kTileKeys + it * RPI + ri)].x;
-    ok = 0;
-#pragma unroll
-    for (int it = 0; it < NI; ++it) {
-      const int s = key_pos(t * kTileKeys + it * RPI + ri, js[it]);
-      const size_t off = (size_t)max(s, 0) * RB + 16 * cc;
-      kr[it] = ld16_nt(kbase + off);
-      vr[it] = ld16_nt(vbase + off);
-      ok |= (s >= 0 ? 1u : 0u) << it;
-    }
-  };
-  // Registers -> LDS (zeros for invalid keys).
-  auto stage = [&](uint4 (&kr)[NI], uint4 (&vr)[NI], uint32_t ok) {
-#pragma unroll
-    for (int it = 0; it < NI; ++it) {
-      kr[it] = keep(kr[it], (ok >> it) & 1u);
-      vr[it] = keep(vr[it], (ok >> it) & 1u);
-      const int key = it * RPI + ri;
-      const int chunk = cc ^ k_swz(key);
-      *reinterpret_cast<uint4*>(s_k + key * Sh::KStride + 16 * chunk) = kr[it];
-    }
-#pragma unroll
-    for (int qi = 0; qi < QPL; ++qi) {
-      const int q = ri + RPI * qi;  // keys q + 8 j sit in instructions qi + QPL j
-#pragma unroll
-      for (int w2 = 0; w2 < 4; ++w2) {
-        const int dim = 8 * cc + 2 * w2;
-        const uint32_t x0 = word(vr[qi], w2), x1 = word(vr[qi + QPL], w2);
-        const uint32_t x2 = word(vr[qi + 2 * QPL], w2), x3 = word(vr[qi + 3 * QPL], w2);
-        // dims `dim` (low halves) and dim + 1 (high halves) of keys q + 8 j
-        const uint2 lo = make_uint2((x0 & 0xffffu) | (x1 << 16), (x2 & 0xffffu) | (x3 << 16));
-        const uint2 hi = make_uint2((x0 >> 16) | (x1 & 0xffff0000u),
-                                    (x2 >> 16) | (x3 & 0xffff0000u));
-        *reinterpret_cast<uint2*>(s_v + (dim * kVtWords + 2 * (q ^ v_swz(dim))) * 4) = lo;
-        *reinterpret_cast<uint2*>(s_v + ((dim + 1) * kVtWords + 2 * (q ^ v_swz(dim + 1))) * 4) =
-            hi;
-      }
-    }
-  };
-  auto compute = [&](int t) {
-    const int r0 = t * kTileKeys;
-    // Scores.
-    floatx4 S[2];
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      const int key = tile_key(st, n);
-      const char* row = s_k + key * Sh::KStride;
-      const int sw = k_swz(key);
-      S[st] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < NK; ++kk) {
-        const uint4 kx = *reinterpret_cast<const uint4*>(row + 16 * ((4 * kk + grp) ^ sw));
-        const bf16x8 kv = __builtin_bit_cast(bf16x8, kx);
-        S[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qhi[kk], S[st], 0, 0, 0);
-        S[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qlo[kk], S[st], 0, 0, 0);
-      }
-    }
-    // Logits, masks and the running max of head n.  Score i of half st is
-    // key 2 grp + st + 8 i of the tile.
-    float lg[8];
-    float tmax = -__builtin_inff();
-    int2 blk[2][4];
-#pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) blk[st][i] = s_blk[slot_of(r0 + 2 * grp + st + 8 * i)];
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int rr = r0 + 2 * grp + st + 8 * i;
-        const int s = key_pos(rr, blk[st][i].x);
-        const bool on = (s >= 0) & (((uint32_t)blk[st][i].y >> n) & 1u);
-        const float d = S[st][i];
-        float lv = d;
-        if (MODE == ETA_LOGIT_GATED && s != T - 1)
-          lv = d * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(fmaf(d, gk1, gk0)));
-        lg[4 * st + i] = on ? lv : -__builtin_inff();
-        tmax = fmaxf(tmax, lg[4 * st + i]);
-      }
-    }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-    // Lazy rescaling: the reference max m of a head moves only when a tile
-    // raises the head's max above m + kLazyRaise (then every head moves to
-    // its own max, one wave-uniform branch).  Weights relative to m stay
-    // below e^kLazyRaise, well inside float32, and the softmax is unchanged
-    // by the choice of reference.
-    if (__ballot(tmax > m + kLazyRaise) != 0ull) {
-      const float mn = fmaxf(m, tmax);
-      const float alpha =
-          mn == -__builtin_inff() ? 1.f : __builtin_amdgcn_exp2f((m - mn) * kLog2e);
-      lsum *= alpha;
-      // O rows are heads 4*grp + i: their factors come from lanes 4*grp + i.
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float al = __shfl(alpha, 4 * grp + i, kWave);
-#pragma unroll
-        for (int nv = 0; nv < NV; ++nv) O[nv][i] *= al;
-      }
-      m = mn;
-    }
-    const float ms2 = m == -__builtin_inff() ? 0.f : m * kLog2e;
-    float pw[8], psum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      pw[i] = __builtin_amdgcn_exp2f(fmaf(lg[i], kLog2e, -ms2));
-      psum += pw[i];
-    }
-    lsum += psum;
-    uint32_t ph[4], pl[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) split_hi_lo(pw[2 * i], pw[2 * i + 1], ph[i], pl[i]);
-    const bf16x8 phi = __builtin_bit_cast(bf16x8, make_uint4(ph[0], ph[1], ph[2], ph[3]));
-    const bf16x8 plo = __builtin_bit_cast(bf16x8, make_uint4(pl[0], pl[1], pl[2], pl[3]));
-    // Values: B operand = dim 16 nv + n, contraction slots 8 grp .. 8 grp + 7.
-#pragma unroll
-    for (int nv = 0; nv < NV; ++nv) {
-      const int dim = 16 * nv + n;
-      const char* vrow = s_v + dim * kVtWords * 4;
-      const uint2 v0 = *reinterpret_cast<const uint2*>(vrow + 8 * ((2 * grp) ^ v_swz(dim)));
-      const uint2 v1 = *reinterpret_cast<const uint2*>(vrow + 8 * ((2 * grp + 1) ^ v_swz(dim)));
-      const bf16x8 vb = __builtin_bit_cast(bf16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
-      O[nv] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi, vb, O[nv], 0, 0, 0);
-      O[nv] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo, vb, O[nv], 0, 0, 0);
-    }
-  };
-
-  {
-    uint4 kr[NI], vr[NI];
-    uint32_t ok = 0;
-    int t = wave;
-    if (t < ntiles) fetch(t, kr, vr, ok);
-    while (t < ntiles) {
-      stage(kr, vr, ok);
-      if (t + W < ntiles) fetch(t + W, kr, vr, ok);
-      wave_lds_sync();
-      compute(t);
-      wave_lds_sync();
-      t += W;
-    }
-  }
-  // Head n's sum over the 4 lane groups (they share the reference max).
-  lsum += __shfl_xor(lsum, 16, kWave);
-  lsum += __shfl_xor(lsum, 32, kWave);
-  __syncthreads();  // every wave is done with its staging area
-  float* so = s_o + wave * 16 * D;
-#pragma unroll
-  for (int nv = 0; nv < NV; ++nv)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) so[(4 * grp + i) * D + 16 * nv + n] = O[nv][i];
-  if (grp == 0) {
-    s_ml[wave][n][0] = m;
-    s_ml[wave][n][1] = lsum;
-  }
-  __syncthreads();
-  // Merge the W waves per (head, dim) in a fixed order.
-  for (int e = threadIdx.x; e < G * D; e += blockDim.x) {
-    const int h = e / D, col = e % D;
-    float mm = s_ml[0][h][0], ll = s_ml[0][h][1];
-    float aa = s_o[h * D + col];
-#pragma unroll
-    for (int w = 1; w < W; ++w) {
-      const float m2 = s_ml[w][h][0], l2 = s_ml[w][h][1], a2 = s_o[(w * 16 + h) * D + col];
-      const float mx = fmaxf(mm, m2);
-      const float ms = (mx == -__builtin_inff()) ? 0.f : mx;
-      const float s1 = __builtin_amdgcn_exp2f((mm - ms) * kLog2e);
-      const float s2 = __builtin_amdgcn_exp2f((m2 - ms) * kLog2e);
-      ll = ll * s1 + l2 * s2;
-      aa = aa * s1 + a2 * s2;
-      mm = mx;
-    }
-    const size_t uq = (size_t)u * G + h;
-    if (nch == 1) {
-      a.out[uq * D + col] = aa / ll;
-    } else {
-      const size_t slot = uq * a.max_chunks + k;
-      a.part_acc[slot * D + col] = aa;
-      if (col == 0) {
-        a.part_m[slot] = mm;
-        a.part_l[slot] = ll;
-      }
-    }
-  }
-}
-
-// Combine of the chunk partials of every query head (log-sum-exp, one pass,
-// 16 waves, 8 partials in flight per wave, fixed-order wave merge); zero
-// output for empty streams.
-template <int D>
-__global__ __launch_bounds__(1024) void combine_gqa_kernel(CacheView c, GqaArgs a, bool dense) {
-  constexpr int W = 16, INF = 8, CPL = D / kWave;
-  __shared__ float s_acc[W][D];
-  __shared__ float s_ml[W][2];
-  const int uq = blockIdx.x, t = threadIdx.x, wave = t >> 6, lane = t & 63;
-  int T, cnt;
-  const int nch = gqa_stream(c, a, dense, uq / a.G, &T, &cnt);
-  if (nch == 0) {
-    if (t < D) a.out[(size_t)uq * D + t] = 0.f;
-    return;
-  }
-  if (nch == 1) return;  // written by the decode kernel
-  const float* pm = a.part_m + (size_t)uq * a.max_chunks;
-  const float* pl = a.part_l + (size_t)uq * a.max_chunks;
-  const float* pa = a.part_acc + (size_t)uq * a.max_chunks * D + lane * CPL;
-  float m = -__builtin_inff(), l = 0.f, acc[CPL];
-#pragma unroll
-  for (int e = 0; e < CPL; ++e) acc[e] = 0.f;
-  for (int base = wave; base < nch; base += W * INF) {
-    float mc[INF], lc[INF], ac[INF][CPL];
-#pragma unroll
-    for (int i = 0; i < INF; ++i) {
-      const int ch = base + W * i;
-      const bool ok = ch < nch;
-      mc[i] = ok ? pm[ch] : -__builtin_inff();
-      lc[i] = ok ? pl[ch] : 0.f;
-#pragma unroll
-      for (int e = 0; e < CPL; ++e) ac[i][e] = ok ? pa[(size_t)ch * D + e] : 0.f;
-    }
-    float mx = m;
-#pragma unroll
-    for (int i = 0; i < INF; ++i) mx = fmaxf(mx, mc[i]);
-    const float ms = (mx == -__builtin_inff()) ? 0.f : mx;
-    const float alpha = __builtin_amdgcn_exp2f((m - ms) * kLog2e);
-    l *= alpha;
-#pragma unroll
-    for (int e = 0; e < CPL; ++e) acc[e] *= alpha;
-#pragma unroll
-    for (int i = 0; i < INF; ++i) {
-      const float wgt = __builtin_amdgcn_exp2f((mc[i] - ms) * kLog2e);
-      l = fmaf(wgt, lc[i], l);
-#pragma unroll
-      for (int e = 0; e < CPL; ++e) acc[e] = fmaf(wgt, ac[i][e], acc[e]);
-    }
-    m = mx;
-  }
-#pragma unroll
-  for (int e = 0; e < CPL; ++e) s_acc[wave][lane * CPL + e] = acc[e];
-  if (lane == 0) {
-    s_ml[wave][0] = m;
-    s_ml[wave][1] = l;
-  }
-  __syncthreads();
-  if (t < D) {
-    float mm = s_ml[0][0], ll = s_ml[0][1], aa = s_acc[0][t];
-    for (int w = 1; w < W; ++w) {
-      const float m2 = s_ml[w][0], l2 = s_ml[w][1], a2 = s_acc[w][t];
-      const float mx = fmaxf(mm, m2);
-      const float ms = (mx == -__builtin_inff()) ? 0.f : mx;
-      const float s1 = __builtin_amdgcn_exp2f((mm - ms) * kLog2e);
-      const float s2 = __builtin_amdgcn_exp2f((m2 - ms) * kLog2e);
-      ll = ll * s1 + l2 * s2;
-      aa = aa * s1 + a2 * s2;
-      mm = mx;
-    }
-    a.out[(size_t)uq * D + t] = aa / ll;
-  }
+  *cnt_out = dense ? nb : max(0, min(a.union_cnt[u], nb));
 }
 
 // ---------------------------------------------------------------------------
-// Balanced grouped decode (d = 64).  As the per-head balanced decode does with
-// the admitted lists, the union lists of all KV streams, concatenated in
-// stream order, are cut into equal contiguous ranges, one per wave; a
-// work-group is one wave and holds no state shared with others.  The wave
-// walks its range in 32-key tiles: coalesced 128-bit loads of whole K and V
-// rows into registers (the next tile's loads in flight while the current one
-// is computed), staged as rows in the wave's LDS area (K chunk-swizzled for
-// the score operand, V for the transposing read of the value operand).  Keys
-// that are not to be read (past the range, the stream, or an out-of-range
-// list entry) load the stream's row 0 instead -- finite data -- and are masked
-// out of the softmax, so their weights are exactly zero.  Scores and values of
-// all G heads run on the matrix cores as in the chunked kernel; the partial
-// of (stream segment, head g) goes to slot (w + u) * G + g.  Measured on
-// 32 x 128K, 38% head density: about 6% faster than the chunked kernel.
+// Grouped decode.  As the per-head balanced decode does with the admitted
+// lists, the union lists of all KV streams, concatenated in stream order, are
+// cut into equal contiguous ranges, one per wave; a work-group is one wave and
+// holds no state shared with others.  The wave walks its range in 32-key
+// tiles: coalesced 128-bit loads of whole K and V rows into registers (the
+// next tiles' loads in flight while the current one is computed), staged as
+// rows in the wave's LDS area (K chunk-swizzled for the score operand, V for
+// the transposing read of the value operand).  Keys that are not to be read
+// (past the range, the stream, or an out-of-range list entry) load the
+// stream's row 0 instead -- finite data -- and are masked out of the softmax,
+// so their weights are exactly zero.  Per tile, on v_mfma_f32_16x16x32_bf16
+// (the group padded to 16 heads):
+//   scores  for each 16-key half st: S[16 keys x 16 heads] = K (A operand:
+//           lane l holds key tile_key(st, l % 16), dims 32 kk + 8 (l / 16)
+//           .. + 7) times Q^T (B: head l % 16, the same dims; q split hi +
+//           lo), so lane l receives head l % 16 and four keys of the half;
+//   softmax per head with a lazily moved reference max; weights split hi + lo;
+//   values  O[16 heads x 16 dims] += P (A: head l % 16, the lane's 8 score
+//           keys as contraction slots) times V (B: dim l % 16, the same
+//           slots, by the transposing LDS read).
+// The partial of (stream segment, head g) goes to slot (w + u) * G + g.
+// Measured on 32 x 128K, 38% head density: about 6% faster than one
+// work-group per chunk of union blocks (the kernel it replaced), and on 8192
+// KV streams x 4K (offsets in global memory) 0.91 against 1.27 ms.
 // Two waves per SIMD at either head dim.  At d = 64 a second tile in flight
 // and the uniform tile checks of the WHOLE form together took the 38% call
 // (32 x 128K) from 0.40 to 0.38 ms (6.2 to 6.5 TB/s; either alone gave at most
 // 3%).  At d = 128 (about 300 registers unconstrained, one wave per SIMD) the bound
 // costs a few spilled registers and gains 12% (32 x 128K, 38% head density:
-// 0.80 ms against 0.91 ms at one wave per SIMD and 0.86 ms for the chunked
-// kernel).
+// 0.80 ms against 0.91 ms at one wave per SIMD).
 template <int D>
 struct GqaFlowShape {
   static constexpr int NK = D / 32;             // 32-dim slabs (score product)
@@ -724,17 +331,20 @@ struct GqaFlowShape {
 // tile, scalar base addresses, and per-key tests only in a stream's last tile.
 // DENSE: every block of every stream, for every head (the dense baseline,
 // RAW logits): the list is the identity and every head mask is full.
-template <int D, int MODE, bool WHOLE, bool DENSE>
+// GS: the stream offsets and each wave's first stream come from global memory
+// (flow_scan_gqa_kernel, for more streams than LDS holds); otherwise every
+// work-group scans the counts into LDS itself.
+template <int D, int MODE, bool WHOLE, bool DENSE, bool GS>
 __global__ __launch_bounds__(64, 2) void decode_gqa_flow_kernel(CacheView c, GqaArgs a) {
   using Sh = GqaFlowShape<D>;
   constexpr int NK = Sh::NK, NV = Sh::NV, RB = Sh::RB, LPR = Sh::LPR, RPI = Sh::RPI;
   constexpr int NI = Sh::NI, TB = Sh::TB;
   __shared__ __align__(16) char s_stage[Sh::StageBytes];
-  extern __shared__ int s_start[];  // [units + 1]
+  extern __shared__ int s_start[];  // [units + 1] (LDS form)
   const int units = c.B * c.H, lane = threadIdx.x, G = a.G;
   // Exclusive prefix sums of the union counts: lane x sums a run of
   // ceil(units / 64) streams, the runs are scanned across the wave.
-  {
+  if constexpr (!GS) {
     const int per = (units + 63) / 64;
     const int u0 = min(units, lane * per), u1 = min(units, u0 + per);
     int sum = 0;
@@ -759,8 +369,9 @@ __global__ __launch_bounds__(64, 2) void decode_gqa_flow_kernel(CacheView c, Gqa
     if (lane == kWave - 1) s_start[units] = off;
     __syncthreads();
   }
-  const FlowPlan plan(s_start[units], gridDim.x, a.split);
-  if (blockIdx.x == 0) {  // for the combine
+  auto start_of = [&](int x) { return GS ? a.flow_start[x] : s_start[x]; };
+  const FlowPlan plan(start_of(units), gridDim.x, a.split);
+  if (!GS && blockIdx.x == 0) {  // for the combine
     for (int u = lane; u <= units; u += kWave) a.flow_start[u] = s_start[u];
     if (lane == 0) a.flow_info[0] = plan.N;
   }
@@ -778,7 +389,9 @@ __global__ __launch_bounds__(64, 2) void decode_gqa_flow_kernel(CacheView c, Gqa
   int p = __builtin_amdgcn_readfirstlane(plan.lo(w));
   const int pend = __builtin_amdgcn_readfirstlane(plan.lo(w + 1));
   int u = 0;  // the last stream with start[u] <= p (so start[u + 1] > p)
-  {
+  if constexpr (GS) {
+    u = __builtin_amdgcn_readfirstlane(a.flow_wave_u[w]);
+  } else {
     int hi = units - 1;
     while (u < hi) {
       const int mid = (u + hi + 1) >> 1;
@@ -787,8 +400,8 @@ __global__ __launch_bounds__(64, 2) void decode_gqa_flow_kernel(CacheView c, Gqa
     u = __builtin_amdgcn_readfirstlane(u);
   }
   while (p < pend) {
-    const int base = __builtin_amdgcn_readfirstlane(s_start[u]);
-    const int i1 = __builtin_amdgcn_readfirstlane(min(pend, s_start[u + 1]) - base);
+    const int base = __builtin_amdgcn_readfirstlane(start_of(u));
+    const int i1 = __builtin_amdgcn_readfirstlane(min(pend, start_of(u + 1)) - base);
     const int i0 = p - base;  // local blocks i0 .. i1 - 1 of stream u
     const int nblk = i1 - i0;
     const int T = c.seq_len[u / c.H];
@@ -982,7 +595,11 @@ __global__ __launch_bounds__(64, 2) void decode_gqa_flow_kernel(CacheView c, Gqa
       }
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-      // Lazy rescaling, as in the chunked kernel.
+      // Lazy rescaling: the reference max m of a head moves only when a tile
+      // raises the head's max above m + kLazyRaise (then every head moves to
+      // its own max, one wave-uniform branch).  Weights relative to m stay
+      // below e^kLazyRaise, well inside float32, and the softmax does not
+      // depend on the choice of reference.
       if (__ballot(tmax > m + kLazyRaise) != 0ull) {
         const float mn = fmaxf(m, tmax);
         const float alpha =
@@ -1074,9 +691,48 @@ __global__ __launch_bounds__(64, 2) void decode_gqa_flow_kernel(CacheView c, Gqa
     }
     p = base + i1;
     if (p < pend) {  // next non-empty stream
-      do ++u; while (s_start[u + 1] <= p);
+      do ++u; while (start_of(u + 1) <= p);
       u = __builtin_amdgcn_readfirstlane(u);
     }
+  }
+}
+
+// Offsets of the balanced grouped decode for more KV streams than LDS holds,
+// by one work-group: flow_start[u] = union blocks of the streams before u
+// (rounds of 1024 streams with a running carry), flow_info[0] = N, and
+// flow_wave_u[w] = the stream holding position lo(w) of wave w's range
+// (lo(w) = floor(w N / wn) >= start[u] exactly when w >= ceil(start[u] wn / N)).
+__global__ __launch_bounds__(1024) void flow_scan_gqa_kernel(CacheView c, GqaArgs a, int waves) {
+  __shared__ int s_w[1024 / kWave];
+  __shared__ int s_carry;
+  const int units = c.B * c.H, t = threadIdx.x;
+  if (t == 0) s_carry = 0;
+  __syncthreads();
+  for (int r = 0; r < units; r += 1024) {
+    const int u = r + t;
+    int T, cnt = 0;
+    if (u < units) gqa_stream(c, a, a.dense, u, &T, &cnt);
+    int total;
+    const int excl = wg_exclusive_scan<1024 / kWave>(cnt, s_w, &total);
+    const int carry = s_carry;
+    if (u < units) a.flow_start[u] = carry + excl;
+    __syncthreads();  // every thread has read s_carry
+    if (t == 0) s_carry = carry + total;
+    __syncthreads();
+  }
+  const int N = s_carry;
+  if (t == 0) {
+    a.flow_start[units] = N;
+    a.flow_info[0] = N;
+  }
+  __syncthreads();  // flow_start is read back below by other threads
+  const FlowPlan plan(N, waves, a.split);
+  if (plan.wn == 0) return;
+  for (int u = t; u < units; u += 1024) {
+    const long long s0 = a.flow_start[u], s1 = a.flow_start[u + 1];
+    const int w0 = (int)((s0 * plan.wn + N - 1) / N);
+    const int w1 = min(plan.wn, (int)((s1 * plan.wn + N - 1) / N));
+    for (int w = w0; w < w1; ++w) a.flow_wave_u[w] = u;
   }
 }
 
@@ -1188,21 +844,15 @@ hipError_t launch_screen_gqa(const CacheView& c, int G, const float* q, const fl
                     : screen_gqa_t<64>(c, G, q, ts, z, scale, idx, mask, cnt, ctr, words, s);
 }
 
-size_t gqa_decode_lds_bytes(int D, int split) {
-  const size_t stage = D == 128 ? (size_t)GqaShape<128>::W * GqaShape<128>::WaveBytes
-                                : (size_t)GqaShape<64>::W * GqaShape<64>::WaveBytes;
-  return stage + (size_t)split * 8;
-}
-
 // Work-groups of the balanced grouped decode: as many as are resident at once
 // (one wave each; registers and LDS set the count).
-template <int D, int MODE, bool WHOLE, bool DENSE>
+template <int D, int MODE, bool WHOLE, bool DENSE, bool GS>
 static int gqa_flow_grid(int units) {
   int per_cu = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
           &per_cu,
-          reinterpret_cast<const void*>(decode_gqa_flow_kernel<D, MODE, WHOLE, DENSE>), 64,
-          (size_t)(units + 1) * 4) != hipSuccess ||
+          reinterpret_cast<const void*>(decode_gqa_flow_kernel<D, MODE, WHOLE, DENSE, GS>), 64,
+          GS ? 0 : (size_t)(units + 1) * 4) != hipSuccess ||
       per_cu < 1)
     per_cu = 1;
   return device_cus() * min(per_cu, kMaxFlowWavesPerCU);
@@ -1210,33 +860,34 @@ static int gqa_flow_grid(int units) {
 
 template <int D, int MODE, bool DENSE>
 static hipError_t decode_gqa_t(const CacheView& c, const GqaDecode& g, hipStream_t s) {
-  const GqaArgs& a = g;
   const int units = c.B * c.H;
-  if (g.use_flow) {
+  {
     GqaArgs f = g;
-    if (c.bs >= kTileKeys) {
-      f.flow_grid = gqa_flow_grid<D, MODE, true, DENSE>(units);
-      hipLaunchKernelGGL((decode_gqa_flow_kernel<D, MODE, true, DENSE>), dim3(f.flow_grid),
-                         dim3(64), (size_t)(units + 1) * 4, s, c, f);
+    hipError_t e;
+    if (f.flow_global) {
+      f.flow_grid = c.bs >= kTileKeys ? gqa_flow_grid<D, MODE, true, DENSE, true>(units)
+                                      : gqa_flow_grid<D, MODE, false, DENSE, true>(units);
+      hipLaunchKernelGGL(flow_scan_gqa_kernel, dim3(1), dim3(1024), 0, s, c, f, f.flow_grid);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      if (c.bs >= kTileKeys)
+        hipLaunchKernelGGL((decode_gqa_flow_kernel<D, MODE, true, DENSE, true>),
+                           dim3(f.flow_grid), dim3(64), 0, s, c, f);
+      else
+        hipLaunchKernelGGL((decode_gqa_flow_kernel<D, MODE, false, DENSE, true>),
+                           dim3(f.flow_grid), dim3(64), 0, s, c, f);
+    } else if (c.bs >= kTileKeys) {
+      f.flow_grid = gqa_flow_grid<D, MODE, true, DENSE, false>(units);
+      hipLaunchKernelGGL((decode_gqa_flow_kernel<D, MODE, true, DENSE, false>),
+                         dim3(f.flow_grid), dim3(64), (size_t)(units + 1) * 4, s, c, f);
     } else {
-      f.flow_grid = gqa_flow_grid<D, MODE, false, DENSE>(units);
-      hipLaunchKernelGGL((decode_gqa_flow_kernel<D, MODE, false, DENSE>), dim3(f.flow_grid),
-                         dim3(64), (size_t)(units + 1) * 4, s, c, f);
+      f.flow_grid = gqa_flow_grid<D, MODE, false, DENSE, false>(units);
+      hipLaunchKernelGGL((decode_gqa_flow_kernel<D, MODE, false, DENSE, false>),
+                         dim3(f.flow_grid), dim3(64), (size_t)(units + 1) * 4, s, c, f);
     }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((combine_gqa_flow_kernel<D>), dim3(units * g.G), dim3(256), 0, s, c, f);
     return hipGetLastError();
   }
-  const long long grid = (long long)g.max_chunks * c.B * c.H;
-  hipLaunchKernelGGL((decode_gqa_kernel<D, MODE, DENSE>), dim3((unsigned)grid),
-                     dim3(GqaShape<D>::W * 64),
-                     gqa_decode_lds_bytes(D, g.split), s, c, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((combine_gqa_kernel<D>), dim3(c.B * c.H * g.G), dim3(1024), 0, s, c, a,
-                     DENSE);
-  return hipGetLastError();
 }
 
 template <int D>

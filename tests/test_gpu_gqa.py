@@ -103,8 +103,8 @@ def _check_dense(w, cache, split):
 
 @pytest.mark.parametrize("block", [16, 32])
 def test_gqa_balanced_decode_at_its_stream_limit(block):
-    # 6143 KV streams, the most the balanced grouped decode keeps offsets for
-    # (block 32: the whole-tile form, one or two tiles per stream).
+    # 6143 KV streams, the most whose offsets the balanced grouped decode keeps
+    # in LDS (block 32: the whole-tile form, one or two tiles per stream).
     w = to_gpu(synth.make("gqa_tiny", seed=31, T=(1, 64), B=6143, H=1, G=2, cap=64,
                           block=block))
     cache = make_cache(w)
@@ -115,19 +115,25 @@ def test_gqa_balanced_decode_at_its_stream_limit(block):
     _check_dense(w, cache, split=2)  # the balanced kernel's dense form
 
 
-def test_gqa_more_streams_than_the_balanced_decode_holds():
-    # 6400 KV streams of 1..64 tokens: more than the balanced grouped decode
-    # keeps offsets for, so eta_decode_gqa runs its chunked kernel instead.
-    w = synth.make("gqa_tiny", seed=23, T=(1, 64), B=1600, H=4, cap=64, pad="nan", block=16,
-                   D=64, G=2)
+@pytest.mark.parametrize("D,block,T", [(64, 16, (1, 64)), (64, 64, (1, 700)),
+                                       (128, 32, (1, 300))])
+def test_gqa_more_streams_than_lds_holds(D, block, T):
+    # 6400 KV streams: more than fit the balanced decode's LDS offsets, so a
+    # scan kernel writes the offsets and each wave's first stream to global
+    # memory (ranges crossing many short streams, or few longer ones).
+    w = synth.make("gqa_tiny", seed=23 + block, T=T, B=1600, H=4, cap=T[1], pad="nan",
+                   block=block, D=D, G=2)
     to_gpu(w)
     cache = make_cache(w)
     assert w.B * w.H > 6143
     c = torch.linspace(0.2, 1.4, w.Hq, device="cuda")
-    g = run_gpu_gqa(cache, w.G, w.q, bias_or_c=c, z=1.0, scale=w.scale, mode=eb.GATED, split=2)
-    st = check_gqa(w, g, W=None, bias_or_c=c, z=1.0, scale=w.scale, mode=eb.GATED)
-    note(f"  D_head {st['d_head']:.3f} D_union {st['d_union']:.3f} out_rel {st['out_rel']:.2e}")
-    _check_dense(w, cache, split=2)  # the chunked kernel's dense form
+    for split in (2, 64):
+        g = run_gpu_gqa(cache, w.G, w.q, bias_or_c=c, z=1.0, scale=w.scale, mode=eb.GATED,
+                        split=split)
+        st = check_gqa(w, g, W=None, bias_or_c=c, z=1.0, scale=w.scale, mode=eb.GATED)
+        note(f"  split {split}: D_head {st['d_head']:.3f} D_union {st['d_union']:.3f} "
+             f"out_rel {st['out_rel']:.2e}")
+    _check_dense(w, cache, split=2)  # the dense form, offsets in global memory
 
 
 @pytest.mark.parametrize("tau", [math.inf, -math.inf])

@@ -123,20 +123,22 @@ size_t decode_slots(long long units, int cap_blocks, int split) {
   return f > g ? f : g;
 }
 
-// Decode workspace: [queue counter, balanced-decode total at byte 64 |
-// chunk_start or stream offsets [units+1] | part_m | part_l | part_acc], each
+// Per-wave first streams of the balanced decode's global form.
+size_t flow_wave_table_bytes() {
+  return align256((size_t)(eta::kFlowThreads / 64) * device_cus() * eta::kFlowWGsPerCU * 4);
+}
+
+// Decode workspace: [balanced-decode total at byte 64 | stream offsets
+// [units+1] | per-wave first streams | part_m | part_l | part_acc], each
 // 256-byte aligned.
 size_t decode_ws_slots(long long units, int D, size_t slots) {
-  return 256 + align256((size_t)(units + 1) * 4) + align256(slots * 4) * 2 +
-         align256(slots * (size_t)D * 4);
+  return 256 + align256((size_t)(units + 1) * 4) + flow_wave_table_bytes() +
+         align256(slots * 4) * 2 + align256(slots * (size_t)D * 4);
 }
 size_t decode_ws(long long units, int D, int cap_blocks, int split) {
   return decode_ws_slots(units, D, decode_slots(units, cap_blocks, split));
 }
 
-#ifndef ETA_QUEUE_WGS_PER_CU
-#define ETA_QUEUE_WGS_PER_CU 8
-#endif
 
 bool bad_float(float x) { return x != x; }
 
@@ -315,9 +317,11 @@ static eta_status decode_common(const eta_cache* c, const float* q, const float*
   const int maxc = eta::ceil_div(v.cap_blocks, split);
   if ((long long)maxc * units > kMaxGrid) return fail(ETA_ERR_BAD_SHAPE, "grid too large");
   // Sparse decode runs balanced (equal ranges of all admitted blocks per
-  // wave) whenever its stream offsets fit in LDS.
-  const bool flow = !dense && units <= eta::kMaxFlowUnits &&
-                    units * (long long)v.cap_blocks < 0x7fffffffLL;
+  // wave); block positions of all streams together are int32, more than any
+  // one device holds (2^31 blocks of at least 4 keys of d >= 64: over 2 TB).
+  if (!dense && units * (long long)v.cap_blocks >= 0x7fffffffLL)
+    return fail(ETA_ERR_BAD_SHAPE, "B*H*cap_blocks must be below 2^31");
+  const bool flow = !dense;
   // A caller's workspace must be as large as the size query says (enough for
   // either path); the static scratch only needs what this call's path uses.
   const size_t slots = flow ? flow_slots(units) : grid_slots(units, v.cap_blocks, split);
@@ -335,7 +339,8 @@ static eta_status decode_common(const eta_cache* c, const float* q, const float*
   }
   char* w = static_cast<char*>(ws);
   const size_t off_start = 256;
-  const size_t off_parts = off_start + align256((size_t)(units + 1) * 4);
+  const size_t off_waves = off_start + align256((size_t)(units + 1) * 4);
+  const size_t off_parts = off_waves + flow_wave_table_bytes();
   eta::DecodeArgs a;
   a.q = q;
   a.tau = tau_gate;
@@ -351,25 +356,14 @@ static eta_status decode_common(const eta_cache* c, const float* q, const float*
   a.part_l = reinterpret_cast<float*>(w + off_parts + align256(slots * 4));
   a.part_acc = reinterpret_cast<float*>(w + off_parts + 2 * align256(slots * 4));
   a.out = out;
-  // Sparse chunks run on the flat stream-major grid (one work-group per
-  // possible chunk) unless that grid would be mostly empty work-groups: when
-  // it exceeds kQueueAboveGrid work-groups (a ragged batch padded to a long
-  // capacity), chunks come from the queue kernel instead.  Measured on MI355X:
-  // flat 507 vs queue 544 us (8 x 128K, 38%), 82 vs 128 us (512K, 10%); queue
-  // 236 vs flat 394 us (ragged 32 x 8K..64K, 10%).  Dense decode has no empty
-  // chunks and always uses the flat grid.  The queue kernel keeps the chunk
-  // table and one chunk's block list in LDS.
-  const bool queue = !dense && (long long)maxc * units > eta::kQueueAboveGrid &&
-                     units <= eta::kMaxQueueUnits &&
-                     (size_t)(units + 1) * 4 + (size_t)split * 4 <= 48 * 1024;
-  a.use_queue = queue;
-  a.queue = reinterpret_cast<int*>(w);
-  a.chunk_start = reinterpret_cast<int*>(w + off_start);
-  a.queue_grid = device_cus() * ETA_QUEUE_WGS_PER_CU;
-  a.use_flow = flow;
+  // Dense decode runs on the flat stream-major grid (one work-group per
+  // chunk); sparse decode balanced, with its offsets in LDS up to
+  // kMaxFlowUnits streams and in global memory above.
   a.flow_grid = device_cus() * eta::kFlowWGsPerCU;
-  a.flow_start = a.chunk_start;
+  a.flow_start = reinterpret_cast<int*>(w + off_start);
   a.flow_info = reinterpret_cast<int*>(w + 64);
+  a.flow_global = units > eta::kMaxFlowUnits;
+  a.flow_wave_u = reinterpret_cast<int*>(w + off_waves);
   return hip_status(eta::launch_decode(v, a, (hipStream_t)stream), "eta_decode launch");
 }
 

@@ -400,24 +400,22 @@ struct DecodeArgs {
   int mode;  // ETA_LOGIT_GATED / ETA_LOGIT_RAW
   bool dense;
   float beta, scale;
-  int split;       // blocks per chunk
+  int split;       // blocks per chunk (dense, fused), least blocks per range (balanced)
   int max_chunks;  // ceil(cap_blocks / split)
-  float* part_m;   // [B*H][max_chunks]
-  float* part_l;   // [B*H][max_chunks]
-  float* part_acc; // [B*H][max_chunks][D]
+  float* part_m;   // partials: [B*H][max_chunks] chunked, slot w + u balanced
+  float* part_l;
+  float* part_acc; // [...][D]
   float* out;
-  int* queue;        // work counter of the queue kernel
-  int* chunk_start;  // [B*H + 1] chunk offsets of the queue kernel
-  bool use_queue;    // queue kernel (else one work-group per possible chunk)
-  int queue_grid;    // work-groups of the queue kernel
-  bool use_flow;     // balanced decode: equal ranges of all admitted blocks per wave
   int flow_grid;     // work-groups of the balanced decode (kFlowThreads each)
-  int* flow_start;   // [B*H + 1] admitted-block offsets, written by the balanced decode
+  int* flow_start;   // [B*H + 1] admitted-block offsets of the balanced decode
   int* flow_info;    // [1] total admitted blocks N
+  bool flow_global;  // offsets in global memory (flow_scan_kernel), not in LDS
+  int* flow_wave_u;  // [waves] first stream of each wave's range (flow_global only)
 };
 // Work-group size and work-groups per compute unit of the balanced decode
 // (2 waves per SIMD, its occupancy: all of them are resident at once) and the
-// stream count up to which it is used (its offsets live in LDS).  Two
+// stream count up to which its work-groups scan the offsets into LDS (above,
+// a one-work-group scan kernel writes them to global memory first).  Two
 // work-groups per CU leave 256 registers per lane (about 171 used, no spills);
 // against three (168 registers, a few spilled) the 38% 128K call went from
 // 0.52 to 0.50-0.51 ms, 10% from 0.152 to 0.147, 512K from 0.274 to
@@ -425,10 +423,6 @@ struct DecodeArgs {
 constexpr int kFlowThreads = 256;
 constexpr int kFlowWGsPerCU = 2;
 constexpr int kMaxFlowUnits = 8191;
-// Streams up to which the queue kernel can be used (its chunk table lives in
-// LDS), and the flat-grid size above which it is.
-constexpr int kMaxQueueUnits = 8192;
-constexpr long long kQueueAboveGrid = 49152;
 hipError_t launch_decode(const CacheView& c, const DecodeArgs& a, hipStream_t s);
 // Fused threshold + screen + decode: the threshold's and the screen's inputs
 // and optional outputs beside the decode arguments (split = blocks per chunk

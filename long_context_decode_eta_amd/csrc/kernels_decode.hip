@@ -121,10 +121,9 @@ __device__ __forceinline__ void merge_groups(RowState<EPL>& st) {
 }
 
 // Where a chunk's block indices come from: consecutive blocks first,
-// first + 1, ... (dense), entries first .. first + nblk - 1 of the stream's
-// admitted list (copied to LDS here), or a list the caller already staged in
-// LDS (the fused screen + decode).
-enum ChunkSrc { kChunkDense = 0, kChunkList = 1, kChunkStaged = 2 };
+// first + 1, ... (dense), or a list the caller staged in LDS (the fused
+// screen + decode).
+enum ChunkSrc { kChunkDense = 0, kChunkStaged = 2 };
 
 // Attention of one chunk (chunk k of stream u, nblk blocks) by the whole
 // work-group.  The chunk's block indices sit in LDS (s_list), so no key or
@@ -144,10 +143,6 @@ __device__ __forceinline__ void chunk_attend(const CacheView& c, const DecodeArg
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane / LPR, li = lane % LPR;
 
-  if constexpr (SRC == kChunkList) {
-    const int32_t* list = a.active_idx + (size_t)u * c.cap_blocks + first;
-    for (int i = threadIdx.x; i < nblk; i += blockDim.x) s_list[i] = list[i];
-  }
   float qs[EPL];
   {
     const float* qu = a.q + (size_t)u * D + li * EPL;
@@ -318,89 +313,13 @@ __device__ void combine_slots(const DecodeArgs& a, int u, size_t slot0, int nch,
   }
 }
 
-// Per-call set-up, one work-group: chunk_start[u] = chunks of the streams
-// before u (exclusive scan; chunk_start[units] = total), the queue counter set
-// to 0, and the zero output of every stream with no chunk (T_b = 0).  Streams
-// in rounds of 1024 with a running carry.
-template <int D>
-__global__ __launch_bounds__(1024) void decode_prepare_kernel(CacheView c, DecodeArgs a) {
-  __shared__ int scan[1024];
-  __shared__ int carry;
-  const int units = c.B * c.H, t = threadIdx.x;
-  if (t == 0) {
-    carry = 0;
-    a.queue[0] = 0;
-  }
-  __syncthreads();
-  for (int base = 0; base < units; base += 1024) {
-    const int u = base + t;
-    int T, cnt;
-    const int n = u < units ? stream_chunks(c, a, u, &T, &cnt) : 0;
-    if (u < units && n == 0)
-      for (int i = 0; i < D; ++i) a.out[(size_t)u * D + i] = 0.f;
-    scan[t] = n;
-    __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-      const int add = t >= off ? scan[t - off] : 0;
-      __syncthreads();
-      scan[t] += add;
-      __syncthreads();
-    }
-    if (u < units) a.chunk_start[u] = carry + scan[t] - n;
-    __syncthreads();
-    if (t == 1023) carry += scan[1023];
-    __syncthreads();
-  }
-  if (t == 0) a.chunk_start[units] = carry;
-}
-
-// Persistent decode: every work-group repeatedly takes the next chunk from a
-// global atomic queue (so the grid never holds empty work-groups and every CU
-// stays busy until the work runs out).  The next index is fetched while the
-// current chunk is processed.  Chunk -> stream by binary search of the
-// chunk_start table held in LDS.
-template <int D, int DT, int MODE, bool DENSE>
-__global__ __launch_bounds__(256) void decode_queue_kernel(CacheView c, DecodeArgs a) {
-  extern __shared__ int s_dyn[];
-  __shared__ float s_acc[4][D];
-  __shared__ float s_ml[4][2];
-  __shared__ int s_next;
-  const int units = c.B * c.H;
-  int* s_start = s_dyn;                // units + 1
-  int* s_list = s_dyn + units + 1;     // split
-  for (int i = threadIdx.x; i <= units; i += blockDim.x) s_start[i] = a.chunk_start[i];
-  if (threadIdx.x == 0) s_next = atomicAdd(a.queue, 1);
-  __syncthreads();
-  const int total = s_start[units];
-  int item = s_next;
-  while (item < total) {
-    __syncthreads();  // everyone has read s_next
-    if (threadIdx.x == 0) s_next = atomicAdd(a.queue, 1);
-    int lo = 0, hi = units - 1;  // last u with s_start[u] <= item
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_start[mid] <= item) lo = mid; else hi = mid - 1;
-    }
-    const int u = lo, k = item - s_start[u];
-    int T, cnt;
-    stream_chunks(c, a, u, &T, &cnt);
-    const int first = k * a.split, nblk = min(a.split, cnt - first);
-    chunk_attend<D, DT, MODE, DENSE ? kChunkDense : kChunkList>(
-        c, a, u, k, T, first, nblk, first == 0 && nblk == cnt,
-        MODE == ETA_LOGIT_GATED ? a.tau[u] : 0.f, s_list, s_acc, s_ml);
-    __syncthreads();  // LDS reuse; s_next is visible
-    item = s_next;
-  }
-}
-
-// Flat-grid decode: one work-group per possible chunk, blockIdx.x =
-// u * max_chunks + (k + u % 8) mod max_chunks (a stream's chunks are
-// dispatched together, which measured faster than chunk-major order, and are
-// rotated so that every XCD gets an even share of them); work-groups past a
-// stream's last chunk exit.
-template <int D, int DT, int MODE, bool DENSE>
+// Dense decode (the baseline): one work-group per possible chunk of `split`
+// consecutive blocks, blockIdx.x = u * max_chunks + (k + u % 8) mod max_chunks
+// (a stream's chunks are dispatched together, which measured faster than
+// chunk-major order, and are rotated so that every XCD gets an even share of
+// them); work-groups past a stream's last chunk exit.  RAW logits.
+template <int D, int DT>
 __global__ __launch_bounds__(256) void decode_grid_kernel(CacheView c, DecodeArgs a) {
-  extern __shared__ int s_list[];
   __shared__ float s_acc[4][D];
   __shared__ float s_ml[4][2];
   const int u = blockIdx.x / a.max_chunks;
@@ -409,9 +328,9 @@ __global__ __launch_bounds__(256) void decode_grid_kernel(CacheView c, DecodeArg
   const int nch = stream_chunks(c, a, u, &T, &cnt);
   if (k >= nch) return;
   const int first = k * a.split, nblk = min(a.split, cnt - first);
-  chunk_attend<D, DT, MODE, DENSE ? kChunkDense : kChunkList>(
-      c, a, u, k, T, first, nblk, first == 0 && nblk == cnt,
-      MODE == ETA_LOGIT_GATED ? a.tau[u] : 0.f, s_list, s_acc, s_ml);
+  chunk_attend<D, DT, ETA_LOGIT_RAW, kChunkDense>(c, a, u, k, T, first, nblk,
+                                                  first == 0 && nblk == cnt, 0.f, nullptr,
+                                                  s_acc, s_ml);
 }
 
 // Combine: one work-group per stream with two or more chunks.
@@ -572,7 +491,10 @@ __device__ __forceinline__ int stream_blocks(const CacheView& c, const DecodeArg
   return max(0, min(a.active_cnt[u], nb));
 }
 
-template <int D, int DT, int MODE>
+// GS: the stream offsets and each wave's first stream come from global memory
+// (flow_scan_kernel, for more streams than LDS holds); otherwise every
+// work-group scans the counts into LDS itself.
+template <int D, int DT, int MODE, bool GS>
 __global__ __launch_bounds__(kFlowThreads, kFlowWGsPerCU) void decode_flow_kernel(CacheView c,
                                                                                   DecodeArgs a) {
   constexpr int EPL = Elt<DT>::kPer16B;
@@ -591,7 +513,7 @@ __global__ __launch_bounds__(kFlowThreads, kFlowWGsPerCU) void decode_flow_kerne
   // Exclusive prefix sums of the admitted counts, every work-group for itself:
   // thread t sums its run of ceil(units / 256) streams, the runs are scanned
   // across the work-group, then written back as offsets.
-  {
+  if constexpr (!GS) {
     const int per = (units + kFlowThreads - 1) / kFlowThreads;
     const int u0 = min(units, tid * per), u1 = min(units, u0 + per);
     int sum = 0;
@@ -618,8 +540,9 @@ __global__ __launch_bounds__(kFlowThreads, kFlowWGsPerCU) void decode_flow_kerne
     if (tid == kFlowThreads - 1) s_start[units] = off;
     __syncthreads();
   }
-  const FlowPlan plan(s_start[units], waves, a.split);
-  if (blockIdx.x == 0) {  // for the combine
+  auto start_of = [&](int x) { return GS ? a.flow_start[x] : s_start[x]; };
+  const FlowPlan plan(start_of(units), waves, a.split);
+  if (!GS && blockIdx.x == 0) {  // for the combine
     for (int u = tid; u <= units; u += kFlowThreads) a.flow_start[u] = s_start[u];
     if (tid == 0) a.flow_info[0] = plan.N;
   }
@@ -630,7 +553,9 @@ __global__ __launch_bounds__(kFlowThreads, kFlowWGsPerCU) void decode_flow_kerne
   // one partial per stream segment, into slot slot_base + u.
   auto walk = [&](int p, const int pend, const size_t slot_base) {
     int u = 0;  // the last stream with start[u] <= p (so start[u + 1] > p)
-    {
+    if constexpr (GS) {
+      u = a.flow_wave_u[w];
+    } else {
       int hi = units - 1;
       while (u < hi) {
         const int mid = (u + hi + 1) >> 1;
@@ -638,8 +563,8 @@ __global__ __launch_bounds__(kFlowThreads, kFlowWGsPerCU) void decode_flow_kerne
       }
     }
     while (p < pend) {
-      const int base = s_start[u];
-      const int i0 = p - base, i1 = min(pend, s_start[u + 1]) - base;  // local blocks
+      const int base = start_of(u);
+      const int i0 = p - base, i1 = min(pend, start_of(u + 1)) - base;  // local blocks
       const int T = c.seq_len[u / c.H];
       const int nb = (T + c.bs - 1) >> c.log2bs;
       const int32_t* list = a.active_idx + (size_t)u * c.cap_blocks + i0;
@@ -716,11 +641,49 @@ __global__ __launch_bounds__(kFlowThreads, kFlowWGsPerCU) void decode_flow_kerne
       }
       p = base + i1;
       if (p < pend)  // next non-empty stream
-        do ++u; while (s_start[u + 1] <= p);
+        do ++u; while (start_of(u + 1) <= p);
     }
   };
 
   walk(plan.lo(w), plan.lo(w + 1), (size_t)w);
+}
+
+// Offsets of the balanced decode for more streams than LDS holds, by one
+// work-group: flow_start[u] = admitted blocks of the streams before u (rounds
+// of 1024 streams with a running carry), flow_info[0] = N, and flow_wave_u[w]
+// = the stream holding position lo(w) of wave w's range (lo(w) =
+// floor(w N / wn) >= start[u] exactly when w >= ceil(start[u] wn / N)).
+__global__ __launch_bounds__(1024) void flow_scan_kernel(CacheView c, DecodeArgs a, int waves) {
+  __shared__ int s_w[1024 / kWave];
+  __shared__ int s_carry;
+  const int units = c.B * c.H, t = threadIdx.x;
+  if (t == 0) s_carry = 0;
+  __syncthreads();
+  for (int r = 0; r < units; r += 1024) {
+    const int u = r + t;
+    const int cnt = u < units ? stream_blocks(c, a, u) : 0;
+    int total;
+    const int excl = wg_exclusive_scan<1024 / kWave>(cnt, s_w, &total);
+    const int carry = s_carry;
+    if (u < units) a.flow_start[u] = carry + excl;
+    __syncthreads();  // every thread has read s_carry
+    if (t == 0) s_carry = carry + total;
+    __syncthreads();
+  }
+  const int N = s_carry;
+  if (t == 0) {
+    a.flow_start[units] = N;
+    a.flow_info[0] = N;
+  }
+  __syncthreads();  // flow_start is read back below by other threads
+  const FlowPlan plan(N, waves, a.split);
+  if (plan.wn == 0) return;
+  for (int u = t; u < units; u += 1024) {
+    const long long s0 = a.flow_start[u], s1 = a.flow_start[u + 1];
+    const int w0 = (int)((s0 * plan.wn + N - 1) / N);
+    const int w1 = min(plan.wn, (int)((s1 * plan.wn + N - 1) / N));
+    for (int w = w0; w < w1; ++w) a.flow_wave_u[w] = u;
+  }
 }
 
 // Combine of the balanced decode: one work-group per stream, merging the
@@ -745,33 +708,31 @@ __global__ __launch_bounds__(kCombWaves * kWave) void combine_flow_kernel(CacheV
 template <int D, int DT, int MODE, bool DENSE>
 static hipError_t decode_t(const CacheView& c, const DecodeArgs& a, hipStream_t s) {
   const int units = c.B * c.H;
-  const size_t list_bytes = DENSE ? 0 : (size_t)a.split * 4;
   hipError_t e;
   if constexpr (!DENSE) {
-    if (a.use_flow) {
-      hipLaunchKernelGGL((decode_flow_kernel<D, DT, MODE>), dim3(a.flow_grid), dim3(kFlowThreads),
-                         (size_t)(units + 1) * 4, s, c, a);
+    // balanced: offsets scanned into LDS, or for more streams written to
+    // global memory by the scan kernel first
+    if (a.flow_global) {
+      hipLaunchKernelGGL(flow_scan_kernel, dim3(1), dim3(1024), 0, s, c, a,
+                         a.flow_grid * (kFlowThreads / kWave));
       if ((e = hipGetLastError()) != hipSuccess) return e;
-      hipLaunchKernelGGL((combine_flow_kernel<D>), dim3(units), dim3(kCombWaves * kWave), 0, s,
-                         c, a);
-      return hipGetLastError();
+      hipLaunchKernelGGL((decode_flow_kernel<D, DT, MODE, true>), dim3(a.flow_grid),
+                         dim3(kFlowThreads), 0, s, c, a);
+    } else {
+      hipLaunchKernelGGL((decode_flow_kernel<D, DT, MODE, false>), dim3(a.flow_grid),
+                         dim3(kFlowThreads), (size_t)(units + 1) * 4, s, c, a);
     }
-  }
-  if (a.use_queue) {
-    // chunk table and queue counter for the persistent grid
-    hipLaunchKernelGGL((decode_prepare_kernel<D>), dim3(1), dim3(1024), 0, s, c, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const size_t lds = (size_t)(units + 1) * 4 + list_bytes;
-    hipLaunchKernelGGL((decode_queue_kernel<D, DT, MODE, DENSE>), dim3(a.queue_grid), dim3(256),
-                       lds, s, c, a);
+    hipLaunchKernelGGL((combine_flow_kernel<D>), dim3(units), dim3(kCombWaves * kWave), 0, s, c,
+                       a);
+    return hipGetLastError();
   } else {
     const long long grid = (long long)a.max_chunks * units;
-    hipLaunchKernelGGL((decode_grid_kernel<D, DT, MODE, DENSE>), dim3((unsigned)grid), dim3(256),
-                       list_bytes, s, c, a);
+    hipLaunchKernelGGL((decode_grid_kernel<D, DT>), dim3((unsigned)grid), dim3(256), 0, s, c, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((combine_kernel<D>), dim3(units), dim3(kCombWaves * kWave), 0, s, c, a);
+    return hipGetLastError();
   }
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((combine_kernel<D>), dim3(units), dim3(kCombWaves * kWave), 0, s, c, a);
-  return hipGetLastError();
 }
 
 template <int D, int DT>

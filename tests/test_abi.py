@@ -134,10 +134,10 @@ def test_decode_noalloc_validation(lib):
     assert L.eta_decode_noalloc(*args(out=None)) == eb.ETA_ERR_NULL_PTR
     assert L.eta_decode_noalloc(*args(c=cache(batch=0, k=None, v=None, mu=None, var=None,
                                                 maxnorm=None, seq_len=None))) == eb.ETA_OK
-    # 8192 streams take the chunk grid: one partial per possible chunk (16 per
-    # stream here) is 64 MiB, beyond the 8 MiB static scratch; refused on the
+    # 16384 streams: one partial slot per stream beyond the waves' (520 bytes
+    # each at d 128) is over 8 MiB, beyond the static scratch; refused on the
     # host, before any HIP call.
-    big = cache(batch=8192, heads=1, head_dim=128, block=4, cap_tokens=64)
+    big = cache(batch=16384, heads=1, head_dim=128, block=4, cap_tokens=64)
     assert L.eta_decode_noalloc(*args(c=big, split=1)) == eb.ETA_ERR_CAPACITY
     assert "scratch" in err(L)
 

@@ -5,8 +5,8 @@ Runs the HIP path (libeta.so) through its C ABI.  Cases: the hand example
 T=2048, b=16, z=1.5, frozen tau), ragged lengths with NaN-filled unused slots
 for every block size and head size, threshold extremes, split-size
 invariance, determinism, the threshold predictor, the dense baseline, many
-short streams, and more streams than the balanced decode handles (queue and
-flat-grid scheduling).
+short streams, and more streams than the balanced decode scans into LDS (its
+offsets then come from a scan kernel in global memory).
 """
 import json
 import math
@@ -217,8 +217,8 @@ def test_balanced_decode_many_short_streams():
 
 
 def test_balanced_decode_at_its_stream_limit():
-    # 8191 streams, the most the balanced decode keeps offsets for (32 KiB of
-    # LDS per work-group): it still runs, and every stream matches the oracle.
+    # 8191 streams, the most whose offsets the balanced decode keeps in LDS
+    # (32 KiB per work-group): it still runs, and every stream matches the oracle.
     w = to_gpu(synth.make("ragged", seed=29, T=(1, 64), B=8191, H=1, D=64, cap=64, block=16,
                           pad="nan"))
     cache = make_cache(w)
@@ -231,10 +231,9 @@ def test_balanced_decode_at_its_stream_limit():
 
 @pytest.mark.parametrize("split", [1, 8])
 def test_more_streams_than_the_balanced_decode_holds(split):
-    # 8192 streams: more than the balanced decode keeps offsets for, so
-    # eta_decode schedules chunks instead -- from its work queue when the flat
-    # grid would be mostly empty (8192 x 8 work-groups at one block per
-    # chunk), else on the flat grid (8192 x 1).
+    # 8192 streams: more than the balanced decode scans into LDS, so a scan
+    # kernel writes the stream offsets and each wave's first stream to global
+    # memory; ranges of one or eight blocks at least, over many short streams.
     w = to_gpu(synth.make("ragged", seed=19, T=(1, 128), B=512, H=16, D=64, cap=128, pad="nan"))
     cache = make_cache(w)
     assert w.B * w.H > 8191

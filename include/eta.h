@@ -180,8 +180,9 @@ eta_status eta_screen(const eta_cache* c, const float* q, const float* tau_scree
  * admitted blocks, one per wavefront; every (range, stream) piece produces a
  * partial (max, sum, weighted V) and one combine pass merges each stream's
  * partials by log-sum-exp into out [batch][heads][head_dim] float32 (device).
- * Above 8191 streams the per-stream lists are cut into chunks of
- * blocks_per_split blocks instead, one work-group each.
+ * Above 8191 streams a one-work-group scan kernel first writes the stream
+ * offsets to the workspace.  batch * heads * cap_blocks must be below 2^31
+ * (ETA_ERR_BAD_SHAPE).
  * Logits, with S_s = scale <q, k_s>:
  *   ETA_LOGIT_GATED  l_s = S_s sigmoid(beta (S_s - tau_gate[b][h])) for
  *                    s != T_b - 1, and l_{T_b-1} = S_{T_b-1} (the query's own
@@ -204,10 +205,10 @@ eta_status eta_decode(const eta_cache* c, const float* q, const float* tau_gate,
  * graph capture, tight serving loops, harnesses that forbid hipMalloc): no
  * workspace argument, the same kernels and the same results as eta_decode.
  * Its scratch is a static device array of 8 MiB that every device the
- * library runs on holds until the process ends; that covers every call on
- * the balanced path (at most 8191 streams, head_dim <= 128).  A call that
- * would need more (more streams: the chunk grid keeps a partial per possible
- * chunk) returns ETA_ERR_CAPACITY and launches nothing.  All such calls on
+ * library runs on holds until the process ends; that covers every call of up
+ * to about 13000 streams at head_dim <= 128 (one partial slot per wave and
+ * per stream).  A call that would need more returns ETA_ERR_CAPACITY and
+ * launches nothing.  All such calls on
  * one device share that array, so calls that overlap in time on one device
  * (two streams, two host threads) race: the caller serialises them.  Nothing
  * in the array needs clearing between calls.

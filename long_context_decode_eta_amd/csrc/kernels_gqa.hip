@@ -334,7 +334,7 @@ struct GqaFlowShape {
 // GS: the stream offsets and each wave's first stream come from global memory
 // (flow_scan_gqa_kernel, for more streams than LDS holds); otherwise every
 // work-group scans the counts into LDS itself.
-template <int D, int MODE, bool WHOLE, bool DENSE, bool GS>
+template <int D, int MODE, bool WHOLE, bool GS, bool DENSE>
 __global__ __launch_bounds__(64, 2) void decode_gqa_flow_kernel(CacheView c, GqaArgs a) {
   using Sh = GqaFlowShape<D>;
   constexpr int NK = Sh::NK, NV = Sh::NV, RB = Sh::RB, LPR = Sh::LPR, RPI = Sh::RPI;
@@ -846,12 +846,12 @@ hipError_t launch_screen_gqa(const CacheView& c, int G, const float* q, const fl
 
 // Work-groups of the balanced grouped decode: as many as are resident at once
 // (one wave each; registers and LDS set the count).
-template <int D, int MODE, bool WHOLE, bool DENSE, bool GS>
+template <int D, int MODE, bool WHOLE, bool GS, bool DENSE>
 static int gqa_flow_grid(int units) {
   int per_cu = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
           &per_cu,
-          reinterpret_cast<const void*>(decode_gqa_flow_kernel<D, MODE, WHOLE, DENSE, GS>), 64,
+          reinterpret_cast<const void*>(decode_gqa_flow_kernel<D, MODE, WHOLE, GS, DENSE>), 64,
           GS ? 0 : (size_t)(units + 1) * 4) != hipSuccess ||
       per_cu < 1)
     per_cu = 1;
@@ -865,23 +865,23 @@ static hipError_t decode_gqa_t(const CacheView& c, const GqaDecode& g, hipStream
     GqaArgs f = g;
     hipError_t e;
     if (f.flow_global) {
-      f.flow_grid = c.bs >= kTileKeys ? gqa_flow_grid<D, MODE, true, DENSE, true>(units)
-                                      : gqa_flow_grid<D, MODE, false, DENSE, true>(units);
+      f.flow_grid = c.bs >= kTileKeys ? gqa_flow_grid<D, MODE, true, true, DENSE>(units)
+                                      : gqa_flow_grid<D, MODE, false, true, DENSE>(units);
       hipLaunchKernelGGL(flow_scan_gqa_kernel, dim3(1), dim3(1024), 0, s, c, f, f.flow_grid);
       if ((e = hipGetLastError()) != hipSuccess) return e;
       if (c.bs >= kTileKeys)
-        hipLaunchKernelGGL((decode_gqa_flow_kernel<D, MODE, true, DENSE, true>),
+        hipLaunchKernelGGL((decode_gqa_flow_kernel<D, MODE, true, true, DENSE>),
                            dim3(f.flow_grid), dim3(64), 0, s, c, f);
       else
-        hipLaunchKernelGGL((decode_gqa_flow_kernel<D, MODE, false, DENSE, true>),
+        hipLaunchKernelGGL((decode_gqa_flow_kernel<D, MODE, false, true, DENSE>),
                            dim3(f.flow_grid), dim3(64), 0, s, c, f);
     } else if (c.bs >= kTileKeys) {
-      f.flow_grid = gqa_flow_grid<D, MODE, true, DENSE, false>(units);
-      hipLaunchKernelGGL((decode_gqa_flow_kernel<D, MODE, true, DENSE, false>),
+      f.flow_grid = gqa_flow_grid<D, MODE, true, false, DENSE>(units);
+      hipLaunchKernelGGL((decode_gqa_flow_kernel<D, MODE, true, false, DENSE>),
                          dim3(f.flow_grid), dim3(64), (size_t)(units + 1) * 4, s, c, f);
     } else {
-      f.flow_grid = gqa_flow_grid<D, MODE, false, DENSE, false>(units);
-      hipLaunchKernelGGL((decode_gqa_flow_kernel<D, MODE, false, DENSE, false>),
+      f.flow_grid = gqa_flow_grid<D, MODE, false, false, DENSE>(units);
+      hipLaunchKernelGGL((decode_gqa_flow_kernel<D, MODE, false, false, DENSE>),
                          dim3(f.flow_grid), dim3(64), (size_t)(units + 1) * 4, s, c, f);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;

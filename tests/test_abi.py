@@ -122,6 +122,10 @@ def test_decode_validation(lib):
     assert L.eta_decode(*args(mode=1, tau=None, wsb=ws - 4)) == eb.ETA_ERR_WORKSPACE
     assert L.eta_dense_decode(cache(), FAKE, 0.088, 16, FAKE, ws - 4, FAKE, None) == eb.ETA_ERR_WORKSPACE
     assert L.eta_dense_decode(cache(), FAKE, -1.0, 16, FAKE, ws, FAKE, None) == eb.ETA_ERR_BAD_ARG
+    # block positions of all streams together must fit int32: 2^14 streams x 2^17 blocks
+    huge = cache(batch=1024, heads=16, head_dim=64, block=4, cap_tokens=1 << 19)
+    assert L.eta_decode(*args(c=huge, wsb=1 << 62)) == eb.ETA_ERR_BAD_SHAPE
+    assert "2^31" in err(L)
 
 
 def test_decode_noalloc_validation(lib):
@@ -236,6 +240,9 @@ def test_gqa_validation(lib):
                                   None) == eb.ETA_ERR_WORKSPACE
     assert L.eta_dense_decode_gqa(cache(kv_dtype=eb.DT_F32), 8, FAKE, 0.088, 16, FAKE, ws, FAKE,
                                   None) == eb.ETA_ERR_BAD_ARG
+    huge = cache(batch=4096, heads=4, head_dim=64, block=4, cap_tokens=1 << 19)
+    assert dec(c=huge, wsb=1 << 62) == eb.ETA_ERR_BAD_SHAPE
+    assert "2^31" in err(L)
 
 
 def test_prefill_validation(lib):

@@ -123,6 +123,7 @@ def test_gqa_more_streams_than_lds_holds(D, block, T):
     # memory (ranges crossing many short streams, or few longer ones).
     w = synth.make("gqa_tiny", seed=23 + block, T=T, B=1600, H=4, cap=T[1], pad="nan",
                    block=block, D=D, G=2)
+    w.seq_len[::7] = 0  # empty sequences among them (zero outputs)
     to_gpu(w)
     cache = make_cache(w)
     assert w.B * w.H > 6143

@@ -345,8 +345,9 @@ __device__ __forceinline__ float block_score(const CacheView& c, int u, int j, b
 // ---------------------------------------------------------------------------
 // Eq. 1 threshold of one (sequence, head), tau = sum_j q_j W[j][h] + bias[h]
 // over the n = H*D entries of the sequence's query, by the 256 threads of a
-// work-group in one fixed order shared by the threshold kernel and the fused
-// screen + decode (so both produce the same bits): thread t adds q_j W[j][h]
+// work-group in one fixed order, which the threshold kernel keeps for all the
+// heads it sums at once (so the fused screen + decode, which calls this, and
+// the threshold kernel produce the same bits): thread t adds q_j W[j][h]
 // for j = t, t + 256, ... in that order (fmaf, eight loads in flight), the 64
 // lanes of a wave are summed by an xor butterfly (every lane ends with the
 // same bits), the four wave sums as (w0 + w1) + (w2 + w3), the bias last.

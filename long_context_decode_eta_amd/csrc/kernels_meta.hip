@@ -215,19 +215,85 @@ __global__ __launch_bounds__(256) void block_meta_kernel(CacheView c, int first,
 }
 
 // ---------------------------------------------------------------------------
-// Threshold (Eq. 1): one work-group of 256 threads per (sequence, head), in
-// the fixed order of tau_of_head (the fused screen + decode computes the
-// same bits).
+// Threshold (Eq. 1) of up to kTauHeads heads of one sequence per work-group
+// of kTauThreads threads, in the summation order of tau_of_head (the fused
+// screen + decode computes the same bits): thread t keeps one partial sum per
+// head of the residue class j = t, t + 256, ... (fmaf in increasing j, the
+// loads of eight j in flight), reading the heads' entries of row j of W, which
+// are contiguous (one work-group per (sequence, head) reading column h would
+// touch a cache line per entry); then per head the xor
+// butterfly over each wave, the four wave sums as (w0 + w1) + (w2 + w3), and
+// the bias.  W == NULL (frozen thresholds) gives bias[h] alone.  VEC: W is
+// 16-byte aligned and H a multiple of 4, so a lane reads its heads of a row as
+// 16-byte loads (a quarter of the cache-line requests of 4-byte loads).
+constexpr int kTauHeads = 8;
+template <bool VEC>
 __global__ __launch_bounds__(kTauThreads) void predict_kernel(int H, int D, const float* q,
                                                               const float* W, const float* bias,
                                                               float a, float* tau,
                                                               float* tau_screen) {
-  __shared__ float s_red[kTauThreads / kWave];
-  const int u = blockIdx.x, b = u / H, h = u % H;
-  const float v = tau_of_head(q + (size_t)b * H * D, W, bias, H, H * D, h, s_red);
-  if (threadIdx.x == 0) {
-    tau[u] = v;
-    tau_screen[u] = v - a;
+  __shared__ float s_red[kTauThreads / kWave][kTauHeads];
+  const int chunks = ceil_div(H, kTauHeads);
+  const int b = blockIdx.x / chunks, h0 = (blockIdx.x % chunks) * kTauHeads;
+  const int nh = min(kTauHeads, H - h0);
+  const int t = threadIdx.x, wave = t / kWave;
+  if (W) {
+    const int n = H * D;
+    const float* qb = q + (size_t)b * n;
+    float acc[kTauHeads];
+#pragma unroll
+    for (int e = 0; e < kTauHeads; ++e) acc[e] = 0.f;
+    int j = t;
+    for (; j + 7 * kTauThreads < n; j += 8 * kTauThreads) {
+      float qv[8], wv[8][kTauHeads];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        qv[r] = qb[j + r * kTauThreads];
+        const float* wr = W + (size_t)(j + r * kTauThreads) * H + h0;
+        if constexpr (VEC) {
+          // nh is a multiple of 4 here (h0 is a multiple of 8 and H of 4)
+#pragma unroll
+          for (int e4 = 0; e4 < kTauHeads; e4 += 4) {
+            const float4 x = e4 < nh ? *reinterpret_cast<const float4*>(wr + e4)
+                                     : make_float4(0.f, 0.f, 0.f, 0.f);
+            wv[r][e4] = x.x;
+            wv[r][e4 + 1] = x.y;
+            wv[r][e4 + 2] = x.z;
+            wv[r][e4 + 3] = x.w;
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < kTauHeads; ++e) wv[r][e] = e < nh ? wr[e] : 0.f;
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+#pragma unroll
+        for (int e = 0; e < kTauHeads; ++e) acc[e] = fmaf(qv[r], wv[r][e], acc[e]);
+      }
+    }
+    for (; j < n; j += kTauThreads) {
+      const float* wr = W + (size_t)j * H + h0;
+#pragma unroll
+      for (int e = 0; e < kTauHeads; ++e) acc[e] = fmaf(qb[j], e < nh ? wr[e] : 0.f, acc[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < kTauHeads; ++e) {
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) acc[e] += __shfl_xor(acc[e], m, kWave);
+    }
+    if ((t & (kWave - 1)) == 0) {
+#pragma unroll
+      for (int e = 0; e < kTauHeads; ++e) s_red[wave][e] = acc[e];
+    }
+    __syncthreads();
+  }
+  if (t < nh) {
+    const int h = h0 + t;
+    const float v = W ? ((s_red[0][t] + s_red[1][t]) + (s_red[2][t] + s_red[3][t])) + bias[h]
+                      : bias[h];
+    tau[(size_t)b * H + h] = v;
+    tau_screen[(size_t)b * H + h] = v - a;
   }
 }
 
@@ -274,8 +340,13 @@ hipError_t launch_block_meta(const CacheView& c, int first, int n, hipStream_t s
 
 hipError_t launch_predict(int B, int H, int D, const float* q, const float* W, const float* bias,
                           float a, float* tau, float* tau_screen, hipStream_t s) {
-  hipLaunchKernelGGL(predict_kernel, dim3(B * H), dim3(kTauThreads), 0, s, H, D, q, W, bias, a,
-                     tau, tau_screen);
+  const dim3 grid(B * ceil_div(H, kTauHeads));
+  if (H % 4 == 0 && reinterpret_cast<uintptr_t>(W) % 16 == 0)
+    hipLaunchKernelGGL(predict_kernel<true>, grid, dim3(kTauThreads), 0, s, H, D, q, W, bias, a,
+                       tau, tau_screen);
+  else
+    hipLaunchKernelGGL(predict_kernel<false>, grid, dim3(kTauThreads), 0, s, H, D, q, W, bias, a,
+                       tau, tau_screen);
   return hipGetLastError();
 }
 

@@ -181,6 +181,26 @@ def test_predictor_dynamic_and_frozen():
             close(ts.cpu().numpy(), tsc, 1e-5, "tau_screen", atol)
 
 
+def test_predictor_same_bits_for_any_alignment_of_W():
+    # W read with 16-byte loads (aligned, H a multiple of 4) or 4-byte loads
+    # (W one float off alignment) sums in the same order: identical bits.
+    rng = np.random.default_rng(12)
+    B, H, D = 4, 32, 64
+    q = torch.from_numpy(rng.standard_normal((B, H, D)).astype(np.float32)).cuda()
+    Wn = (rng.standard_normal((H * D, H)) / math.sqrt(D)).astype(np.float32)
+    bias = torch.from_numpy(rng.standard_normal(H).astype(np.float32)).cuda()
+    flat = torch.zeros(H * D * H + 4, device="cuda")
+    outs = []
+    for off in (0, 1):
+        W = flat[off:off + H * D * H].view(H * D, H)
+        W.copy_(torch.from_numpy(Wn))
+        assert (W.data_ptr() % 16 == 0) == (off == 0)
+        tg = torch.zeros((B, H), device="cuda"); ts = torch.zeros_like(tg)
+        eb.predict_tau(q, W, bias, 0.25, tg, ts)
+        outs.append((tg.clone(), ts.clone()))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
 def test_predictor_zero_init():
     q = torch.randn((2, 4, 64), device="cuda")
     W = torch.zeros((256, 4), device="cuda")

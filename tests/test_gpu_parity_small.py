@@ -157,7 +157,10 @@ def test_split_invariance_and_determinism():
 
 def test_predictor_dynamic_and_frozen():
     rng = np.random.default_rng(5)
-    for B, H, D in [(1, 4, 64), (8, 16, 128), (3, 5, 64), (2, 256, 64)]:
+    # H = 12 and 20 end in a partial chunk of 4 heads (16-byte loads), H = 7
+    # and 5 use 4-byte loads.
+    for B, H, D in [(1, 4, 64), (8, 16, 128), (3, 5, 64), (2, 256, 64), (2, 12, 64),
+                    (3, 20, 64), (2, 7, 128)]:
         q = rng.standard_normal((B, H, D)).astype(np.float32)
         W = (rng.standard_normal((H * D, H)) / math.sqrt(D)).astype(np.float32)
         bias = rng.standard_normal(H).astype(np.float32)

@@ -64,6 +64,30 @@ MUTANTS = {
                           "int bb = uq / Hq, kv = (uq % Hq) % Hkv;", 2),
     "gqa_union_counts_first_head": ("for (int g = 0; g < G; ++g) on |= active",
                                     "for (int g = 0; g < 1; ++g) on |= active"),
+    "gqa_union_intersection": ("uint8_t on = 0;\n      for (int g = 0; g < G; ++g) on |= active",
+                               "uint8_t on = 1;\n      for (int g = 0; g < G; ++g) on &= active"),
+    "values_from_keys": ("out[i] += w * elem(V, dtype, (size_t)s * d + i);",
+                         "out[i] += w * elem(K, dtype, (size_t)s * d + i);", 2),
+    "attend_unscaled": ("    S *= scale;\n    double l = S;", "    double l = S;"),
+    "dense_unscaled": ("S[s] = scale * x;", "S[s] = x;"),
+    "attend_denominator_counts_keys": ("    double w = exp(logit[s] - top);\n    den += w;",
+                                       "    double w = exp(logit[s] - top);\n    den += 1.0;"),
+    "predictor_first_sequence_only": ("(double)q[(size_t)bb * H * d + j]", "(double)q[(size_t)j]"),
+    "calibration_count_rounded_down": ("long long k = (long long)floor(want + 0.5);",
+                                       "long long k = (long long)floor(want);"),
+    "ceiling_norm_from_mean": ("qq += qi * qi;", "qq += qi * mu[i];"),
+    "maxnorm_of_last_key": ("if (n > best) best = n;", "best = n;"),
+    "variance_about_zero": ("double x = elem(K, dtype, (size_t)(j * b + r) * d + i) - m;",
+                            "double x = elem(K, dtype, (size_t)(j * b + r) * d + i);"),
+    "meta_partial_block_counted": ("int nbc = T / b;\n  for (int j = 0; j < nbc; ++j) {",
+                                   "int nbc = (T + b - 1) / b;\n  for (int j = 0; j < nbc; ++j) {"),
+    "prefill_values_from_keys": ("o[i] += w * elem(Vu, dtype, (size_t)s * d + i);",
+                                 "o[i] += w * elem(Ku, dtype, (size_t)s * d + i);"),
+    "prefill_unscaled": ("      S *= scale;\n      double m =", "      double m ="),
+    "prefill_gate_on_raw_dot": ("double m = 1.0 / (1.0 + exp(-beta * (S - tt)));",
+                                "double m = 1.0 / (1.0 + exp(-beta * (S / scale - tt)));"),
+    "prefill_threshold_of_next_row": ("double tt = tau[row];",
+                                      "double tt = tau[t + 1 < T ? row + 1 : row];"),
 }
 
 

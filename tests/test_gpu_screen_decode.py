@@ -10,8 +10,9 @@ against the oracle only, outputs within the cache dtype's bar and the 1e-5
 internal bar).  Cases: the hand example, the tiny fp32 workload, ragged
 lengths around block and chunk boundaries with an empty stream and NaN-filled
 unused slots, every chunk size shape (1, 3, 8, 32 blocks), both logit modes,
-threshold extremes and offsets, 40 heads, determinism, and the single 32K sequence at its full size
-(all 16 heads against the oracle) at 10%, 38% and 70% density.
+threshold extremes and offsets, 40 heads, determinism, streams of over a
+thousand blocks, and the single 32K sequence at its full size (all 16 heads
+against the oracle) at 10%, 38% and 70% density.
 """
 import math
 
@@ -98,6 +99,29 @@ def test_ragged_edges(kv, D, block):
             assert not np.isnan(g.out).any()
             assert np.all(g.out[0] == 0)  # the empty stream
     note(f"  density {st['density']:.3f} out_rel {st['out_rel']:.2e}")
+
+
+@pytest.mark.parametrize("cap", [4096, 4500])
+def test_long_block_lists(cap):
+    # Block 4 and up to 4500 positions: 1024 and 1125 blocks per stream (128
+    # and 141 chunks of 8), ragged lengths up to the capacity, an empty stream.
+    lens = [0, 5, 2049, cap - 3, cap]
+    w = synth.make("tiny", seed=41, T=lens, B=len(lens), H=3, cap=cap, pad="nan", block=4)
+    to_gpu(w)
+    cache = make_cache(w)
+    rng = np.random.default_rng(5)
+    W = torch.from_numpy((rng.standard_normal((3 * 64, 3)) / 8.0).astype(np.float32)).cuda()
+    c = torch.tensor([0.2, 0.6, 1.0], dtype=torch.float32, device="cuda")
+    for mode in (eb.GATED, eb.RAW):
+        s = run_gpu(cache, w.q, W=W, bias_or_c=c, z=1.0, scale=w.scale, mode=mode)
+        for chunk in (8, 32):
+            g = run_gpu_fused(cache, w.q, W=W, bias_or_c=c, z=1.0, scale=w.scale, mode=mode,
+                              chunk=chunk, build_meta=False)
+            _same_as_separate(g, s)
+            st = check_against_oracle(w, g, cache, W=W, bias_or_c=c, z=1.0, scale=w.scale,
+                                      mode=mode, check_meta=False)
+            assert np.all(g.out[0] == 0)  # the empty stream
+    note(f"  cap {cap}: density {st['density']:.3f} out_rel {st['out_rel']:.2e}")
 
 
 @pytest.mark.parametrize("a", [-0.5, 0.7])

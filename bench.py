@@ -79,6 +79,8 @@ def parse():
                     help="run only the gated prefill section and print its JSON")
     ap.add_argument("--gqa-only", action="store_true",
                     help="run only the grouped-query section and print its JSON")
+    ap.add_argument("--gqa-dim", type=int, default=64, choices=(64, 128),
+                    help="head dim of the --gqa-only run (and of its counter summary)")
     ap.add_argument("--gqa-rho", default="0.38,0.25,0.10",
                     help="head densities of the grouped-query section")
     ap.add_argument("--configs", default="ctx512k,ragged,ctx32k",
@@ -270,7 +272,11 @@ def summarize_counters(args):
         # dense baseline shares the combine kernel, so that row averages both.
         if any(short.startswith(f"eta::{p}<") for p in parts) and not short.endswith("true>"):
             total += rd + wr
-    workload = "gqa128k" if gqa else args.workload + ("_fused" if fused else "")
+    # the grouped workload is named by the head dim its decode kernel was built for
+    gqa_d128 = gqa and any(k.startswith("void eta::decode_gqa_flow_kernel<128,")
+                           for k, c, v in frows)
+    workload = (("gqa128k_d128" if gqa_d128 else "gqa128k") if gqa
+                else args.workload + ("_fused" if fused else ""))
     path = GQA_COUNTERS if gqa else COUNTERS
     cj = json.load(open(path)) if os.path.exists(path) else {}
     files = GQA_SRC if gqa else DECODE_SRC
@@ -620,7 +626,7 @@ def main():
         return
     if args.gqa_only:
         print(json.dumps(gqa_bench(torch, np, eb, synth, args.steps, args.warmup, args.seed,
-                                   gqa_rhos)), flush=True)
+                                   gqa_rhos, D=args.gqa_dim)), flush=True)
         return
     # room for the appends of the upkeep measurement (4 blocks per stream)
     hb = DecodeBench(torch, np, eb, synth, args.workload, args.seed, split=args.split,

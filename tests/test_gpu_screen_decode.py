@@ -101,10 +101,10 @@ def test_ragged_edges(kv, D, block):
     note(f"  density {st['density']:.3f} out_rel {st['out_rel']:.2e}")
 
 
-@pytest.mark.parametrize("cap", [4096, 4500])
+@pytest.mark.parametrize("cap", [4096, 8196])
 def test_long_block_lists(cap):
-    # Block 4 and up to 4500 positions: 1024 and 1125 blocks per stream (128
-    # and 141 chunks of 8), ragged lengths up to the capacity, an empty stream.
+    # Block 4: 1024 and 2049 blocks per stream (128 and 257 chunks of 8),
+    # ragged lengths up to the capacity and an empty stream.
     lens = [0, 5, 2049, cap - 3, cap]
     w = synth.make("tiny", seed=41, T=lens, B=len(lens), H=3, cap=cap, pad="nan", block=4)
     to_gpu(w)
